@@ -1,0 +1,184 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention (KDA) library.
+ *
+ * The library evaluates the KDA gated delta rule, per head, on a 128 x 128
+ * FP32 state S (row = key channel, column = value channel):
+ *
+ *   S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
+ *   o_t = scale * S_t^T q_t
+ *
+ * through two calls:
+ *
+ *   kda_prefill  -- chunked prefill over packed variable-length sequences
+ *                   ("FlashInfer PR #4262: CAKE KDA Prefill Highlights",
+ *                   sections 1-3: 32-token chunks, fixed exponent anchor,
+ *                   the fused per-chunk pipeline; and flashinfer PR #4571,
+ *                   "optimize small-BH recurrent-KDA prefill": packed
+ *                   layout with sequence offsets, caller-owned outputs,
+ *                   caller's stream).
+ *   kda_decode   -- the T=1 step over a slot-indexed state pool, updated in
+ *                   place (flashinfer PR #5551, "Kimi K3 TP12 H=8 fused KDA
+ *                   decode": positive unique slots, FP32 and BF16 state,
+ *                   64-bit slot offsets).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers on the current HIP device, owned
+ *   by the caller; the library allocates nothing per call and keeps no
+ *   pointer after returning.
+ * - bf16 means IEEE bfloat16 stored as uint16; fp32 is IEEE binary32.
+ * - Work is enqueued on `stream` (NULL = the legacy default stream) and runs
+ *   asynchronously.  No call synchronises the device or reads device memory
+ *   on the host, so calls may be captured into a hipGraph.
+ * - Return value: KDA_OK (0), or a negative kda_status.  Arguments are
+ *   validated on the host before anything is enqueued; on error nothing is
+ *   enqueued and kda_last_error() describes the problem.  Faults inside a
+ *   kernel surface, as usual in HIP, at the caller's next synchronisation.
+ * - Device-side preconditions that are NOT checked (they would need a
+ *   device read): cu_seqlens non-decreasing with cu_seqlens[0] = 0 and
+ *   cu_seqlens[N] = total_tokens; lower_bound <= g <= 0 for prefill;
+ *   beta in [0, 1]; decode slot indices unique among the non-negative ones.
+ *   Kernels clamp every index they read so that a violated precondition
+ *   gives wrong numbers, never an out-of-bounds access.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+#define KDA_HEAD_DIM 128
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_INVALID_ARGUMENT = -1, /* null pointer, bad size, misalignment   */
+  KDA_ERR_UNSUPPORTED = -2,      /* valid but not implemented (e.g. dk!=128) */
+  KDA_ERR_WORKSPACE = -3,        /* workspace missing or too small          */
+  KDA_ERR_HIP = -4               /* a HIP runtime call failed               */
+} kda_status;
+
+typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
+
+/* Prefill kernels ("routes").  AUTO lets kda_prefill_plan choose. */
+typedef enum {
+  KDA_ROUTE_AUTO = -1,
+  KDA_ROUTE_SERIAL = 0, /* token-serial FP32 recurrence, no MFMA            */
+  KDA_ROUTE_CHUNK = 1   /* 32-token chunks on bf16/fp16 MFMA (see below)    */
+} kda_prefill_route;
+
+/* Exponent handling of the chunk route's pairwise (Mqk, Akk) products,
+ * "FlashInfer PR #4262: CAKE KDA Prefill Highlights", section 1. */
+typedef enum {
+  KDA_ANCHOR_FIXED = 0,  /* one anchor C = 16 * lower_bound * log2(e) per chunk:
+                            operand exponents stay within 16|lb|log2e <= 126,
+                            i.e. usable for lower_bound >= -5.45            */
+  KDA_ANCHOR_SPLIT16 = 1 /* per 16-token half anchors ("ordinary SafeGate"
+                            16-token blocks), for wider bounds             */
+} kda_anchor_mode;
+
+/* What kda_prefill will launch for a problem (a pure host function of the
+ * sizes, the bound and the device's compute-unit count). */
+typedef struct {
+  int32_t route;       /* kda_prefill_route actually used                  */
+  int32_t anchor_mode; /* kda_anchor_mode (chunk route only)               */
+  int32_t dv_split;    /* value-column slices per (sequence, head)         */
+  int32_t block_threads;
+  int64_t grid_blocks;
+  float anchor_log2;   /* C = 16 * lower_bound * log2(e), as used on device */
+} kda_prefill_plan_t;
+
+/* ------------------------------------------------------------- prefill --
+ * Packed varlen prefill.
+ *
+ *  q, k, g     bf16 [total_tokens, num_heads, 128], row-major, 16-byte aligned.
+ *              g is the per-channel natural-log decay, lower_bound <= g <= 0.
+ *              q and k are used as given (normalise them beforehand).
+ *  v           bf16 [total_tokens, num_heads, 128], 16-byte aligned.
+ *  beta        bf16 [total_tokens, num_heads], post-sigmoid write strength.
+ *  cu_seqlens  int32 [num_seqs + 1] sequence offsets into the token axis.
+ *  num_seqs    N >= 0 (0 = nothing to do).
+ *  total_tokens  T_tot = cu_seqlens[N] (host copy, used for validation and
+ *              to clamp device reads), 0 <= T_tot < 2^31.
+ *  num_heads   H >= 1.
+ *  head_dim_k, head_dim_v   must both be 128 (else KDA_ERR_UNSUPPORTED).
+ *  scale       output scale (finite), e.g. 1/sqrt(128).
+ *  lower_bound finite, < 0: the bound g >= lower_bound that fixes the anchor.
+ *  initial_state  fp32 [N, H, 128, 128] (dv contiguous) or NULL for zeros.
+ *  final_state    fp32 [N, H, 128, 128] or NULL (not stored).  May equal
+ *              initial_state (each sequence-head reads its slice before it
+ *              writes it); must not partially overlap it.
+ *  out         bf16 [total_tokens, num_heads, 128]; must not alias inputs.
+ *  workspace, workspace_bytes   device scratch of at least
+ *              kda_prefill_workspace_size(...) bytes (currently 0; NULL ok).
+ *  stream      HIP stream the kernels are enqueued on.
+ * Sequences of length 0 copy initial_state to final_state. */
+int kda_prefill(const void* q, const void* k, const void* v, const void* g,
+                const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                int32_t head_dim_v, float scale, float lower_bound,
+                const float* initial_state, float* final_state, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace kda_prefill needs for these sizes (0 today). */
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
+                                  int32_t num_heads);
+
+/* Fill *plan with what kda_prefill would launch.  `num_cus` is the device's
+ * compute-unit count (<= 0: query the current device).  `route` forces a
+ * route (KDA_ROUTE_AUTO to let the planner choose).  Pure host function:
+ * it enqueues nothing and touches no device memory. */
+int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                     float lower_bound, int32_t num_cus, int32_t route,
+                     kda_prefill_plan_t* plan);
+
+/* Process-wide route override used by kda_prefill (KDA_ROUTE_AUTO restores
+ * automatic selection).  Returns KDA_OK, or KDA_ERR_INVALID_ARGUMENT for an
+ * unknown route (the override is then unchanged).  Intended for tests and
+ * benchmarks that compare routes. */
+int kda_set_prefill_route(int32_t route);
+
+/* -------------------------------------------------------------- decode --
+ * One T=1 step for each row against a slot-indexed state pool.
+ *
+ *  q, k, g, v  bf16 [rows, num_heads, 128], 16-byte aligned; g = per-channel
+ *              natural-log decay (any value <= 0; no bound is needed at T=1).
+ *  beta        bf16 [rows, num_heads], post-sigmoid.
+ *  state_pool  [num_slots, num_heads, 128, 128] (dv contiguous) of fp32
+ *              (KDA_STATE_F32) or bf16 (KDA_STATE_BF16), 16-byte aligned,
+ *              read and written in place.  BF16 states are widened to fp32,
+ *              updated in fp32 and rounded back to nearest-even.
+ *  num_slots   >= 1; offsets are computed in 64 bits (pools above 2^31
+ *              elements are fine).
+ *  slot_indices  int32 [rows]: pool slot of each row.  A negative entry
+ *              skips the row (its out is zero-filled and no slot is touched);
+ *              entries >= num_slots are treated the same way.  Non-negative
+ *              entries must be unique.
+ *  rows        >= 0 (0 = nothing to do).
+ *  num_heads   >= 1;  head_dim_k = head_dim_v = 128.
+ *  scale       output scale (finite).
+ *  out         bf16 [rows, num_heads, 128].
+ *  stream      HIP stream. */
+int kda_decode(const void* q, const void* k, const void* v, const void* g,
+               const void* beta, void* state_pool, int32_t state_dtype,
+               int64_t num_slots, const int32_t* slot_indices, int32_t rows,
+               int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+               float scale, void* out, hipStream_t stream);
+
+/* ---------------------------------------------------------------- misc -- */
+/* Text describing the last non-OK return on the calling thread ("" if none). */
+const char* kda_last_error(void);
+/* KDA_ABI_VERSION of the built library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,199 @@
+"""ctypes binding of ``libkda.so`` (include/kda.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, output
+buffers are allocated with PyTorch when the caller passes none, and the raw
+device pointers plus the current HIP stream go to the C ABI.  Every step of
+the computation runs in the library's HIP kernels; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from .build import library_path
+
+KDA_OK = 0
+KDA_ERR_INVALID_ARGUMENT = -1
+KDA_ERR_UNSUPPORTED = -2
+KDA_ERR_WORKSPACE = -3
+KDA_ERR_HIP = -4
+
+ROUTE_AUTO = -1
+ROUTE_SERIAL = 0
+ROUTE_CHUNK = 1
+
+ANCHOR_FIXED = 0
+ANCHOR_SPLIT16 = 1
+
+STATE_F32 = 0
+STATE_BF16 = 1
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"[{code}] {msg}")
+        self.code = code
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("route", ctypes.c_int32), ("anchor_mode", ctypes.c_int32),
+                ("dv_split", ctypes.c_int32), ("block_threads", ctypes.c_int32),
+                ("grid_blocks", ctypes.c_int64), ("anchor_log2", ctypes.c_float)]
+
+
+@dataclass
+class Plan:
+    route: int
+    anchor_mode: int
+    dv_split: int
+    block_threads: int
+    grid_blocks: int
+    anchor_log2: float
+
+
+def load():
+    """Load libkda.so from the package directory (raises if it is not built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = library_path()
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built: run `python -m kimi_delta_attention_prefill_amd.build`"
+                          " (or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    vp, i32, i64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_float,
+                             ctypes.c_size_t)
+    lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32, vp, vp,
+                                vp, vp, sz, vp]
+    lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32]
+    lib.kda_prefill_workspace_size.restype = sz
+    lib.kda_prefill_plan.argtypes = [i32, i64, i32, f32, i32, i32, ctypes.POINTER(_Plan)]
+    lib.kda_prefill_plan.restype = ctypes.c_int
+    lib.kda_set_prefill_route.argtypes = [i32]
+    lib.kda_set_prefill_route.restype = ctypes.c_int
+    lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
+    lib.kda_decode.restype = ctypes.c_int
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_abi_version.argtypes = []
+    lib.kda_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def last_error() -> str:
+    return load().kda_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != KDA_OK:
+        raise KdaError(rc, last_error())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream))
+
+
+def _need(t, name, dtype, shape, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+
+
+def workspace_size(num_seqs: int, total_tokens: int, num_heads: int) -> int:
+    return int(load().kda_prefill_workspace_size(num_seqs, total_tokens, num_heads))
+
+
+def plan(num_seqs: int, total_tokens: int, num_heads: int, lower_bound: float,
+         num_cus: int = 0, route: int = ROUTE_AUTO) -> Plan:
+    """What kda_prefill would launch (pure host function)."""
+    p = _Plan()
+    _check(load().kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, num_cus, route,
+                                   ctypes.byref(p)))
+    return Plan(p.route, p.anchor_mode, p.dv_split, p.block_threads, p.grid_blocks, p.anchor_log2)
+
+
+def set_prefill_route(route: int) -> None:
+    """Force a prefill route process-wide (ROUTE_AUTO restores automatic selection)."""
+    _check(load().kda_set_prefill_route(route))
+
+
+def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=None,
+            final_state=None, out=None, workspace=None, stream=None):
+    """Packed varlen KDA prefill on the GPU.
+
+    q, k, v, g: bf16 [T, H, 128]; beta: bf16 [T, H]; cu_seqlens: int32 [N+1]
+    (device); initial_state: fp32 [N, H, 128, 128] or None (zeros).
+    ``final_state``: an fp32 [N, H, 128, 128] tensor to write into, True to
+    allocate one, or None/False to skip it.  Returns (out, final_state).
+    """
+    dev = q.device
+    T, H, D = q.shape
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _need(t, name, torch.bfloat16, (T, H, D), dev)
+    _need(beta, "beta", torch.bfloat16, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, D, D), dev)
+    if final_state is True:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, D, D), dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, D), dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                              N, T, H, D, D, float(scale), float(lower_bound), _ptr(initial_state),
+                              _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
+                              _stream(stream)))
+    return out, final_state
+
+
+def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, stream=None):
+    """One T=1 step per row against ``state_pool`` (fp32 or bf16), in place.
+
+    q, k, v, g: bf16 [rows, H, 128]; beta: bf16 [rows, H];
+    state_pool: [num_slots, H, 128, 128]; slot_indices: int32 [rows].
+    Returns out (bf16 [rows, H, 128]).
+    """
+    dev = q.device
+    R, H, D = q.shape
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _need(t, name, torch.bfloat16, (R, H, D), dev)
+    _need(beta, "beta", torch.bfloat16, (R, H), dev)
+    _need(slot_indices, "slot_indices", torch.int32, (R,), dev)
+    if state_pool.dtype == torch.float32:
+        sd = STATE_F32
+    elif state_pool.dtype == torch.bfloat16:
+        sd = STATE_BF16
+    else:
+        raise TypeError("state_pool must be float32 or bfloat16")
+    _need(state_pool, "state_pool", state_pool.dtype, (state_pool.shape[0], H, D, D), dev)
+    if out is None:
+        out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (R, H, D), dev)
+    _check(load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), sd,
+                             state_pool.shape[0], _ptr(slot_indices), R, H, D, D, float(scale),
+                             _ptr(out), _stream(stream)))
+    return out

@@ -1,0 +1,245 @@
+// C ABI of the KDA library: host-side validation, route planning and launch.
+// See include/kda.h for the contract of every entry point.
+#include "kda.h"
+
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+std::atomic<int> g_forced_route{KDA_ROUTE_AUTO};
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return KDA_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Compute-unit count of the current device, cached per device id.
+int current_device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(cus, std::memory_order_relaxed);
+  return cus;
+}
+
+// Largest |exponent| of an anchored chunk-32 operand factor 2^{G-C} or
+// 2^{C-G} when lower_bound <= g <= 0: 16 |lb| log2(e) (CAKE prefill note,
+// section 1).  bf16/fp32 normals need it <= 126.
+bool fixed_anchor_fits(float lower_bound) {
+  return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kda_last_error(void) { return g_last_error; }
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int kda_set_prefill_route(int32_t route) {
+  if (route != KDA_ROUTE_AUTO && route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_set_prefill_route: unknown route %d", route);
+  g_forced_route.store(route);
+  return ok();
+}
+
+size_t kda_prefill_workspace_size(int32_t, int64_t, int32_t) { return 0; }
+
+int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                     float lower_bound, int32_t num_cus, int32_t route,
+                     kda_prefill_plan_t* plan) {
+  if (!plan) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: plan is NULL");
+  if (num_seqs < 0 || total_tokens < 0 || num_heads < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: bad sizes (N=%d, T=%lld, H=%d)",
+                num_seqs, (long long)total_tokens, num_heads);
+  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "kda_prefill_plan: lower_bound must be finite and < 0 (got %g)",
+                (double)lower_bound);
+  if (num_cus <= 0) num_cus = current_device_cus();
+  if (num_cus <= 0) num_cus = 256;
+  if (route == KDA_ROUTE_AUTO) route = KDA_ROUTE_SERIAL;
+  if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
+  std::memset(plan, 0, sizeof(*plan));
+  plan->route = route;
+  plan->anchor_mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
+  plan->anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
+  const int64_t units = (int64_t)num_seqs * num_heads;
+  if (route == KDA_ROUTE_SERIAL) {
+    // 16 value columns per wave; fewer waves per block (more blocks) when
+    // there are few (sequence, head) units to spread over the compute units.
+    int waves = 4;
+    if (2 * units < (int64_t)num_cus) waves = 4 * units < (int64_t)num_cus ? 1 : 2;
+    plan->dv_split = 8 / waves;
+    plan->block_threads = 64 * waves;
+    plan->grid_blocks = units * plan->dv_split;
+  } else {
+    plan->dv_split = 1;
+    plan->block_threads = 256;
+    plan->grid_blocks = units;
+  }
+  return ok();
+}
+
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
+                float lower_bound, const float* initial_state, float* final_state, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (head_dim_k != KDA_HEAD_DIM || head_dim_v != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: head dims must be 128 (got dk=%d, dv=%d)",
+                head_dim_k, head_dim_v);
+  if (num_seqs < 0 || num_heads < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: num_seqs=%d num_heads=%d", num_seqs,
+                num_heads);
+  if (total_tokens < 0 || total_tokens > INT32_MAX)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: total_tokens=%lld out of [0, 2^31)",
+                (long long)total_tokens);
+  if (!std::isfinite(scale))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: scale is not finite");
+  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "kda_prefill: lower_bound must be finite and < 0 (got %g)", (double)lower_bound);
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: cu_seqlens is NULL");
+  if (total_tokens > 0) {
+    const void* need[] = {q, k, v, g, beta, out};
+    const char* names[] = {"q", "k", "v", "g", "beta", "out"};
+    for (int i = 0; i < 6; ++i)
+      if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: %s is NULL", names[i]);
+    const void* al16[] = {q, k, v, g, out};
+    const char* n16[] = {"q", "k", "v", "g", "out"};
+    for (int i = 0; i < 5; ++i)
+      if (!aligned(al16[i], 16))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: %s is not 16-byte aligned", n16[i]);
+    if (!aligned(beta, 2))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: beta is not 2-byte aligned");
+  }
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: states must be 16-byte aligned");
+  if (initial_state && final_state && initial_state != final_state) {
+    const size_t bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    const char* a0 = reinterpret_cast<const char*>(initial_state);
+    const char* b0 = reinterpret_cast<const char*>(final_state);
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "kda_prefill: final_state partially overlaps initial_state");
+  }
+  const size_t ws_need = kda_prefill_workspace_size(num_seqs, total_tokens, num_heads);
+  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
+    return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace of %zu bytes needed", ws_need);
+
+  kda_prefill_plan_t plan;
+  int rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0,
+                            g_forced_route.load(), &plan);
+  if (rc != KDA_OK) return rc;
+
+  kda::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = static_cast<const uint16_t*>(g);
+  a.beta = static_cast<const uint16_t*>(beta);
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = (int32_t)total_tokens;
+  a.num_heads = num_heads;
+  a.scale = scale;
+  a.anchor_log2 = plan.anchor_log2;
+  a.half_anchor_log2 = (float)(8.0 * (double)lower_bound * 1.4426950408889634);
+  a.s0 = initial_state;
+  a.s1 = final_state;
+  a.out = static_cast<uint16_t*>(out);
+
+  hipError_t e;
+  if (plan.route == KDA_ROUTE_SERIAL)
+    e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
+  else
+    e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
+  if (e == hipErrorNotSupported)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: route %d is not available", plan.route);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_prefill: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               void* state_pool, int32_t state_dtype, int64_t num_slots,
+               const int32_t* slot_indices, int32_t rows, int32_t num_heads, int32_t head_dim_k,
+               int32_t head_dim_v, float scale, void* out, hipStream_t stream) {
+  if (head_dim_k != KDA_HEAD_DIM || head_dim_v != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "kda_decode: head dims must be 128 (got dk=%d, dv=%d)",
+                head_dim_k, head_dim_v);
+  if (state_dtype != KDA_STATE_F32 && state_dtype != KDA_STATE_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: unknown state dtype %d", state_dtype);
+  if (rows < 0 || num_heads < 1 || num_slots < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: rows=%d num_heads=%d num_slots=%lld",
+                rows, num_heads, (long long)num_slots);
+  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: scale not finite");
+  if ((int64_t)rows * num_heads * 4 > (int64_t)UINT32_MAX)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: rows * num_heads too large");
+  if (rows == 0) return ok();
+  const void* need[] = {q, k, v, g, beta, state_pool, slot_indices, out};
+  const char* names[] = {"q", "k", "v", "g", "beta", "state_pool", "slot_indices", "out"};
+  for (int i = 0; i < 8; ++i)
+    if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: %s is NULL", names[i]);
+  const void* al16[] = {q, k, v, g, out, state_pool};
+  const char* n16[] = {"q", "k", "v", "g", "out", "state_pool"};
+  for (int i = 0; i < 6; ++i)
+    if (!aligned(al16[i], 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: %s is not 16-byte aligned", n16[i]);
+  if (!aligned(beta, 2) || !aligned(slot_indices, 4))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: beta/slot_indices misaligned");
+
+  kda::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = static_cast<const uint16_t*>(g);
+  a.beta = static_cast<const uint16_t*>(beta);
+  a.pool = state_pool;
+  a.slots = slot_indices;
+  a.num_slots = num_slots;
+  a.rows = rows;
+  a.num_heads = num_heads;
+  a.scale = scale;
+  a.out = static_cast<uint16_t*>(out);
+
+  // Narrow value-column slices when there are too few items to fill the chip.
+  int cus = current_device_cus();
+  if (cus <= 0) cus = 256;
+  const int64_t items = (int64_t)rows * num_heads;
+  const int cols = items >= 2LL * cus ? 128 : (items >= cus ? 64 : 32);
+  hipError_t e = kda::launch_decode(a, state_dtype == KDA_STATE_BF16, cols, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_decode: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,31 @@
+// Small device helpers shared by the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// bf16 (stored as uint16) -> fp32: exact, a 16-bit left shift.
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+// Low / high bf16 of a packed 32-bit word -> fp32.
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16, round to nearest even (lowers to v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = static_cast<__bf16>(x);
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// 2^x on the hardware exponential unit (v_exp_f32).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Clamp a device-read sequence offset into [0, total].
+__device__ __forceinline__ int clamp_offset(int x, int total) {
+  return x < 0 ? 0 : (x > total ? total : x);
+}
+
+}  // namespace kda

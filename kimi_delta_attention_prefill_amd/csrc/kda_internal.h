@@ -1,0 +1,54 @@
+// Internal launcher interface between the C ABI (kda_api.cpp) and the HIP
+// kernels.  Not installed; the public interface is include/kda.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+constexpr int kHeadDim = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct PrefillArgs {
+  const uint16_t* q;      // bf16 [T, H, 128]
+  const uint16_t* k;      // bf16 [T, H, 128]
+  const uint16_t* v;      // bf16 [T, H, 128]
+  const uint16_t* g;      // bf16 [T, H, 128], natural-log decay
+  const uint16_t* beta;   // bf16 [T, H]
+  const int32_t* cu_seqlens;  // int32 [N + 1]
+  int32_t num_seqs;
+  int32_t total_tokens;
+  int32_t num_heads;
+  float scale;
+  float anchor_log2;      // C = 16 * lower_bound * log2(e)  (chunk route)
+  float half_anchor_log2; // 8 * lower_bound * log2(e)     (split-16 mode)
+  const float* s0;        // fp32 [N, H, 128, 128] or null
+  float* s1;              // fp32 [N, H, 128, 128] or null
+  uint16_t* out;          // bf16 [T, H, 128]
+};
+
+struct DecodeArgs {
+  const uint16_t* q;
+  const uint16_t* k;
+  const uint16_t* v;
+  const uint16_t* g;
+  const uint16_t* beta;
+  void* pool;             // fp32 or bf16 [num_slots, H, 128, 128]
+  const int32_t* slots;   // int32 [rows]
+  int64_t num_slots;
+  int32_t rows;
+  int32_t num_heads;
+  float scale;
+  uint16_t* out;          // bf16 [rows, H, 128]
+};
+
+// Token-serial FP32 prefill; `waves` value-column tiles of 16 per block.
+hipError_t launch_prefill_serial(const PrefillArgs& a, int waves, hipStream_t s);
+// Chunk-32 MFMA prefill.
+hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_split,
+                                hipStream_t s);
+// Decode step; `cols` = value columns per block (32, 64 or 128).
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
+
+}  // namespace kda

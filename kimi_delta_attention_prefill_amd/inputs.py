@@ -22,7 +22,8 @@ synthetic, there is no dataset):
   pool's slots (unique, scattered).
 
 Draw order per case: lengths (varlen only), q, k, v, gate logits, beta
-logits, state, slots.
+logits, then for prefill the initial state, for decode the slots and then
+the pool (last, so a caller can supply its own pool and keep the same rows).
 """
 from __future__ import annotations
 
@@ -35,7 +36,7 @@ HEAD_DIM = 128
 SCALE = 1.0 / (HEAD_DIM ** 0.5)
 BASE_SEED = 20260
 
-__all__ = ["PrefillCase", "DecodeCase", "make_prefill_case", "make_decode_case",
+__all__ = ["PrefillCase", "DecodeCase", "make_prefill_case", "make_decode_case", "make_decode_pool",
            "prefill_config", "decode_config", "PREFILL_CONFIGS", "SCALE", "HEAD_DIM",
            "BASE_SEED"]
 
@@ -75,7 +76,7 @@ class DecodeCase:
     v: torch.Tensor
     g: torch.Tensor             # bf16 [rows, H, 128]
     beta: torch.Tensor          # bf16 [rows, H]
-    pool: torch.Tensor          # fp32 or bf16 [num_slots, H, 128, 128]
+    pool: Optional[torch.Tensor]  # fp32 or bf16 [num_slots, H, 128, 128]
     slots: torch.Tensor         # int32 [rows]
     scale: float = SCALE
     seed: int = 0
@@ -147,10 +148,12 @@ def prefill_config(i: int, seed: Optional[int] = None) -> PrefillCase:
 
 def make_decode_case(rows, num_heads=8, num_slots=4096, state_dtype=torch.float32,
                      init_std=0.02, seed=BASE_SEED + 4, name="", dk=HEAD_DIM,
-                     dv=HEAD_DIM) -> DecodeCase:
+                     dv=HEAD_DIM, with_pool=True) -> DecodeCase:
     """T=1 decode inputs: scattered unique slots into a random state pool.
 
-    The bf16 pool holds the bf16 rounding of the same fp32 draw.
+    The bf16 pool holds the bf16 rounding of the same fp32 draw.  With
+    ``with_pool=False`` the pool is not drawn (``pool`` is None) and every
+    other tensor is unchanged.
     """
     gen = torch.Generator().manual_seed(int(seed))
     R, H = int(rows), int(num_heads)
@@ -161,13 +164,24 @@ def make_decode_case(rows, num_heads=8, num_slots=4096, state_dtype=torch.float3
     v = torch.randn(R, H, dv, generator=gen).to(torch.bfloat16)
     g = (-torch.nn.functional.softplus(torch.randn(R, H, dk, generator=gen))).to(torch.bfloat16)
     beta = torch.sigmoid(torch.randn(R, H, generator=gen)).to(torch.bfloat16)
-    pool = float(init_std) * torch.randn(int(num_slots), H, dk, dv, generator=gen)
-    if state_dtype == torch.bfloat16:
-        pool = pool.to(torch.bfloat16)
-    elif state_dtype != torch.float32:
-        raise ValueError("state dtype must be float32 or bfloat16")
     slots = torch.randperm(int(num_slots), generator=gen)[:R].to(torch.int32)
+    pool = None
+    if with_pool:
+        pool = make_decode_pool(num_slots, H, state_dtype, init_std, gen, dk, dv)
     return DecodeCase(q, k, v, g, beta, pool, slots, SCALE, int(seed), name)
+
+
+def make_decode_pool(num_slots, num_heads, state_dtype=torch.float32, init_std=0.02,
+                     gen=None, dk=HEAD_DIM, dv=HEAD_DIM) -> torch.Tensor:
+    """State pool [num_slots, H, dk, dv]: init_std * N(0, 1) in fp32 (bf16: rounded)."""
+    if gen is None or isinstance(gen, int):
+        gen = torch.Generator().manual_seed(BASE_SEED + 4 if gen is None else int(gen))
+    pool = float(init_std) * torch.randn(int(num_slots), int(num_heads), dk, dv, generator=gen)
+    if state_dtype == torch.bfloat16:
+        return pool.to(torch.bfloat16)
+    if state_dtype != torch.float32:
+        raise ValueError("state dtype must be float32 or bfloat16")
+    return pool
 
 
 def decode_config(rows: int, state_dtype=torch.float32, seed: Optional[int] = None,

@@ -1,0 +1,135 @@
+"""CPU-only checks of the C ABI: the library loads, exports what include/kda.h
+declares, plans routes as a pure function, and rejects bad arguments on the
+host before anything is enqueued (no compute call needs a GPU here)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import kimi_delta_attention_prefill_amd as kda
+from kimi_delta_attention_prefill_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = kda.load()
+    names = _declared_functions()
+    assert {"kda_prefill", "kda_decode", "kda_last_error"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), f"libkda.so does not export {name}"
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define KDA_ABI_VERSION (\d+)", text).group(1))
+    assert kda.load().kda_abi_version() == ver
+
+
+def test_plan_anchor_mode_boundary():
+    # fixed anchor iff 16 |lb| log2(e) <= 126  <=>  |lb| <= 5.4592...
+    assert kda.plan(1, 64, 2, -5.0, 256).anchor_mode == kda.ANCHOR_FIXED
+    assert kda.plan(1, 64, 2, -5.45, 256).anchor_mode == kda.ANCHOR_FIXED
+    assert kda.plan(1, 64, 2, -5.47, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    assert kda.plan(4, 32768, 64, -8.0, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    p = kda.plan(1, 64, 2, -5.0, 256)
+    assert abs(p.anchor_log2 - 16 * -5.0 * 1.4426950408889634) < 1e-4
+
+
+@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK])
+def test_plan_grid_covers_every_unit(route):
+    for N, H, cus in ((1, 8, 256), (16, 32, 256), (4, 64, 256), (1, 1, 256), (3, 5, 80)):
+        p = kda.plan(N, 100 * N, H, -5.0, cus, route)
+        assert p.route == route
+        assert p.dv_split >= 1 and 128 % p.dv_split == 0
+        assert p.grid_blocks == N * H * p.dv_split
+        assert p.block_threads % 64 == 0 and 64 <= p.block_threads <= 1024
+
+
+def test_plan_rejects_bad_inputs():
+    for args in ((-1, 0, 1, -5.0), (1, -1, 1, -5.0), (1, 0, 0, -5.0), (1, 0, 1, 0.0),
+                 (1, 0, 1, float("nan")), (1, 0, 1, float("-inf")), (1, 0, 1, 1.0)):
+        with pytest.raises(kda.KdaError) as e:
+            kda.plan(*args, num_cus=256)
+        assert e.value.code == _lib.KDA_ERR_INVALID_ARGUMENT
+        assert kda.last_error()
+    with pytest.raises(kda.KdaError):
+        kda.plan(1, 0, 1, -5.0, 256, route=7)
+
+
+def test_set_route_validates():
+    with pytest.raises(kda.KdaError):
+        kda.set_prefill_route(5)
+    kda.set_prefill_route(kda.ROUTE_AUTO)
+
+
+def _prefill_raw(**over):
+    a = dict(q=16, k=16, v=16, g=16, beta=16, cu=16, N=1, T=4, H=1, dk=128, dv=128, scale=1.0,
+             lb=-5.0, s0=None, s1=None, out=16, ws=None, ws_bytes=0)
+    a.update(over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.load().kda_prefill(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                  P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["scale"],
+                                  a["lb"], P(a["s0"]), P(a["s1"]), P(a["out"]), P(a["ws"]),
+                                  a["ws_bytes"], None)
+
+
+def test_prefill_host_validation():
+    E, U = _lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED
+    # Every case below is rejected before any device work (pointers are never dereferenced).
+    assert _prefill_raw(dk=64) == U
+    assert _prefill_raw(dv=256) == U
+    assert _prefill_raw(H=0) == E
+    assert _prefill_raw(N=-1) == E
+    assert _prefill_raw(T=-1) == E
+    assert _prefill_raw(T=2 ** 31) == E
+    assert _prefill_raw(lb=0.0) == E
+    assert _prefill_raw(lb=float("nan")) == E
+    assert _prefill_raw(scale=float("inf")) == E
+    assert _prefill_raw(cu=None) == E
+    assert _prefill_raw(q=None) == E
+    assert _prefill_raw(out=None) == E
+    assert _prefill_raw(q=0x1008) == E          # misaligned bf16 tensor
+    assert _prefill_raw(beta=0x1001) == E       # misaligned beta
+    assert _prefill_raw(s0=0x1004) == E         # misaligned state
+    assert _prefill_raw(s0=0x10000, s1=0x10000 + 4096) == E   # partial overlap
+    assert "overlap" in kda.last_error()
+    # N == 0 is a valid no-op that touches nothing.
+    assert _prefill_raw(N=0, q=None, k=None, v=None, g=None, beta=None, cu=None, out=None) == 0
+
+
+def _decode_raw(**over):
+    a = dict(q=16, k=16, v=16, g=16, beta=16, pool=16, dtype=0, slots_n=4, idx=16, rows=2, H=8,
+             dk=128, dv=128, scale=1.0, out=16)
+    a.update(over)
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    return kda.load().kda_decode(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                 P(a["pool"]), a["dtype"], a["slots_n"], P(a["idx"]), a["rows"],
+                                 a["H"], a["dk"], a["dv"], a["scale"], P(a["out"]), None)
+
+
+def test_decode_host_validation():
+    E, U = _lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED
+    assert _decode_raw(dk=64) == U
+    assert _decode_raw(dtype=3) == E
+    assert _decode_raw(rows=-1) == E
+    assert _decode_raw(H=0) == E
+    assert _decode_raw(slots_n=0) == E
+    assert _decode_raw(scale=float("nan")) == E
+    assert _decode_raw(pool=None) == E
+    assert _decode_raw(idx=None) == E
+    assert _decode_raw(pool=0x1008) == E
+    assert _decode_raw(idx=0x1002) == E
+    assert _decode_raw(rows=0, q=None, pool=None, idx=None, out=None) == 0
+
+
+def test_workspace_size_is_zero():
+    assert kda.workspace_size(16, 40000, 32) == 0

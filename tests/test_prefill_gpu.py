@@ -1,0 +1,217 @@
+"""GPU parity of kda_prefill against the FP64 oracle (through the C ABI).
+
+Small cases are compared element by element in full; the full-size
+workloads run exactly as the benchmark launches them and are compared on
+sampled (sequence, head) units, which the oracle computes independently.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_prefill_amd as kda
+import oracle
+from kimi_delta_attention_prefill_amd.inputs import make_prefill_case, prefill_config
+from _checks import check_out, check_state
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = [kda.ROUTE_SERIAL]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    kda.load()  # the HIP library must be present on a GPU host
+    return torch.device("cuda:0")
+
+
+def run_gpu(case, route, dev, with_state=True, final=True, out=None, final_state=None):
+    to = lambda t: None if t is None else t.to(dev)
+    _say(f"[gpu] prefill {case.name or 'case'} route={route} N={case.num_seqs} "
+         f"T={case.total_tokens} H={case.num_heads} lb={case.lower_bound}")
+    kda.set_prefill_route(route)
+    try:
+        o, f = kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                           to(case.cu_seqlens), scale=case.scale, lower_bound=case.lower_bound,
+                           initial_state=to(case.initial_state) if with_state else None,
+                           final_state=final_state if final_state is not None else final,
+                           out=out)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    return o, f
+
+
+def sub_inputs(case, seqs=None, heads=None):
+    """Inputs of the chosen sequences and heads, as the oracle takes them."""
+    cu = case.cu_seqlens.long().tolist()
+    seqs = list(range(case.num_seqs)) if seqs is None else list(seqs)
+    heads = list(range(case.num_heads)) if heads is None else list(heads)
+    idx = np.concatenate([np.arange(cu[n], cu[n + 1]) for n in seqs]).astype(np.int64)
+    lens = [cu[n + 1] - cu[n] for n in seqs]
+    sub_cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    pick = lambda t: t[idx][:, heads]
+    s0 = None
+    if case.initial_state is not None:
+        s0 = case.initial_state[seqs][:, heads]
+    return dict(q=pick(case.q), k=pick(case.k), v=pick(case.v), g=pick(case.g),
+                beta=case.beta[idx][:, heads], cu=sub_cu, s0=s0, idx=idx, seqs=seqs, heads=heads)
+
+
+def run_oracle(case, seqs=None, heads=None):
+    s = sub_inputs(case, seqs, heads)
+    out, fin = oracle.prefill(s["q"], s["k"], s["v"], s["g"], s["beta"], s["cu"], case.scale,
+                              s["s0"])
+    return out, fin, s
+
+
+def compare(case, o_gpu, f_gpu, seqs=None, heads=None):
+    ref_o, ref_f, s = run_oracle(case, seqs, heads)
+    g_o = o_gpu.cpu()[torch.as_tensor(s["idx"])][:, s["heads"]]
+    r1 = check_out(g_o, ref_o)
+    r2 = None
+    if f_gpu is not None:
+        g_f = f_gpu.cpu()[s["seqs"]][:, s["heads"]]
+        r2 = check_state(g_f, ref_f)
+    _say(f"   out {r1}  state {r2}")
+    return r1, r2
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_config0_full(dev, route):
+    case = prefill_config(0)
+    o, f = run_gpu(case, route, dev)
+    compare(case, o, f)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("lb", [-5.0, -8.0, -1.0])
+def test_ragged_lengths(dev, route, lb):
+    """Lengths 0, 1 and around chunk multiples, ring wraps (>= 3 chunks), a ragged tail."""
+    case = make_prefill_case([1, 31, 32, 33, 95, 0, 64, 7, 200], 3, lb, 0.02, seed=99,
+                             name=f"ragged_lb{lb}")
+    o, f = run_gpu(case, route, dev)
+    compare(case, o, f)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_config1_full(dev, route):
+    case = prefill_config(1)
+    o, f = run_gpu(case, route, dev)
+    compare(case, o, f)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_config2_sampled_heads(dev, route):
+    case = prefill_config(2)
+    o, f = run_gpu(case, route, dev)
+    compare(case, o, f, heads=[0, 13, 31])
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_config3_sampled_units(dev, route):
+    case = prefill_config(3)
+    o, f = run_gpu(case, route, dev)
+    compare(case, o, f, seqs=[0, 3], heads=[0, 37, 63])
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_write_guards_and_state_alias(dev, route):
+    """Nothing outside out/final_state is written; final_state may alias initial_state."""
+    case = make_prefill_case([70, 33], 2, -5.0, 0.02, seed=5, name="guards")
+    T, H = case.total_tokens, case.num_heads
+    canary = -12345.0
+    big = torch.full((T + 2, H, 128), canary, dtype=torch.bfloat16, device=dev)
+    out_view = big[1:T + 1]
+    sbig = torch.full((case.num_seqs + 2, H, 128, 128), canary, dtype=torch.float32, device=dev)
+    sview = sbig[1:case.num_seqs + 1]
+    sview.copy_(case.initial_state.to(dev))
+    to = lambda t: t.to(dev)
+    kda.set_prefill_route(route)
+    try:
+        kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                    to(case.cu_seqlens), scale=case.scale, lower_bound=case.lower_bound,
+                    initial_state=sview, final_state=sview, out=out_view)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    assert torch.all(big[0] == canary) and torch.all(big[T + 1] == canary)
+    assert torch.all(sbig[0] == canary) and torch.all(sbig[-1] == canary)
+    compare(case, out_view, sview)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_zero_length_and_no_state(dev, route):
+    case = make_prefill_case([0, 5, 0], 2, -5.0, 0.02, seed=6, name="zero_len")
+    o, f = run_gpu(case, route, dev)
+    assert torch.equal(f[0].cpu(), case.initial_state[0])
+    assert torch.equal(f[2].cpu(), case.initial_state[2])
+    compare(case, o, f)
+    # no initial state (zeros) and no final state requested
+    case0 = make_prefill_case([40], 2, -5.0, None, seed=7, name="no_state")
+    o, f = run_gpu(case0, route, dev, final=False)
+    assert f is None
+    compare(case0, o, None)
+
+
+def test_empty_call_is_noop(dev):
+    z = torch.empty((0, 2, 128), dtype=torch.bfloat16, device=dev)
+    cu = torch.zeros(1, dtype=torch.int32, device=dev)
+    out, fin = kda.prefill(z, z, z, z, torch.empty((0, 2), dtype=torch.bfloat16, device=dev), cu,
+                           scale=0.1, lower_bound=-5.0, final_state=True)
+    torch.cuda.synchronize()
+    assert out.shape == (0, 2, 128) and fin.shape == (0, 2, 128, 128)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_deterministic(dev, route):
+    case = make_prefill_case([300, 45], 4, -5.0, 0.02, seed=8, name="determinism")
+    o1, f1 = run_gpu(case, route, dev)
+    o2, f2 = run_gpu(case, route, dev)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_stream_and_graph_replay(dev, route):
+    """Runs on a non-default stream and inside a captured graph, replayed with eager
+    work and synchronisations in between; every replay matches the eager result."""
+    case = make_prefill_case([130, 64], 2, -5.0, 0.02, seed=9, name="graph")
+    to = lambda t: t.to(dev)
+    q, k, v, g, b, cu, s0 = (to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                             to(case.cu_seqlens), to(case.initial_state))
+    out = torch.empty((case.total_tokens, 2, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty_like(s0)
+    kda.set_prefill_route(route)
+    try:
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
+                        initial_state=s0, final_state=fin, out=out)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        ref_o, ref_f = out.clone(), fin.clone()
+        graph = torch.cuda.CUDAGraph()
+        out.zero_()
+        with torch.cuda.graph(graph):
+            kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
+                        initial_state=s0, final_state=fin, out=out)
+        for _ in range(3):
+            out.fill_(0)
+            fin.fill_(0)
+            _ = torch.randn(1000, device=dev).sum()  # unrelated eager work
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(fin, ref_f)
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    compare(case, ref_o, ref_f)
