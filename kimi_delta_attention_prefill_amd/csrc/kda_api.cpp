@@ -83,7 +83,7 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                 (double)lower_bound);
   if (num_cus <= 0) num_cus = current_device_cus();
   if (num_cus <= 0) num_cus = 256;
-  if (route == KDA_ROUTE_AUTO) route = KDA_ROUTE_SERIAL;
+  if (route == KDA_ROUTE_AUTO) route = KDA_ROUTE_CHUNK;
   if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
   std::memset(plan, 0, sizeof(*plan));
@@ -100,9 +100,12 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     plan->block_threads = 64 * waves;
     plan->grid_blocks = units * plan->dv_split;
   } else {
-    plan->dv_split = 1;
+    // One block per (sequence, head, value slice).  Two 64-column slices
+    // halve the per-block chain work at the cost of duplicated chunk
+    // preparation; worth it only while every block still gets its own CU.
+    plan->dv_split = 2 * units <= (int64_t)num_cus ? 2 : 1;
     plan->block_threads = 256;
-    plan->grid_blocks = units;
+    plan->grid_blocks = units * plan->dv_split;
   }
   return ok();
 }

@@ -17,7 +17,7 @@ from _checks import check_out, check_state
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = [kda.ROUTE_SERIAL]
+ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK]
 
 
 def _say(*a):
