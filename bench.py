@@ -83,7 +83,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--decode-rows", type=int, default=4096)
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
-    ap.add_argument("--route", choices=["auto", "serial", "chunk"], default="auto")
+    ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -99,8 +99,8 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     kda.load()
-    route = {"auto": kda.ROUTE_AUTO, "serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK}[
-        args.route]
+    route = {"auto": kda.ROUTE_AUTO, "serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK,
+             "split": kda.ROUTE_SPLIT}[args.route]
     kda.set_prefill_route(route)
 
     log("[bench] generating inputs")
@@ -116,6 +116,8 @@ def main():
              slots=to(dc.slots), pool=to(dc.pool))
     d_out = torch.empty_like(D["q"])
     plan = kda.plan(pc.num_seqs, pc.total_tokens, pc.num_heads, pc.lower_bound, 0, route)
+    ws_bytes = kda.workspace_size(pc.num_seqs, pc.total_tokens, pc.num_heads)
+    p_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
@@ -123,7 +125,7 @@ def main():
             ev[0].record(stream)
         kda.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], scale=pc.scale,
                     lower_bound=pc.lower_bound, initial_state=P["s0"], final_state=p_fin,
-                    out=p_out, stream=stream)
+                    out=p_out, workspace=p_ws, stream=stream)
         if ev is not None:
             ev[1].record(stream)
         kda.decode(D["q"], D["k"], D["v"], D["g"], D["beta"], D["pool"], D["slots"],
@@ -158,7 +160,8 @@ def main():
     state_b = STATE_BYTES if args.decode_state == "f32" else STATE_BYTES // 2
     dbytes = items * (2 * state_b + DECODE_IO_BYTES_PER_ITEM)
     achieved_gbs = dbytes / (dec_avg * 1e-3) / 1e9
-    route_name = {kda.ROUTE_SERIAL: "serial", kda.ROUTE_CHUNK: "chunk"}[plan.route]
+    route_name = {kda.ROUTE_SERIAL: "serial", kda.ROUTE_CHUNK: "chunk",
+                  kda.ROUTE_SPLIT: "split"}[plan.route]
 
     result = {
         "metric": "KDA prefill tokens*heads/s + MFMA util; decode HBM GB/s at H=8",

@@ -70,7 +70,13 @@ typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
 typedef enum {
   KDA_ROUTE_AUTO = -1,
   KDA_ROUTE_SERIAL = 0, /* token-serial FP32 recurrence, no MFMA            */
-  KDA_ROUTE_CHUNK = 1   /* 32-token chunks on bf16/fp16 MFMA (see below)    */
+  KDA_ROUTE_CHUNK = 1,  /* 32-token chunks on bf16/fp16 MFMA, each block
+                           prepares and consumes its own chunks (many
+                           (sequence, head) units)                         */
+  KDA_ROUTE_SPLIT = 2   /* same chunk math in two passes: all chunks are
+                           prepared in parallel into the workspace, then a
+                           short serial chain per (sequence, head) consumes
+                           them (few units, long sequences)                */
 } kda_prefill_route;
 
 /* Exponent handling of the chunk route's pairwise (Mqk, Akk) products,
@@ -116,7 +122,10 @@ typedef struct {
  *              writes it); must not partially overlap it.
  *  out         bf16 [total_tokens, num_heads, 128]; must not alias inputs.
  *  workspace, workspace_bytes   device scratch of at least
- *              kda_prefill_workspace_size(...) bytes (currently 0; NULL ok).
+ *              kda_prefill_workspace_size(...) bytes, owned by the caller,
+ *              16-byte aligned; its contents on entry do not matter and it
+ *              may be reused by the next call once this one has completed on
+ *              `stream`.  NULL / 0 is fine when the size is 0.
  *  stream      HIP stream the kernels are enqueued on.
  * Sequences of length 0 copy initial_state to final_state. */
 int kda_prefill(const void* q, const void* k, const void* v, const void* g,
@@ -126,7 +135,9 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g,
                 const float* initial_state, float* final_state, void* out,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 
-/* Bytes of workspace kda_prefill needs for these sizes (0 today). */
+/* Bytes of workspace kda_prefill needs for these sizes with the route it
+ * would choose on the current device (or the forced route): 0 for SERIAL and
+ * CHUNK, (N + T_tot / 32 + 1) * H * 45056 for SPLIT. */
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t num_heads);
 

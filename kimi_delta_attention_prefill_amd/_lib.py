@@ -24,6 +24,7 @@ KDA_ERR_HIP = -4
 ROUTE_AUTO = -1
 ROUTE_SERIAL = 0
 ROUTE_CHUNK = 1
+ROUTE_SPLIT = 2
 
 ANCHOR_FIXED = 0
 ANCHOR_SPLIT16 = 1
@@ -139,6 +140,9 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
             final_state=None, out=None, workspace=None, stream=None):
     """Packed varlen KDA prefill on the GPU.
 
+    ``workspace``: a device uint8 tensor of at least ``workspace_size(N, T, H)``
+    bytes (allocated here when None and the chosen route needs one).
+
     q, k, v, g: bf16 [T, H, 128]; beta: bf16 [T, H]; cu_seqlens: int32 [N+1]
     (device); initial_state: fp32 [N, H, 128, 128] or None (zeros).
     ``final_state``: an fp32 [N, H, 128, 128] tensor to write into, True to
@@ -162,6 +166,10 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
     if out is None:
         out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (T, H, D), dev)
+    if workspace is None:
+        need = workspace_size(N, T, H)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
                               N, T, H, D, D, float(scale), float(lower_bound), _ptr(initial_state),

@@ -1,0 +1,298 @@
+// Pieces shared by the chunk-32 prefill kernels (fused and split routes):
+// MFMA operand types, the K-slot permutation, and the per-chunk preparation
+// steps 1-3 of "FlashInfer PR #4262: CAKE KDA Prefill Highlights", section 2
+// (gate prefix and anchored operands; causal Mqk and the triangular system;
+// the 32x32 unit-lower-triangular inverse), with the fixed exponent anchor of
+// section 1 or its 16-token split.
+#pragma once
+
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+namespace chunk {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int CH = 32;          // chunk length
+constexpr int D = kHeadDim;     // 128
+constexpr int RP = D + 8;       // padded row (elements) of [32 x 128] 16-bit arrays
+constexpr int GP = D + 4;       // padded row of the FP32 gate prefix
+constexpr int TP = CH + 8;      // padded row of [* x 32] fp16 arrays
+
+// An accumulator tile of v_mfma_f32_16x16x32 gives lane l rows 4(l/16)+i of
+// column l%16; two stacked tiles give rows {4(l/16)+i, 16+4(l/16)+i}.  Using
+// that set as the lane's 8 K-slots lets an FP32 accumulator become the next
+// product's B operand by a register conversion.  kslot(x) is the slot of
+// K-index x (0..31): slot 8*grp + j holds index j<4 ? 4grp+j : 16+4grp+j-4.
+__device__ __forceinline__ int kslot(int x) {
+  const int hi = x >> 4, r = x & 15;
+  return ((r >> 2) << 3) + (r & 3) + (hi << 2);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
+  hi = static_cast<__bf16>(x);
+  lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
+  hi = static_cast<_Float16>(x);
+  lo = static_cast<_Float16>(x - static_cast<float>(hi));
+}
+
+// LDS used by the preparation steps.  DVS = value columns staged.
+template <int DVS>
+struct PrepSmem {
+  uint16_t qraw[CH][RP];       // bf16 chunk inputs (padding tokens are zero)
+  uint16_t kraw[CH][RP];
+  uint16_t graw[CH][RP];
+  uint16_t vraw[CH][DVS];
+  float G[CH][GP];             // log2-domain inclusive gate prefix
+  float EL[D];                 // fixed anchor: 2^{G_L - C}
+  float dec[D];                // 2^{G_L}: chunk decay of each key row
+  float beta[CH];
+  float part[4][6][64][4];     // split-K partials of the six Mqk/Akk tiles
+  float A[CH][CH + 1];         // Diag(b) stril(Akk), FP32
+  float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
+  float X[16][17];             // A21 T11
+  float Mq[CH][CH + 1];        // causal Mqk, FP32 (masked)
+};
+
+// Step 1: stage the chunk [t0, t0 + L) of (sequence, head h): q, k, g rows,
+// the value columns [col0, col0 + DVS) and beta.  Tokens >= L are zero.
+template <int DVS>
+__device__ __forceinline__ void load_chunk(PrepSmem<DVS>& sm, const PrefillArgs& a, int t0, int L,
+                                           int h, int col0, int tid, int nthreads) {
+  const int H = a.num_heads;
+  for (int e = tid; e < CH * 16; e += nthreads) {
+    const int t = e >> 4, c8 = (e & 15) * 8;
+    uint4 wq = {0, 0, 0, 0}, wk = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
+    if (t < L) {
+      const int64_t off = ((int64_t)(t0 + t) * H + h) * D + c8;
+      wq = *reinterpret_cast<const uint4*>(a.q + off);
+      wk = *reinterpret_cast<const uint4*>(a.k + off);
+      wg = *reinterpret_cast<const uint4*>(a.g + off);
+    }
+    *reinterpret_cast<uint4*>(&sm.qraw[t][c8]) = wq;
+    *reinterpret_cast<uint4*>(&sm.kraw[t][c8]) = wk;
+    *reinterpret_cast<uint4*>(&sm.graw[t][c8]) = wg;
+  }
+  for (int e = tid; e < CH * (DVS / 8); e += nthreads) {
+    const int t = e / (DVS / 8), c8 = (e % (DVS / 8)) * 8;
+    uint4 wv = {0, 0, 0, 0};
+    if (t < L)
+      wv = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + c8);
+    *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = wv;
+  }
+  if (tid < CH) sm.beta[tid] = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
+}
+
+// Step 2: inclusive gate prefix per channel (threads 0..127), chunk decay,
+// and for the fixed anchor 2^{G_L - C}.
+template <int MODE, int DVS>
+__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, float C, int tid) {
+  if (tid < D) {
+    float acc = 0.f;
+#pragma unroll
+    for (int t = 0; t < CH; ++t) {
+      acc += bf16_to_f32(sm.graw[t][tid]);
+      sm.G[t][tid] = acc * kLog2e;
+    }
+    const float GL = acc * kLog2e;
+    sm.dec[tid] = fast_exp2(GL);
+    sm.EL[tid] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
+  }
+}
+
+// Operands of one lane for the pairwise products: A rows (Qc, Kc') and B
+// columns (Kc), hi and lo, for its two tokens (l%16 and l%16+16) and 8 key
+// channels.  "o" variants feed the off-diagonal 16x16 tile.
+struct PairOps {
+  bf16x8 q0h, q0l, q1h, q1l, qoh, qol;
+  bf16x8 k0h, k0l, k1h, k1l, koh, kol;
+  bf16x8 b0h, b0l, b1h, b1l, boh, bol;
+};
+
+// Step 3: anchored operands and the split-K pairwise products.  Wave w (of 4)
+// owns key channels 32w..32w+31; lane (g4, l16) owns channels 32w+8g4+j and
+// tokens l16, l16+16.  For every (token t, channel c) owned, emit(t, c, kf, qf,
+// P, R) receives the raw k and q values, P = 2^{G_t} and R = 2^{G_L - G_t}
+// (both <= 1) so the caller can form Kg, Qg and Kr.  The six lower tiles of
+// Mqk and Akk (as partial sums over this wave's channels) go to sm.part.
+template <int MODE, int DVS, class Emit>
+__device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillArgs& a, float C,
+                                              float exp2C, int wave, int lane, Emit&& emit) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int cb = 32 * wave, cl = 8 * g4;
+  PairOps op;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int t = l16 + 16 * half;
+    const f32x4 G0 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl]);
+    const f32x4 G1 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl + 4]);
+    const uint4 qw = *reinterpret_cast<const uint4*>(&sm.qraw[t][cb + cl]);
+    const uint4 kw = *reinterpret_cast<const uint4*>(&sm.kraw[t][cb + cl]);
+    f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1;
+    if (MODE == 1) {
+      Gs0 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl]);
+      Gs1 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl + 4]);
+      GL0 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl]);
+      GL1 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl + 4]);
+    } else {
+      EL0 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl]);
+      EL1 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl + 4]);
+    }
+    const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
+    const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
+    float kv[8], qv[8], Pv[8], Rv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float Gv = j < 4 ? G0[j] : G1[j - 4];
+      const float qf = (j & 1) ? bf16hi(qu[j >> 1]) : bf16lo(qu[j >> 1]);
+      const float kf = (j & 1) ? bf16hi(ku[j >> 1]) : bf16lo(ku[j >> 1]);
+      float ep, em, P, R, fo = 0.f;
+      if (MODE == 0) {
+        ep = fast_exp2(Gv - C);                       // 2^{G-C}, |exponent| <= 16|b|
+        em = fast_exp2(C - Gv);                       // 2^{C-G}
+        P = ep * exp2C;                               // 2^G
+        R = (j < 4 ? EL0[j] : EL1[j - 4]) * em;       // 2^{G_L - G}
+      } else {
+        const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
+        const float gl = j < 4 ? GL0[j] : GL1[j - 4];
+        const float Ch = (half ? g15 : 0.f) + a.half_anchor_log2;
+        ep = fast_exp2(Gv - Ch);
+        em = fast_exp2(Ch - Gv);
+        fo = half ? fast_exp2(Gv - g15) : fast_exp2(g15 - Gv);  // both <= 1
+        P = fast_exp2(Gv);
+        R = fast_exp2(gl - Gv);
+      }
+      __bf16 h1, l1, h2, l2, h3, l3;
+      split_bf16(qf * ep, h1, l1);
+      split_bf16(kf * ep, h2, l2);
+      split_bf16(kf * em, h3, l3);
+      if (half == 0) {
+        op.q0h[j] = h1; op.q0l[j] = l1;
+        op.k0h[j] = h2; op.k0l[j] = l2;
+        op.b0h[j] = h3; op.b0l[j] = l3;
+      } else {
+        op.q1h[j] = h1; op.q1l[j] = l1;
+        op.k1h[j] = h2; op.k1l[j] = l2;
+        op.b1h[j] = h3; op.b1l[j] = l3;
+      }
+      if (MODE == 0) {
+        // one anchor for the whole chunk: the off-diagonal tile reuses the diagonal operands
+        if (half == 1) { op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2; }
+        else { op.boh[j] = h3; op.bol[j] = l3; }
+      } else {
+        if (half == 1) {
+          split_bf16(qf * fo, h1, l1);
+          split_bf16(kf * fo, h2, l2);
+          op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2;
+        } else {
+          split_bf16(kf * fo, h3, l3);
+          op.boh[j] = h3; op.bol[j] = l3;
+        }
+      }
+      kv[j] = kf; qv[j] = qf; Pv[j] = P; Rv[j] = R;
+    }
+    emit(t, cb + cl, kv, qv, Pv, Rv);
+  }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[6];
+  acc[0] = mfma_bf16(op.q0h, op.b0h, z);
+  acc[0] = mfma_bf16(op.q0h, op.b0l, acc[0]);
+  acc[0] = mfma_bf16(op.q0l, op.b0h, acc[0]);
+  acc[1] = mfma_bf16(op.qoh, op.boh, z);
+  acc[1] = mfma_bf16(op.qoh, op.bol, acc[1]);
+  acc[1] = mfma_bf16(op.qol, op.boh, acc[1]);
+  acc[2] = mfma_bf16(op.q1h, op.b1h, z);
+  acc[2] = mfma_bf16(op.q1h, op.b1l, acc[2]);
+  acc[2] = mfma_bf16(op.q1l, op.b1h, acc[2]);
+  acc[3] = mfma_bf16(op.k0h, op.b0h, z);
+  acc[3] = mfma_bf16(op.k0h, op.b0l, acc[3]);
+  acc[3] = mfma_bf16(op.k0l, op.b0h, acc[3]);
+  acc[4] = mfma_bf16(op.koh, op.boh, z);
+  acc[4] = mfma_bf16(op.koh, op.bol, acc[4]);
+  acc[4] = mfma_bf16(op.kol, op.boh, acc[4]);
+  acc[5] = mfma_bf16(op.k1h, op.b1h, z);
+  acc[5] = mfma_bf16(op.k1h, op.b1l, acc[5]);
+  acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
+#pragma unroll
+  for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(&sm.part[wave][p][lane][0]) = acc[p];
+}
+
+// Step 3b: sum the four split-K partials in a fixed order, mask the causal
+// triangles by select (masked anchored entries may be inf or NaN) and scale
+// Akk by beta.  Writes sm.Mq (FP32) and sm.A; emit_mqk(r, s, value) sees every
+// Mqk entry (zero above the diagonal).  256 threads.
+template <int DVS, class EmitMqk>
+__device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk&& emit_mqk) {
+  for (int e = tid; e < 8 * 256; e += 256) {
+    const int tile = e >> 8, q4 = tile & 3;
+    const int ln = (e >> 2) & 63, i = e & 3;
+    const int mt = (q4 == 1 || q4 == 2) ? 1 : 0;
+    const int nt = (q4 == 2 || q4 == 3) ? 1 : 0;
+    const int r = 16 * mt + 4 * (ln >> 4) + i, s = 16 * nt + (ln & 15);
+    float val = 0.f;
+    if (q4 != 3) {
+      const int p = (tile < 4 ? 0 : 3) + q4;
+      val = ((sm.part[0][p][ln][i] + sm.part[1][p][ln][i]) + sm.part[2][p][ln][i]) +
+            sm.part[3][p][ln][i];
+    }
+    if (tile < 4) {
+      const float m = s <= r ? val : 0.f;
+      sm.Mq[r][s] = m;
+      emit_mqk(r, s, m);
+    } else {
+      sm.A[r][s] = s < r ? sm.beta[r] * val : 0.f;
+    }
+  }
+}
+
+// Steps 4a-4c: T = (I + A)^{-1} in FP32 into sm.Tf.  The 16x16 diagonal
+// blocks by forward substitution (wave 0, one column per lane), then
+// T21 = -T22 A21 T11 and T12 = 0.  256 threads; contains barriers.
+template <int DVS>
+__device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid) {
+  const int wave = tid >> 6, lane = tid & 63;
+  if (wave == 0 && lane < 32) {
+    const int base = 16 * (lane >> 4), m = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-sm.A[base + i][base + j], x[j], x[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sm.Tf[base + i][base + m] = x[i];
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 4, m = tid & 15;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc = fmaf(sm.A[16 + i][j], sm.Tf[j][m], acc);
+    sm.X[i][m] = acc;
+  }
+  __syncthreads();
+  {
+    const int i = tid >> 4, m = tid & 15;
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) acc = fmaf(sm.Tf[16 + i][16 + j], sm.X[j][m], acc);
+    sm.Tf[16 + i][m] = -acc;
+    sm.Tf[i][16 + m] = 0.f;
+  }
+}
+
+}  // namespace chunk
+}  // namespace kda

@@ -57,18 +57,30 @@ bool fixed_anchor_fits(float lower_bound) {
 
 extern "C" {
 
+size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
+  if (num_seqs <= 0 || total_tokens < 0 || num_heads < 1) return 0;
+  kda_prefill_plan_t plan;
+  // The workspace does not depend on the bound; any valid one gives the route.
+  if (kda_prefill_plan(num_seqs, total_tokens, num_heads, -1.0f, 0, g_forced_route.load(),
+                       &plan) != KDA_OK)
+    return 0;
+  return plan.route == KDA_ROUTE_SPLIT
+             ? kda::split_workspace_bytes(num_seqs, total_tokens, num_heads)
+             : 0;
+}
+
 const char* kda_last_error(void) { return g_last_error; }
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
 int kda_set_prefill_route(int32_t route) {
-  if (route != KDA_ROUTE_AUTO && route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK)
+  if (route != KDA_ROUTE_AUTO && route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK &&
+      route != KDA_ROUTE_SPLIT)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_set_prefill_route: unknown route %d", route);
   g_forced_route.store(route);
   return ok();
 }
 
-size_t kda_prefill_workspace_size(int32_t, int64_t, int32_t) { return 0; }
 
 int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                      float lower_bound, int32_t num_cus, int32_t route,
@@ -83,14 +95,19 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                 (double)lower_bound);
   if (num_cus <= 0) num_cus = current_device_cus();
   if (num_cus <= 0) num_cus = 256;
-  if (route == KDA_ROUTE_AUTO) route = KDA_ROUTE_CHUNK;
-  if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK)
+  const int64_t units = (int64_t)num_seqs * num_heads;
+  if (route == KDA_ROUTE_AUTO) {
+    // Few recurrences: one block per (sequence, head) would idle most of the
+    // chip and serialise chunk preparation, so prepare all chunks in
+    // parallel first.  Many recurrences: keep everything in one pass.
+    route = 8 * units <= (int64_t)num_cus ? KDA_ROUTE_SPLIT : KDA_ROUTE_CHUNK;
+  }
+  if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
   std::memset(plan, 0, sizeof(*plan));
   plan->route = route;
   plan->anchor_mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
   plan->anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
-  const int64_t units = (int64_t)num_seqs * num_heads;
   if (route == KDA_ROUTE_SERIAL) {
     // 16 value columns per wave; fewer waves per block (more blocks) when
     // there are few (sequence, head) units to spread over the compute units.
@@ -98,6 +115,13 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     if (2 * units < (int64_t)num_cus) waves = 4 * units < (int64_t)num_cus ? 1 : 2;
     plan->dv_split = 8 / waves;
     plan->block_threads = 64 * waves;
+    plan->grid_blocks = units * plan->dv_split;
+  } else if (route == KDA_ROUTE_SPLIT) {
+    // Chain pass: each 16-column state chain gets a block (and so a CU's LDS
+    // bandwidth) of its own when that still fits the chip; otherwise four
+    // chains share a block.  Both add four loader waves.
+    plan->dv_split = 8 * units <= (int64_t)num_cus ? 8 : 2;
+    plan->block_threads = 64 * (8 / plan->dv_split + 4);
     plan->grid_blocks = units * plan->dv_split;
   } else {
     // One block per (sequence, head, value slice).  Two 64-column slices
@@ -154,14 +178,18 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
       return fail(KDA_ERR_INVALID_ARGUMENT,
                   "kda_prefill: final_state partially overlaps initial_state");
   }
-  const size_t ws_need = kda_prefill_workspace_size(num_seqs, total_tokens, num_heads);
-  if (ws_need > 0 && (!workspace || workspace_bytes < ws_need))
-    return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace of %zu bytes needed", ws_need);
-
   kda_prefill_plan_t plan;
   int rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0,
                             g_forced_route.load(), &plan);
   if (rc != KDA_OK) return rc;
+  if (plan.route == KDA_ROUTE_SPLIT) {
+    const size_t ws_need = kda::split_workspace_bytes(num_seqs, total_tokens, num_heads);
+    if (!workspace || workspace_bytes < ws_need)
+      return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace of %zu bytes needed (got %zu)",
+                  ws_need, workspace_bytes);
+    if (!aligned(workspace, 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: workspace is not 16-byte aligned");
+  }
 
   kda::PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
@@ -183,6 +211,8 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
   hipError_t e;
   if (plan.route == KDA_ROUTE_SERIAL)
     e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
+  else if (plan.route == KDA_ROUTE_SPLIT)
+    e = kda::launch_prefill_split(a, plan.anchor_mode, plan.dv_split, workspace, stream);
   else
     e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
   if (e == hipErrorNotSupported)

@@ -23,6 +23,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // 2^x on the hardware exponential unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Raw buffer resource over [base, base + bytes): buffer loads outside return
+// 0 and buffer stores outside are dropped by the hardware (gfx9 word 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
+}
+// 16-bit store through a buffer resource at byte offset `off` (unconditional
+// instruction; out-of-range offsets are discarded).
+__device__ __forceinline__ void buffer_store_u16(uint16_t v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+}
+
 // Clamp a device-read sequence offset into [0, total].
 __device__ __forceinline__ int clamp_offset(int x, int total) {
   return x < 0 ? 0 : (x > total ? total : x);

@@ -48,6 +48,12 @@ hipError_t launch_prefill_serial(const PrefillArgs& a, int waves, hipStream_t s)
 // Chunk-32 MFMA prefill.
 hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 hipStream_t s);
+// Two-pass chunk-32 prefill (parallel chunk preparation, then the serial
+// state chain); needs split_workspace_bytes() of device workspace.
+// dv_split 8: one 16-column chain per block; 2: four chains per block.
+hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
+                                void* workspace, hipStream_t s);
+size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
 // Decode step; `cols` = value columns per block (32, 64 or 128).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
 

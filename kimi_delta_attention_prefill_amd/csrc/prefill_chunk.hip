@@ -47,44 +47,16 @@
 // stored in LDS with their K index in that permuted order.
 #include <cmath>
 
-#include "kda_device.h"
-#include "kda_internal.h"
+#include "chunk_common.h"
 
 namespace kda {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
-constexpr int CH = 32;          // chunk length
-constexpr int D = kHeadDim;     // 128
-constexpr int RP = D + 8;       // padded row (elements) of [32 x 128] 16-bit arrays
-constexpr int GP = D + 4;       // padded row of the FP32 gate prefix
-constexpr int TP = CH + 8;      // padded row of [* x 32] fp16 arrays
-
-// Slot of K-index x (0..31) in the permuted order: slot = 8 * group + j holds
-// index (j < 4 ? 4 * group + j : 16 + 4 * group + j - 4).
-__device__ __forceinline__ int kslot(int x) {
-  const int hi = x >> 4, r = x & 15;
-  return ((r >> 2) << 3) + (r & 3) + (hi << 2);
-}
+using namespace chunk;
 
 template <int DVS>
-struct ChunkSmem {
-  uint16_t qraw[CH][RP];       // bf16 chunk inputs
-  uint16_t kraw[CH][RP];
-  uint16_t graw[CH][RP];
-  uint16_t vraw[CH][DVS];
-  float G[CH][GP];             // log2-domain inclusive gate prefix
-  float EL[D];                 // fixed anchor: 2^{G_L - C}
-  float dec[D];                // 2^{G_L}: chunk decay of each key row
-  float beta[CH];
-  float part[4][6][64][4];     // split-K partials of the six Mqk/Akk tiles
-  float A[CH][CH + 1];         // Diag(b) stril(Akk), FP32
-  float Tf[CH][CH + 1];        // diagonal blocks of the inverse, FP32
-  float X[16][17];             // A21 T11
+struct FusedSmem {
+  PrepSmem<DVS> p;
   _Float16 Kg[CH][RP];         // k 2^G      [token][dk, permuted]
   _Float16 Qg[CH][RP];         // q 2^G      [token][dk, permuted]
   _Float16 KrT[D][TP];         // (k 2^{G_L-G})^T [dk][token, permuted]
@@ -92,35 +64,12 @@ struct ChunkSmem {
   _Float16 Mqk[CH][TP];        // causal Mqk       [token][token, permuted]
 };
 
-__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
-}
-__device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
-  hi = static_cast<__bf16>(x);
-  lo = static_cast<__bf16>(x - static_cast<float>(hi));
-}
-__device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
-  hi = static_cast<_Float16>(x);
-  lo = static_cast<_Float16>(x - static_cast<float>(hi));
-}
-
-// Operands of one lane for the pairwise products: A rows (Qc, Kc') and B
-// columns (Kc), hi and lo, for its two tokens (l%16 and l%16 + 16) and its 8
-// key channels.  "o" variants feed the off-diagonal 16x16 tile.
-struct PairOps {
-  bf16x8 q0h, q0l, q1h, q1l, qoh, qol;   // A rows: tokens l%16 (0), l%16+16 (1), off-diag
-  bf16x8 k0h, k0l, k1h, k1l, koh, kol;   // A rows for Akk
-  bf16x8 b0h, b0l, b1h, b1l, boh, bol;   // B columns
-};
-
 template <int MODE, int NT>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float exp2C) {
   constexpr int DVS = 64 * NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  ChunkSmem<DVS>& sm = *reinterpret_cast<ChunkSmem<DVS>*>(smem_raw);
+  FusedSmem<DVS>& sm = *reinterpret_cast<FusedSmem<DVS>*>(smem_raw);
+  PrepSmem<DVS>& ps = sm.p;
 
   const int H = a.num_heads;
   const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
@@ -150,211 +99,45 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
   for (int t0 = bos; t0 < eos; t0 += CH) {
     const int L = min(CH, eos - t0);
     __syncthreads();  // the previous chunk's chain is done with the LDS operands
-
-    // ---- 1. load the chunk (16-byte coalesced rows; padding tokens are zero)
-    for (int e = tid; e < CH * 16; e += 256) {
-      const int t = e >> 4, c8 = (e & 15) * 8;
-      uint4 wq = {0, 0, 0, 0}, wk = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
-      if (t < L) {
-        const int64_t off = ((int64_t)(t0 + t) * H + h) * D + c8;
-        wq = *reinterpret_cast<const uint4*>(a.q + off);
-        wk = *reinterpret_cast<const uint4*>(a.k + off);
-        wg = *reinterpret_cast<const uint4*>(a.g + off);
-      }
-      *reinterpret_cast<uint4*>(&sm.qraw[t][c8]) = wq;
-      *reinterpret_cast<uint4*>(&sm.kraw[t][c8]) = wk;
-      *reinterpret_cast<uint4*>(&sm.graw[t][c8]) = wg;
-    }
-    for (int e = tid; e < CH * (DVS / 8); e += 256) {
-      const int t = e / (DVS / 8), c8 = (e % (DVS / 8)) * 8;
-      uint4 wv = {0, 0, 0, 0};
-      if (t < L)
-        wv = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + t) * H + h) * D + col_base + c8);
-      *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = wv;
-    }
-    if (tid < CH) sm.beta[tid] = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
+    load_chunk(ps, a, t0, L, h, col_base, tid, 256);
     __syncthreads();
-
-    // ---- 2. gate prefix: one channel per thread, 32 serial FP32 adds
-    if (tid < D) {
-      float acc = 0.f;
-#pragma unroll
-      for (int t = 0; t < CH; ++t) {
-        acc += bf16_to_f32(sm.graw[t][tid]);
-        sm.G[t][tid] = acc * kLog2e;
-      }
-      const float GL = acc * kLog2e;
-      sm.dec[tid] = fast_exp2(GL);
-      sm.EL[tid] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
-    }
+    gate_prefix<MODE>(ps, C, tid);
     __syncthreads();
-
-    // ---- 3. operands and the split-K pairwise products (wave = key block)
-    {
-      const int cb = 32 * wave;          // key block of this wave
-      const int cl = 8 * g4;             // lane's 8 channels within the block
-      PairOps op;
+    pair_products<MODE>(ps, a, C, exp2C, wave, lane,
+                        [&](int t, int c0, const float* kv, const float* qv, const float* P,
+                            const float* R) {
+                          const int cb = c0 & ~31, cl = c0 & 31;
+                          f16x4 kg_lo, kg_hi, qg_lo, qg_hi;
 #pragma unroll
-      for (int half = 0; half < 2; ++half) {
-        const int t = l16 + 16 * half;
-        const f32x4 G0 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl]);
-        const f32x4 G1 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl + 4]);
-        const uint4 qw = *reinterpret_cast<const uint4*>(&sm.qraw[t][cb + cl]);
-        const uint4 kw = *reinterpret_cast<const uint4*>(&sm.kraw[t][cb + cl]);
-        f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1;
-        if (MODE == 1) {
-          Gs0 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl]);
-          Gs1 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl + 4]);
-          GL0 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl]);
-          GL1 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl + 4]);
-        } else {
-          EL0 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl]);
-          EL1 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl + 4]);
-        }
-        const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
-        const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
-        f16x4 kg_lo, kg_hi, qg_lo, qg_hi;   // channels cl+0..3 and cl+4..7 (fp16)
+                          for (int j = 0; j < 4; ++j) {
+                            kg_lo[j] = static_cast<_Float16>(kv[j] * P[j]);
+                            kg_hi[j] = static_cast<_Float16>(kv[4 + j] * P[4 + j]);
+                            qg_lo[j] = static_cast<_Float16>(qv[j] * P[j]);
+                            qg_hi[j] = static_cast<_Float16>(qv[4 + j] * P[4 + j]);
+                          }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float Gv = j < 4 ? G0[j] : G1[j - 4];
-          const float qf = (j & 1) ? bf16hi(qu[j >> 1]) : bf16lo(qu[j >> 1]);
-          const float kf = (j & 1) ? bf16hi(ku[j >> 1]) : bf16lo(ku[j >> 1]);
-          float ep, em, P, R, fo = 0.f;
-          if (MODE == 0) {
-            ep = fast_exp2(Gv - C);
-            em = fast_exp2(C - Gv);
-            P = ep * exp2C;                                   // 2^G
-            R = (j < 4 ? EL0[j] : EL1[j - 4]) * em;           // 2^{G_L - G}
-          } else {
-            const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
-            const float gl = j < 4 ? GL0[j] : GL1[j - 4];
-            const float Ch = (half ? g15 : 0.f) + a.half_anchor_log2;
-            ep = fast_exp2(Gv - Ch);
-            em = fast_exp2(Ch - Gv);
-            fo = half ? fast_exp2(Gv - g15) : fast_exp2(g15 - Gv);  // both <= 1
-            P = fast_exp2(Gv);
-            R = fast_exp2(gl - Gv);
-          }
-          __bf16 h1, l1, h2, l2, h3, l3;
-          split_bf16(qf * ep, h1, l1);
-          split_bf16(kf * ep, h2, l2);
-          split_bf16(kf * em, h3, l3);
-          if (half == 0) {
-            op.q0h[j] = h1; op.q0l[j] = l1;
-            op.k0h[j] = h2; op.k0l[j] = l2;
-            op.b0h[j] = h3; op.b0l[j] = l3;
-          } else {
-            op.q1h[j] = h1; op.q1l[j] = l1;
-            op.k1h[j] = h2; op.k1l[j] = l2;
-            op.b1h[j] = h3; op.b1l[j] = l3;
-          }
-          if (MODE == 0) {
-            // one anchor for the whole chunk: the off-diagonal tile reuses the diagonal operands
-            if (half == 1) { op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2; }
-            else { op.boh[j] = h3; op.bol[j] = l3; }
-          } else {
-            if (half == 1) {
-              split_bf16(qf * fo, h1, l1);
-              split_bf16(kf * fo, h2, l2);
-              op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2;
-            } else {
-              split_bf16(kf * fo, h3, l3);
-              op.boh[j] = h3; op.bol[j] = l3;
-            }
-          }
-          const _Float16 kgv = static_cast<_Float16>(kf * P);
-          const _Float16 qgv = static_cast<_Float16>(qf * P);
-          if (j < 4) { kg_lo[j] = kgv; qg_lo[j] = qgv; } else { kg_hi[j - 4] = kgv; qg_hi[j - 4] = qgv; }
-          sm.KrT[cb + cl + j][kslot(t)] = static_cast<_Float16>(kf * R);
-        }
-        // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 permuted slots
-        *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl)]) = kg_lo;
-        *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
-        *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl)]) = qg_lo;
-        *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
-      }
-      // six tiles: Mqk (0,0), (1,0), (1,1) and Akk (0,0), (1,0), (1,1); (0,1) is masked
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 acc[6];
-      acc[0] = mfma_bf16(op.q0h, op.b0h, z);
-      acc[0] = mfma_bf16(op.q0h, op.b0l, acc[0]);
-      acc[0] = mfma_bf16(op.q0l, op.b0h, acc[0]);
-      acc[1] = mfma_bf16(op.qoh, op.boh, z);
-      acc[1] = mfma_bf16(op.qoh, op.bol, acc[1]);
-      acc[1] = mfma_bf16(op.qol, op.boh, acc[1]);
-      acc[2] = mfma_bf16(op.q1h, op.b1h, z);
-      acc[2] = mfma_bf16(op.q1h, op.b1l, acc[2]);
-      acc[2] = mfma_bf16(op.q1l, op.b1h, acc[2]);
-      acc[3] = mfma_bf16(op.k0h, op.b0h, z);
-      acc[3] = mfma_bf16(op.k0h, op.b0l, acc[3]);
-      acc[3] = mfma_bf16(op.k0l, op.b0h, acc[3]);
-      acc[4] = mfma_bf16(op.koh, op.boh, z);
-      acc[4] = mfma_bf16(op.koh, op.bol, acc[4]);
-      acc[4] = mfma_bf16(op.kol, op.boh, acc[4]);
-      acc[5] = mfma_bf16(op.k1h, op.b1h, z);
-      acc[5] = mfma_bf16(op.k1h, op.b1l, acc[5]);
-      acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
-#pragma unroll
-      for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(&sm.part[wave][p][lane][0]) = acc[p];
+                          for (int j = 0; j < 8; ++j)
+                            sm.KrT[c0 + j][kslot(t)] = static_cast<_Float16>(kv[j] * R[j]);
+                          // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 slots
+                          *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl)]) = kg_lo;
+                          *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
+                          *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl)]) = qg_lo;
+                          *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
+                        });
+    __syncthreads();
+    reduce_pairs(ps, tid, [&](int r, int s, float m) {
+      sm.Mqk[r][kslot(s)] = static_cast<_Float16>(m);
+    });
+    __syncthreads();
+    invert_unit_lower(ps, tid);
+    __syncthreads();
+    for (int e = tid; e < CH * CH; e += 256) {
+      const int r = e >> 5, s = e & 31;
+      sm.T[r][kslot(s)] = static_cast<_Float16>(ps.Tf[r][s]);
     }
     __syncthreads();
 
-    // ---- 4. sum the partials in a fixed order, mask, scale by beta
-    for (int e = tid; e < 8 * 256; e += 256) {
-      const int tile = e >> 8, q4 = tile & 3;
-      const int ln = (e >> 2) & 63, i = e & 3;
-      const int mt = (q4 == 1 || q4 == 2) ? 1 : 0;
-      const int nt = (q4 == 2 || q4 == 3) ? 1 : 0;
-      const int r = 16 * mt + 4 * (ln >> 4) + i, s = 16 * nt + (ln & 15);
-      float val = 0.f;
-      if (q4 != 3) {
-        const int p = (tile < 4 ? 0 : 3) + q4;
-        val = ((sm.part[0][p][ln][i] + sm.part[1][p][ln][i]) + sm.part[2][p][ln][i]) +
-              sm.part[3][p][ln][i];
-      }
-      if (tile < 4)
-        sm.Mqk[r][kslot(s)] = static_cast<_Float16>(s <= r ? val : 0.f);
-      else
-        sm.A[r][s] = s < r ? sm.beta[r] * val : 0.f;
-    }
-    __syncthreads();
-
-    // ---- 5. T = (I + A)^{-1}: 16x16 diagonal blocks by forward substitution,
-    //         then T21 = -T22 A21 T11.
-    if (wave == 0 && lane < 32) {
-      const int base = 16 * (lane >> 4), m = lane & 15;
-      float x[16];
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-#pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-sm.A[base + i][base + j], x[j], x[i]);
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sm.Tf[base + i][base + m] = x[i];
-    }
-    __syncthreads();
-    {
-      const int i = tid >> 4, m = tid & 15;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc = fmaf(sm.A[16 + i][j], sm.Tf[j][m], acc);
-      sm.X[i][m] = acc;
-    }
-    __syncthreads();
-    {
-      const int i = tid >> 4, m = tid & 15;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc = fmaf(sm.Tf[16 + i][16 + j], sm.X[j][m], acc);
-      sm.T[16 + i][kslot(m)] = static_cast<_Float16>(-acc);
-      sm.T[i][kslot(m)] = static_cast<_Float16>(sm.Tf[i][m]);
-      sm.T[16 + i][kslot(16 + m)] = static_cast<_Float16>(sm.Tf[16 + i][16 + m]);
-      sm.T[i][kslot(16 + m)] = static_cast<_Float16>(0.f);
-    }
-    __syncthreads();
-
-    // ---- 6. the state chain on this wave's 16 * NT value columns
+    // ---- the state chain on this wave's 16 * NT value columns
     {
       f16x8 Sb[4][NT];
 #pragma unroll
@@ -394,7 +177,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * mt + 4 * g4 + i;
             const float vp =
-                sm.beta[t] * (bf16_to_f32(sm.vraw[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
+                ps.beta[t] * (bf16_to_f32(ps.vraw[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
             _Float16 hh, ll;
             split_f16(vp, hh, ll);
             Vh[nt][4 * mt + i] = hh;
@@ -426,7 +209,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         const f16x8 akr = *reinterpret_cast<const f16x8*>(&sm.KrT[16 * mt + l16][8 * g4]);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&sm.dec[16 * mt + 4 * g4]);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(&ps.dec[16 * mt + 4 * g4]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -469,7 +252,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
 
 template <int MODE, int NT>
 hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
-  constexpr size_t bytes = sizeof(ChunkSmem<64 * NT>);
+  constexpr size_t bytes = sizeof(FusedSmem<64 * NT>);
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_chunk_kernel<MODE, NT>),

@@ -44,7 +44,7 @@ def test_plan_anchor_mode_boundary():
     assert abs(p.anchor_log2 - 16 * -5.0 * 1.4426950408889634) < 1e-4
 
 
-@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK])
+@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT])
 def test_plan_grid_covers_every_unit(route):
     for N, H, cus in ((1, 8, 256), (16, 32, 256), (4, 64, 256), (1, 1, 256), (3, 5, 80)):
         p = kda.plan(N, 100 * N, H, -5.0, cus, route)
@@ -131,5 +131,30 @@ def test_decode_host_validation():
     assert _decode_raw(rows=0, q=None, pool=None, idx=None, out=None) == 0
 
 
-def test_workspace_size_is_zero():
-    assert kda.workspace_size(16, 40000, 32) == 0
+def test_auto_route_and_workspace():
+    # few (sequence, head) units: two-pass split route; many: fused chunk route
+    assert kda.plan(1, 8192, 8, -5.0, 256).route == kda.ROUTE_SPLIT
+    assert kda.plan(1, 64, 2, -5.0, 256).route == kda.ROUTE_SPLIT
+    assert kda.plan(16, 35000, 32, -5.0, 256).route == kda.ROUTE_CHUNK
+    assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
+    try:
+        kda.set_prefill_route(kda.ROUTE_SPLIT)
+        assert kda.workspace_size(1, 8192, 8) == (1 + 8192 // 32 + 1) * 8 * 45056
+        assert kda.workspace_size(3, 100, 2) == (3 + 3 + 1) * 2 * 45056
+        kda.set_prefill_route(kda.ROUTE_CHUNK)
+        assert kda.workspace_size(16, 40000, 32) == 0
+        kda.set_prefill_route(kda.ROUTE_SERIAL)
+        assert kda.workspace_size(1, 8192, 8) == 0
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+
+
+def test_split_route_requires_workspace():
+    try:
+        kda.set_prefill_route(kda.ROUTE_SPLIT)
+        rc = _prefill_raw(ws=None, ws_bytes=0)
+        assert rc == _lib.KDA_ERR_WORKSPACE and "workspace" in kda.last_error()
+        rc = _prefill_raw(ws=0x10000, ws_bytes=100)
+        assert rc == _lib.KDA_ERR_WORKSPACE
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)

@@ -17,7 +17,7 @@ from _checks import check_out, check_state
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK]
+ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT]
 
 
 def _say(*a):
@@ -191,11 +191,13 @@ def test_stream_and_graph_replay(dev, route):
     fin = torch.empty_like(s0)
     kda.set_prefill_route(route)
     try:
+        need = kda.workspace_size(case.num_seqs, case.total_tokens, 2)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev) if need else None
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
             kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
-                        initial_state=s0, final_state=fin, out=out)
+                        initial_state=s0, final_state=fin, out=out, workspace=ws)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         ref_o, ref_f = out.clone(), fin.clone()
@@ -203,7 +205,7 @@ def test_stream_and_graph_replay(dev, route):
         out.zero_()
         with torch.cuda.graph(graph):
             kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
-                        initial_state=s0, final_state=fin, out=out)
+                        initial_state=s0, final_state=fin, out=out, workspace=ws)
         for _ in range(3):
             out.fill_(0)
             fin.fill_(0)
