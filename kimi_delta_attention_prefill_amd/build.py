@@ -35,9 +35,15 @@ def _flags():
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
+# Per-source extra flags.  The split-route chain keeps its FP32 state in the
+# MFMA accumulators for the whole sequence and also updates it with VALU
+# ops; accumulators in AGPRs would cost two register moves per touch.
+_EXTRA = {"prefill_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc()] + _flags() + ["-c", src, "-o", obj]
+    cmd = [hipcc()] + _flags() + _EXTRA.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     if src.endswith(".hip"):
         cmd[1:1] = ["-x", "hip"]
     r = subprocess.run(cmd, capture_output=True, text=True)

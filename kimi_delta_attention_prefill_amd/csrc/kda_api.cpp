@@ -117,12 +117,11 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     plan->block_threads = 64 * waves;
     plan->grid_blocks = units * plan->dv_split;
   } else if (route == KDA_ROUTE_SPLIT) {
-    // Chain pass: each 16-column state chain gets a block (and so a CU's LDS
-    // bandwidth) of its own when that still fits the chip; otherwise four
-    // chains share a block.  Both add four loader waves.
-    plan->dv_split = 8 * units <= (int64_t)num_cus ? 8 : 2;
-    plan->block_threads = 64 * (8 / plan->dv_split + 4);
-    plan->grid_blocks = units * plan->dv_split;
+    // Chain pass: one block (state, output and two loader waves) per
+    // 16-column value tile of each (sequence, head).
+    plan->dv_split = 8;
+    plan->block_threads = 256;
+    plan->grid_blocks = units * 8;
   } else {
     // One block per (sequence, head, value slice).  Two 64-column slices
     // halve the per-block chain work at the cost of duplicated chunk

@@ -50,7 +50,7 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
                                 hipStream_t s);
 // Two-pass chunk-32 prefill (parallel chunk preparation, then the serial
 // state chain); needs split_workspace_bytes() of device workspace.
-// dv_split 8: one 16-column chain per block; 2: four chains per block.
+// dv_split must be 8: one 16-column chain per block.
 hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 void* workspace, hipStream_t s);
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);

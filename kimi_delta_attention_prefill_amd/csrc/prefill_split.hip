@@ -39,6 +39,7 @@
 // slot of chunk c of sequence n is n + floor(cu[n] / 32) + c, unique and
 // below N + T / 32 + 1.
 #include <cmath>
+#include <type_traits>
 
 #include "chunk_common.h"
 
@@ -185,92 +186,160 @@ __global__ __launch_bounds__(256) void prefill_split_prep(PrefillArgs a, float e
     reinterpret_cast<uint4*>(rec)[e] = reinterpret_cast<const uint4*>(sm.frag)[e];
 }
 
-// Chain-block LDS stage of one chunk: the staged record part, then the U0
-// tiles of the block's CW 16-column tiles (record bytes
-// [kRecOffU0 + first_tile * 2048, + CW * 2048), contiguous).
-template <int CW>
-struct ChainStage {
-  static constexpr int kU0Bytes = CW * 2048;
-  static constexpr int kBytes = kRecStageBytes + kU0Bytes;
-  static constexpr int kRounds = (kBytes / 16 + 255) / 256;   // 16-byte loads per loader lane
-};
-
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Chain pass.  Block = CW compute waves + 4 loader waves.  Each compute wave
-// runs the state chain on one 16-column tile; the loader waves only move
-// data.  Chunks are consumed in groups of K: while the compute waves work
-// through group g from LDS, the loader waves hold group g+1 in registers
-// (global loads issued a whole group earlier) and write it to the K LDS
-// stages at the group boundary.  The compute waves keep no prefetch
-// registers (the state stays in VGPRs) and never wait on global memory.
-// Block b handles (sequence, head) unit b % units and tile group b / units,
-// so when the unit count is a multiple of 8 all tile groups of one unit run
-// on the same XCD (blocks are dealt to the 8 XCDs round-robin) and share
-// that XCD's L2 copy of the records.
-template <int K, int CW>
-__global__ __launch_bounds__(64 * (CW + 4)) void prefill_split_chain(PrefillArgs a,
-                                                                      const uint8_t* __restrict__ ws) {
-  using Stage = ChainStage<CW>;
-  extern __shared__ __align__(16) unsigned char stage_raw[];
+// Chain pass.  One block per (sequence, head, 16-column value tile), four
+// waves with fixed roles, one barrier per chunk step:
+//   wave 0 (state):  the serial recurrence only -- U = U0 + (-M) S0, the decay
+//                    and S += Kr^T U -- with the state in registers for the
+//                    whole sequence; during step c it already reads chunk
+//                    c+1's operands from LDS.  It hands fp16 S0 and U (hi, lo)
+//                    of chunk c to the output wave through LDS.
+//   wave 1 (output): in step c computes O = scale (Qg S0 + Mqk U) for chunk
+//                    c-1 and stores it.
+//   waves 2-3 (loaders): in step c copy chunk c+2's record into the LDS ring
+//                    (from registers loaded three steps earlier) and start
+//                    loading chunk c+5.
+// LDS ring of 4 chunk slots: in step c the state wave reads slot c+1, the
+// output wave slot c-1 and the loaders write slot c+2 (mod 4), all distinct.
+// Loads and stores are buffer operations issued unconditionally (a chunk past
+// the end has an empty range: loads return zeros, stores are dropped), so
+// every path issues the same memory operations and the compiler's wait
+// counts stay exact.  Value columns evolve independently, so tiles never
+// communicate.  Block b handles (sequence, head) unit b % units and tile
+// b / units: with a unit count divisible by 8, all tiles of a unit run on
+// one XCD and share its L2 copy of the records.
+constexpr int kChainStage = kRecStageBytes + 2048;        // staged record + one U0 tile
+constexpr int kChainSlots = 4;
+constexpr int kExchBytes = 6 * 64 * 16;                   // Sb[4], Uh, Ul fragments
+constexpr int kChainLds = kChainSlots * kChainStage + 2 * kExchBytes;
+constexpr int kLoaderVecs = kChainStage / 16 / 128;      // 15 x 16 B per loader lane
+constexpr int kLoadAhead = 3;                             // chunks in loader registers
+static_assert(kChainStage % (16 * 128) == 0, "stage must split evenly over two loader waves");
+
+// Operands of the first products of a chunk step, read one step ahead.
+struct StateFrag {
+  f16x8 am[2][4];   // -M fragments, [mt][kstep]
+  f32x4 u0[2];      // U0 accumulator tiles
+};
+
+__global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
+                                                            const uint8_t* __restrict__ ws) {
+  extern __shared__ __align__(16) unsigned char lds[];
   const int H = a.num_heads;
   const int units = a.num_seqs * H;
-  const int unit = blockIdx.x % units, tgroup = blockIdx.x / units;
+  const int unit = blockIdx.x % units, tile = blockIdx.x / units;
   const int n = unit / H, h = unit % H;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool loader = wave >= CW;
   const int g4 = lane >> 4;
-  const int tile0 = tgroup * CW;              // first 16-column tile of this block
+  const int col = 16 * tile + (lane & 15);
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
   const int nch = (eos - bos + CH - 1) / CH;
   const int64_t slot0 = (int64_t)n + bos / CH;
 
-  if (loader) {
-    const int lt = tid - 64 * CW;                // 0..255
-    u32x4 buf[K][Stage::kRounds];
-    auto issue = [&](u32x4* dst, int c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t r =
-          make_buffer(ws + ((slot0 + c) * H + h) * kRecBytes, (uint32_t)kRecBytes);
+  auto slot = [&](int c) __attribute__((always_inline)) {
+    return lds + (c & (kChainSlots - 1)) * kChainStage;
+  };
+  auto exch = [&](int c) __attribute__((always_inline)) {
+    return lds + kChainSlots * kChainStage + (c & 1) * kExchBytes;
+  };
+
+  if (wave >= 2) {
+    // ------------------------------------------------------------ loaders
+    const int lt = tid - 128;
+    auto load = [&](u32x4* dst, int c) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t r = make_buffer(
+          ws + ((slot0 + c) * H + h) * kRecBytes, c < nch ? (uint32_t)kRecBytes : 0u);
 #pragma unroll
-      for (int m = 0; m < Stage::kRounds; ++m) {
-        const int v = lt + 256 * m;          // 16-byte vector of the stage
-        // staged record part, then this block's U0 tiles; vectors past the
-        // stage read beyond the record and come back as zeros
-        const int off = v < kRecStageBytes / 16
-                            ? v * 16
-                            : kRecOffU0 + tile0 * 2048 + (v - kRecStageBytes / 16) * 16;
-        dst[m] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                       r, (uint32_t)(v < Stage::kBytes / 16 ? off : kRecBytes), 0, 0));
+      for (int m = 0; m < kLoaderVecs; ++m) {
+        const int v = lt + 128 * m;
+        const int off = v < kRecStageBytes / 16 ? v * 16
+                                                : kRecOffU0 + tile * 2048 + (v - kRecStageBytes / 16) * 16;
+        dst[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)off, 0, 0));
       }
     };
+    auto store = [&](const u32x4* src, int c) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < K; ++i)
-      if (i < nch) issue(buf[i], i);
-    for (int c0 = 0; c0 < nch; c0 += K) {
-      __syncthreads();  // the compute waves are done with the previous group
+      for (int m = 0; m < kLoaderVecs; ++m)
+        reinterpret_cast<u32x4*>(slot(c))[lt + 128 * m] = src[m];
+    };
+    u32x4 buf[kLoadAhead][kLoaderVecs];
+    load(buf[0], 0);
+    store(buf[0], 0);
+    load(buf[0], 1);
+    store(buf[0], 1);
 #pragma unroll
-      for (int i = 0; i < K; ++i)
-        if (c0 + i < nch) {
-#pragma unroll
-          for (int m = 0; m < Stage::kRounds; ++m) {
-            const int v = lt + 256 * m;
-            if (Stage::kBytes % 4096 == 0 || v < Stage::kBytes / 16)
-              reinterpret_cast<u32x4*>(stage_raw + i * Stage::kBytes)[v] = buf[i][m];
-          }
-        }
-      __syncthreads();  // the group's stages are complete
-#pragma unroll
-      for (int i = 0; i < K; ++i)
-        if (c0 + K + i < nch) issue(buf[i], c0 + K + i);
+    for (int i = 0; i < kLoadAhead; ++i) load(buf[i], 2 + i);
+    __syncthreads();
+    auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
+      constexpr int I = decltype(I_const)::value;
+      store(buf[I], c + 2);               // loaded three steps ago
+      load(buf[I], c + 2 + kLoadAhead);
+      __syncthreads();
+    };
+    for (int c = 0; c <= nch; c += kLoadAhead) {
+      step(std::integral_constant<int, 0>{}, c);
+      if (c + 1 > nch) break;
+      step(std::integral_constant<int, 1>{}, c + 1);
+      if (c + 2 > nch) break;
+      step(std::integral_constant<int, 2>{}, c + 2);
     }
     return;
   }
 
-  const int ntg = tile0 + wave;               // this wave's 16-column tile
-  const int col = 16 * ntg + (lane & 15);
+  if (wave == 1) {
+    // ------------------------------------------------------------- output
+    __syncthreads();
+    for (int c = 0; c <= nch; ++c) {
+      if (c >= 1) {
+        const int cp = c - 1;
+        const uint8_t* st = slot(cp);
+        const uint8_t* ex = exch(cp);
+        f16x8 aq[2][4], amq[2], sb[4], uh, ul;
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+          for (int p = 0; p < 4; ++p)
+            aq[mt][p] = *reinterpret_cast<const f16x8*>(st + kRecOffQg + ((mt * 4 + p) * 64 + lane) * 16);
+          amq[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffMqk + (mt * 64 + lane) * 16);
+        }
+#pragma unroll
+        for (int p = 0; p < 4; ++p) sb[p] = *reinterpret_cast<const f16x8*>(ex + (p * 64 + lane) * 16);
+        uh = *reinterpret_cast<const f16x8*>(ex + (4 * 64 + lane) * 16);
+        ul = *reinterpret_cast<const f16x8*>(ex + (5 * 64 + lane) * 16);
+        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+        f32x4 O[2] = {z, z};
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) O[mt] = mfma_f16(aq[mt][p], sb[p], O[mt]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          O[mt] = mfma_f16(amq[mt], uh, O[mt]);
+          O[mt] = mfma_f16(amq[mt], ul, O[mt]);
+        }
+        // rows t >= L of a final partial chunk fall outside the range and are dropped
+        const int t0 = bos + CH * cp;
+        const int L = min(CH, eos - t0);
+        const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
+            a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            const int t = 16 * mt + 4 * g4 + i2;
+            buffer_store_u16(f32_to_bf16(a.scale * O[mt][i2]), orsrc,
+                             (uint32_t)((t * H * D + col) * 2));
+          }
+      }
+      __syncthreads();
+    }
+    return;
+  }
+
+  // --------------------------------------------------------------- state
   const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4 S[8];
   if (a.s0) {
@@ -282,45 +351,35 @@ __global__ __launch_bounds__(64 * (CW + 4)) void prefill_split_chain(PrefillArgs
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-
-  for (int c0 = 0; c0 < nch; c0 += K) {
-    __syncthreads();
-    __syncthreads();
+  auto read_frag = [&](StateFrag& F, int c) __attribute__((always_inline)) {
+    const uint8_t* st = slot(c);
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      const int c = c0 + i;
-      if (c >= nch) break;
-      const uint8_t* st = stage_raw + i * Stage::kBytes;
-      // All of the chunk's operands are read from LDS up front (one latency
-      // per chunk rather than one per product); the scheduling barrier keeps
-      // the compiler from sinking the reads back next to their uses.
-      f16x8 am[2][4], aq[2][4], ak[8], amq[2];
-      f32x4 U[2], dv[8];
+    for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          am[mt][p] = *reinterpret_cast<const f16x8*>(
-              st + kRecOffMneg + ((mt * 4 + p) * 64 + lane) * 16);
-        U[mt] = *reinterpret_cast<const f32x4*>(st + kRecStageBytes +
-                                                ((wave * 2 + mt) * 64 + lane) * 16);
-      }
+      for (int p = 0; p < 4; ++p)
+        F.am[mt][p] = *reinterpret_cast<const f16x8*>(st + kRecOffMneg + ((mt * 4 + p) * 64 + lane) * 16);
+      F.u0[mt] = *reinterpret_cast<const f32x4*>(st + kRecStageBytes + (mt * 64 + lane) * 16);
+    }
+  };
+  StateFrag F[2];
+  __syncthreads();
+  read_frag(F[0], 0);
+  auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
+    constexpr int I = decltype(I_const)::value;
+    if (c < nch) {
+      // Kr^T and the decay are first needed after the U products: read them
+      // now, then the next step's -M and U0.
+      const uint8_t* st = slot(c);
+      f16x8 ak[8];
+      f32x4 dv[8];
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         ak[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffKrT + (mt * 64 + lane) * 16);
         dv[mt] = *reinterpret_cast<const f32x4*>(st + kRecOffDec + (16 * mt + 4 * g4) * 4);
       }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-          aq[mt][p] = *reinterpret_cast<const f16x8*>(
-              st + kRecOffQg + ((mt * 4 + p) * 64 + lane) * 16);
-        amq[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffMqk + (mt * 64 + lane) * 16);
-      }
+      read_frag(F[1 - I], c + 1);         // unused past the end
       __builtin_amdgcn_sched_barrier(0);
-
-      // U = U0 + (-M) S0 (S0 as fp16 B operand, K = dk permuted)
+      const StateFrag& f = F[I];
       f16x8 Sb[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -329,15 +388,19 @@ __global__ __launch_bounds__(64 * (CW + 4)) void prefill_split_chain(PrefillArgs
           Sb[p][i2] = static_cast<_Float16>(S[2 * p][i2]);
           Sb[p][4 + i2] = static_cast<_Float16>(S[2 * p + 1][i2]);
         }
+      f32x4 U[2] = {f.u0[0], f.u0[1]};
 #pragma unroll
       for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma_f16(am[mt][p], Sb[p], U[mt]);
-      // the decay does not depend on U: let it fill the MFMA latency
+        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma_f16(f.am[mt][p], Sb[p], U[mt]);
+      // the decay does not depend on U: it fills the MFMA latency
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int i2 = 0; i2 < 4; ++i2) S[mt][i2] *= dv[mt][i2];
+      uint8_t* ex = exch(c);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) *reinterpret_cast<f16x8*>(ex + (p * 64 + lane) * 16) = Sb[p];
       f16x8 Uh, Ul;
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
@@ -348,39 +411,21 @@ __global__ __launch_bounds__(64 * (CW + 4)) void prefill_split_chain(PrefillArgs
           Uh[4 * mt + i2] = hh;
           Ul[4 * mt + i2] = ll;
         }
-      // S = Diag(2^{G_L}) S + Kr^T U
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
         S[mt] = mfma_f16(ak[mt], Uh, S[mt]);
         S[mt] = mfma_f16(ak[mt], Ul, S[mt]);
       }
-      // O = scale (Qg S0 + Mqk U), off the state's critical path.  Rows t >= L
-      // of a final partial chunk fall outside the buffer range and are
-      // dropped, so every lane issues the same stores.
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 O[2] = {z, z};
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma_f16(aq[mt][p], Sb[p], O[mt]);
-      const int t0 = bos + CH * c;
-      const int L = min(CH, eos - t0);
-      const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
-          a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        O[mt] = mfma_f16(amq[mt], Uh, O[mt]);
-        O[mt] = mfma_f16(amq[mt], Ul, O[mt]);
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          const int t = 16 * mt + 4 * g4 + i2;
-          buffer_store_u16(f32_to_bf16(a.scale * O[mt][i2]), orsrc,
-                           (uint32_t)((t * H * D + col) * 2));
-        }
-      }
+      *reinterpret_cast<f16x8*>(ex + (4 * 64 + lane) * 16) = Uh;
+      *reinterpret_cast<f16x8*>(ex + (5 * 64 + lane) * 16) = Ul;
     }
+    __syncthreads();
+  };
+  for (int c = 0; c <= nch; c += 2) {
+    step(std::integral_constant<int, 0>{}, c);
+    if (c + 1 > nch) break;
+    step(std::integral_constant<int, 1>{}, c + 1);
   }
-
   if (a.s1) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -406,18 +451,16 @@ hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int K, int CW>
 hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) {
-  constexpr size_t bytes = (size_t)K * ChainStage<CW>::kBytes;
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_chain<K, CW>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_chain),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kChainLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * (8 / CW);
-  prefill_split_chain<K, CW><<<dim3((unsigned)blocks), 64 * (CW + 4), bytes, s>>>(a, ws);
+  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * 8;
+  prefill_split_chain<<<dim3((unsigned)blocks), 256, kChainLds, s>>>(a, ws);
   return hipGetLastError();
 }
 
@@ -425,13 +468,12 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
 
 hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 void* workspace, hipStream_t s) {
-  const int cw = dv_split == 8 ? 1 : 4;   // compute waves (16-column tiles) per chain block
-  if (dv_split != 8 && dv_split != 2) return hipErrorInvalidValue;
+  if (dv_split != 8) return hipErrorInvalidValue;   // one 16-column tile per chain block
   if (a.num_seqs <= 0) return hipSuccess;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   hipError_t e = anchor_mode == 0 ? launch_prep<0>(a, ws, s) : launch_prep<1>(a, ws, s);
   if (e != hipSuccess) return e;
-  return cw == 1 ? launch_chain<4, 1>(a, ws, s) : launch_chain<4, 4>(a, ws, s);
+  return launch_chain(a, ws, s);
 }
 
 }  // namespace kda
