@@ -8,23 +8,23 @@
 // chunk-local preparation is parallel, state evolution is serial) across
 // kernels instead of across warps:
 //
-//   pass 1 (prefill_split_prep): one block per (chunk, head), all chunks of
+//   pass 1 (prefill_split_prep): one wave per (chunk, head), all chunks of
 //     all sequences at once.  Steps 1-3 of section 2 (gate prefix, anchored
 //     Mqk/Akk, the 32x32 inverse T) and then everything that depends only on
 //     the chunk:
 //        U0 = T Diag(b) V          (what U would be from a zero state)
 //        M  = T Diag(b) Kg         (how U depends on the incoming state)
 //     so that U = U0 - M S0.  Results go to a workspace record per
-//     (chunk, head), laid out in MFMA-fragment order.
-//   pass 2 (prefill_split_chain): one block per (sequence, head, 64 value
-//     columns); each wave owns 16 columns and walks the chunks in order:
+//     (chunk, head), laid out in MFMA-fragment order and written straight
+//     from registers.
+//   pass 2 (prefill_split_chain): one block per (sequence, head, 16 value
+//     columns) walks the chunks in order:
 //        U  = U0 + (-M) S0                    (fp16 MFMA, FP32 accumulate)
 //        S1 = Diag(2^{G_L}) S0 + Kr^T U       (U as hi + lo fp16)
 //        O  = scale (Qg S0 + Mqk U)
 //     i.e. the note's fused [S | O] update, with the state resident in the
-//     accumulators.  Chunk records are prefetched several chunks ahead into
-//     registers and staged through a double-buffered LDS area shared by the
-//     four waves.
+//     accumulators of one wave while other waves compute O and stream the
+//     records through an LDS ring.
 //
 // Workspace record of (chunk slot s, head h) at ((s * H + h) * kRecBytes):
 //   [0, 8192)        -M    fp16 A fragments [mt 2][kstep 4][lane 64][8]
@@ -32,8 +32,8 @@
 //   [16384, 24576)   Kr^T  fp16 A fragments [mt 8][lane 64][8]
 //   [24576, 26624)   Mqk   fp16 A fragments [mt 2][lane 64][8]
 //   [26624, 27136)   2^{G_L} fp32 [128]
-//   [27136, 28672)   zero padding (the staged part is 7 x 4 KiB: one 16-byte
-//                    load per thread per 4 KiB, no tail)
+//   [27136, 28672)   padding, never written or used (the staged part is
+//                    7 x 4 KiB: one 16-byte load per thread per 4 KiB)
 //   [28672, 45056)   U0    fp32 accumulator tiles [nt 8][mt 2][lane 64][4]
 // Fragment K indices use the permuted slot order of chunk_common.h.  The chunk
 // slot of chunk c of sequence n is n + floor(cu[n] / 32) + c, unique and
@@ -63,30 +63,50 @@ namespace {
 
 using namespace chunk;
 
-struct PrepOut {
-  PrepSmem<D> p;
-  _Float16 frag[kRecStageBytes / 2];  // record bytes [0, kRecStageBytes), staged
-  float bkgT[D][CH + 4];              // b_t k_t 2^{G_t}, transposed [channel][token]
-};
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// fp16 element index (within a record) of A-fragment entry (row, k) of a
-// fragment set with 32-long K blocks: [row/16][k/32][lane][8].
-__device__ __forceinline__ int frag_rowk(int row, int k, int ksteps) {
-  const int s = kslot(k & 31);
-  const int L = (row & 15) + ((s >> 3) << 4);
-  return ((((row >> 4) * ksteps + (k >> 5)) * 64 + L) << 3) + (s & 7);
+// Inclusive prefix sum over the 16 lanes of each DPP row (lane i of a row
+// ends with the sum of lanes 0..i of that row).
+__device__ __forceinline__ float row_scan16(float x) {
+  auto shr = [](float v, auto ctrl) __attribute__((always_inline)) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(
+        0, __builtin_bit_cast(int, v), decltype(ctrl)::value, 0xF, 0xF, true));
+  };
+  x += shr(x, std::integral_constant<int, 0x111>{});   // row_shr:1
+  x += shr(x, std::integral_constant<int, 0x112>{});   // row_shr:2
+  x += shr(x, std::integral_constant<int, 0x114>{});   // row_shr:4
+  x += shr(x, std::integral_constant<int, 0x118>{});   // row_shr:8
+  return x;
 }
 
+__device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
+  return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]);
+}
+
+// Preparation pass: one wave per (chunk slot, head), no block barrier beyond
+// the wave's own, LDS only for the 32x32 triangular inverse.
+//
+// Lane (g4 = lane/16, l16 = lane%16) owns tokens l16 and l16+16 of the chunk
+// and, for each 32-channel K step p, the channels whose fragment K-slots are
+// 8g4..8g4+7 (32p + 4g4 + {0..3} and 32p + 16 + 4g4 + {0..3}).  In that layout
+//  - the gate prefix over tokens is a scan across the 16 lanes of a row;
+//  - q 2^G is already the Qg A fragment of the record;
+//  - the pairwise products are taken transposed (column side as the A
+//    operand), so the accumulators of Mqk^T are the Mqk A fragments;
+//  - Kr, b Kg and V, whose products contract over tokens, are transposed by
+//    an MFMA against a one-hot matrix (exact: one nonzero product per output);
+//    the transposed b Kg then gives M^T = (b Kg)^T T^T whose accumulators are
+//    the -M A fragments.
 template <int MODE>
-__global__ __launch_bounds__(256) void prefill_split_prep(PrefillArgs a, float exp2C,
-                                                           uint8_t* __restrict__ ws) {
-  extern __shared__ __align__(16) unsigned char smem_raw[];
-  PrepOut& sm = *reinterpret_cast<PrepOut*>(smem_raw);
-  PrepSmem<D>& ps = sm.p;
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_split_prep(PrefillArgs a, float exp2C,
+                                                          uint8_t* __restrict__ ws) {
+  __shared__ __align__(16) float Al[CH][36];   // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
+  __shared__ __align__(16) float Tl[CH][36];   // (I + A)^{-1}, lower triangle
+  __shared__ __align__(16) float bl[CH];
   const int H = a.num_heads, N = a.num_seqs, T = a.total_tokens;
   const int slot = blockIdx.x, h = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int l16 = lane & 15, g4 = lane >> 4;
+  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   const float C = a.anchor_log2;
 
   // Which (sequence, chunk) owns this slot: the largest n with
@@ -105,88 +125,329 @@ __global__ __launch_bounds__(256) void prefill_split_prep(PrefillArgs a, float e
   const int L = min(CH, eos - t0);
   uint8_t* rec = ws + ((int64_t)slot * H + h) * kRecBytes;
 
-  load_chunk(ps, a, t0, L, h, 0, tid, 256);
-  __syncthreads();
-  gate_prefix<MODE>(ps, C, tid);
-  __syncthreads();
-  pair_products<MODE>(ps, a, C, exp2C, wave, lane,
-                      [&](int t, int c0, const float* kv, const float* qv, const float* P,
-                          const float* R) {
-                        const float bt = ps.beta[t];
+  // Rows t >= L of a final partial chunk lie outside these ranges and read as zero.
+  const int64_t base = ((int64_t)t0 * H + h) * D;
+  const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
+  const __amdgpu_buffer_rsrc_t rq = make_buffer(a.q + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_buffer(a.k + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_buffer(a.g + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rb =
+      make_buffer(a.beta + (int64_t)t0 * H + h, (uint32_t)(((L - 1) * H + 1) * 2));
+  const uint32_t tok_bytes = (uint32_t)H * D * 2;
+  const float beta[2] = {
+      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0)),
+      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((l16 + 16) * H * 2), 0, 0))};
+  auto load8 = [&](__amdgpu_buffer_rsrc_t r, int hf, int p) __attribute__((always_inline)) {
+    const uint32_t off = (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 4 * g4) * 2;
+    const u32x2 x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+    const u32x2 x1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 32, 0, 0));
+    return u32x4{x0[0], x0[1], x1[0], x1[1]};
+  };
+
+  // One-hot transposers.  E[e] selects, for output column l16, the K-slot of
+  // channel 16e + l16 of a 32-channel step in K-slot order; Ev[e] the same
+  // for natural column order (value rows).
+  f16x8 E[2];
+  bf16x8 Ev[2];
 #pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                          const int ch = c0 + j;
-                          sm.frag[kRecOffQg / 2 + frag_rowk(t, ch, 4)] =
-                              static_cast<_Float16>(qv[j] * P[j]);
-                          sm.frag[kRecOffKrT / 2 + frag_rowk(ch, t, 1)] =
-                              static_cast<_Float16>(kv[j] * R[j]);
-                          sm.bkgT[ch][t] = bt * (kv[j] * P[j]);
-                        }
-                      });
-  __syncthreads();
-  reduce_pairs(ps, tid, [&](int r, int s, float m) {
-    sm.frag[kRecOffMqk / 2 + frag_rowk(r, s, 1)] = static_cast<_Float16>(m);
-  });
-  __syncthreads();
-  invert_unit_lower(ps, tid);
+  for (int e = 0; e < 2; ++e)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      E[e][j] = (_Float16)((j == l16 - 4 * g4 + 4 * e && l16 - 4 * g4 >= 0 && l16 - 4 * g4 < 4) ? 1.f : 0.f);
+      Ev[e][j] = (__bf16)(j == 16 * e + l16 - 8 * g4 ? 1.f : 0.f);
+    }
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+
+  f32x4 acc[6] = {z, z, z, z, z, z};   // Mqk^T tiles (0,0) (0,1) (1,1), Akk^T tiles likewise
+  // (b Kg)^T A fragments per 16-channel tile (hi, lo) wait for T in the
+  // record's -M and U0 areas, which are written last: each lane reads back
+  // only what it wrote.
+  uint8_t* const xh_park = rec + kRecOffMneg;
+  uint8_t* const xl_park = rec + kRecOffU0;
+
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    u32x4 qw[2], kw[2], gw[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      qw[hf] = load8(rq, hf, p);
+      kw[hf] = load8(rk, hf, p);
+      gw[hf] = load8(rg, hf, p);
+    }
+    // gate prefix (log2 domain) of both halves, and G at tokens 15 and 31
+    float G[2][8], G15[8], GL[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float s0 = row_scan16(bf16_elem(gw[0], j));
+      const float b0 = __shfl(s0, 15, 16);
+      const float s1 = row_scan16(bf16_elem(gw[1], j)) + b0;
+      G[0][j] = s0 * kLog2e;
+      G[1][j] = s1 * kLog2e;
+      G15[j] = b0 * kLog2e;
+      GL[j] = __shfl(s1, 15, 16) * kLog2e;
+    }
+    if (l16 == 0) {
+      f32x4 d0, d1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        d0[i] = fast_exp2(GL[i]);
+        d1[i] = fast_exp2(GL[4 + i]);
+      }
+      *reinterpret_cast<f32x4*>(rec + kRecOffDec + (32 * p + 4 * g4) * 4) = d0;
+      *reinterpret_cast<f32x4*>(rec + kRecOffDec + (32 * p + 16 + 4 * g4) * 4) = d1;
+    }
+    float EL[8];
+    if (MODE == 0) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) EL[j] = fast_exp2(GL[j] - C);
+    }
+    // anchored operands: row side (qa, ka), column side (kb); "o" = off-diagonal tile
+    bf16x8 qah[2], qal[2], kah[2], kal[2], kbh[2], kbl[2];
+    bf16x8 qoh, qol, koh, kol, boh, bol;
+    f16x8 Qg[2], Kr[2], Bh[2], Bl[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float qf = bf16_elem(qw[hf], j), kf = bf16_elem(kw[hf], j);
+        const float Gv = G[hf][j];
+        float ep, em, P, R, fo = 0.f;
+        if (MODE == 0) {
+          ep = fast_exp2(Gv - C);                 // 2^{G-C}, |exponent| <= 16|b|
+          em = fast_exp2(C - Gv);
+          P = ep * exp2C;                         // 2^G
+          R = EL[j] * em;                         // 2^{G_L - G}
+        } else {
+          const float Ch = (hf ? G15[j] : 0.f) + a.half_anchor_log2;
+          ep = fast_exp2(Gv - Ch);
+          em = fast_exp2(Ch - Gv);
+          fo = hf ? fast_exp2(Gv - G15[j]) : fast_exp2(G15[j] - Gv);   // both <= 1
+          P = fast_exp2(Gv);
+          R = fast_exp2(GL[j] - Gv);
+        }
+        __bf16 h1, l1, h2, l2, h3, l3;
+        split_bf16(qf * ep, h1, l1);
+        split_bf16(kf * ep, h2, l2);
+        split_bf16(kf * em, h3, l3);
+        qah[hf][j] = h1; qal[hf][j] = l1;
+        kah[hf][j] = h2; kal[hf][j] = l2;
+        kbh[hf][j] = h3; kbl[hf][j] = l3;
+        if (MODE == 1) {
+          if (hf == 1) {
+            split_bf16(qf * fo, h1, l1);
+            split_bf16(kf * fo, h2, l2);
+            qoh[j] = h1; qol[j] = l1; koh[j] = h2; kol[j] = l2;
+          } else {
+            split_bf16(kf * fo, h3, l3);
+            boh[j] = h3; bol[j] = l3;
+          }
+        }
+        Qg[hf][j] = static_cast<_Float16>(qf * P);
+        Kr[hf][j] = static_cast<_Float16>(kf * R);
+        _Float16 xh, xl;
+        split_f16(beta[hf] * (kf * P), xh, xl);
+        Bh[hf][j] = xh;
+        Bl[hf][j] = xl;
+      }
+    if (MODE == 0) {
+      // one anchor for the whole chunk: the off-diagonal tile reuses the diagonal operands
+      qoh = qah[1]; qol = qal[1]; koh = kah[1]; kol = kal[1]; boh = kbh[0]; bol = kbl[0];
+    }
+    // transposed pairwise products, split K over the four steps
+    acc[0] = mfma_bf16(kbh[0], qah[0], acc[0]);
+    acc[0] = mfma_bf16(kbh[0], qal[0], acc[0]);
+    acc[0] = mfma_bf16(kbl[0], qah[0], acc[0]);
+    acc[1] = mfma_bf16(boh, qoh, acc[1]);
+    acc[1] = mfma_bf16(boh, qol, acc[1]);
+    acc[1] = mfma_bf16(bol, qoh, acc[1]);
+    acc[2] = mfma_bf16(kbh[1], qah[1], acc[2]);
+    acc[2] = mfma_bf16(kbh[1], qal[1], acc[2]);
+    acc[2] = mfma_bf16(kbl[1], qah[1], acc[2]);
+    acc[3] = mfma_bf16(kbh[0], kah[0], acc[3]);
+    acc[3] = mfma_bf16(kbh[0], kal[0], acc[3]);
+    acc[3] = mfma_bf16(kbl[0], kah[0], acc[3]);
+    acc[4] = mfma_bf16(boh, koh, acc[4]);
+    acc[4] = mfma_bf16(boh, kol, acc[4]);
+    acc[4] = mfma_bf16(bol, koh, acc[4]);
+    acc[5] = mfma_bf16(kbh[1], kah[1], acc[5]);
+    acc[5] = mfma_bf16(kbh[1], kal[1], acc[5]);
+    acc[5] = mfma_bf16(kbl[1], kah[1], acc[5]);
+    // Qg fragments go out as they are
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      *reinterpret_cast<f16x8*>(rec + kRecOffQg + ((hf * 4 + p) * 64 + lane) * 16) = Qg[hf];
+    // transposes of Kr (stored) and b Kg (kept for M)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x4 r0 = mfma_f16(Kr[0], E[e], z), r1 = mfma_f16(Kr[1], E[e], z);
+      const f32x4 h0 = mfma_f16(Bh[0], E[e], z), h1 = mfma_f16(Bh[1], E[e], z);
+      const f32x4 w0 = mfma_f16(Bl[0], E[e], z), w1 = mfma_f16(Bl[1], E[e], z);
+      f16x8 kt, xh, xl;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        kt[i] = (_Float16)r0[i];  kt[4 + i] = (_Float16)r1[i];
+        xh[i] = (_Float16)h0[i];  xh[4 + i] = (_Float16)h1[i];
+        xl[i] = (_Float16)w0[i];  xl[4 + i] = (_Float16)w1[i];
+      }
+      *reinterpret_cast<f16x8*>(rec + kRecOffKrT + ((2 * p + e) * 64 + lane) * 16) = kt;
+      *reinterpret_cast<f16x8*>(xh_park + ((2 * p + e) * 64 + lane) * 16) = xh;
+      *reinterpret_cast<f16x8*>(xl_park + ((2 * p + e) * 64 + lane) * 16) = xl;
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Mqk fragments straight from the Mqk^T accumulators (rows s = 16a + 4g4 + i,
+  // column r = 16b + l16), causal mask by select; A = Diag(b) stril(Akk) to LDS.
+  {
+    f16x8 m0, m1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = 4 * g4 + i;
+      m0[i] = (_Float16)(s <= l16 ? acc[0][i] : 0.f);
+      m0[4 + i] = (_Float16)0.f;
+      m1[i] = (_Float16)acc[1][i];
+      m1[4 + i] = (_Float16)(s <= l16 ? acc[2][i] : 0.f);
+      Al[l16][s] = s < l16 ? beta[0] * acc[3][i] : 0.f;
+      Al[16 + l16][s] = beta[1] * acc[4][i];
+      Al[16 + l16][16 + s] = s < l16 ? beta[1] * acc[5][i] : 0.f;
+    }
+    *reinterpret_cast<f16x8*>(rec + kRecOffMqk + lane * 16) = m0;
+    *reinterpret_cast<f16x8*>(rec + kRecOffMqk + (64 + lane) * 16) = m1;
+    if (g4 == 0) {
+      bl[l16] = beta[0];
+      bl[16 + l16] = beta[1];
+    }
+  }
+  // value rows for U0, consumed after the inverse
+  u32x4 vw[4][2];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf)
+      vw[p][hf] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+          rv, (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 8 * g4) * 2, 0, 0));
   __syncthreads();
 
-  // U0 = T Diag(b) V and M = T Diag(b) Kg: wave w computes value / key
-  // columns 32w..32w+31 for all 32 tokens, with hi + lo fp16 operands on both
-  // sides (three products), so both are accurate to FP32 level.
+  // T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane m
+  // of each half-wave owns column m), then T21 = -T22 (A21 T11).
+  if (lane < 32) {
+    const int b0 = 16 * (lane >> 4), m = lane & 15;
+    float x[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j)
+#pragma unroll
+      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-Al[b0 + i][b0 + j], x[j], x[i]);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) Tl[b0 + i][b0 + m] = x[i];
+  }
+  __syncthreads();
   {
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f16x8 th[2], tl[2];
+    const int m = l16;
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int j = 0; j < 16; ++j) {
+      const float t = Tl[j][m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc4[i] = fmaf(Al[16 + 4 * g4 + i][j], t, acc4[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Al[4 * g4 + i][16 + m] = acc4[i];
+  }
+  __syncthreads();
+  {
+    const int m = l16;
+    float acc4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const float xv = Al[j][16 + m];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc4[i] = fmaf(Tl[16 + 4 * g4 + i][16 + j], xv, acc4[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Tl[16 + 4 * g4 + i][m] = -acc4[i];
+  }
+  __syncthreads();
+
+  // T and T Diag(b) as fp16 hi / lo A fragments (row t = 16mt + l16, K-slot
+  // 8g4 + j <-> token 4g4 + j or 16 + 4g4 + j - 4); T12 = 0.
+  f16x8 th[2], tl[2], tbh[2], tbl[2];
+  {
+    const f32x4 bb0 = *reinterpret_cast<const f32x4*>(&bl[4 * g4]);
+    const f32x4 bb1 = *reinterpret_cast<const f32x4*>(&bl[16 + 4 * g4]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+      const f32x4 ta = *reinterpret_cast<const f32x4*>(&Tl[16 * mt + l16][4 * g4]);
+      const f32x4 tb = mt ? *reinterpret_cast<const f32x4*>(&Tl[16 + l16][16 + 4 * g4]) : z;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
+        const float tv = j < 4 ? ta[j] : tb[j - 4];
+        const float bv = j < 4 ? bb0[j] : bb1[j - 4];
         _Float16 hh, ll;
-        split_f16(ps.Tf[16 * mt + l16][8 * g4 + j], hh, ll);
-        th[mt][j] = hh;
-        tl[mt][j] = ll;
-      }
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      const int nt = 2 * wave + q;
-      const int col = 16 * nt + l16;
-      f16x8 vh, vl, kh, kl;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int t = 8 * g4 + j;
-        _Float16 hh, ll;
-        split_f16(ps.beta[t] * bf16_to_f32(ps.vraw[t][col]), hh, ll);
-        vh[j] = hh;
-        vl[j] = ll;
-        split_f16(sm.bkgT[col][t], hh, ll);
-        kh[j] = hh;
-        kl[j] = ll;
-      }
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        f32x4 u = mfma_f16(th[mt], vh, z);
-        u = mfma_f16(th[mt], vl, u);
-        u = mfma_f16(tl[mt], vh, u);
-        f32x4 m = mfma_f16(th[mt], kh, z);
-        m = mfma_f16(th[mt], kl, m);
-        m = mfma_f16(tl[mt], kh, m);
-        *reinterpret_cast<f32x4*>(rec + kRecOffU0 + ((nt * 2 + mt) * 64 + lane) * 16) = u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          sm.frag[kRecOffMneg / 2 + frag_rowk(16 * mt + 4 * g4 + i, col, 4)] =
-              static_cast<_Float16>(-m[i]);
+        split_f16(tv, hh, ll);
+        th[mt][j] = hh; tl[mt][j] = ll;
+        split_f16(tv * bv, hh, ll);
+        tbh[mt][j] = hh; tbl[mt][j] = ll;
       }
     }
   }
-  if (tid < D) reinterpret_cast<float*>(&sm.frag[kRecOffDec / 2])[tid] = ps.dec[tid];
-  for (int e = (kRecOffDec + 4 * D) / 16 + tid; e < kRecStageBytes / 16; e += 256)
-    reinterpret_cast<uint4*>(sm.frag)[e] = make_uint4(0, 0, 0, 0);
-  __syncthreads();
-  for (int e = tid; e < kRecStageBytes / 16; e += 256)
-    reinterpret_cast<uint4*>(rec)[e] = reinterpret_cast<const uint4*>(sm.frag)[e];
+
+  // Read the parked (b Kg)^T fragments back before their areas are overwritten
+  // (all earlier stores have completed first).
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  f16x8 Xh[8], Xl[8];
+#pragma unroll
+  for (int mc = 0; mc < 8; ++mc) {
+    Xh[mc] = *reinterpret_cast<const f16x8*>(xh_park + (mc * 64 + lane) * 16);
+    Xl[mc] = *reinterpret_cast<const f16x8*>(xl_park + (mc * 64 + lane) * 16);
+  }
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the reads complete before any store below
+  __builtin_amdgcn_sched_barrier(0);
+
+  // U0 = T Diag(b) V per 16-column tile: V transposed by the one-hot product.
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+      const f32x4 v0 = mfma_bf16(__builtin_bit_cast(bf16x8, vw[p][0]), Ev[e], z);
+      const f32x4 v1 = mfma_bf16(__builtin_bit_cast(bf16x8, vw[p][1]), Ev[e], z);
+      f16x8 vt;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vt[i] = (_Float16)v0[i];
+        vt[4 + i] = (_Float16)v1[i];
+      }
+      const int nt = 2 * p + e;
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        f32x4 u = mfma_f16(tbh[mt], vt, z);
+        u = mfma_f16(tbl[mt], vt, u);
+        *reinterpret_cast<f32x4*>(rec + kRecOffU0 + ((nt * 2 + mt) * 64 + lane) * 16) = u;
+      }
+    }
+
+  // M^T = (b Kg)^T T^T: accumulator rows are channels 16mc + 4g4 + i, column
+  // token 16tt + l16, i.e. the -M A fragments of K step mc/2.
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f16x8 mf;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int mc = 2 * p + e;
+        f32x4 m = mfma_f16(Xh[mc], th[tt], z);
+        m = mfma_f16(Xh[mc], tl[tt], m);
+        m = mfma_f16(Xl[mc], th[tt], m);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mf[4 * e + i] = (_Float16)(-m[i]);
+      }
+      *reinterpret_cast<f16x8*>(rec + kRecOffMneg + ((tt * 4 + p) * 64 + lane) * 16) = mf;
+    }
 }
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Chain pass.  One block per (sequence, head, 16-column value tile), four
 // waves with fixed roles, one barrier per chunk step:
@@ -437,17 +698,9 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
 
 template <int MODE>
 hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
-  constexpr size_t bytes = sizeof(PrepOut);
-  static bool attr_set = false;   // idempotent; a race only repeats the call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_prep<MODE>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e != hipSuccess) return e;
-    attr_set = true;
-  }
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
   const int64_t slots = (int64_t)a.num_seqs + a.total_tokens / CH + 1;
-  prefill_split_prep<MODE><<<dim3((unsigned)slots, a.num_heads), 256, bytes, s>>>(a, exp2C, ws);
+  prefill_split_prep<MODE><<<dim3((unsigned)slots, a.num_heads), 64, 0, s>>>(a, exp2C, ws);
   return hipGetLastError();
 }
 
