@@ -478,10 +478,14 @@ constexpr int kLoaderVecs = kChainStage / 16 / 128;      // 15 x 16 B per loader
 constexpr int kLoadAhead = 3;                             // chunks in loader registers
 static_assert(kChainStage % (16 * 128) == 0, "stage must split evenly over two loader waves");
 
-// Operands of the first products of a chunk step, read one step ahead.
-struct StateFrag {
+// Operands of one chunk step of the state wave.
+struct MUOps {
   f16x8 am[2][4];   // -M fragments, [mt][kstep]
   f32x4 u0[2];      // U0 accumulator tiles
+};
+struct KDOps {
+  f16x8 ak[8];      // Kr^T fragments
+  f32x4 dv[8];      // 2^{G_L} of the lane's state rows
 };
 
 __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
@@ -612,7 +616,11 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  auto read_frag = [&](StateFrag& F, int c) __attribute__((always_inline)) {
+  // All operands of a chunk step come from its ring slot, read early enough
+  // that a step never waits on LDS: Kr^T and the decay of chunk c+1 at the
+  // start of step c (double-buffered), -M and U0 of chunk c+1 as soon as the
+  // U products of step c have consumed those of chunk c.
+  auto read_mu = [&](MUOps& F, int c) __attribute__((always_inline)) {
     const uint8_t* st = slot(c);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
@@ -622,25 +630,24 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
       F.u0[mt] = *reinterpret_cast<const f32x4*>(st + kRecStageBytes + (mt * 64 + lane) * 16);
     }
   };
-  StateFrag F[2];
+  auto read_kd = [&](KDOps& K, int c) __attribute__((always_inline)) {
+    const uint8_t* st = slot(c);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+      K.ak[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffKrT + (mt * 64 + lane) * 16);
+      K.dv[mt] = *reinterpret_cast<const f32x4*>(st + kRecOffDec + (16 * mt + 4 * g4) * 4);
+    }
+  };
+  MUOps F;
+  KDOps K[2];
   __syncthreads();
-  read_frag(F[0], 0);
+  read_mu(F, 0);
+  read_kd(K[0], 0);
   auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
     constexpr int I = decltype(I_const)::value;
     if (c < nch) {
-      // Kr^T and the decay are first needed after the U products: read them
-      // now, then the next step's -M and U0.
-      const uint8_t* st = slot(c);
-      f16x8 ak[8];
-      f32x4 dv[8];
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        ak[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffKrT + (mt * 64 + lane) * 16);
-        dv[mt] = *reinterpret_cast<const f32x4*>(st + kRecOffDec + (16 * mt + 4 * g4) * 4);
-      }
-      read_frag(F[1 - I], c + 1);         // unused past the end
-      __builtin_amdgcn_sched_barrier(0);
-      const StateFrag& f = F[I];
+      read_kd(K[1 - I], c + 1);           // unused past the end
+      const KDOps& k = K[I];
       f16x8 Sb[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p)
@@ -649,16 +656,17 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
           Sb[p][i2] = static_cast<_Float16>(S[2 * p][i2]);
           Sb[p][4 + i2] = static_cast<_Float16>(S[2 * p + 1][i2]);
         }
-      f32x4 U[2] = {f.u0[0], f.u0[1]};
+      f32x4 U[2] = {F.u0[0], F.u0[1]};
 #pragma unroll
       for (int p = 0; p < 4; ++p)
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma_f16(f.am[mt][p], Sb[p], U[mt]);
+        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma_f16(F.am[mt][p], Sb[p], U[mt]);
+      read_mu(F, c + 1);                  // unused past the end
       // the decay does not depend on U: it fills the MFMA latency
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) S[mt][i2] *= dv[mt][i2];
+        for (int i2 = 0; i2 < 4; ++i2) S[mt][i2] *= k.dv[mt][i2];
       uint8_t* ex = exch(c);
 #pragma unroll
       for (int p = 0; p < 4; ++p) *reinterpret_cast<f16x8*>(ex + (p * 64 + lane) * 16) = Sb[p];
@@ -674,8 +682,8 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
         }
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        S[mt] = mfma_f16(ak[mt], Uh, S[mt]);
-        S[mt] = mfma_f16(ak[mt], Ul, S[mt]);
+        S[mt] = mfma_f16(k.ak[mt], Uh, S[mt]);
+        S[mt] = mfma_f16(k.ak[mt], Ul, S[mt]);
       }
       *reinterpret_cast<f16x8*>(ex + (4 * 64 + lane) * 16) = Uh;
       *reinterpret_cast<f16x8*>(ex + (5 * 64 + lane) * 16) = Ul;
