@@ -2,14 +2,17 @@
 """Benchmark of the KDA hot path on one MI355X.
 
 One step = one pass of the whole path on resident synthetic inputs:
-  1. kda_prefill on the small-batch*heads workload: 1 sequence x T=8192
+  1. the prefill of the small-batch*heads workload: 1 sequence x T=8192
      tokens, H=8 heads, dk=dv=128, bf16 q/k/v/g/beta, FP32 initial state,
-     lower_bound = -5;
+     lower_bound = -5.  With the two-pass route (the one chosen for this
+     shape) it runs as kda_prefill_prepare + kda_prefill_chain, the same two
+     kernels kda_prefill launches, so that each kernel can be timed;
   2. kda_decode at H=8 over a 4096-slot FP32 pool with 4096 scattered rows.
-Each leg is bracketed by HIP events on the stream it runs on.  ``value`` is
-the prefill leg's tokens*heads/s (the headline metric); ``roofline`` is the
-prefill kernel against the bf16 MFMA peak; ``decode`` carries the decode
-kernel's achieved HBM bandwidth against 8 TB/s.  ``cpu_baseline`` times the
+Every kernel is bracketed by HIP events on the stream it runs on.  ``value``
+is the prefill's tokens*heads/s (the headline metric); ``roofline`` is the
+dominant prefill kernel (by measured time) against its roofline; ``decode``
+carries the decode kernel's HBM bandwidth against 8 TB/s and against a
+device-to-device copy timed in the same run.  ``cpu_baseline`` times the
 FP64 oracle (test infrastructure) on the same prefill workload on the host.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -29,7 +32,13 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense bf16/fp16 MFMA
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PREFILL_FLOP_PER_TOKHEAD = 131072   # 8 * dk * dv: Akk, Mqk, [Kg;Qg]S, T V', [Kr^T;Mqk]U
+# Split of those FLOPs between the two kernels of the two-pass route:
+# preparation = Akk + Mqk + T V' (3 x 32 x 128 MAC per token*head),
+# chain = [Kg;Qg] S (64 x 128 x 128 / 32) + the fused [S;O] update (160 x 128).
+PREP_FLOP_PER_TOKHEAD = 24576
+CHAIN_FLOP_PER_TOKHEAD = 106496
 PREFILL_BYTES_PER_TOKHEAD = 1282    # q,k,v,g (4 x 256 B) + beta (2 B) + o (256 B)
+PREP_BYTES_PER_TOKHEAD = 1026       # the preparation pass reads q,k,v,g,beta
 STATE_BYTES = 128 * 128 * 4
 DECODE_IO_BYTES_PER_ITEM = 1282
 
@@ -60,27 +69,56 @@ def stored_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def cpu_baseline():
+def stats(ms):
+    a = sorted(ms)
+    pick = lambda f: a[min(len(a) - 1, max(0, int(round(f * (len(a) - 1)))))]
+    return {"median_ms": pick(0.5), "p10_ms": pick(0.1), "p90_ms": pick(0.9),
+            "mean_ms": sum(a) / len(a)}
+
+
+def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
+    """Device-to-device copy GB/s (read + write) on the same GPU and stream."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) / reps * 1e-3
+    del src, dst
+    return 2 * nbytes / t / 1e9
+
+
+def cpu_baseline(min_seconds=10.0, max_runs=50):
+    """The FP64 oracle on the whole prefill workload, repeated until about
+    `min_seconds` of wall time have passed; reports the mean rate."""
     import oracle
     from kimi_delta_attention_prefill_amd.inputs import prefill_config
 
     c = prefill_config(1)
     threads = min(oracle.default_threads(), c.num_seqs * c.num_heads)
-    t0 = time.perf_counter()
-    oracle.prefill(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.scale, c.initial_state,
-                   threads=threads)
-    dt = time.perf_counter() - t0
+    runs, t0 = 0, time.perf_counter()
+    while runs < max_runs and (runs == 0 or time.perf_counter() - t0 < min_seconds):
+        oracle.prefill(c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens, c.scale, c.initial_state,
+                       threads=threads)
+        runs += 1
+    dt = (time.perf_counter() - t0) / runs
     return {"value": c.total_tokens * c.num_heads / dt, "unit": "tokens*heads/s",
             "cores": threads, "kind": "oracle",
             "sample": (f"whole prefill workload ({c.num_seqs} x {c.total_tokens} tokens x "
-                       f"{c.num_heads} heads), FP64 token recurrence, {dt:.2f} s wall")}
+                       f"{c.num_heads} heads), FP64 token recurrence, {runs} runs, "
+                       f"{dt:.3f} s wall each on {threads} threads")}
 
 
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-rows", type=int, default=4096)
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
@@ -116,28 +154,38 @@ def main():
              slots=to(dc.slots), pool=to(dc.pool))
     d_out = torch.empty_like(D["q"])
     plan = kda.plan(pc.num_seqs, pc.total_tokens, pc.num_heads, pc.lower_bound, 0, route)
+    two_pass = plan.route == kda.ROUTE_SPLIT
     ws_bytes = kda.workspace_size(pc.num_seqs, pc.total_tokens, pc.num_heads)
+    if two_pass:
+        ws_bytes = kda.records_size(pc.num_seqs, pc.total_tokens, pc.num_heads)
     p_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
     def step(ev=None):
-        if ev is not None:
-            ev[0].record(stream)
-        kda.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], scale=pc.scale,
-                    lower_bound=pc.lower_bound, initial_state=P["s0"], final_state=p_fin,
-                    out=p_out, workspace=p_ws, stream=stream)
-        if ev is not None:
-            ev[1].record(stream)
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        rec(0)
+        if two_pass:
+            kda.prefill_prepare(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"],
+                                lower_bound=pc.lower_bound, records=p_ws, stream=stream)
+            rec(1)
+            kda.prefill_chain(p_ws, P["cu"], pc.num_heads, scale=pc.scale,
+                              total_tokens=pc.total_tokens, initial_state=P["s0"],
+                              final_state=p_fin, out=p_out, stream=stream)
+        else:
+            kda.prefill(P["q"], P["k"], P["v"], P["g"], P["beta"], P["cu"], scale=pc.scale,
+                        lower_bound=pc.lower_bound, initial_state=P["s0"], final_state=p_fin,
+                        out=p_out, workspace=p_ws, stream=stream)
+            rec(1)
+        rec(2)
         kda.decode(D["q"], D["k"], D["v"], D["g"], D["beta"], D["pool"], D["slots"],
                    scale=dc.scale, out=d_out, stream=stream)
-        if ev is not None:
-            ev[2].record(stream)
+        rec(3)
 
     log(f"[bench] warmup {args.warmup} steps (plan {plan})")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     log(f"[bench] timing {args.steps} steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -145,27 +193,68 @@ def main():
         step(events[i])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    pre_ms = [e[0].elapsed_time(e[1]) for e in events]
-    dec_ms = [e[1].elapsed_time(e[2]) for e in events]
-    pre_avg = sum(pre_ms) / len(pre_ms)
-    dec_avg = sum(dec_ms) / len(dec_ms)
-    log(f"[bench] prefill {pre_avg:.4f} ms  decode {dec_avg:.4f} ms  wall/step "
-        f"{1e3 * wall / args.steps:.4f} ms")
+    pre_ms = [e[0].elapsed_time(e[2]) for e in events]
+    k1_ms = [e[0].elapsed_time(e[1]) for e in events]
+    k2_ms = [e[1].elapsed_time(e[2]) for e in events]
+    dec_ms = [e[2].elapsed_time(e[3]) for e in events]
+    pre, dec = stats(pre_ms), stats(dec_ms)
+    log(f"[bench] prefill {pre['mean_ms']:.4f} ms  decode {dec['mean_ms']:.4f} ms  "
+        f"wall/step {1e3 * wall / args.steps:.4f} ms")
+    log("[bench] timing a device-to-device copy")
+    copy_gbs = copy_bandwidth(torch, dev)
 
     tokheads = pc.total_tokens * pc.num_heads
+    chunks = (pc.total_tokens + 31) // 32
     flops = tokheads * PREFILL_FLOP_PER_TOKHEAD
     pbytes = tokheads * PREFILL_BYTES_PER_TOKHEAD + 2 * pc.num_seqs * pc.num_heads * STATE_BYTES
-    achieved_tf = flops / (pre_avg * 1e-3) / 1e12
     items = args.decode_rows * 8
     state_b = STATE_BYTES if args.decode_state == "f32" else STATE_BYTES // 2
     dbytes = items * (2 * state_b + DECODE_IO_BYTES_PER_ITEM)
-    achieved_gbs = dbytes / (dec_avg * 1e-3) / 1e9
+    achieved_gbs = dbytes / (dec["mean_ms"] * 1e-3) / 1e9
     route_name = {kda.ROUTE_SERIAL: "serial", kda.ROUTE_CHUNK: "chunk",
                   kda.ROUTE_SPLIT: "split"}[plan.route]
+    units = pc.num_seqs * pc.num_heads
+
+    kernels = {}
+    if two_pass:
+        k1, k2 = stats(k1_ms), stats(k2_ms)
+        prep_tf = tokheads * PREP_FLOP_PER_TOKHEAD / (k1["mean_ms"] * 1e-3) / 1e12
+        prep_gbs = tokheads * PREP_BYTES_PER_TOKHEAD / (k1["mean_ms"] * 1e-3) / 1e9
+        chain_tf = tokheads * CHAIN_FLOP_PER_TOKHEAD / (k2["mean_ms"] * 1e-3) / 1e12
+        chain_cus = min(256, units * plan.dv_split)
+        kernels["prefill_split_prep"] = dict(
+            k1, bound="hbm", achieved=prep_gbs, peak=PEAK_HBM_GBPS, unit="GB/s",
+            frac=prep_gbs / PEAK_HBM_GBPS, traffic=stored_traffic("prefill_split_prep_T8192_H8"),
+            algorithmic_bytes_per_launch=tokheads * PREP_BYTES_PER_TOKHEAD,
+            algorithmic_flop_per_launch=tokheads * PREP_FLOP_PER_TOKHEAD, mfma_tflops=prep_tf)
+        kernels["prefill_split_chain"] = dict(
+            k2, bound="mfma", achieved=chain_tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+            frac=chain_tf / PEAK_BF16_TFLOPS,
+            traffic=stored_traffic("prefill_split_chain_T8192_H8"),
+            algorithmic_flop_per_launch=tokheads * CHAIN_FLOP_PER_TOKHEAD,
+            active_cus=chain_cus,
+            frac_of_active_cus=chain_tf / (PEAK_BF16_TFLOPS * chain_cus / 256),
+            us_per_chunk_step=1e3 * k2["mean_ms"] / chunks)
+        dom = max(kernels, key=lambda n: kernels[n]["median_ms"])
+    else:
+        dom = f"prefill_{route_name}"
+        tf = flops / (pre["mean_ms"] * 1e-3) / 1e12
+        kernels[dom] = dict(pre, bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                            frac=tf / PEAK_BF16_TFLOPS,
+                            traffic=stored_traffic(f"{dom}_T8192_H8"),
+                            algorithmic_flop_per_launch=flops)
+    d = kernels[dom]
+    roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
+                "unit": d["unit"], "frac": d["frac"], "traffic": d["traffic"],
+                "avg_launch_ms": d["mean_ms"], "median_launch_ms": d["median_ms"]}
+    for key in ("algorithmic_flop_per_launch", "algorithmic_bytes_per_launch", "active_cus",
+                "frac_of_active_cus", "us_per_chunk_step"):
+        if key in d:
+            roofline[key] = d[key]
 
     result = {
         "metric": "KDA prefill tokens*heads/s + MFMA util; decode HBM GB/s at H=8",
-        "value": tokheads / (pre_avg * 1e-3),
+        "value": tokheads / (pre["mean_ms"] * 1e-3),
         "unit": "tokens*heads/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -187,25 +276,21 @@ def main():
                        "state_dtype": args.decode_state},
             "parallelism": "single GPU",
         },
-        "roofline": {
-            "kernel": f"prefill ({route_name} route)",
-            "bound": "mfma", "achieved": achieved_tf, "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s", "frac": achieved_tf / PEAK_BF16_TFLOPS,
-            "traffic": stored_traffic(f"prefill_{route_name}_T8192_H8"),
-            "algorithmic_flop_per_launch": flops,
-            "algorithmic_bytes_per_launch": pbytes,
-            "hbm_gbps": pbytes / (pre_avg * 1e-3) / 1e9,
-            "avg_launch_ms": pre_avg,
-            "us_per_chunk": 1e3 * pre_avg / ((pc.total_tokens + 31) // 32),
-        },
-        "decode": {
-            "value": achieved_gbs, "unit": "GB/s", "avg_launch_ms": dec_avg,
-            "roofline": {"bound": "hbm", "achieved": achieved_gbs, "peak": PEAK_HBM_GBPS,
-                         "unit": "GB/s", "frac": achieved_gbs / PEAK_HBM_GBPS,
-                         "traffic": stored_traffic(
-                             f"decode_{args.decode_state}_rows{args.decode_rows}_H8"),
-                         "algorithmic_bytes_per_launch": dbytes},
-        },
+        "roofline": roofline,
+        "prefill": dict(pre, tokheads_per_s=tokheads / (pre["mean_ms"] * 1e-3),
+                        mfma_tflops=flops / (pre["mean_ms"] * 1e-3) / 1e12,
+                        mfma_frac=flops / (pre["mean_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
+                        algorithmic_flop_per_call=flops, algorithmic_bytes_per_call=pbytes,
+                        hbm_gbps=pbytes / (pre["mean_ms"] * 1e-3) / 1e9,
+                        us_per_chunk=1e3 * pre["mean_ms"] / chunks, kernels=kernels),
+        "decode": dict(dec, value=achieved_gbs, unit="GB/s",
+                       copy_gbps_same_run=copy_gbs, frac_of_copy=achieved_gbs / copy_gbs,
+                       roofline={"bound": "hbm", "achieved": achieved_gbs,
+                                 "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                                 "frac": achieved_gbs / PEAK_HBM_GBPS,
+                                 "traffic": stored_traffic(
+                                     f"decode_{args.decode_state}_rows{args.decode_rows}_H8"),
+                                 "algorithmic_bytes_per_launch": dbytes}),
         "context": {"b200_small_bh_h8_tokheads_per_s_derived": 2.07e8,
                     "b200_prefill_speedup_vs_flashkda_geomean": 2.0512},
         "source_digest": source_digest(),

@@ -7,7 +7,7 @@
  *   S_t = (I - beta_t k_t k_t^T) Diag(exp(g_t)) S_{t-1} + beta_t k_t v_t^T
  *   o_t = scale * S_t^T q_t
  *
- * through two calls:
+ * through these calls:
  *
  *   kda_prefill  -- chunked prefill over packed variable-length sequences
  *                   ("FlashInfer PR #4262: CAKE KDA Prefill Highlights",
@@ -16,6 +16,12 @@
  *                   "optimize small-BH recurrent-KDA prefill": packed
  *                   layout with sequence offsets, caller-owned outputs,
  *                   caller's stream).
+ *   kda_prefill_prepare, kda_prefill_chain
+ *                -- the two passes of kda_prefill's SPLIT route as separate
+ *                   calls (the note's section 5: chunk preparation is
+ *                   parallel, state evolution is serial), so that a caller
+ *                   can time them or overlap one batch's preparation with
+ *                   another's chain.
  *   kda_decode   -- the T=1 step over a slot-indexed state pool, updated in
  *                   place (flashinfer PR #5551, "Kimi K3 TP12 H=8 fused KDA
  *                   decode": positive unique slots, FP32 and BF16 state,
@@ -53,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -154,6 +160,42 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
  * unknown route (the override is then unchanged).  Intended for tests and
  * benchmarks that compare routes. */
 int kda_set_prefill_route(int32_t route);
+
+/* ------------------------------------------------- two-pass prefill --
+ * kda_prefill_prepare followed by kda_prefill_chain computes exactly what
+ * kda_prefill computes with the SPLIT route (bit for bit), whatever route
+ * kda_prefill itself would choose.
+ *
+ * kda_prefill_prepare: every 32-token chunk of every (sequence, head) is
+ *   prepared independently ("FlashInfer PR #4262: CAKE KDA Prefill
+ *   Highlights", section 2, steps 1-3: gate prefix, anchored Mqk/Akk, the
+ *   32x32 inverse T) and turned into a chunk record in `records`: the decayed
+ *   queries and restored keys, Mqk, the chunk decay, and U0 = T Diag(b) V and
+ *   M = T Diag(b) Kg, so that the chunk's U = U0 - M S for incoming state S.
+ *   Inputs, lower_bound and the size arguments are as for kda_prefill.
+ *
+ * kda_prefill_chain: walks the records of each (sequence, head) in order
+ *   (steps 4-7: U, the state update and the outputs) and writes out and
+ *   final_state, as kda_prefill.  cu_seqlens, num_seqs, total_tokens and
+ *   num_heads must be those the records were prepared with, and the prepare
+ *   call must be ordered before it (same stream, or an event).
+ *
+ * records, records_bytes: caller-owned device memory of at least
+ *   kda_prefill_records_size(num_seqs, total_tokens, num_heads) bytes,
+ *   16-byte aligned (KDA_ERR_WORKSPACE if missing or too small).  The chain
+ *   only reads it; it may be reused once the chain has completed. */
+int kda_prefill_prepare(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                        int32_t head_dim_v, float lower_bound, void* records,
+                        size_t records_bytes, hipStream_t stream);
+int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      int32_t num_heads, float scale, const float* initial_state,
+                      float* final_state, void* out, const void* records,
+                      size_t records_bytes, hipStream_t stream);
+/* (N + T_tot / 32 + 1) * H * 45056: one 45,056-byte record per chunk slot
+ * and head (0 for invalid sizes). */
+size_t kda_prefill_records_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
 
 /* -------------------------------------------------------------- decode --
  * One T=1 step for each row against a slot-indexed state pool.

@@ -78,6 +78,13 @@ def load():
     lib.kda_prefill_plan.restype = ctypes.c_int
     lib.kda_set_prefill_route.argtypes = [i32]
     lib.kda_set_prefill_route.restype = ctypes.c_int
+    lib.kda_prefill_prepare.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, vp,
+                                        sz, vp]
+    lib.kda_prefill_prepare.restype = ctypes.c_int
+    lib.kda_prefill_chain.argtypes = [vp, i32, i64, i32, f32, vp, vp, vp, vp, sz, vp]
+    lib.kda_prefill_chain.restype = ctypes.c_int
+    lib.kda_prefill_records_size.argtypes = [i32, i64, i32]
+    lib.kda_prefill_records_size.restype = sz
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
@@ -175,6 +182,56 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
                               N, T, H, D, D, float(scale), float(lower_bound), _ptr(initial_state),
                               _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
                               _stream(stream)))
+    return out, final_state
+
+
+def records_size(num_seqs: int, total_tokens: int, num_heads: int) -> int:
+    """Bytes of chunk records kda_prefill_prepare / kda_prefill_chain need."""
+    return int(load().kda_prefill_records_size(num_seqs, total_tokens, num_heads))
+
+
+def prefill_prepare(q, k, v, g, beta, cu_seqlens, *, lower_bound, records=None, stream=None):
+    """First pass of the two-pass prefill: chunk records into ``records``
+    (a device uint8 tensor of at least ``records_size(N, T, H)`` bytes,
+    allocated here when None).  Returns ``records``."""
+    dev = q.device
+    T, H, D = q.shape
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _need(t, name, torch.bfloat16, (T, H, D), dev)
+    _need(beta, "beta", torch.bfloat16, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if records is None:
+        records = torch.empty(max(records_size(N, T, H), 16), dtype=torch.uint8, device=dev)
+    _check(load().kda_prefill_prepare(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), N, T, H, D, D, float(lower_bound),
+                                      _ptr(records), records.numel() * records.element_size(),
+                                      _stream(stream)))
+    return records
+
+
+def prefill_chain(records, cu_seqlens, num_heads, *, scale, total_tokens, initial_state=None,
+                  final_state=None, out=None, stream=None):
+    """Second pass of the two-pass prefill: the serial chain over ``records``.
+    ``final_state`` as in :func:`prefill`.  Returns (out, final_state)."""
+    dev = records.device
+    N = cu_seqlens.numel() - 1
+    T, H, D = int(total_tokens), int(num_heads), 128
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, D, D), dev)
+    if final_state is True:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, D, D), dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, D), dev)
+    _check(load().kda_prefill_chain(_ptr(cu_seqlens), N, T, H, float(scale), _ptr(initial_state),
+                                    _ptr(final_state), _ptr(out), _ptr(records),
+                                    records.numel() * records.element_size(), _stream(stream)))
     return out, final_state
 
 

@@ -53,6 +53,95 @@ bool fixed_anchor_fits(float lower_bound) {
   return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
 }
 
+// Argument checks shared by the prefill entry points; each returns KDA_OK or
+// records the error and returns its code.
+int check_sizes(const char* fn, int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                int32_t head_dim_k, int32_t head_dim_v) {
+  if (head_dim_k != KDA_HEAD_DIM || head_dim_v != KDA_HEAD_DIM)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: head dims must be 128 (got dk=%d, dv=%d)", fn,
+                head_dim_k, head_dim_v);
+  if (num_seqs < 0 || num_heads < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_seqs=%d num_heads=%d", fn, num_seqs, num_heads);
+  if (total_tokens < 0 || total_tokens > INT32_MAX)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: total_tokens=%lld out of [0, 2^31)", fn,
+                (long long)total_tokens);
+  return KDA_OK;
+}
+
+int check_bound(const char* fn, float lower_bound) {
+  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: lower_bound must be finite and < 0 (got %g)", fn,
+                (double)lower_bound);
+  return KDA_OK;
+}
+
+int check_inputs(const char* fn, const void* q, const void* k, const void* v, const void* g,
+                 const void* beta, const int32_t* cu_seqlens, int64_t total_tokens) {
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if (total_tokens == 0) return KDA_OK;
+  const void* need[] = {q, k, v, g, beta};
+  const char* names[] = {"q", "k", "v", "g", "beta"};
+  for (int i = 0; i < 5; ++i) {
+    if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %s is NULL", fn, names[i]);
+    if (i < 4 && !aligned(need[i], 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: %s is not 16-byte aligned", fn, names[i]);
+  }
+  if (!aligned(beta, 2))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: beta is not 2-byte aligned", fn);
+  return KDA_OK;
+}
+
+int check_outputs(const char* fn, const float* initial_state, const float* final_state,
+                  const void* out, int32_t num_seqs, int32_t num_heads, int64_t total_tokens) {
+  if (total_tokens > 0) {
+    if (!out) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: out is NULL", fn);
+    if (!aligned(out, 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: out is not 16-byte aligned", fn);
+  }
+  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: states must be 16-byte aligned", fn);
+  if (initial_state && final_state && initial_state != final_state) {
+    const size_t bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
+    const char* a0 = reinterpret_cast<const char*>(initial_state);
+    const char* b0 = reinterpret_cast<const char*>(final_state);
+    if (a0 < b0 + bytes && b0 < a0 + bytes)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: final_state partially overlaps initial_state", fn);
+  }
+  return KDA_OK;
+}
+
+int check_records(const char* fn, const void* ws, size_t bytes, size_t need) {
+  if (!ws || bytes < need)
+    return fail(KDA_ERR_WORKSPACE, "%s: workspace of %zu bytes needed (got %zu)", fn, need, bytes);
+  if (!aligned(ws, 16))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: workspace is not 16-byte aligned", fn);
+  return KDA_OK;
+}
+
+kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const void* g,
+                           const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                           int64_t total_tokens, int32_t num_heads, float scale,
+                           float lower_bound, const float* initial_state, float* final_state,
+                           void* out) {
+  kda::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = static_cast<const uint16_t*>(g);
+  a.beta = static_cast<const uint16_t*>(beta);
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = (int32_t)total_tokens;
+  a.num_heads = num_heads;
+  a.scale = scale;
+  a.anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
+  a.half_anchor_log2 = (float)(8.0 * (double)lower_bound * 1.4426950408889634);
+  a.s0 = initial_state;
+  a.s1 = final_state;
+  a.out = static_cast<uint16_t*>(out);
+  return a;
+}
+
 }  // namespace
 
 extern "C" {
@@ -138,75 +227,28 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
                 int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
                 float lower_bound, const float* initial_state, float* final_state, void* out,
                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  if (head_dim_k != KDA_HEAD_DIM || head_dim_v != KDA_HEAD_DIM)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: head dims must be 128 (got dk=%d, dv=%d)",
-                head_dim_k, head_dim_v);
-  if (num_seqs < 0 || num_heads < 1)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: num_seqs=%d num_heads=%d", num_seqs,
-                num_heads);
-  if (total_tokens < 0 || total_tokens > INT32_MAX)
-    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: total_tokens=%lld out of [0, 2^31)",
-                (long long)total_tokens);
-  if (!std::isfinite(scale))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: scale is not finite");
-  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
-    return fail(KDA_ERR_INVALID_ARGUMENT,
-                "kda_prefill: lower_bound must be finite and < 0 (got %g)", (double)lower_bound);
-  if (num_seqs == 0) return ok();
-  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: cu_seqlens is NULL");
-  if (total_tokens > 0) {
-    const void* need[] = {q, k, v, g, beta, out};
-    const char* names[] = {"q", "k", "v", "g", "beta", "out"};
-    for (int i = 0; i < 6; ++i)
-      if (!need[i]) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: %s is NULL", names[i]);
-    const void* al16[] = {q, k, v, g, out};
-    const char* n16[] = {"q", "k", "v", "g", "out"};
-    for (int i = 0; i < 5; ++i)
-      if (!aligned(al16[i], 16))
-        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: %s is not 16-byte aligned", n16[i]);
-    if (!aligned(beta, 2))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: beta is not 2-byte aligned");
-  }
-  if ((initial_state && !aligned(initial_state, 16)) || (final_state && !aligned(final_state, 16)))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: states must be 16-byte aligned");
-  if (initial_state && final_state && initial_state != final_state) {
-    const size_t bytes = (size_t)num_seqs * num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM * 4;
-    const char* a0 = reinterpret_cast<const char*>(initial_state);
-    const char* b0 = reinterpret_cast<const char*>(final_state);
-    if (a0 < b0 + bytes && b0 < a0 + bytes)
-      return fail(KDA_ERR_INVALID_ARGUMENT,
-                  "kda_prefill: final_state partially overlaps initial_state");
-  }
-  kda_prefill_plan_t plan;
-  int rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0,
-                            g_forced_route.load(), &plan);
+  const char* fn = "kda_prefill";
+  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v);
   if (rc != KDA_OK) return rc;
-  if (plan.route == KDA_ROUTE_SPLIT) {
-    const size_t ws_need = kda::split_workspace_bytes(num_seqs, total_tokens, num_heads);
-    if (!workspace || workspace_bytes < ws_need)
-      return fail(KDA_ERR_WORKSPACE, "kda_prefill: workspace of %zu bytes needed (got %zu)",
-                  ws_need, workspace_bytes);
-    if (!aligned(workspace, 16))
-      return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill: workspace is not 16-byte aligned");
-  }
+  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if ((rc = check_inputs(fn, q, k, v, g, beta, cu_seqlens, total_tokens)) != KDA_OK) return rc;
+  if ((rc = check_outputs(fn, initial_state, final_state, out, num_seqs, num_heads,
+                          total_tokens)) != KDA_OK)
+    return rc;
+  kda_prefill_plan_t plan;
+  rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0, g_forced_route.load(),
+                        &plan);
+  if (rc != KDA_OK) return rc;
+  if (plan.route == KDA_ROUTE_SPLIT &&
+      (rc = check_records(fn, workspace, workspace_bytes,
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+    return rc;
 
-  kda::PrefillArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.g = static_cast<const uint16_t*>(g);
-  a.beta = static_cast<const uint16_t*>(beta);
-  a.cu_seqlens = cu_seqlens;
-  a.num_seqs = num_seqs;
-  a.total_tokens = (int32_t)total_tokens;
-  a.num_heads = num_heads;
-  a.scale = scale;
-  a.anchor_log2 = plan.anchor_log2;
-  a.half_anchor_log2 = (float)(8.0 * (double)lower_bound * 1.4426950408889634);
-  a.s0 = initial_state;
-  a.s1 = final_state;
-  a.out = static_cast<uint16_t*>(out);
-
+  const kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                       num_heads, scale, lower_bound, initial_state, final_state,
+                                       out);
   hipError_t e;
   if (plan.route == KDA_ROUTE_SERIAL)
     e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
@@ -215,9 +257,59 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
   else
     e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
   if (e == hipErrorNotSupported)
-    return fail(KDA_ERR_UNSUPPORTED, "kda_prefill: route %d is not available", plan.route);
-  if (e != hipSuccess)
-    return fail(KDA_ERR_HIP, "kda_prefill: launch failed: %s", hipGetErrorString(e));
+    return fail(KDA_ERR_UNSUPPORTED, "%s: route %d is not available", fn, plan.route);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+size_t kda_prefill_records_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
+  if (num_seqs <= 0 || total_tokens < 0 || total_tokens > INT32_MAX || num_heads < 1) return 0;
+  return kda::split_workspace_bytes(num_seqs, total_tokens, num_heads);
+}
+
+int kda_prefill_prepare(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                        int32_t head_dim_v, float lower_bound, void* records,
+                        size_t records_bytes, hipStream_t stream) {
+  const char* fn = "kda_prefill_prepare";
+  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v);
+  if (rc != KDA_OK) return rc;
+  if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  if (num_seqs == 0) return ok();
+  if ((rc = check_inputs(fn, q, k, v, g, beta, cu_seqlens, total_tokens)) != KDA_OK) return rc;
+  if ((rc = check_records(fn, records, records_bytes,
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+    return rc;
+  const kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
+                                       num_heads, 1.f, lower_bound, nullptr, nullptr, nullptr);
+  const int mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
+  const hipError_t e = kda::launch_prefill_split_prepare(a, mode, records, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                      int32_t num_heads, float scale, const float* initial_state,
+                      float* final_state, void* out, const void* records, size_t records_bytes,
+                      hipStream_t stream) {
+  const char* fn = "kda_prefill_chain";
+  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, KDA_HEAD_DIM, KDA_HEAD_DIM);
+  if (rc != KDA_OK) return rc;
+  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if (num_seqs == 0) return ok();
+  if (!cu_seqlens) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: cu_seqlens is NULL", fn);
+  if ((rc = check_outputs(fn, initial_state, final_state, out, num_seqs, num_heads,
+                          total_tokens)) != KDA_OK)
+    return rc;
+  if ((rc = check_records(fn, records, records_bytes,
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+    return rc;
+  const kda::PrefillArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens,
+                                       num_seqs, total_tokens, num_heads, scale, -1.f,
+                                       initial_state, final_state, out);
+  const hipError_t e = kda::launch_prefill_split_chain(a, records, stream);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
 

@@ -53,6 +53,12 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
 // dv_split must be 8: one 16-column chain per block.
 hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 void* workspace, hipStream_t s);
+// Its two passes on their own (the chain reads only cu_seqlens, the sizes,
+// scale, s0, s1 and out of `a`).
+hipError_t launch_prefill_split_prepare(const PrefillArgs& a, int anchor_mode, void* workspace,
+                                        hipStream_t s);
+hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspace,
+                                      hipStream_t s);
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
 // Decode step; `cols` = value columns per block (32, 64 or 128).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);

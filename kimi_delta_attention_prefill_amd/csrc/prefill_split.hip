@@ -727,14 +727,25 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
 
 }  // namespace
 
+hipError_t launch_prefill_split_prepare(const PrefillArgs& a, int anchor_mode, void* workspace,
+                                        hipStream_t s) {
+  if (a.num_seqs <= 0) return hipSuccess;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  return anchor_mode == 0 ? launch_prep<0>(a, ws, s) : launch_prep<1>(a, ws, s);
+}
+
+hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspace,
+                                      hipStream_t s) {
+  if (a.num_seqs <= 0) return hipSuccess;
+  return launch_chain(a, static_cast<const uint8_t*>(workspace), s);
+}
+
 hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 void* workspace, hipStream_t s) {
   if (dv_split != 8) return hipErrorInvalidValue;   // one 16-column tile per chain block
-  if (a.num_seqs <= 0) return hipSuccess;
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  hipError_t e = anchor_mode == 0 ? launch_prep<0>(a, ws, s) : launch_prep<1>(a, ws, s);
+  hipError_t e = launch_prefill_split_prepare(a, anchor_mode, workspace, s);
   if (e != hipSuccess) return e;
-  return launch_chain(a, ws, s);
+  return launch_prefill_split_chain(a, workspace, s);
 }
 
 }  // namespace kda

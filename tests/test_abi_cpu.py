@@ -158,3 +158,41 @@ def test_split_route_requires_workspace():
         assert rc == _lib.KDA_ERR_WORKSPACE
     finally:
         kda.set_prefill_route(kda.ROUTE_AUTO)
+
+
+def test_two_pass_host_validation():
+    lib = kda.load()
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+    need = kda.records_size(1, 4, 1)
+    assert need == (1 + 0 + 1) * 1 * 45056
+    assert kda.records_size(3, 100, 2) == (3 + 3 + 1) * 2 * 45056
+    assert kda.records_size(0, 0, 1) == 0 and kda.records_size(1, -1, 1) == 0
+
+    def prep(**o):
+        a = dict(q=16, k=16, v=16, g=16, beta=16, cu=16, N=1, T=4, H=1, dk=128, dv=128, lb=-5.0,
+                 rec=0x10000, nbytes=need)
+        a.update(o)
+        return lib.kda_prefill_prepare(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                       P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"], a["lb"],
+                                       P(a["rec"]), a["nbytes"], None)
+
+    def chain(**o):
+        a = dict(cu=16, N=1, T=4, H=1, scale=1.0, s0=None, s1=None, out=16, rec=0x10000,
+                 nbytes=need)
+        a.update(o)
+        return lib.kda_prefill_chain(P(a["cu"]), a["N"], a["T"], a["H"], a["scale"], P(a["s0"]),
+                                     P(a["s1"]), P(a["out"]), P(a["rec"]), a["nbytes"], None)
+
+    E, U, W = _lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED, _lib.KDA_ERR_WORKSPACE
+    assert prep(dk=64) == U
+    assert prep(lb=0.0) == E
+    assert prep(q=None) == E and prep(q=0x1008) == E and prep(cu=None) == E
+    assert prep(rec=None) == W and "workspace" in kda.last_error()
+    assert prep(nbytes=need - 1) == W
+    assert prep(rec=0x10008) == E
+    assert prep(N=0, q=None, cu=None, rec=None, nbytes=0) == 0
+    assert chain(scale=float("nan")) == E
+    assert chain(out=None) == E and chain(cu=None) == E
+    assert chain(s0=0x20000, s1=0x20000 + 4096) == E and "overlap" in kda.last_error()
+    assert chain(rec=None) == W and chain(nbytes=100) == W
+    assert chain(N=0, cu=None, out=None, rec=None, nbytes=0) == 0

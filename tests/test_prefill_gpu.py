@@ -217,3 +217,31 @@ def test_stream_and_graph_replay(dev, route):
     finally:
         kda.set_prefill_route(kda.ROUTE_AUTO)
     compare(case, ref_o, ref_f)
+
+
+@pytest.mark.parametrize("which", ["config0", "ragged", "config1"])
+def test_two_pass_equals_split_route(dev, which):
+    """kda_prefill_prepare + kda_prefill_chain reproduce the SPLIT route of
+    kda_prefill bit for bit, with the records on a side stream's timeline."""
+    if which == "config0":
+        case = prefill_config(0)
+    elif which == "ragged":
+        case = make_prefill_case([1, 31, 32, 33, 95, 0, 64, 7, 200], 3, -8.0, 0.02, seed=99,
+                                 name="ragged_two_pass")
+    else:
+        case = prefill_config(1)
+    o_ref, f_ref = run_gpu(case, kda.ROUTE_SPLIT, dev)
+    to = lambda t: None if t is None else t.to(dev)
+    cu = to(case.cu_seqlens)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        rec = kda.prefill_prepare(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta), cu,
+                                  lower_bound=case.lower_bound)
+        o, f = kda.prefill_chain(rec, cu, case.num_heads, scale=case.scale,
+                                 total_tokens=case.total_tokens,
+                                 initial_state=to(case.initial_state), final_state=True)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    assert rec.numel() >= kda.records_size(case.num_seqs, case.total_tokens, case.num_heads)
+    assert torch.equal(o, o_ref) and torch.equal(f, f_ref)
