@@ -143,7 +143,7 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g,
 
 /* Bytes of workspace kda_prefill needs for these sizes with the route it
  * would choose on the current device (or the forced route): 0 for SERIAL and
- * CHUNK, (N + T_tot / 32 + 1) * H * 45056 for SPLIT. */
+ * CHUNK, (N + T_tot / 32 + 1) * H * 49152 for SPLIT. */
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t num_heads);
 
@@ -193,7 +193,7 @@ int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
                       int32_t num_heads, float scale, const float* initial_state,
                       float* final_state, void* out, const void* records,
                       size_t records_bytes, hipStream_t stream);
-/* (N + T_tot / 32 + 1) * H * 45056: one 45,056-byte record per chunk slot
+/* (N + T_tot / 32 + 1) * H * 49152: one 49,152-byte record per chunk slot
  * and head (0 for invalid sizes). */
 size_t kda_prefill_records_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
 

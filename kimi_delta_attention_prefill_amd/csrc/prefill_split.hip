@@ -27,14 +27,22 @@
 //     records through an LDS ring.
 //
 // Workspace record of (chunk slot s, head h) at ((s * H + h) * kRecBytes):
-//   [0, 8192)        -M    fp16 A fragments [mt 2][kstep 4][lane 64][8]
+//   [0, 8192)        -M'   fp16 A fragments [mt 2][kstep 4][lane 64][8]
 //   [8192, 16384)    Qg    fp16 A fragments [mt 2][kstep 4][lane 64][8]
 //   [16384, 24576)   Kr^T  fp16 A fragments [mt 8][lane 64][8]
 //   [24576, 26624)   Mqk   fp16 A fragments [mt 2][lane 64][8]
 //   [26624, 27136)   2^{G_L} fp32 [128]
-//   [27136, 28672)   padding, never written or used (the staged part is
-//                    7 x 4 KiB: one 16-byte load per thread per 4 KiB)
-//   [28672, 45056)   U0    fp32 accumulator tiles [nt 8][mt 2][lane 64][4]
+//   [27136, 28672)   padding, never written or used
+//   [28672, 30720)   -W    fp16 A fragments, hi part [mt 2][lane 64][8]
+//   [30720, 32768)   -W    lo part (the staged part is 8 x 4 KiB)
+//   [32768, 49152)   U0    fp32 accumulator tiles [nt 8][mt 2][lane 64][4]
+// where, for chunk c of a sequence, M' = M Diag(2^{G_L}) and W = M Kr^T with
+// the decay and restored keys of chunk c-1 (chunk 0: M' = M, W = 0).  They
+// let the chain form U of chunk c from the state and U of chunk c-1:
+//   S_c = Diag(2^{G_L,c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1},  U_c = U0_c - M_c S_c
+//   =>  U_c = U0_c - M'_c S_{c-1} - W_c U_{c-1},
+// so the serial dependency from one chunk to the next is the 32-deep W U
+// product instead of the 128-deep M S product behind a state update.
 // Fragment K indices use the permuted slot order of chunk_common.h.  The chunk
 // slot of chunk c of sequence n is n + floor(cu[n] / 32) + c, unique and
 // below N + T / 32 + 1.
@@ -50,9 +58,11 @@ constexpr int kRecOffQg = 8192;
 constexpr int kRecOffKrT = 16384;
 constexpr int kRecOffMqk = 24576;
 constexpr int kRecOffDec = 26624;
-constexpr int kRecStageBytes = 28672;
-constexpr int kRecOffU0 = 28672;
-constexpr int kRecBytes = 45056;
+constexpr int kRecOffWh = 28672;
+constexpr int kRecOffWl = 30720;
+constexpr int kRecStageBytes = 32768;
+constexpr int kRecOffU0 = 32768;
+constexpr int kRecBytes = 49152;
 
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
   const int64_t slots = (int64_t)num_seqs + total_tokens / 32 + 1;
@@ -134,6 +144,13 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rb =
       make_buffer(a.beta + (int64_t)t0 * H + h, (uint32_t)(((L - 1) * H + 1) * 2));
+  // The previous chunk of the same sequence (chunk 0: an empty range, so its
+  // keys and gates read as zero, which gives W = 0 and M' = M).
+  const bool has_prev = c > 0;
+  const int64_t base_prev = has_prev ? base - (int64_t)CH * H * D : base;
+  const uint32_t prev_bytes = has_prev ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
+  const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
+  const __amdgpu_buffer_rsrc_t rgp = make_buffer(a.g + base_prev, prev_bytes);
   const uint32_t tok_bytes = (uint32_t)H * D * 2;
   const float beta[2] = {
       bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0)),
@@ -429,12 +446,35 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     }
 
   // M^T = (b Kg)^T T^T: accumulator rows are channels 16mc + 4g4 + i, column
-  // token 16tt + l16, i.e. the -M A fragments of K step mc/2.
+  // token 16tt + l16, i.e. the M A fragments of K step mc/2.  Per K step the
+  // previous chunk's restored keys Kr_p (this lane's tokens and channels, in
+  // FP32 then fp16) and decay d_p give -M' = -M Diag(d_p) and accumulate
+  // W^T = Kr_p M^T (M as fp16 hi + lo), whose accumulators (rows = previous
+  // tokens s, column = token t) are the W A fragments.
+  f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
 #pragma unroll
-  for (int p = 0; p < 4; ++p)
+  for (int p = 0; p < 4; ++p) {
+    u32x4 kpw[2], gpw[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      kpw[hf] = load8(rkp, hf, p);
+      gpw[hf] = load8(rgp, hf, p);
+    }
+    float dp[8];
+    f16x8 krp[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float s0 = row_scan16(bf16_elem(gpw[0], j));
+      const float b0 = __shfl(s0, 15, 16);
+      const float s1 = row_scan16(bf16_elem(gpw[1], j)) + b0;
+      const float gl = __shfl(s1, 15, 16) * kLog2e;
+      dp[j] = fast_exp2(gl);
+      krp[0][j] = static_cast<_Float16>(bf16_elem(kpw[0], j) * fast_exp2(gl - s0 * kLog2e));
+      krp[1][j] = static_cast<_Float16>(bf16_elem(kpw[1], j) * fast_exp2(gl - s1 * kLog2e));
+    }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      f16x8 mf;
+      float mv[8];
 #pragma unroll
       for (int e = 0; e < 2; ++e) {
         const int mc = 2 * p + e;
@@ -442,54 +482,98 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
         m = mfma_f16(Xh[mc], tl[tt], m);
         m = mfma_f16(Xl[mc], th[tt], m);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) mf[4 * e + i] = (_Float16)(-m[i]);
+        for (int i = 0; i < 4; ++i) mv[4 * e + i] = m[i];
+      }
+      f16x8 mf, mh, ml;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        mf[j] = static_cast<_Float16>(-(mv[j] * dp[j]));
+        _Float16 hh, ll;
+        split_f16(mv[j], hh, ll);
+        mh[j] = hh;
+        ml[j] = ll;
       }
       *reinterpret_cast<f16x8*>(rec + kRecOffMneg + ((tt * 4 + p) * 64 + lane) * 16) = mf;
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        wacc[sh][tt] = mfma_f16(krp[sh], mh, wacc[sh][tt]);
+        wacc[sh][tt] = mfma_f16(krp[sh], ml, wacc[sh][tt]);
+      }
     }
+  }
+  // -W fragments: row t = 16tt + l16, K-slot 8g4 + i + 4sh <-> previous token 16sh + 4g4 + i.
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    f16x8 wh, wl;
+#pragma unroll
+    for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        _Float16 hh, ll;
+        split_f16(-wacc[sh][tt][i], hh, ll);
+        wh[4 * sh + i] = hh;
+        wl[4 * sh + i] = ll;
+      }
+    *reinterpret_cast<f16x8*>(rec + kRecOffWh + (tt * 64 + lane) * 16) = wh;
+    *reinterpret_cast<f16x8*>(rec + kRecOffWl + (tt * 64 + lane) * 16) = wl;
+  }
 }
 
 
 // Chain pass.  One block per (sequence, head, 16-column value tile), four
-// waves with fixed roles, one barrier per chunk step:
-//   wave 0 (state):  the serial recurrence only -- U = U0 + (-M) S0, the decay
-//                    and S += Kr^T U -- with the state in registers for the
-//                    whole sequence; during step c it already reads chunk
-//                    c+1's operands from LDS.  It hands fp16 S0 and U (hi, lo)
-//                    of chunk c to the output wave through LDS.
-//   wave 1 (output): in step c computes O = scale (Qg S0 + Mqk U) for chunk
-//                    c-1 and stores it.
-//   waves 2-3 (loaders): in step c copy chunk c+2's record into the LDS ring
-//                    (from registers loaded three steps earlier) and start
-//                    loading chunk c+5.
-// LDS ring of 4 chunk slots: in step c the state wave reads slot c+1, the
-// output wave slot c-1 and the loaders write slot c+2 (mod 4), all distinct.
-// Loads and stores are buffer operations issued unconditionally (a chunk past
-// the end has an empty range: loads return zeros, stores are dropped), so
-// every path issues the same memory operations and the compiler's wait
-// counts stay exact.  Value columns evolve independently, so tiles never
-// communicate.  Block b handles (sequence, head) unit b % units and tile
-// b / units: with a unit count divisible by 8, all tiles of a unit run on
-// one XCD and share its L2 copy of the records.
-constexpr int kChainStage = kRecStageBytes + 2048;        // staged record + one U0 tile
-constexpr int kChainSlots = 4;
-constexpr int kExchBytes = 6 * 64 * 16;                   // Sb[4], Uh, Ul fragments
-constexpr int kChainLds = kChainSlots * kChainStage + 2 * kExchBytes;
-constexpr int kLoaderVecs = kChainStage / 16 / 128;      // 15 x 16 B per loader lane
-constexpr int kLoadAhead = 3;                             // chunks in loader registers
-static_assert(kChainStage % (16 * 128) == 0, "stage must split evenly over two loader waves");
+// waves with fixed roles and one barrier per chunk step.  With the records'
+// M' and W the recurrence splits into two coupled chains, each advanced from
+// the other's previous value (S_{-1} = initial state, U_{-1} = 0):
+//   P_c = U0_c - M'_c S_{c-1}                       (needs the previous state)
+//   U_c = P_c - W_c U_{c-1}                          (the only 1-step dependency)
+//   S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1} (c >= 1; S_0 = S_{-1})
+//   O_c = scale (Qg_c S_c + Mqk_c U_c)
+// so in step c every wave only consumes what others produced in step c-1:
+//   waves 0-1 (state halves, key rows 0-63 / 64-127): S_c from U_{c-1}; fp16
+//            S_c for the output; their K-half of P_{c+1} (wave 0 adds U0);
+//            the state stays in VGPRs for the whole sequence;
+//   wave 2 (U):   U_c = (P_c halves summed) - W_c U_{c-1}, split into fp16
+//            hi + lo for the state waves and the output;
+//   wave 3 (output): O_{c-1} from fp16 S_{c-1}, U_{c-1} and the record.
+// Each wave loads the record fragments it needs itself, straight into
+// registers, three chunks ahead of use (a ring of three register sets per
+// operand stream).  LDS carries only the step-to-step exchange (fp16 S, the P
+// halves, U hi/lo), double-buffered by step parity.  Loads and stores are
+// buffer operations issued unconditionally (a chunk past the end has an empty
+// range: loads return zeros, stores are dropped), so every path issues the
+// same memory operations and the compiler's wait counts stay exact.  Value
+// columns evolve independently, so tiles never communicate.  Block b handles
+// (sequence, head) unit b % units and tile b / units: with a unit count
+// divisible by 8, all tiles of a unit run on one XCD and share its L2 copy of
+// the records.
+constexpr int kExSb = 0;                                   // fp16 S_c, [kstep 4][lane][8]
+constexpr int kExUh = 4096, kExUl = 5120;                  // U_c hi / lo, [lane][8]
+constexpr int kExP = 6144;                                 // P halves, [half 2][mt 2][lane][4] f32
+constexpr int kExchBytes = 10240;
+constexpr int kDecSlots = 4;                               // chunk decays, 512 B each
+constexpr int kChainLds = 2 * kExchBytes + kDecSlots * 512;
+constexpr int kChainThreads = 256;
+constexpr int kAhead = 3;                                  // register sets per operand stream
 
-// Operands of one chunk step of the state wave.
-struct MUOps {
-  f16x8 am[2][4];   // -M fragments, [mt][kstep]
-  f32x4 u0[2];      // U0 accumulator tiles
+// Record fragments, as each wave consumes them.
+struct AOps {            // state half: -M' (its K half) and U0, of chunk c+1
+  f16x8 am[2][2];
+  f32x4 u0[2];
 };
-struct KDOps {
-  f16x8 ak[8];      // Kr^T fragments
-  f32x4 dv[8];      // 2^{G_L} of the lane's state rows
+struct BOps {            // state half: Kr^T rows of chunk c-1
+  f16x8 ak[4];
+};
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+struct WOps {            // U wave: -W hi / lo of chunk c, and its decays (two per lane)
+  f16x8 wh[2], wl[2];
+  f32x2 dec;
+};
+struct QOps {            // output wave: Qg and Mqk of chunk c-1
+  f16x8 aq[2][4], amq[2];
 };
 
-__global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
-                                                            const uint8_t* __restrict__ ws) {
+__global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs a,
+                                                                     const uint8_t* __restrict__ ws) {
   extern __shared__ __align__(16) unsigned char lds[];
   const int H = a.num_heads;
   const int units = a.num_seqs * H;
@@ -498,53 +582,98 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4;
   const int col = 16 * tile + (lane & 15);
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
   const int nch = (eos - bos + CH - 1) / CH;
   const int64_t slot0 = (int64_t)n + bos / CH;
 
-  auto slot = [&](int c) __attribute__((always_inline)) {
-    return lds + (c & (kChainSlots - 1)) * kChainStage;
+  auto exch = [&](int c) __attribute__((always_inline)) { return lds + (c & 1) * kExchBytes; };
+  // Chunk c's 128 decays 2^{G_L}, written by the U wave from its record loads
+  // (one copy per block instead of one per lane that needs them).
+  auto decs = [&](int c) __attribute__((always_inline)) {
+    return reinterpret_cast<float*>(lds + 2 * kExchBytes + (c & (kDecSlots - 1)) * 512);
   };
-  auto exch = [&](int c) __attribute__((always_inline)) {
-    return lds + kChainSlots * kChainStage + (c & 1) * kExchBytes;
+  auto xfrag = [&](const uint8_t* base, int idx) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f16x8*>(base + (idx * 64 + lane) * 16);
+  };
+  auto xacc = [&](const uint8_t* base, int idx) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(base + (idx * 64 + lane) * 16);
+  };
+  // Record of chunk c (an empty range for c outside [0, nch)).
+  auto rec = [&](int c) __attribute__((always_inline)) {
+    const bool in = c >= 0 && c < nch;
+    return make_buffer(ws + ((slot0 + (in ? c : 0)) * H + h) * kRecBytes,
+                       in ? (uint32_t)kRecBytes : 0u);
+  };
+  auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int off) __attribute__((always_inline)) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)off, 0, 0);
+  };
+  auto gfrag = [&](__amdgpu_buffer_rsrc_t r, int base, int idx) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f16x8, ld16(r, base + (idx * 64 + lane) * 16));
+  };
+  auto gacc = [&](__amdgpu_buffer_rsrc_t r, int base, int idx) __attribute__((always_inline)) {
+    return __builtin_bit_cast(f32x4, ld16(r, base + (idx * 64 + lane) * 16));
   };
 
-  if (wave >= 2) {
-    // ------------------------------------------------------------ loaders
-    const int lt = tid - 128;
-    auto load = [&](u32x4* dst, int c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t r = make_buffer(
-          ws + ((slot0 + c) * H + h) * kRecBytes, c < nch ? (uint32_t)kRecBytes : 0u);
+  if (wave == 3) {
+    // ------------------------------------------------------------- output
+    QOps q[kAhead];
+    auto load_q = [&](QOps& o, int c) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t r = rec(c);
 #pragma unroll
-      for (int m = 0; m < kLoaderVecs; ++m) {
-        const int v = lt + 128 * m;
-        const int off = v < kRecStageBytes / 16 ? v * 16
-                                                : kRecOffU0 + tile * 2048 + (v - kRecStageBytes / 16) * 16;
-        dst[m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)off, 0, 0));
+      for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+        for (int p = 0; p < 4; ++p) o.aq[mt][p] = gfrag(r, kRecOffQg, mt * 4 + p);
+        o.amq[mt] = gfrag(r, kRecOffMqk, mt);
       }
     };
-    auto store = [&](const u32x4* src, int c) __attribute__((always_inline)) {
 #pragma unroll
-      for (int m = 0; m < kLoaderVecs; ++m)
-        reinterpret_cast<u32x4*>(slot(c))[lt + 128 * m] = src[m];
-    };
-    u32x4 buf[kLoadAhead][kLoaderVecs];
-    load(buf[0], 0);
-    store(buf[0], 0);
-    load(buf[0], 1);
-    store(buf[0], 1);
-#pragma unroll
-    for (int i = 0; i < kLoadAhead; ++i) load(buf[i], 2 + i);
-    __syncthreads();
+    for (int i = 0; i < kAhead; ++i) load_q(q[i], i);
+    __syncthreads();   // P_0 published
+    __syncthreads();   // step 0
+    // step c >= 1: O_{c-1}, whose fragments sit in set (c-1) % 3
     auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(I_const)::value;
-      store(buf[I], c + 2);               // loaded three steps ago
-      load(buf[I], c + 2 + kLoadAhead);
+      const QOps& o = q[I];
+      const uint8_t* ex = exch(c - 1);
+      f16x8 sb[4];
+#pragma unroll
+      for (int p = 0; p < 4; ++p) sb[p] = xfrag(ex + kExSb, p);
+      const f16x8 uh = xfrag(ex + kExUh, 0), ul = xfrag(ex + kExUl, 0);
+      // O^T = S^T Qg^T + U^T Mqk^T: the same fragments with A and B swapped;
+      // lane (g4, l16) gets value columns 4g4..4g4+3 of token 16mt + l16.
+      f32x4 O[2] = {z, z};
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma_f16(sb[p], o.aq[mt][p], O[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        O[mt] = mfma_f16(uh, o.amq[mt], O[mt]);
+        O[mt] = mfma_f16(ul, o.amq[mt], O[mt]);
+      }
+      load_q(q[I], c - 1 + kAhead);
+      // rows t >= L of a final partial chunk fall outside the range and are dropped
+      const int t0 = bos + CH * (c - 1);
+      const int L = min(CH, eos - t0);
+      const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
+          a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const int t = 16 * mt + (lane & 15);
+        u32x2 pk;
+        pk[0] = (uint32_t)f32_to_bf16(a.scale * O[mt][0]) |
+                ((uint32_t)f32_to_bf16(a.scale * O[mt][1]) << 16);
+        pk[1] = (uint32_t)f32_to_bf16(a.scale * O[mt][2]) |
+                ((uint32_t)f32_to_bf16(a.scale * O[mt][3]) << 16);
+        __builtin_amdgcn_raw_buffer_store_b64(pk, orsrc,
+                                              (uint32_t)((t * H * D + 16 * tile + 4 * g4) * 2), 0, 0);
+      }
       __syncthreads();
     };
-    for (int c = 0; c <= nch; c += kLoadAhead) {
+    for (int c = 1; c <= nch; c += kAhead) {
       step(std::integral_constant<int, 0>{}, c);
       if (c + 1 > nch) break;
       step(std::integral_constant<int, 1>{}, c + 1);
@@ -554,123 +683,48 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
     return;
   }
 
-  if (wave == 1) {
-    // ------------------------------------------------------------- output
-    __syncthreads();
-    for (int c = 0; c <= nch; ++c) {
-      if (c >= 1) {
-        const int cp = c - 1;
-        const uint8_t* st = slot(cp);
-        const uint8_t* ex = exch(cp);
-        f16x8 aq[2][4], amq[2], sb[4], uh, ul;
+  if (wave == 2) {
+    // ------------------------------------------------------------------ U
+    WOps w[kAhead];
+    auto load_w = [&](WOps& o, int c) __attribute__((always_inline)) {
+      const __amdgpu_buffer_rsrc_t r = rec(c);
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-          for (int p = 0; p < 4; ++p)
-            aq[mt][p] = *reinterpret_cast<const f16x8*>(st + kRecOffQg + ((mt * 4 + p) * 64 + lane) * 16);
-          amq[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffMqk + (mt * 64 + lane) * 16);
-        }
-#pragma unroll
-        for (int p = 0; p < 4; ++p) sb[p] = *reinterpret_cast<const f16x8*>(ex + (p * 64 + lane) * 16);
-        uh = *reinterpret_cast<const f16x8*>(ex + (4 * 64 + lane) * 16);
-        ul = *reinterpret_cast<const f16x8*>(ex + (5 * 64 + lane) * 16);
-        const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-        f32x4 O[2] = {z, z};
-#pragma unroll
-        for (int p = 0; p < 4; ++p)
-#pragma unroll
-          for (int mt = 0; mt < 2; ++mt) O[mt] = mfma_f16(aq[mt][p], sb[p], O[mt]);
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          O[mt] = mfma_f16(amq[mt], uh, O[mt]);
-          O[mt] = mfma_f16(amq[mt], ul, O[mt]);
-        }
-        // rows t >= L of a final partial chunk fall outside the range and are dropped
-        const int t0 = bos + CH * cp;
-        const int L = min(CH, eos - t0);
-        const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
-            a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i2 = 0; i2 < 4; ++i2) {
-            const int t = 16 * mt + 4 * g4 + i2;
-            buffer_store_u16(f32_to_bf16(a.scale * O[mt][i2]), orsrc,
-                             (uint32_t)((t * H * D + col) * 2));
-          }
+      for (int mt = 0; mt < 2; ++mt) {
+        o.wh[mt] = gfrag(r, kRecOffWh, mt);
+        o.wl[mt] = gfrag(r, kRecOffWl, mt);
       }
-      __syncthreads();
+      o.dec = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+          r, (uint32_t)(kRecOffDec + lane * 8), 0, 0));
+    };
+    auto put_dec = [&](const WOps& o, int c) __attribute__((always_inline)) {
+      *reinterpret_cast<f32x2*>(decs(c) + 2 * lane) = o.dec;
+    };
+#pragma unroll
+    for (int i = 0; i < kAhead; ++i) load_w(w[i], i);
+    put_dec(w[0], 0);                 // decays of chunk 0, used in step 1
+    f16x8 Uh, Ul;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      Uh[j] = static_cast<_Float16>(0.f);
+      Ul[j] = static_cast<_Float16>(0.f);
     }
-    return;
-  }
-
-  // --------------------------------------------------------------- state
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
-  f32x4 S[8];
-  if (a.s0) {
+    __syncthreads();   // P_0 published
+    // step c: U_c from P_c and U_{c-1}; W_c sits in set c % 3
+    auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
+      constexpr int I = decltype(I_const)::value;
+      const WOps& o = w[I];
+      const uint8_t* ex = exch(c - 1);
+      f32x4 U[2];
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+      for (int mt = 0; mt < 2; ++mt) U[mt] = xacc(ex + kExP, mt) + xacc(ex + kExP, 2 + mt);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S[mt][i] = a.s0[sbase + (int64_t)(16 * mt + 4 * g4 + i) * D + col];
-  } else {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) S[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
-  // All operands of a chunk step come from its ring slot, read early enough
-  // that a step never waits on LDS: Kr^T and the decay of chunk c+1 at the
-  // start of step c (double-buffered), -M and U0 of chunk c+1 as soon as the
-  // U products of step c have consumed those of chunk c.
-  auto read_mu = [&](MUOps& F, int c) __attribute__((always_inline)) {
-    const uint8_t* st = slot(c);
-#pragma unroll
-    for (int mt = 0; mt < 2; ++mt) {
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        F.am[mt][p] = *reinterpret_cast<const f16x8*>(st + kRecOffMneg + ((mt * 4 + p) * 64 + lane) * 16);
-      F.u0[mt] = *reinterpret_cast<const f32x4*>(st + kRecStageBytes + (mt * 64 + lane) * 16);
-    }
-  };
-  auto read_kd = [&](KDOps& K, int c) __attribute__((always_inline)) {
-    const uint8_t* st = slot(c);
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-      K.ak[mt] = *reinterpret_cast<const f16x8*>(st + kRecOffKrT + (mt * 64 + lane) * 16);
-      K.dv[mt] = *reinterpret_cast<const f32x4*>(st + kRecOffDec + (16 * mt + 4 * g4) * 4);
-    }
-  };
-  MUOps F;
-  KDOps K[2];
-  __syncthreads();
-  read_mu(F, 0);
-  read_kd(K[0], 0);
-  auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
-    constexpr int I = decltype(I_const)::value;
-    if (c < nch) {
-      read_kd(K[1 - I], c + 1);           // unused past the end
-      const KDOps& k = K[I];
-      f16x8 Sb[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          Sb[p][i2] = static_cast<_Float16>(S[2 * p][i2]);
-          Sb[p][4 + i2] = static_cast<_Float16>(S[2 * p + 1][i2]);
-        }
-      f32x4 U[2] = {F.u0[0], F.u0[1]};
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) U[mt] = mfma_f16(F.am[mt][p], Sb[p], U[mt]);
-      read_mu(F, c + 1);                  // unused past the end
-      // the decay does not depend on U: it fills the MFMA latency
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) S[mt][i2] *= k.dv[mt][i2];
-      uint8_t* ex = exch(c);
-#pragma unroll
-      for (int p = 0; p < 4; ++p) *reinterpret_cast<f16x8*>(ex + (p * 64 + lane) * 16) = Sb[p];
-      f16x8 Uh, Ul;
+      for (int mt = 0; mt < 2; ++mt) {
+        U[mt] = mfma_f16(o.wh[mt], Uh, U[mt]);
+        U[mt] = mfma_f16(o.wh[mt], Ul, U[mt]);
+        U[mt] = mfma_f16(o.wl[mt], Uh, U[mt]);
+      }
+      load_w(w[I], c + kAhead);
+      put_dec(w[(I + 1) % kAhead], c + 1);   // used in step c+2
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -680,27 +734,133 @@ __global__ __launch_bounds__(256) void prefill_split_chain(PrefillArgs a,
           Uh[4 * mt + i2] = hh;
           Ul[4 * mt + i2] = ll;
         }
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) {
-        S[mt] = mfma_f16(k.ak[mt], Uh, S[mt]);
-        S[mt] = mfma_f16(k.ak[mt], Ul, S[mt]);
-      }
-      *reinterpret_cast<f16x8*>(ex + (4 * 64 + lane) * 16) = Uh;
-      *reinterpret_cast<f16x8*>(ex + (5 * 64 + lane) * 16) = Ul;
+      uint8_t* exw = exch(c);
+      *reinterpret_cast<f16x8*>(exw + kExUh + lane * 16) = Uh;
+      *reinterpret_cast<f16x8*>(exw + kExUl + lane * 16) = Ul;
+      __syncthreads();
+    };
+    // steps 0..nch (the last one's U is never read)
+    for (int c = 0; c <= nch; c += kAhead) {
+      step(std::integral_constant<int, 0>{}, c);
+      if (c + 1 > nch) break;
+      step(std::integral_constant<int, 1>{}, c + 1);
+      if (c + 2 > nch) break;
+      step(std::integral_constant<int, 2>{}, c + 2);
     }
+    return;
+  }
+
+  // --------------------------------------------------------- state halves
+  // Wave hs owns key rows 64hs..64hs+63: accumulator tiles mt = 4hs..4hs+3,
+  // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.
+  const int hs = wave;
+  const int64_t sbase = ((int64_t)n * H + h) * D * D;
+  f32x4 S[4];
+  if (a.s0) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        S[m][i] = a.s0[sbase + (int64_t)(16 * (4 * hs + m) + 4 * g4 + i) * D + col];
+  } else {
+#pragma unroll
+    for (int m = 0; m < 4; ++m) S[m] = z;
+  }
+  AOps A[kAhead];
+  BOps B[kAhead];
+  auto load_a = [&](AOps& o, int c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = rec(c);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) o.am[mt][q] = gfrag(r, kRecOffMneg, mt * 4 + 2 * hs + q);
+      o.u0[mt] = gacc(r, kRecOffU0 + tile * 2048, mt);
+    }
+  };
+  auto load_b = [&](BOps& o, int c) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = rec(c);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) o.ak[m] = gfrag(r, kRecOffKrT, 4 * hs + m);
+  };
+  auto to_f16 = [&](f16x8* Sb) __attribute__((always_inline)) {
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) {
+        Sb[q][i2] = static_cast<_Float16>(S[2 * q][i2]);
+        Sb[q][4 + i2] = static_cast<_Float16>(S[2 * q + 1][i2]);
+      }
+  };
+  // fp16 S_c to exchange(c) and this half's share of P_{c+1} = U0_{c+1} -
+  // M'_{c+1} S_c from the fragments of chunk c+1.
+  auto publish = [&](const AOps& o, int c) __attribute__((always_inline)) {
+    f16x8 Sb[2];
+    to_f16(Sb);
+    uint8_t* ex = exch(c);
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+      *reinterpret_cast<f16x8*>(ex + kExSb + ((2 * hs + q) * 64 + lane) * 16) = Sb[q];
+    f32x4 P[2];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt) P[mt] = hs == 0 ? o.u0[mt] : z;
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) P[mt] = mfma_f16(o.am[mt][q], Sb[q], P[mt]);
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+      *reinterpret_cast<f32x4*>(ex + kExP + ((2 * hs + mt) * 64 + lane) * 16) = P[mt];
+  };
+  // A set k % 3 holds chunk k's -M', U0 (consumed in step k-1); B set k % 3
+  // holds chunk k's Kr^T and decays (consumed in step k+1).
+#pragma unroll
+  for (int i = 0; i < kAhead; ++i) {
+    load_a(A[i], i);
+    load_b(B[i], i);
+  }
+  publish(A[0], -1);               // fp16 S_{-1} (unused) and P_0 from the initial state
+  load_a(A[0], kAhead);
+  __syncthreads();                 // P_0 published
+  publish(A[1], 0);                // step 0: S_0 = S_{-1}; P_1
+  load_a(A[1], 1 + kAhead);
+  __syncthreads();
+  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1}
+  auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
+    constexpr int I = decltype(I_const)::value;   // = c % 3 for the B set of chunk c-1: (I+2)%3
+    constexpr int IB = (I + 2) % 3, IA = (I + 1) % 3;
+    const BOps& kb = B[IB];
+    const uint8_t* ex = exch(c - 1);
+    const f16x8 uh = xfrag(ex + kExUh, 0), ul = xfrag(ex + kExUl, 0);
+    const float* dc = decs(c - 1);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const f32x4 dv = *reinterpret_cast<const f32x4*>(dc + 16 * (4 * hs + m) + 4 * g4);
+#pragma unroll
+      for (int i2 = 0; i2 < 4; ++i2) S[m][i2] *= dv[i2];
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      S[m] = mfma_f16(kb.ak[m], uh, S[m]);
+      S[m] = mfma_f16(kb.ak[m], ul, S[m]);
+    }
+    load_b(B[IB], c - 1 + kAhead);
+    publish(A[IA], c);                                // unused past the end
+    load_a(A[IA], c + 1 + kAhead);
     __syncthreads();
   };
-  for (int c = 0; c <= nch; c += 2) {
-    step(std::integral_constant<int, 0>{}, c);
+  for (int c = 1; c <= nch; c += kAhead) {
+    step(std::integral_constant<int, 1>{}, c);
     if (c + 1 > nch) break;
-    step(std::integral_constant<int, 1>{}, c + 1);
+    step(std::integral_constant<int, 2>{}, c + 1);
+    if (c + 2 > nch) break;
+    step(std::integral_constant<int, 0>{}, c + 2);
   }
   if (a.s1) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a.s1[sbase + (int64_t)(16 * mt + 4 * g4 + i) * D + col] = S[mt][i];
+        a.s1[sbase + (int64_t)(16 * (4 * hs + m) + 4 * g4 + i) * D + col] = S[m][i];
   }
 }
 
@@ -721,7 +881,7 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
     attr_set = true;
   }
   const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * 8;
-  prefill_split_chain<<<dim3((unsigned)blocks), 256, kChainLds, s>>>(a, ws);
+  prefill_split_chain<<<dim3((unsigned)blocks), kChainThreads, kChainLds, s>>>(a, ws);
   return hipGetLastError();
 }
 

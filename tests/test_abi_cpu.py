@@ -139,8 +139,8 @@ def test_auto_route_and_workspace():
     assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
     try:
         kda.set_prefill_route(kda.ROUTE_SPLIT)
-        assert kda.workspace_size(1, 8192, 8) == (1 + 8192 // 32 + 1) * 8 * 45056
-        assert kda.workspace_size(3, 100, 2) == (3 + 3 + 1) * 2 * 45056
+        assert kda.workspace_size(1, 8192, 8) == (1 + 8192 // 32 + 1) * 8 * 49152
+        assert kda.workspace_size(3, 100, 2) == (3 + 3 + 1) * 2 * 49152
         kda.set_prefill_route(kda.ROUTE_CHUNK)
         assert kda.workspace_size(16, 40000, 32) == 0
         kda.set_prefill_route(kda.ROUTE_SERIAL)
@@ -164,8 +164,8 @@ def test_two_pass_host_validation():
     lib = kda.load()
     P = lambda x: None if x is None else ctypes.c_void_p(x)
     need = kda.records_size(1, 4, 1)
-    assert need == (1 + 0 + 1) * 1 * 45056
-    assert kda.records_size(3, 100, 2) == (3 + 3 + 1) * 2 * 45056
+    assert need == (1 + 0 + 1) * 1 * 49152
+    assert kda.records_size(3, 100, 2) == (3 + 3 + 1) * 2 * 49152
     assert kda.records_size(0, 0, 1) == 0 and kda.records_size(1, -1, 1) == 0
 
     def prep(**o):
