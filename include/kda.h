@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -104,6 +104,9 @@ typedef struct {
   int32_t block_threads;
   int64_t grid_blocks;
   float anchor_log2;   /* C = 16 * lower_bound * log2(e), as used on device */
+  int32_t windows;     /* SPLIT route: windows the chain of a single long
+                          sequence is cut into (1 = none); see below       */
+  int32_t window_chunks; /* chunks per window (0 when windows == 1)       */
 } kda_prefill_plan_t;
 
 /* ------------------------------------------------------------- prefill --
@@ -143,14 +146,25 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g,
 
 /* Bytes of workspace kda_prefill needs for these sizes with the route it
  * would choose on the current device (or the forced route): 0 for SERIAL and
- * CHUNK, (N + T_tot / 32 + 1) * H * 49152 for SPLIT. */
+ * CHUNK; for SPLIT (N + T_tot / 32 + 1) * H * 49152 bytes of chunk records,
+ * plus N * H * windows * 3 * 65536 bytes of window states when the plan cuts
+ * the chain into windows. */
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t num_heads);
 
 /* Fill *plan with what kda_prefill would launch.  `num_cus` is the device's
  * compute-unit count (<= 0: query the current device).  `route` forces a
  * route (KDA_ROUTE_AUTO to let the planner choose).  Pure host function:
- * it enqueues nothing and touches no device memory. */
+ * it enqueues nothing and touches no device memory.
+ *
+ * Windows (SPLIT route, one sequence): the chunk recurrence is affine in the
+ * state, S_end = P S_in + B over any run of chunks ([SBH]'s affine-composite
+ * windows).  When one sequence's chain would occupy only a small part of the
+ * device, the plan cuts it into `windows` runs of `window_chunks` chunks: the
+ * maps (P, B) of the inner windows are computed concurrently with the first
+ * window, the true initial state of each window follows by a short carry, and
+ * all later windows then run concurrently.  The result equals the unwindowed
+ * computation up to rounding. */
 int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                      float lower_bound, int32_t num_cus, int32_t route,
                      kda_prefill_plan_t* plan);
@@ -193,8 +207,9 @@ int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
                       int32_t num_heads, float scale, const float* initial_state,
                       float* final_state, void* out, const void* records,
                       size_t records_bytes, hipStream_t stream);
-/* (N + T_tot / 32 + 1) * H * 49152: one 49,152-byte record per chunk slot
- * and head (0 for invalid sizes). */
+/* Bytes kda_prefill_prepare / kda_prefill_chain need on the current device:
+ * the SPLIT route's workspace of kda_prefill_workspace_size (0 for invalid
+ * sizes). */
 size_t kda_prefill_records_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
 
 /* -------------------------------------------------------------- decode --

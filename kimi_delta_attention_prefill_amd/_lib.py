@@ -44,7 +44,8 @@ class KdaError(RuntimeError):
 class _Plan(ctypes.Structure):
     _fields_ = [("route", ctypes.c_int32), ("anchor_mode", ctypes.c_int32),
                 ("dv_split", ctypes.c_int32), ("block_threads", ctypes.c_int32),
-                ("grid_blocks", ctypes.c_int64), ("anchor_log2", ctypes.c_float)]
+                ("grid_blocks", ctypes.c_int64), ("anchor_log2", ctypes.c_float),
+                ("windows", ctypes.c_int32), ("window_chunks", ctypes.c_int32)]
 
 
 @dataclass
@@ -55,6 +56,8 @@ class Plan:
     block_threads: int
     grid_blocks: int
     anchor_log2: float
+    windows: int = 1
+    window_chunks: int = 0
 
 
 def load():
@@ -135,7 +138,8 @@ def plan(num_seqs: int, total_tokens: int, num_heads: int, lower_bound: float,
     p = _Plan()
     _check(load().kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, num_cus, route,
                                    ctypes.byref(p)))
-    return Plan(p.route, p.anchor_mode, p.dv_split, p.block_threads, p.grid_blocks, p.anchor_log2)
+    return Plan(p.route, p.anchor_mode, p.dv_split, p.block_threads, p.grid_blocks, p.anchor_log2,
+                p.windows, p.window_chunks)
 
 
 def set_prefill_route(route: int) -> None:

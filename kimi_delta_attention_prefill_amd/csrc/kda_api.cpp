@@ -2,6 +2,7 @@
 // See include/kda.h for the contract of every entry point.
 #include "kda.h"
 
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -139,6 +140,8 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.s0 = initial_state;
   a.s1 = final_state;
   a.out = static_cast<uint16_t*>(out);
+  a.windows = 1;
+  a.window_chunks = 0;
   return a;
 }
 
@@ -154,7 +157,7 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_
                        &plan) != KDA_OK)
     return 0;
   return plan.route == KDA_ROUTE_SPLIT
-             ? kda::split_workspace_bytes(num_seqs, total_tokens, num_heads)
+             ? kda::split_workspace_bytes(num_seqs, total_tokens, num_heads, plan.windows)
              : 0;
 }
 
@@ -195,6 +198,7 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
   std::memset(plan, 0, sizeof(*plan));
   plan->route = route;
+  plan->windows = 1;
   plan->anchor_mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
   plan->anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
   if (route == KDA_ROUTE_SERIAL) {
@@ -206,11 +210,27 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     plan->block_threads = 64 * waves;
     plan->grid_blocks = units * plan->dv_split;
   } else if (route == KDA_ROUTE_SPLIT) {
-    // Chain pass: one block (state, output and two loader waves) per
-    // 16-column value tile of each (sequence, head).
+    // Chain pass: one block (two state waves, a U wave and an output wave)
+    // per 16-column value tile of each (sequence, head); two blocks fit a CU.
     plan->dv_split = 8;
     plan->block_threads = 256;
     plan->grid_blocks = units * 8;
+    plan->windows = 1;
+    // One long sequence whose chain fills a small part of the device: cut it
+    // into windows so that phase A (first window + inner windows' maps, 1 +
+    // 2 (W - 2) chains) and phase C (W - 1 chains) each fit two blocks per CU.
+    const int64_t chunks = (total_tokens + 31) / 32;
+    if (num_seqs == 1) {
+      const int64_t tiles = units * 8, slots = 2 * (int64_t)num_cus;
+      int64_t w = 1;
+      while (w < 8 && tiles * (1 + 2 * (w + 1 - 2)) <= slots && tiles * w <= slots) ++w;
+      w = std::min<int64_t>(w, chunks / 8);   // windows of at least 8 chunks
+      if (w >= 3) {
+        const int64_t wc = (chunks + w - 1) / w;
+        plan->window_chunks = (int32_t)wc;
+        plan->windows = (int32_t)((chunks + wc - 1) / wc);
+      }
+    }
   } else {
     // One block per (sequence, head, value slice).  Two 64-column slices
     // halve the per-block chain work at the cost of duplicated chunk
@@ -243,12 +263,14 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
   if (rc != KDA_OK) return rc;
   if (plan.route == KDA_ROUTE_SPLIT &&
       (rc = check_records(fn, workspace, workspace_bytes,
-                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads,
+                                                     plan.windows))) != KDA_OK)
     return rc;
 
-  const kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                       num_heads, scale, lower_bound, initial_state, final_state,
-                                       out);
+  kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                                 scale, lower_bound, initial_state, final_state, out);
+  a.windows = plan.windows;
+  a.window_chunks = plan.window_chunks;
   hipError_t e;
   if (plan.route == KDA_ROUTE_SERIAL)
     e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
@@ -262,9 +284,22 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
   return ok();
 }
 
+// The SPLIT route's plan for these sizes on the current device.
+int split_plan(const char* fn, int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+               float lower_bound, kda_prefill_plan_t* plan) {
+  const int rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0,
+                                  KDA_ROUTE_SPLIT, plan);
+  if (rc != KDA_OK) return fail(rc, "%s: %s", fn, kda_last_error());
+  return KDA_OK;
+}
+
 size_t kda_prefill_records_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
   if (num_seqs <= 0 || total_tokens < 0 || total_tokens > INT32_MAX || num_heads < 1) return 0;
-  return kda::split_workspace_bytes(num_seqs, total_tokens, num_heads);
+  kda_prefill_plan_t plan;
+  if (kda_prefill_plan(num_seqs, total_tokens, num_heads, -1.0f, 0, KDA_ROUTE_SPLIT, &plan) !=
+      KDA_OK)
+    return 0;
+  return kda::split_workspace_bytes(num_seqs, total_tokens, num_heads, plan.windows);
 }
 
 int kda_prefill_prepare(const void* q, const void* k, const void* v, const void* g,
@@ -278,13 +313,18 @@ int kda_prefill_prepare(const void* q, const void* k, const void* v, const void*
   if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
   if (num_seqs == 0) return ok();
   if ((rc = check_inputs(fn, q, k, v, g, beta, cu_seqlens, total_tokens)) != KDA_OK) return rc;
-  if ((rc = check_records(fn, records, records_bytes,
-                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+  kda_prefill_plan_t plan;
+  if ((rc = split_plan(fn, num_seqs, total_tokens, num_heads, lower_bound, &plan)) != KDA_OK)
     return rc;
-  const kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens,
-                                       num_heads, 1.f, lower_bound, nullptr, nullptr, nullptr);
-  const int mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
-  const hipError_t e = kda::launch_prefill_split_prepare(a, mode, records, stream);
+  if ((rc = check_records(fn, records, records_bytes,
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads,
+                                                     plan.windows))) != KDA_OK)
+    return rc;
+  kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                                 1.f, lower_bound, nullptr, nullptr, nullptr);
+  a.windows = plan.windows;
+  a.window_chunks = plan.window_chunks;
+  const hipError_t e = kda::launch_prefill_split_prepare(a, plan.anchor_mode, records, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();
 }
@@ -302,12 +342,17 @@ int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
   if ((rc = check_outputs(fn, initial_state, final_state, out, num_seqs, num_heads,
                           total_tokens)) != KDA_OK)
     return rc;
+  kda_prefill_plan_t plan;
+  if ((rc = split_plan(fn, num_seqs, total_tokens, num_heads, -1.f, &plan)) != KDA_OK) return rc;
   if ((rc = check_records(fn, records, records_bytes,
-                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads))) != KDA_OK)
+                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads,
+                                                     plan.windows))) != KDA_OK)
     return rc;
-  const kda::PrefillArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens,
-                                       num_seqs, total_tokens, num_heads, scale, -1.f,
-                                       initial_state, final_state, out);
+  kda::PrefillArgs a = make_args(nullptr, nullptr, nullptr, nullptr, nullptr, cu_seqlens,
+                                 num_seqs, total_tokens, num_heads, scale, -1.f, initial_state,
+                                 final_state, out);
+  a.windows = plan.windows;
+  a.window_chunks = plan.window_chunks;
   const hipError_t e = kda::launch_prefill_split_chain(a, records, stream);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
   return ok();

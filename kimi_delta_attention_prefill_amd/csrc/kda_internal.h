@@ -26,6 +26,8 @@ struct PrefillArgs {
   const float* s0;        // fp32 [N, H, 128, 128] or null
   float* s1;              // fp32 [N, H, 128, 128] or null
   uint16_t* out;          // bf16 [T, H, 128]
+  int32_t windows;        // split route: windows per sequence (1 = none)
+  int32_t window_chunks;  // split route: chunks per window (0 = none)
 };
 
 struct DecodeArgs {
@@ -59,7 +61,8 @@ hipError_t launch_prefill_split_prepare(const PrefillArgs& a, int anchor_mode, v
                                         hipStream_t s);
 hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspace,
                                       hipStream_t s);
-size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads);
+size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                             int32_t windows);
 // Decode step; `cols` = value columns per block (32, 64 or 128).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
 

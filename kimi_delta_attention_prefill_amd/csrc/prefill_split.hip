@@ -64,9 +64,21 @@ constexpr int kRecStageBytes = 32768;
 constexpr int kRecOffU0 = 32768;
 constexpr int kRecBytes = 49152;
 
-size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
+// Window states after the records: per (sequence, head, window) the end
+// state E (zero-state end for windows >= 1, true end for window 0), the map
+// P and the true initial state SI, 64 KiB each.
+constexpr int64_t kStateBytes = 128 * 128 * 4;
+
+size_t split_records_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {
   const int64_t slots = (int64_t)num_seqs + total_tokens / 32 + 1;
   return (size_t)slots * (size_t)num_heads * (size_t)kRecBytes;
+}
+
+size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
+                             int32_t windows) {
+  size_t b = split_records_bytes(num_seqs, total_tokens, num_heads);
+  if (windows > 1) b += (size_t)num_seqs * num_heads * windows * 3 * kStateBytes;
+  return b;
 }
 
 namespace {
@@ -144,9 +156,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rb =
       make_buffer(a.beta + (int64_t)t0 * H + h, (uint32_t)(((L - 1) * H + 1) * 2));
-  // The previous chunk of the same sequence (chunk 0: an empty range, so its
-  // keys and gates read as zero, which gives W = 0 and M' = M).
-  const bool has_prev = c > 0;
+  // The previous chunk of the same sequence (chunk 0, and the first chunk of
+  // a window: an empty range, so its keys and gates read as zero, which
+  // gives W = 0 and M' = M and lets a chain start there).
+  const bool has_prev = c > 0 && (a.window_chunks <= 0 || c % a.window_chunks != 0);
   const int64_t base_prev = has_prev ? base - (int64_t)CH * H * D : base;
   const uint32_t prev_bytes = has_prev ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
@@ -572,13 +585,21 @@ struct QOps {            // output wave: Qg and Mqk of chunk c-1
   f16x8 aq[2][4], amq[2];
 };
 
-__global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs a,
-                                                                     const uint8_t* __restrict__ ws) {
-  extern __shared__ __align__(16) unsigned char lds[];
+// One chain run: chunks [cb, ce) of sequence n, head h, 16-column tile.
+struct ChainJob {
+  int n, h, tile;
+  int cb, ce;
+  const float* s_init;   // [128][128] state entering chunk cb, or null
+  bool identity;         // start from the identity instead (a window's map)
+  bool with_u0;          // false: drop U0 (the map of a window is linear)
+  bool with_out;         // store the outputs of the chunks
+  float* s_final;        // [128][128] state after chunk ce-1, or null
+};
+
+__device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* __restrict__ ws,
+                                           unsigned char* lds, const ChainJob job) {
   const int H = a.num_heads;
-  const int units = a.num_seqs * H;
-  const int unit = blockIdx.x % units, tile = blockIdx.x / units;
-  const int n = unit / H, h = unit % H;
+  const int n = job.n, h = job.h, tile = job.tile;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4;
   const int col = 16 * tile + (lane & 15);
@@ -586,8 +607,9 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const int nch = (eos - bos + CH - 1) / CH;
-  const int64_t slot0 = (int64_t)n + bos / CH;
+  const int nch = max(0, job.ce - job.cb);             // chunks of this run
+  const int64_t slot0 = (int64_t)n + bos / CH + job.cb;
+  const int tok0 = bos + CH * job.cb;
 
   auto exch = [&](int c) __attribute__((always_inline)) { return lds + (c & 1) * kExchBytes; };
   // Chunk c's 128 decays 2^{G_L}, written by the U wave from its record loads
@@ -619,6 +641,10 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
 
   if (wave == 3) {
     // ------------------------------------------------------------- output
+    if (!job.with_out) {
+      for (int c = 0; c < nch + 2; ++c) __syncthreads();
+      return;
+    }
     QOps q[kAhead];
     auto load_q = [&](QOps& o, int c) __attribute__((always_inline)) {
       const __amdgpu_buffer_rsrc_t r = rec(c);
@@ -656,7 +682,7 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
       }
       load_q(q[I], c - 1 + kAhead);
       // rows t >= L of a final partial chunk fall outside the range and are dropped
-      const int t0 = bos + CH * (c - 1);
+      const int t0 = tok0 + CH * (c - 1);
       const int L = min(CH, eos - t0);
       const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
           a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
@@ -754,18 +780,14 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
   // Wave hs owns key rows 64hs..64hs+63: accumulator tiles mt = 4hs..4hs+3,
   // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.
   const int hs = wave;
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
   f32x4 S[4];
-  if (a.s0) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[m][i] = a.s0[sbase + (int64_t)(16 * (4 * hs + m) + 4 * g4 + i) * D + col];
-  } else {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) S[m] = z;
-  }
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * (4 * hs + m) + 4 * g4 + i;
+      S[m][i] = job.s_init ? job.s_init[row * D + col] : (job.identity && row == col ? 1.f : 0.f);
+    }
   AOps A[kAhead];
   BOps B[kAhead];
   auto load_a = [&](AOps& o, int c) __attribute__((always_inline)) {
@@ -802,7 +824,7 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
       *reinterpret_cast<f16x8*>(ex + kExSb + ((2 * hs + q) * 64 + lane) * 16) = Sb[q];
     f32x4 P[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) P[mt] = hs == 0 ? o.u0[mt] : z;
+    for (int mt = 0; mt < 2; ++mt) P[mt] = (hs == 0 && job.with_u0) ? o.u0[mt] : z;
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -855,13 +877,208 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
     if (c + 2 > nch) break;
     step(std::integral_constant<int, 0>{}, c + 2);
   }
-  if (a.s1) {
+  if (job.s_final) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        a.s1[sbase + (int64_t)(16 * (4 * hs + m) + 4 * g4 + i) * D + col] = S[m][i];
+        job.s_final[(16 * (4 * hs + m) + 4 * g4 + i) * D + col] = S[m][i];
   }
+}
+
+__global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs a,
+                                                                     const uint8_t* __restrict__ ws) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int H = a.num_heads;
+  const int units = a.num_seqs * H;
+  const int unit = blockIdx.x % units, tile = blockIdx.x / units;
+  const int n = unit / H, h = unit % H;
+  const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
+  const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
+  const int64_t sb = ((int64_t)n * H + h) * D * D;
+  ChainJob job;
+  job.n = n; job.h = h; job.tile = tile;
+  job.cb = 0; job.ce = (eos - bos + CH - 1) / CH;
+  job.s_init = a.s0 ? a.s0 + sb : nullptr;
+  job.identity = false; job.with_u0 = true; job.with_out = true;
+  job.s_final = a.s1 ? a.s1 + sb : nullptr;
+  chain_body(a, ws, lds, job);
+}
+
+// ------------------------------------------------------------ windows
+// A long sequence is cut into windows of `window_chunks` chunks whose first
+// chunks carry M' = M and W = 0, so a chain can start at any window.  The
+// state map of a window is affine, S_end = P_w S_in + B_w, which gives
+//   phase A (all at once): window 0 from the initial state; for every window
+//            w that is neither first nor last, B_w (its chain from zero) and
+//            P_w (its chain from the identity, without U0);
+//   carry:   S_in(1) = end of window 0, S_in(w+1) = P_w S_in(w) + B_w;
+//   phase C (all at once): windows 1.. from S_in(w), with outputs.
+// About 2 x window_chunks chain steps instead of the sequence's chunk count.
+struct WinView {
+  float* base;
+  int H, W;
+  __device__ float* at(int n, int h, int w, int kind) const {   // kind 0 E, 1 P, 2 SI
+    return base + ((((int64_t)n * H + h) * W + w) * 3 + kind) * (128 * 128);
+  }
+};
+
+__device__ __forceinline__ int seq_chunks(const PrefillArgs& a, int n) {
+  const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
+  const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
+  return (eos - bos + CH - 1) / CH;
+}
+
+__global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillArgs a,
+                                                                        const uint8_t* __restrict__ ws,
+                                                                        WinView wv) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows, WC = a.window_chunks;
+  const int jobs = 1 + 2 * (W - 2);
+  const int tile = blockIdx.x / (units * jobs), r = blockIdx.x % (units * jobs);
+  const int unit = r % units, j = r / units;
+  const int n = unit / H, h = unit % H;
+  const int nch = seq_chunks(a, n);
+  const int nwin = max(1, (nch + WC - 1) / WC);
+  const int64_t sb = ((int64_t)n * H + h) * D * D;
+  ChainJob job;
+  job.n = n; job.h = h; job.tile = tile;
+  if (j == 0) {
+    job.cb = 0; job.ce = min(WC, nch);
+    job.s_init = a.s0 ? a.s0 + sb : nullptr;
+    job.identity = false; job.with_u0 = true; job.with_out = true;
+    job.s_final = nwin <= 1 ? (a.s1 ? a.s1 + sb : nullptr) : wv.at(n, h, 0, 0);
+  } else {
+    const bool map = j > W - 2;
+    const int w = map ? j - (W - 2) : j;
+    if (w >= nwin - 1) return;            // the last window needs neither
+    job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
+    job.s_init = nullptr;
+    job.identity = map; job.with_u0 = !map; job.with_out = false;
+    job.s_final = wv.at(n, h, w, map ? 1 : 0);
+  }
+  chain_body(a, ws, lds, job);
+}
+
+// S_in(w+1) = P_w S_in(w) + B_w for w = 1 .. nwin-2 (S_in(1) = E_0, read in
+// place by window 1), for one (sequence, head) and 16-column tile.  Wave q
+// owns output row tiles 2q, 2q+1; P as fp16 hi + lo A fragments straight from
+// memory (next step's prefetched), the current S tile as fp16 hi + lo B
+// fragments in LDS (a step's accumulators are the next step's K step q), three
+// products per pair, FP32 accumulation on B_w.
+__global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinView wv) {
+  __shared__ f16x8 xh[4][64], xl[4][64];
+  const int H = a.num_heads, units = a.num_seqs * H, WC = a.window_chunks;
+  const int unit = blockIdx.x % units, tile = blockIdx.x / units;
+  const int n = unit / H, h = unit % H;
+  const int nch = seq_chunks(a, n);
+  const int nwin = max(1, (nch + WC - 1) / WC);
+  if (nwin < 3) return;
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int col = 16 * tile + l16;
+  // rows of this lane's accumulator entries: tile 2q+e, row 16(2q+e) + 4g4 + i
+  auto row_of = [&](int e, int i) __attribute__((always_inline)) { return 32 * q + 16 * e + 4 * g4 + i; };
+  auto put_frags = [&](const float* v) __attribute__((always_inline)) {
+    f16x8 hi, lo;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      _Float16 hh, ll;
+      split_f16(v[j], hh, ll);
+      hi[j] = hh;
+      lo[j] = ll;
+    }
+    xh[q][lane] = hi;
+    xl[q][lane] = lo;
+  };
+  typedef float f32x4v __attribute__((ext_vector_type(4)));
+  // P_w fragments of this wave's row tiles: [e][kstep p][half of the K-slots]
+  auto load_p = [&](f32x4v (&pf)[2][4][2], int w) __attribute__((always_inline)) {
+    const float* P = wv.at(n, h, w, 1);
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const float* r = P + (32 * q + 16 * e + l16) * 128 + 32 * p + 4 * g4;
+        pf[e][p][0] = *reinterpret_cast<const f32x4v*>(r);
+        pf[e][p][1] = *reinterpret_cast<const f32x4v*>(r + 16);
+      }
+  };
+  {
+    const float* e0 = wv.at(n, h, 0, 0);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * e + i] = e0[row_of(e, i) * 128 + col];
+    put_frags(v);
+  }
+  f32x4v pf[2][4][2];
+  load_p(pf, 1);
+  for (int w = 1; w + 1 < nwin; ++w) {
+    __syncthreads();
+    f16x8 sh[4], sl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      sh[p] = xh[p][lane];
+      sl[p] = xl[p][lane];
+    }
+    const float* B = wv.at(n, h, w, 0);
+    f32x4 acc[2];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[e][i] = B[row_of(e, i) * 128 + col];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        f16x8 ph, pl;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          _Float16 hh, ll;
+          split_f16(pf[e][p][j >> 2][j & 3], hh, ll);
+          ph[j] = hh;
+          pl[j] = ll;
+        }
+        acc[e] = mfma_f16(ph, sh[p], acc[e]);
+        acc[e] = mfma_f16(ph, sl[p], acc[e]);
+        acc[e] = mfma_f16(pl, sh[p], acc[e]);
+      }
+    if (w + 2 < nwin) load_p(pf, w + 1);
+    float* si = wv.at(n, h, w + 1, 2);
+    float v[8];
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        v[4 * e + i] = acc[e][i];
+        si[row_of(e, i) * 128 + col] = acc[e][i];
+      }
+    __syncthreads();
+    put_frags(v);
+  }
+}
+
+__global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillArgs a,
+                                                                        const uint8_t* __restrict__ ws,
+                                                                        WinView wv) {
+  extern __shared__ __align__(16) unsigned char lds[];
+  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows, WC = a.window_chunks;
+  const int tile = blockIdx.x / (units * (W - 1)), r = blockIdx.x % (units * (W - 1));
+  const int unit = r % units, w = 1 + r / units;
+  const int n = unit / H, h = unit % H;
+  const int nch = seq_chunks(a, n);
+  const int nwin = max(1, (nch + WC - 1) / WC);
+  if (w >= nwin) return;
+  const int64_t sb = ((int64_t)n * H + h) * D * D;
+  ChainJob job;
+  job.n = n; job.h = h; job.tile = tile;
+  job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
+  job.s_init = w == 1 ? wv.at(n, h, 0, 0) : wv.at(n, h, w, 2);
+  job.identity = false; job.with_u0 = true; job.with_out = true;
+  job.s_final = w == nwin - 1 ? (a.s1 ? a.s1 + sb : nullptr) : nullptr;
+  chain_body(a, ws, lds, job);
 }
 
 template <int MODE>
@@ -872,16 +1089,38 @@ hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <class K>
+hipError_t set_lds(K* kernel, bool& done) {
+  if (done) return hipSuccess;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, kChainLds);
+  if (e == hipSuccess) done = true;   // idempotent; a race only repeats the call
+  return e;
+}
+
 hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) {
-  static bool attr_set = false;   // idempotent; a race only repeats the call
-  if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_split_chain),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kChainLds);
+  const int64_t units = (int64_t)a.num_seqs * a.num_heads;
+  if (a.windows <= 1) {
+    static bool done = false;
+    hipError_t e = set_lds(&prefill_split_chain, done);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    prefill_split_chain<<<dim3((unsigned)(units * 8)), kChainThreads, kChainLds, s>>>(a, ws);
+    return hipGetLastError();
   }
-  const int64_t blocks = (int64_t)a.num_seqs * a.num_heads * 8;
-  prefill_split_chain<<<dim3((unsigned)blocks), kChainThreads, kChainLds, s>>>(a, ws);
+  static bool done_a = false, done_c = false;
+  hipError_t e = set_lds(&prefill_split_window_a, done_a);
+  if (e == hipSuccess) e = set_lds(&prefill_split_window_c, done_c);
+  if (e != hipSuccess) return e;
+  WinView wv;
+  wv.base = reinterpret_cast<float*>(const_cast<uint8_t*>(ws) +
+                                     split_records_bytes(a.num_seqs, a.total_tokens, a.num_heads));
+  wv.H = a.num_heads;
+  wv.W = a.windows;
+  const int jobs = 1 + 2 * (a.windows - 2);
+  prefill_split_window_a<<<dim3((unsigned)(units * jobs * 8)), kChainThreads, kChainLds, s>>>(a, ws, wv);
+  prefill_split_carry<<<dim3((unsigned)(units * 8)), 256, 0, s>>>(a, wv);
+  prefill_split_window_c<<<dim3((unsigned)(units * (a.windows - 1) * 8)), kChainThreads, kChainLds, s>>>(
+      a, ws, wv);
   return hipGetLastError();
 }
 

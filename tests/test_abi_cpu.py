@@ -139,7 +139,9 @@ def test_auto_route_and_workspace():
     assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
     try:
         kda.set_prefill_route(kda.ROUTE_SPLIT)
-        assert kda.workspace_size(1, 8192, 8) == (1 + 8192 // 32 + 1) * 8 * 49152
+        # one long sequence: records plus the window states (E, P, SI per window and head)
+        assert kda.workspace_size(1, 8192, 8) == ((1 + 8192 // 32 + 1) * 8 * 49152
+                                                  + 1 * 8 * 5 * 3 * 65536)
         assert kda.workspace_size(3, 100, 2) == (3 + 3 + 1) * 2 * 49152
         kda.set_prefill_route(kda.ROUTE_CHUNK)
         assert kda.workspace_size(16, 40000, 32) == 0
@@ -196,3 +198,20 @@ def test_two_pass_host_validation():
     assert chain(s0=0x20000, s1=0x20000 + 4096) == E and "overlap" in kda.last_error()
     assert chain(rec=None) == W and chain(nbytes=100) == W
     assert chain(N=0, cu=None, out=None, rec=None, nbytes=0) == 0
+
+
+def test_plan_windows():
+    # one sequence whose chain would use few CUs is cut into windows such that
+    # phase A (1 + 2 (W - 2) chains) and phase C (W - 1 chains) fit two blocks per CU
+    p = kda.plan(1, 8192, 8, -5.0, 256, kda.ROUTE_SPLIT)
+    assert (p.windows, p.window_chunks) == (5, 52)
+    assert 64 * (1 + 2 * (p.windows - 2)) <= 512 and 64 * (p.windows - 1) <= 512
+    p = kda.plan(1, 3000, 3, -8.0, 256, kda.ROUTE_SPLIT)
+    assert p.windows == 8 and p.window_chunks == 12          # 94 chunks: 7 x 12 + 10
+    assert (p.windows - 1) * p.window_chunks < 94 <= p.windows * p.window_chunks
+    p = kda.plan(1, 1000, 8, -5.0, 256, kda.ROUTE_SPLIT)   # 32 chunks: windows of >= 8 chunks
+    assert (p.windows, p.window_chunks) == (4, 8)
+    for args in ((1, 64, 2), (2, 345, 4), (1, 8192, 32), (1, 700, 8)):
+        p = kda.plan(*args, -5.0, 256, kda.ROUTE_SPLIT)
+        assert (p.windows, p.window_chunks) == (1, 0), args   # too short, too many units, or N > 1
+    assert kda.plan(1, 8192, 8, -5.0, 256, kda.ROUTE_CHUNK).windows == 1

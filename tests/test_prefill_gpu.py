@@ -245,3 +245,48 @@ def test_two_pass_equals_split_route(dev, which):
     torch.cuda.synchronize()
     assert rec.numel() >= kda.records_size(case.num_seqs, case.total_tokens, case.num_heads)
     assert torch.equal(o, o_ref) and torch.equal(f, f_ref)
+
+
+@pytest.mark.parametrize("T,H,lb,state", [(3000, 3, -8.0, 0.02), (5003, 1, -5.0, 0.02),
+                                          (1500, 2, -1.0, None)])
+def test_split_windows(dev, T, H, lb, state):
+    """One long sequence on the split route is cut into windows (maps of the inner
+    windows, carry, windows from their true initial states); ragged tails, split-16
+    anchoring and a missing initial state included."""
+    plan = kda.plan(1, T, H, lb, 0, kda.ROUTE_SPLIT)
+    assert plan.windows >= 3
+    case = make_prefill_case([T], H, lb, state, seed=17 + T, name=f"windows_T{T}_H{H}")
+    o, f = run_gpu(case, kda.ROUTE_SPLIT, dev)
+    compare(case, o, f)
+
+
+def test_split_windows_graph_replay(dev):
+    case = make_prefill_case([1500], 2, -5.0, 0.02, seed=23, name="windows_graph")
+    to = lambda t: t.to(dev)
+    q, k, v, g, b, cu, s0 = (to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                             to(case.cu_seqlens), to(case.initial_state))
+    out = torch.empty((case.total_tokens, 2, 128), dtype=torch.bfloat16, device=dev)
+    fin = torch.empty_like(s0)
+    kda.set_prefill_route(kda.ROUTE_SPLIT)
+    try:
+        assert kda.plan(1, case.total_tokens, 2, -5.0, 0, kda.ROUTE_SPLIT).windows >= 3
+        ws = torch.empty(kda.workspace_size(1, case.total_tokens, 2), dtype=torch.uint8, device=dev)
+        kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
+                    initial_state=s0, final_state=fin, out=out, workspace=ws)
+        torch.cuda.synchronize()
+        ref_o, ref_f = out.clone(), fin.clone()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            kda.prefill(q, k, v, g, b, cu, scale=case.scale, lower_bound=case.lower_bound,
+                        initial_state=s0, final_state=fin, out=out, workspace=ws)
+        for _ in range(3):
+            out.fill_(0)
+            fin.fill_(0)
+            _ = torch.randn(1000, device=dev).sum()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref_o) and torch.equal(fin, ref_f)
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    compare(case, ref_o, ref_f)
