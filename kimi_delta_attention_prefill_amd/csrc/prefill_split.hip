@@ -349,14 +349,28 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
       bl[16 + l16] = beta[1];
     }
   }
-  // value rows for U0, consumed after the inverse
-  u32x4 vw[4][2];
+  // Everything the rest reads from memory is requested now, so that the
+  // inverse hides the latency: the parked (b Kg)^T fragments (once this
+  // wave's stores have completed: each lane reads back what it wrote), the
+  // value rows, and the previous chunk's keys and gates.
+  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
+  __builtin_amdgcn_sched_barrier(0);
+  f16x8 Xh[8], Xl[8];
+#pragma unroll
+  for (int mc = 0; mc < 8; ++mc) {
+    Xh[mc] = *reinterpret_cast<const f16x8*>(xh_park + (mc * 64 + lane) * 16);
+    Xl[mc] = *reinterpret_cast<const f16x8*>(xl_park + (mc * 64 + lane) * 16);
+  }
+  u32x4 vw[4][2], kpw[4][2], gpw[4][2];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf)
+    for (int hf = 0; hf < 2; ++hf) {
       vw[p][hf] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
           rv, (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 8 * g4) * 2, 0, 0));
+      kpw[p][hf] = load8(rkp, hf, p);
+      gpw[p][hf] = load8(rgp, hf, p);
+    }
   __syncthreads();
 
   // T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane m
@@ -424,16 +438,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     }
   }
 
-  // Read the parked (b Kg)^T fragments back before their areas are overwritten
-  // (all earlier stores have completed first).
+  // The parked fragments must have arrived before their areas are overwritten.
   __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  f16x8 Xh[8], Xl[8];
-#pragma unroll
-  for (int mc = 0; mc < 8; ++mc) {
-    Xh[mc] = *reinterpret_cast<const f16x8*>(xh_park + (mc * 64 + lane) * 16);
-    Xl[mc] = *reinterpret_cast<const f16x8*>(xl_park + (mc * 64 + lane) * 16);
-  }
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0): the reads complete before any store below
   __builtin_amdgcn_sched_barrier(0);
 
   // U0 = T Diag(b) V per 16-column tile: V transposed by the one-hot product.
@@ -467,23 +473,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
-    u32x4 kpw[2], gpw[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      kpw[hf] = load8(rkp, hf, p);
-      gpw[hf] = load8(rgp, hf, p);
-    }
     float dp[8];
     f16x8 krp[2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s0 = row_scan16(bf16_elem(gpw[0], j));
+      const float s0 = row_scan16(bf16_elem(gpw[p][0], j));
       const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(bf16_elem(gpw[1], j)) + b0;
+      const float s1 = row_scan16(bf16_elem(gpw[p][1], j)) + b0;
       const float gl = __shfl(s1, 15, 16) * kLog2e;
       dp[j] = fast_exp2(gl);
-      krp[0][j] = static_cast<_Float16>(bf16_elem(kpw[0], j) * fast_exp2(gl - s0 * kLog2e));
-      krp[1][j] = static_cast<_Float16>(bf16_elem(kpw[1], j) * fast_exp2(gl - s1 * kLog2e));
+      krp[0][j] = static_cast<_Float16>(bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
+      krp[1][j] = static_cast<_Float16>(bf16_elem(kpw[p][1], j) * fast_exp2(gl - s1 * kLog2e));
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
