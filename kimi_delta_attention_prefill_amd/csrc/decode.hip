@@ -28,14 +28,21 @@ constexpr int kThreads = 256;
 template <bool BF16>
 struct StateIO;
 
+// The state of a row is read once and written once per step, so its traffic
+// is marked non-temporal (streamed past the caches).
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
+
 template <>
 struct StateIO<false> {
   using elem = float;
   static __device__ __forceinline__ float4 load(const float* p) {
-    return *reinterpret_cast<const float4*>(p);
+    const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
   }
   static __device__ __forceinline__ void store(float* p, float4 x) {
-    *reinterpret_cast<float4*>(p) = x;
+    const f32x4v v = {x.x, x.y, x.z, x.w};
+    __builtin_nontemporal_store(v, reinterpret_cast<f32x4v*>(p));
   }
 };
 
@@ -43,14 +50,14 @@ template <>
 struct StateIO<true> {
   using elem = uint16_t;
   static __device__ __forceinline__ float4 load(const uint16_t* p) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    return make_float4(bf16lo(w.x), bf16hi(w.x), bf16lo(w.y), bf16hi(w.y));
+    const u32x2v w = __builtin_nontemporal_load(reinterpret_cast<const u32x2v*>(p));
+    return make_float4(bf16lo(w[0]), bf16hi(w[0]), bf16lo(w[1]), bf16hi(w[1]));
   }
   static __device__ __forceinline__ void store(uint16_t* p, float4 x) {
-    uint2 w;
-    w.x = (uint32_t)f32_to_bf16(x.x) | ((uint32_t)f32_to_bf16(x.y) << 16);
-    w.y = (uint32_t)f32_to_bf16(x.z) | ((uint32_t)f32_to_bf16(x.w) << 16);
-    *reinterpret_cast<uint2*>(p) = w;
+    u32x2v w;
+    w[0] = (uint32_t)f32_to_bf16(x.x) | ((uint32_t)f32_to_bf16(x.y) << 16);
+    w[1] = (uint32_t)f32_to_bf16(x.z) | ((uint32_t)f32_to_bf16(x.w) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x2v*>(p));
   }
 };
 
