@@ -54,6 +54,10 @@ def _load():
                                        ctypes.c_int, ctypes.c_int, ctypes.c_double, dp, dp, dp,
                                        ctypes.c_int]
     lib.kda_oracle_prefill.restype = ctypes.c_int
+    lib.kda_oracle_prefill_snapshots.argtypes = [dp, dp, dp, dp, dp, ip, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_double, dp,
+                                                 dp, dp, ctypes.c_int64, dp, ctypes.c_int]
+    lib.kda_oracle_prefill_snapshots.restype = ctypes.c_int
     lib.kda_oracle_decode.argtypes = [dp, dp, dp, dp, dp, dp, ctypes.c_int64, ip, ctypes.c_int,
                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_double, dp,
                                       ctypes.c_int]
@@ -86,12 +90,14 @@ def _ptr(a: np.ndarray | None):
 
 
 def prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None, want_final=True,
-            threads=None):
+            threads=None, snapshot_every=None):
     """Token-serial FP64 prefill over packed sequences.
 
     q, k, g: [T, H, dk]; v: [T, H, dv]; beta: [T, H]; cu_seqlens: [N+1];
     initial_state: [N, H, dk, dv] or None (zeros).
-    Returns (out [T, H, dv] float64, final_state [N, H, dk, dv] float64 or None).
+    Returns (out [T, H, dv] float64, final_state [N, H, dk, dv] float64 or None),
+    and with ``snapshot_every = I`` also a list over sequences of the states
+    after I, 2I, ... tokens ([floor(len_n / I), H, dk, dv] float64 each).
     """
     q, k, v, g, beta = (_f64(x) for x in (q, k, v, g, beta))
     cu = np.ascontiguousarray(np.asarray(
@@ -106,13 +112,22 @@ def prefill(q, k, v, g, beta, cu_seqlens, scale, initial_state=None, want_final=
         assert s0.shape == (N, H, dk, dv)
     out = np.zeros((T, H, dv), dtype=np.float64)
     s1 = np.zeros((N, H, dk, dv), dtype=np.float64) if want_final else None
-    rc = _load().kda_oracle_prefill(
+    every = int(snapshot_every or 0)
+    counts = [int(cu[n + 1] - cu[n]) // every for n in range(N)] if every else []
+    snaps = np.zeros((max(1, sum(counts)), H, dk, dv), dtype=np.float64) if every else None
+    rc = _load().kda_oracle_prefill_snapshots(
         _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), N, H, dk, dv, float(scale),
-        _ptr(s0), _ptr(s1), _ptr(out), int(threads or default_threads()))
+        _ptr(s0), _ptr(s1), _ptr(out), every, _ptr(snaps), int(threads or default_threads()))
     if rc != 0:
         raise ValueError(f"kda_oracle_prefill failed with code {rc}")
-    return out, s1
+    if not every:
+        return out, s1
+    per_seq, at = [], 0
+    for cnt in counts:
+        per_seq.append(snaps[at:at + cnt])
+        at += cnt
+    return out, s1, per_seq
 
 
 def decode(q, k, v, g, beta, pool, slot_indices, scale, threads=None):

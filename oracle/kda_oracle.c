@@ -147,6 +147,9 @@ typedef struct {
   double scale;
   const double *s0;
   double *s1, *out;
+  int64_t snap_every;      /* 0: no snapshots */
+  double *snaps;           /* [sum_n floor(len_n / snap_every)][H][dk][dv] */
+  const int64_t *snap_base;/* first snapshot row of each sequence */
 } prefill_ctx;
 
 static void prefill_unit(void *vctx, int64_t unit, double *scratch) {
@@ -163,10 +166,23 @@ static void prefill_unit(void *vctx, int64_t unit, double *scratch) {
     const int64_t th = t * H + h;
     kda_step(S, dk, dv, c->q + th * dk, c->k + th * dk, c->v + th * dv,
              c->g + th * dk, c->beta[th], c->scale, w, u, c->out + th * dv);
+    const int64_t done = t + 1 - c->cu[n];   /* tokens of this sequence processed */
+    if (c->snap_every > 0 && done % c->snap_every == 0) {
+      const int64_t row = c->snap_base[n] + done / c->snap_every - 1;
+      memcpy(c->snaps + (row * H + h) * sz, S, sizeof(double) * (size_t)sz);
+    }
   }
   if (c->s1)
     memcpy(c->s1 + ((int64_t)n * H + h) * sz, S, sizeof(double) * (size_t)sz);
 }
+
+int kda_oracle_prefill_snapshots(const double *q, const double *k, const double *v,
+                                 const double *g, const double *beta,
+                                 const int64_t *cu_seqlens, int num_seqs, int num_heads,
+                                 int dk, int dv, double scale,
+                                 const double *initial_state, double *final_state,
+                                 double *out, int64_t snap_every, double *snapshots,
+                                 int num_threads);
 
 /* Packed variable-length prefill.  initial_state may be NULL (zeros);
  * final_state may be NULL (not stored) and may equal initial_state.
@@ -184,12 +200,47 @@ int kda_oracle_prefill(const double *q, const double *k, const double *v,
     if (cu_seqlens[n + 1] < cu_seqlens[n]) return KDA_ORACLE_EINVAL;
   if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !g || !beta || !out))
     return KDA_ORACLE_EINVAL;
+  return kda_oracle_prefill_snapshots(q, k, v, g, beta, cu_seqlens, num_seqs, num_heads, dk,
+                                      dv, scale, initial_state, final_state, out, 0, NULL,
+                                      num_threads);
+}
+
+/* As kda_oracle_prefill, and in addition the state after every `snap_every`
+ * tokens of each sequence (after tokens snap_every, 2 snap_every, ... up to
+ * the sequence length), stored row by row in sequence order:
+ * snapshots[sum_{m<n} floor(len_m / snap_every) + j - 1] is the state of
+ * sequence n after j * snap_every tokens, [H][dk][dv] each. */
+int kda_oracle_prefill_snapshots(const double *q, const double *k, const double *v,
+                                 const double *g, const double *beta,
+                                 const int64_t *cu_seqlens, int num_seqs, int num_heads,
+                                 int dk, int dv, double scale,
+                                 const double *initial_state, double *final_state,
+                                 double *out, int64_t snap_every, double *snapshots,
+                                 int num_threads) {
+  if (num_seqs < 0 || num_heads < 1 || dk < 1 || dv < 1 || !cu_seqlens)
+    return KDA_ORACLE_EINVAL;
+  if (cu_seqlens[0] != 0) return KDA_ORACLE_EINVAL;
+  for (int n = 0; n < num_seqs; ++n)
+    if (cu_seqlens[n + 1] < cu_seqlens[n]) return KDA_ORACLE_EINVAL;
+  if (cu_seqlens[num_seqs] > 0 && (!q || !k || !v || !g || !beta || !out))
+    return KDA_ORACLE_EINVAL;
+  if (snap_every < 0 || (snap_every > 0 && !snapshots)) return KDA_ORACLE_EINVAL;
+  int64_t *base = NULL;
+  if (snap_every > 0) {
+    base = (int64_t *)malloc(sizeof(int64_t) * (size_t)(num_seqs + 1));
+    if (!base) return KDA_ORACLE_ENOMEM;
+    base[0] = 0;
+    for (int n = 0; n < num_seqs; ++n)
+      base[n + 1] = base[n] + (cu_seqlens[n + 1] - cu_seqlens[n]) / snap_every;
+  }
   prefill_ctx c = {q, k, v, g, beta, cu_seqlens, num_seqs, num_heads, dk, dv,
-                   scale, initial_state, final_state, out};
+                   scale, initial_state, final_state, out, snap_every, snapshots, base};
   /* final_state == initial_state is allowed: each unit copies its slice in
    * before the loop and out after it, and units touch disjoint slices. */
-  return run_units((int64_t)num_seqs * num_heads, num_threads,
-                   (size_t)dk * dv + 2 * (size_t)dv, prefill_unit, &c);
+  const int rc = run_units((int64_t)num_seqs * num_heads, num_threads,
+                           (size_t)dk * dv + 2 * (size_t)dv, prefill_unit, &c);
+  free(base);
+  return rc;
 }
 
 /* ---------------------------------------------------------------- decode */

@@ -297,3 +297,25 @@ def test_oracle_rejects_bad_arguments():
     with pytest.raises(ValueError):   # decreasing cu_seqlens
         oracle.prefill(c["q"], c["k"], c["v"], c["g"], c["beta"], np.array([0, 3, 2, 4]), 1.0,
                        None)
+
+
+def test_snapshots_equal_truncated_prefills():
+    """State snapshots every I tokens equal the final states of independent prefills of
+    the first j*I tokens of each sequence (and the last one equals the final state when
+    the length is a multiple of I)."""
+    from kimi_delta_attention_prefill_amd.inputs import make_prefill_case
+    case = make_prefill_case([130, 64, 40, 96], 2, -5.0, 0.02, seed=31, name="snapshots")
+    I = 32
+    out, fin, snaps = oracle.prefill(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens,
+                                     case.scale, case.initial_state, snapshot_every=I)
+    cu = case.cu_seqlens.long().tolist()
+    for n in range(case.num_seqs):
+        L = cu[n + 1] - cu[n]
+        assert snaps[n].shape[0] == L // I
+        for j in range(1, L // I + 1):
+            sl = slice(cu[n], cu[n] + j * I)
+            _, f = oracle.prefill(case.q[sl], case.k[sl], case.v[sl], case.g[sl], case.beta[sl],
+                                  np.array([0, j * I]), case.scale, case.initial_state[n:n + 1])
+            assert np.array_equal(snaps[n][j - 1], f[0])
+        if L % I == 0 and L > 0:
+            assert np.array_equal(snaps[n][-1], fin[n])
