@@ -22,6 +22,9 @@
  *                   parallel, state evolution is serial), so that a caller
  *                   can time them or overlap one batch's preparation with
  *                   another's chain.
+ *   kda_prefill_pool
+ *                -- kda_prefill with states in a slot-indexed FP32 pool and
+ *                   optional intermediate-state checkpoints.
  *   kda_decode   -- the T=1 step over a slot-indexed state pool, updated in
  *                   place (flashinfer PR #5551, "Kimi K3 TP12 H=8 fused KDA
  *                   decode": positive unique slots, FP32 and BF16 state,
@@ -59,7 +62,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -143,6 +146,41 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g,
                 int32_t head_dim_v, float scale, float lower_bound,
                 const float* initial_state, float* final_state, void* out,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* --------------------------------------------------- pooled prefill --
+ * kda_prefill with the states of a serving engine: each sequence starts from
+ * and ends in a slot of an FP32 state pool, updated in place ([SBH]'s "FP32
+ * pool with state indices"), and optionally the state after every
+ * `checkpoint_tokens` tokens of each sequence is stored ([SBH]'s checkpoint
+ * rows, "every 64 tokens").  All other arguments, the routes and the
+ * workspace are those of kda_prefill.
+ *
+ *  state_pool   fp32 [num_slots, H, 128, 128] (dv contiguous), 16-byte
+ *               aligned, or NULL (zero initial states, final states not
+ *               stored).
+ *  num_slots    >= 1 when state_pool is set.
+ *  slot_indices int32 [N] device array: the slot of each sequence.  A slot
+ *               outside [0, num_slots) starts from zeros and is not stored.
+ *               Slots in range must be unique.
+ *  checkpoints  fp32 [kda_prefill_checkpoint_slots(N, T_tot, checkpoint_tokens),
+ *               H, 128, 128], 16-byte aligned, or NULL (none).  The state of
+ *               sequence n after j * checkpoint_tokens tokens (j = 1 ..
+ *               floor(len_n / checkpoint_tokens)) is stored at slot
+ *               n + floor(cu_seqlens[n] / checkpoint_tokens) + j - 1 (unique per
+ *               (n, j)); other slots are not written.
+ *  checkpoint_tokens  a positive multiple of 32 when checkpoints is set. */
+int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                     int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                     int32_t head_dim_v, float scale, float lower_bound, float* state_pool,
+                     int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
+                     int32_t checkpoint_tokens, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/* N + T_tot / checkpoint_tokens + 1: the [H, 128, 128] slots a checkpoint
+ * buffer of kda_prefill_pool must hold (0 for invalid arguments). */
+size_t kda_prefill_checkpoint_slots(int32_t num_seqs, int64_t total_tokens,
+                                    int32_t checkpoint_tokens);
 
 /* Bytes of workspace kda_prefill needs for these sizes with the route it
  * would choose on the current device (or the forced route): 0 for SERIAL and

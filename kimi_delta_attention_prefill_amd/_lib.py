@@ -88,6 +88,11 @@ def load():
     lib.kda_prefill_chain.restype = ctypes.c_int
     lib.kda_prefill_records_size.argtypes = [i32, i64, i32]
     lib.kda_prefill_records_size.restype = sz
+    lib.kda_prefill_pool.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32, vp,
+                                     i64, vp, vp, i32, vp, vp, sz, vp]
+    lib.kda_prefill_pool.restype = ctypes.c_int
+    lib.kda_prefill_checkpoint_slots.argtypes = [i32, i64, i32]
+    lib.kda_prefill_checkpoint_slots.restype = sz
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
     lib.kda_decode.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
@@ -187,6 +192,56 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
                               _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
                               _stream(stream)))
     return out, final_state
+
+
+def checkpoint_slots(num_seqs: int, total_tokens: int, checkpoint_tokens: int) -> int:
+    """Slots ([H, 128, 128] each) a checkpoint buffer of prefill_pool must hold."""
+    return int(load().kda_prefill_checkpoint_slots(num_seqs, total_tokens, checkpoint_tokens))
+
+
+def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scale, lower_bound,
+                 checkpoints=None, checkpoint_tokens=64, out=None, workspace=None, stream=None):
+    """Packed varlen prefill whose states live in ``state_pool`` (fp32
+    [num_slots, H, 128, 128], updated in place; None: zero start, nothing
+    stored), one ``slot_indices`` entry (int32, device) per sequence.
+
+    ``checkpoints``: an fp32 [checkpoint_slots(N, T, checkpoint_tokens), H, 128, 128]
+    tensor to fill, True to allocate one (zero-filled), or None for none.
+    Returns (out, checkpoints).
+    """
+    dev = q.device
+    T, H, D = q.shape
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _need(t, name, torch.bfloat16, (T, H, D), dev)
+    _need(beta, "beta", torch.bfloat16, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    _need(slot_indices, "slot_indices", torch.int32, (N,), dev)
+    num_slots = 0
+    if state_pool is not None:
+        _need(state_pool, "state_pool", torch.float32, (state_pool.shape[0], H, D, D), dev)
+        num_slots = state_pool.shape[0]
+    if checkpoints is True:
+        checkpoints = torch.zeros((checkpoint_slots(N, T, checkpoint_tokens), H, D, D),
+                                  dtype=torch.float32, device=dev)
+    if checkpoints is not None:
+        _need(checkpoints, "checkpoints", torch.float32,
+              (checkpoint_slots(N, T, checkpoint_tokens), H, D, D), dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, D), dev)
+    if workspace is None:
+        need = workspace_size(N, T, H)
+        if need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(load().kda_prefill_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                   _ptr(cu_seqlens), N, T, H, D, D, float(scale),
+                                   float(lower_bound), _ptr(state_pool), num_slots,
+                                   _ptr(slot_indices), _ptr(checkpoints),
+                                   int(checkpoint_tokens) if checkpoints is not None else 0,
+                                   _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    return out, checkpoints
 
 
 def records_size(num_seqs: int, total_tokens: int, num_heads: int) -> int:

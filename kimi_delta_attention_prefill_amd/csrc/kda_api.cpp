@@ -142,6 +142,11 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.out = static_cast<uint16_t*>(out);
   a.windows = 1;
   a.window_chunks = 0;
+  a.pool = nullptr;
+  a.slots = nullptr;
+  a.num_slots = 0;
+  a.ckpt = nullptr;
+  a.ckpt_tokens = 0;
   return a;
 }
 
@@ -242,6 +247,42 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
   return ok();
 }
 
+}  // extern "C"
+
+namespace {
+
+// Plan, check the workspace and launch a prefill whose arguments have been
+// validated.
+int run_prefill(const char* fn, kda::PrefillArgs a, float lower_bound, void* workspace,
+                size_t workspace_bytes, hipStream_t stream) {
+  kda_prefill_plan_t plan;
+  int rc = kda_prefill_plan(a.num_seqs, a.total_tokens, a.num_heads, lower_bound, 0,
+                            g_forced_route.load(), &plan);
+  if (rc != KDA_OK) return rc;
+  if (plan.route == KDA_ROUTE_SPLIT &&
+      (rc = check_records(fn, workspace, workspace_bytes,
+                          kda::split_workspace_bytes(a.num_seqs, a.total_tokens, a.num_heads,
+                                                     plan.windows))) != KDA_OK)
+    return rc;
+  a.windows = plan.windows;
+  a.window_chunks = plan.window_chunks;
+  hipError_t e;
+  if (plan.route == KDA_ROUTE_SERIAL)
+    e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
+  else if (plan.route == KDA_ROUTE_SPLIT)
+    e = kda::launch_prefill_split(a, plan.anchor_mode, plan.dv_split, workspace, stream);
+  else
+    e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
+  if (e == hipErrorNotSupported)
+    return fail(KDA_ERR_UNSUPPORTED, "%s: route %d is not available", fn, plan.route);
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
 int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
                 const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
                 int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
@@ -257,31 +298,58 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g, cons
   if ((rc = check_outputs(fn, initial_state, final_state, out, num_seqs, num_heads,
                           total_tokens)) != KDA_OK)
     return rc;
-  kda_prefill_plan_t plan;
-  rc = kda_prefill_plan(num_seqs, total_tokens, num_heads, lower_bound, 0, g_forced_route.load(),
-                        &plan);
-  if (rc != KDA_OK) return rc;
-  if (plan.route == KDA_ROUTE_SPLIT &&
-      (rc = check_records(fn, workspace, workspace_bytes,
-                          kda::split_workspace_bytes(num_seqs, total_tokens, num_heads,
-                                                     plan.windows))) != KDA_OK)
-    return rc;
+  return run_prefill(fn,
+                     make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                               scale, lower_bound, initial_state, final_state, out),
+                     lower_bound, workspace, workspace_bytes, stream);
+}
 
+int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                     int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                     int32_t head_dim_v, float scale, float lower_bound, float* state_pool,
+                     int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
+                     int32_t checkpoint_tokens, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  const char* fn = "kda_prefill_pool";
+  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v);
+  if (rc != KDA_OK) return rc;
+  if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
+  if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  if (state_pool) {
+    if (num_slots < 1)
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_slots=%lld", fn, (long long)num_slots);
+    if (!aligned(state_pool, 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool is not 16-byte aligned", fn);
+  }
+  if (checkpoints) {
+    if (checkpoint_tokens <= 0 || checkpoint_tokens % 32 != 0)
+      return fail(KDA_ERR_INVALID_ARGUMENT,
+                  "%s: checkpoint_tokens must be a positive multiple of 32 (got %d)", fn,
+                  checkpoint_tokens);
+    if (!aligned(checkpoints, 16))
+      return fail(KDA_ERR_INVALID_ARGUMENT, "%s: checkpoints are not 16-byte aligned", fn);
+  }
+  if (num_seqs == 0) return ok();
+  if (state_pool && (!slot_indices || !aligned(slot_indices, 4)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: slot_indices is NULL or misaligned", fn);
+  if ((rc = check_inputs(fn, q, k, v, g, beta, cu_seqlens, total_tokens)) != KDA_OK) return rc;
+  if ((rc = check_outputs(fn, nullptr, nullptr, out, num_seqs, num_heads, total_tokens)) != KDA_OK)
+    return rc;
   kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
-                                 scale, lower_bound, initial_state, final_state, out);
-  a.windows = plan.windows;
-  a.window_chunks = plan.window_chunks;
-  hipError_t e;
-  if (plan.route == KDA_ROUTE_SERIAL)
-    e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
-  else if (plan.route == KDA_ROUTE_SPLIT)
-    e = kda::launch_prefill_split(a, plan.anchor_mode, plan.dv_split, workspace, stream);
-  else
-    e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
-  if (e == hipErrorNotSupported)
-    return fail(KDA_ERR_UNSUPPORTED, "%s: route %d is not available", fn, plan.route);
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));
-  return ok();
+                                 scale, lower_bound, nullptr, nullptr, out);
+  a.pool = state_pool;
+  a.slots = slot_indices;
+  a.num_slots = num_slots;
+  a.ckpt = checkpoints;
+  a.ckpt_tokens = checkpoints ? checkpoint_tokens : 0;
+  return run_prefill(fn, a, lower_bound, workspace, workspace_bytes, stream);
+}
+
+size_t kda_prefill_checkpoint_slots(int32_t num_seqs, int64_t total_tokens,
+                                    int32_t checkpoint_tokens) {
+  if (num_seqs < 0 || total_tokens < 0 || checkpoint_tokens <= 0) return 0;
+  return (size_t)num_seqs + (size_t)(total_tokens / checkpoint_tokens) + 1;
 }
 
 // The SPLIT route's plan for these sizes on the current device.

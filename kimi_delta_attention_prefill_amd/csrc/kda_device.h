@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_internal.h"
+
 namespace kda {
 
 // bf16 (stored as uint16) -> fp32: exact, a 16-bit left shift.
@@ -37,6 +39,31 @@ __device__ __forceinline__ void buffer_store_u16(uint16_t v, __amdgpu_buffer_rsr
 // Clamp a device-read sequence offset into [0, total].
 __device__ __forceinline__ int clamp_offset(int x, int total) {
   return x < 0 ? 0 : (x > total ? total : x);
+}
+
+// The [128][128] FP32 state a prefill of (sequence n, head h) starts from
+// (null: zeros) and the one it ends in (null: not stored).
+__device__ __forceinline__ float* prefill_pool_state(const PrefillArgs& a, int n, int h) {
+  const int64_t s = a.slots[n];
+  return (s >= 0 && s < a.num_slots) ? a.pool + (s * a.num_heads + h) * (int64_t)(kHeadDim * kHeadDim)
+                                     : nullptr;
+}
+__device__ __forceinline__ const float* prefill_initial_state(const PrefillArgs& a, int n, int h) {
+  if (a.pool) return prefill_pool_state(a, n, h);
+  return a.s0 ? a.s0 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr;
+}
+__device__ __forceinline__ float* prefill_final_state(const PrefillArgs& a, int n, int h) {
+  if (a.pool) return prefill_pool_state(a, n, h);
+  return a.s1 ? a.s1 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr;
+}
+// Where the state after `done` tokens of sequence n (starting at token bos)
+// is checkpointed, or null when checkpoints are off or `done` is not a
+// positive multiple of the interval.
+__device__ __forceinline__ float* prefill_checkpoint(const PrefillArgs& a, int n, int h, int bos,
+                                                     int done) {
+  if (!a.ckpt || done <= 0 || done % a.ckpt_tokens != 0) return nullptr;
+  const int64_t slot = (int64_t)n + bos / a.ckpt_tokens + done / a.ckpt_tokens - 1;
+  return a.ckpt + (slot * a.num_heads + h) * (int64_t)(kHeadDim * kHeadDim);
 }
 
 }  // namespace kda

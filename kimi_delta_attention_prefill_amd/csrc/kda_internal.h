@@ -28,6 +28,17 @@ struct PrefillArgs {
   uint16_t* out;          // bf16 [T, H, 128]
   int32_t windows;        // split route: windows per sequence (1 = none)
   int32_t window_chunks;  // split route: chunks per window (0 = none)
+  // State pool addressing (kda_prefill_pool): when `pool` is set, s0/s1 are
+  // unused and sequence n starts from and ends in pool slot slots[n] (a slot
+  // outside [0, num_slots) starts from zeros and is not stored).
+  float* pool;            // fp32 [num_slots, H, 128, 128] or null
+  const int32_t* slots;   // int32 [N]
+  int64_t num_slots;
+  // Checkpoints: the state after every `ckpt_tokens` tokens (a multiple of
+  // 32) of each sequence; the j-th (j >= 1) of sequence n goes to slot
+  // n + floor(cu[n] / ckpt_tokens) + j - 1 of ckpt [., H, 128, 128].
+  float* ckpt;            // fp32 or null
+  int32_t ckpt_tokens;
 };
 
 struct DecodeArgs {

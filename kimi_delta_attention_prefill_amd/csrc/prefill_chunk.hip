@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const int64_t sbase = ((int64_t)n * H + h) * D * D;
+  const float* s0 = prefill_initial_state(a, n, h);
 
   // State accumulators: tile (mt, nt) holds rows 16 mt + 4 g4 + i and column
   // col_base + colw + 16 nt + l16.
@@ -92,9 +92,16 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
     for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        S[mt][nt][i] = a.s0 ? a.s0[sbase + (int64_t)(16 * mt + 4 * g4 + i) * D + col_base + colw +
-                                   16 * nt + l16]
-                            : 0.f;
+        S[mt][nt][i] = s0 ? s0[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] : 0.f;
+  auto store_state = [&](float* dst) __attribute__((always_inline)) {
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = S[mt][nt][i];
+  };
 
   for (int t0 = bos; t0 < eos; t0 += CH) {
     const int L = min(CH, eos - t0);
@@ -236,18 +243,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
         }
       }
     }
+    if (float* cp = prefill_checkpoint(a, n, h, bos, t0 + L - bos)) store_state(cp);
   }
 
-  if (a.s1) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          a.s1[sbase + (int64_t)(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] =
-              S[mt][nt][i];
-  }
+  if (float* s1 = prefill_final_state(a, n, h)) store_state(s1);
 }
 
 template <int MODE, int NT>

@@ -43,12 +43,11 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const int64_t sbase = ((int64_t)n * H + h) * kHeadDim * kHeadDim;
+  const float* s0 = prefill_initial_state(a, n, h);
 
   float S[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i)
-    S[i] = a.s0 ? a.s0[sbase + (int64_t)(4 * i + rg) * kHeadDim + col] : 0.f;
+  for (int i = 0; i < 32; ++i) S[i] = s0 ? s0[(4 * i + rg) * kHeadDim + col] : 0.f;
 
   for (int t0 = bos; t0 < eos; t0 += kStage) {
     const int L = min(kStage, eos - t0);
@@ -107,11 +106,15 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
       for (int i = 0; i < 32; ++i) S[i] = fmaf(sk[t][4 * i + rg], u, S[i]);
       if (rg == 0)
         a.out[((int64_t)(t0 + t) * H + h) * kHeadDim + col] = f32_to_bf16(a.scale * fmaf(qk, u, p));
+      if (float* cp = prefill_checkpoint(a, n, h, bos, t0 + t + 1 - bos)) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) cp[(4 * i + rg) * kHeadDim + col] = S[i];
+      }
     }
   }
-  if (a.s1) {
+  if (float* s1 = prefill_final_state(a, n, h)) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) a.s1[sbase + (int64_t)(4 * i + rg) * kHeadDim + col] = S[i];
+    for (int i = 0; i < 32; ++i) s1[(4 * i + rg) * kHeadDim + col] = S[i];
   }
 }
 

@@ -593,6 +593,7 @@ struct ChainJob {
   bool identity;         // start from the identity instead (a window's map)
   bool with_u0;          // false: drop U0 (the map of a window is linear)
   bool with_out;         // store the outputs of the chunks
+  bool ckpt;             // store checkpoints (runs of the true state only)
   float* s_final;        // [128][128] state after chunk ce-1, or null
 };
 
@@ -846,9 +847,12 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   publish(A[1], 0);                // step 0: S_0 = S_{-1}; P_1
   load_a(A[1], 1 + kAhead);
   __syncthreads();
-  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1}
-  auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
+  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1};
+  // with checkpoints, S_c is stored when its token count is a multiple of the
+  // interval (an unconditional store with an empty range otherwise).
+  auto step = [&](auto I_const, auto ck_const, int c) __attribute__((always_inline)) {
     constexpr int I = decltype(I_const)::value;   // = c % 3 for the B set of chunk c-1: (I+2)%3
+    constexpr bool CK = decltype(ck_const)::value;
     constexpr int IB = (I + 2) % 3, IA = (I + 1) % 3;
     const BOps& kb = B[IB];
     const uint8_t* ex = exch(c - 1);
@@ -865,18 +869,38 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       S[m] = mfma_f16(kb.ak[m], uh, S[m]);
       S[m] = mfma_f16(kb.ak[m], ul, S[m]);
     }
+    if (CK) {
+      float* cp = prefill_checkpoint(a, n, h, bos, min(CH * (job.cb + c), eos - bos));
+      const __amdgpu_buffer_rsrc_t cr =
+          make_buffer(cp ? cp : a.ckpt, cp ? (uint32_t)(D * D * 4) : 0u);
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float sv = S[m][i];   // a scalar first: a vector element is not a bit_cast source
+          __builtin_amdgcn_raw_buffer_store_b32(
+              __builtin_bit_cast(uint32_t, sv), cr,
+              (uint32_t)(((16 * (4 * hs + m) + 4 * g4 + i) * D + col) * 4), 0, 0);
+        }
+    }
     load_b(B[IB], c - 1 + kAhead);
     publish(A[IA], c);                                // unused past the end
     load_a(A[IA], c + 1 + kAhead);
     __syncthreads();
   };
-  for (int c = 1; c <= nch; c += kAhead) {
-    step(std::integral_constant<int, 1>{}, c);
-    if (c + 1 > nch) break;
-    step(std::integral_constant<int, 2>{}, c + 1);
-    if (c + 2 > nch) break;
-    step(std::integral_constant<int, 0>{}, c + 2);
-  }
+  auto run = [&](auto ck) __attribute__((always_inline)) {
+    for (int c = 1; c <= nch; c += kAhead) {
+      step(std::integral_constant<int, 1>{}, ck, c);
+      if (c + 1 > nch) break;
+      step(std::integral_constant<int, 2>{}, ck, c + 1);
+      if (c + 2 > nch) break;
+      step(std::integral_constant<int, 0>{}, ck, c + 2);
+    }
+  };
+  if (job.ckpt && a.ckpt)
+    run(std::integral_constant<bool, true>{});
+  else
+    run(std::integral_constant<bool, false>{});
   if (job.s_final) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -895,13 +919,12 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
   const int n = unit / H, h = unit % H;
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const int64_t sb = ((int64_t)n * H + h) * D * D;
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
   job.cb = 0; job.ce = (eos - bos + CH - 1) / CH;
-  job.s_init = a.s0 ? a.s0 + sb : nullptr;
-  job.identity = false; job.with_u0 = true; job.with_out = true;
-  job.s_final = a.s1 ? a.s1 + sb : nullptr;
+  job.s_init = prefill_initial_state(a, n, h);
+  job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
+  job.s_final = prefill_final_state(a, n, h);
   chain_body(a, ws, lds, job);
 }
 
@@ -940,21 +963,20 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillA
   const int n = unit / H, h = unit % H;
   const int nch = seq_chunks(a, n);
   const int nwin = max(1, (nch + WC - 1) / WC);
-  const int64_t sb = ((int64_t)n * H + h) * D * D;
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
   if (j == 0) {
     job.cb = 0; job.ce = min(WC, nch);
-    job.s_init = a.s0 ? a.s0 + sb : nullptr;
-    job.identity = false; job.with_u0 = true; job.with_out = true;
-    job.s_final = nwin <= 1 ? (a.s1 ? a.s1 + sb : nullptr) : wv.at(n, h, 0, 0);
+    job.s_init = prefill_initial_state(a, n, h);
+    job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
+    job.s_final = nwin <= 1 ? prefill_final_state(a, n, h) : wv.at(n, h, 0, 0);
   } else {
     const bool map = j > W - 2;
     const int w = map ? j - (W - 2) : j;
     if (w >= nwin - 1) return;            // the last window needs neither
     job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
     job.s_init = nullptr;
-    job.identity = map; job.with_u0 = !map; job.with_out = false;
+    job.identity = map; job.with_u0 = !map; job.with_out = false; job.ckpt = false;
     job.s_final = wv.at(n, h, w, map ? 1 : 0);
   }
   chain_body(a, ws, lds, job);
@@ -1071,13 +1093,12 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillA
   const int nch = seq_chunks(a, n);
   const int nwin = max(1, (nch + WC - 1) / WC);
   if (w >= nwin) return;
-  const int64_t sb = ((int64_t)n * H + h) * D * D;
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
   job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
   job.s_init = w == 1 ? wv.at(n, h, 0, 0) : wv.at(n, h, w, 2);
-  job.identity = false; job.with_u0 = true; job.with_out = true;
-  job.s_final = w == nwin - 1 ? (a.s1 ? a.s1 + sb : nullptr) : nullptr;
+  job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
+  job.s_final = w == nwin - 1 ? prefill_final_state(a, n, h) : nullptr;
   chain_body(a, ws, lds, job);
 }
 

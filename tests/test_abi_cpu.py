@@ -215,3 +215,33 @@ def test_plan_windows():
         p = kda.plan(*args, -5.0, 256, kda.ROUTE_SPLIT)
         assert (p.windows, p.window_chunks) == (1, 0), args   # too short, too many units, or N > 1
     assert kda.plan(1, 8192, 8, -5.0, 256, kda.ROUTE_CHUNK).windows == 1
+
+
+def test_pool_prefill_host_validation():
+    lib = kda.load()
+    P = lambda x: None if x is None else ctypes.c_void_p(x)
+
+    def call(**o):
+        a = dict(q=16, k=16, v=16, g=16, beta=16, cu=16, N=2, T=4, H=1, dk=128, dv=128, scale=1.0,
+                 lb=-5.0, pool=0x10000, slots_n=4, idx=16, ck=None, ckt=0, out=16, ws=None,
+                 ws_bytes=0)
+        a.update(o)
+        return lib.kda_prefill_pool(P(a["q"]), P(a["k"]), P(a["v"]), P(a["g"]), P(a["beta"]),
+                                    P(a["cu"]), a["N"], a["T"], a["H"], a["dk"], a["dv"],
+                                    a["scale"], a["lb"], P(a["pool"]), a["slots_n"], P(a["idx"]),
+                                    P(a["ck"]), a["ckt"], P(a["out"]), P(a["ws"]), a["ws_bytes"],
+                                    None)
+
+    E, U = _lib.KDA_ERR_INVALID_ARGUMENT, _lib.KDA_ERR_UNSUPPORTED
+    assert call(dk=64) == U
+    assert call(slots_n=0) == E
+    assert call(pool=0x10008) == E
+    assert call(idx=None) == E and call(idx=0x1002) == E
+    assert call(ck=0x20000, ckt=48) == E and "multiple of 32" in kda.last_error()
+    assert call(ck=0x20000, ckt=0) == E
+    assert call(ck=0x20008, ckt=64) == E
+    assert call(out=None) == E
+    assert call(N=0, q=None, cu=None, idx=None, out=None) == 0
+    assert kda.checkpoint_slots(3, 1000, 64) == 3 + 1000 // 64 + 1
+    assert kda.checkpoint_slots(1, 8192, 64) == 1 + 128 + 1
+    assert kda.checkpoint_slots(1, 10, 0) == 0
