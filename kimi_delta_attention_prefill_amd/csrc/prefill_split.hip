@@ -46,6 +46,7 @@
 // Fragment K indices use the permuted slot order of chunk_common.h.  The chunk
 // slot of chunk c of sequence n is n + floor(cu[n] / 32) + c, unique and
 // below N + T / 32 + 1.
+#include <climits>
 #include <cmath>
 #include <type_traits>
 
@@ -847,12 +848,19 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   publish(A[1], 0);                // step 0: S_0 = S_{-1}; P_1
   load_a(A[1], 1 + kAhead);
   __syncthreads();
-  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1};
-  // with checkpoints, S_c is stored when its token count is a multiple of the
-  // interval (an unconditional store with an empty range otherwise).
-  auto step = [&](auto I_const, auto ck_const, int c) __attribute__((always_inline)) {
+  // Checkpoints: after step c the state has consumed chunks 0..k-1 of the
+  // sequence (k = cb + c); it is stored when k is a multiple of the interval
+  // in chunks and those k chunks are full.  The next such k and its row are
+  // kept as uniform counters (one loop for both cases, so the checkpoint
+  // stores cost no registers beyond one offset).
+  const int ck_per = (job.ckpt && a.ckpt) ? a.ckpt_tokens / CH : 0;
+  const int ck_full = (eos - bos) / CH;
+  int ck_next = ck_per ? ck_per * ((job.cb + ck_per) / ck_per) : INT_MAX;   // first multiple > cb
+  int64_t ck_row = ck_per ? ((int64_t)n + bos / a.ckpt_tokens + ck_next / ck_per - 1) : 0;
+  const uint32_t ck_off = (uint32_t)(((64 * hs + 4 * g4) * D + col) * 4);
+  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1}.
+  auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
     constexpr int I = decltype(I_const)::value;   // = c % 3 for the B set of chunk c-1: (I+2)%3
-    constexpr bool CK = decltype(ck_const)::value;
     constexpr int IB = (I + 2) % 3, IA = (I + 1) % 3;
     const BOps& kb = B[IB];
     const uint8_t* ex = exch(c - 1);
@@ -869,38 +877,34 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       S[m] = mfma_f16(kb.ak[m], uh, S[m]);
       S[m] = mfma_f16(kb.ak[m], ul, S[m]);
     }
-    if (CK) {
-      float* cp = prefill_checkpoint(a, n, h, bos, min(CH * (job.cb + c), eos - bos));
-      const __amdgpu_buffer_rsrc_t cr =
-          make_buffer(cp ? cp : a.ckpt, cp ? (uint32_t)(D * D * 4) : 0u);
+    if (job.cb + c == ck_next) {
+      if (ck_next <= ck_full) {
+        const __amdgpu_buffer_rsrc_t cr =
+            make_buffer(a.ckpt + (ck_row * H + h) * (int64_t)(D * D), (uint32_t)(D * D * 4));
 #pragma unroll
-      for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float sv = S[m][i];   // a scalar first: a vector element is not a bit_cast source
-          __builtin_amdgcn_raw_buffer_store_b32(
-              __builtin_bit_cast(uint32_t, sv), cr,
-              (uint32_t)(((16 * (4 * hs + m) + 4 * g4 + i) * D + col) * 4), 0, 0);
-        }
+          for (int i = 0; i < 4; ++i) {
+            const float sv = S[m][i];   // a scalar first: a vector element is not a bit_cast source
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), cr,
+                                                  ck_off + (uint32_t)(i * D * 4), 16 * m * D * 4, 0);
+          }
+      }
+      ck_next += ck_per;
+      ++ck_row;
     }
     load_b(B[IB], c - 1 + kAhead);
     publish(A[IA], c);                                // unused past the end
     load_a(A[IA], c + 1 + kAhead);
     __syncthreads();
   };
-  auto run = [&](auto ck) __attribute__((always_inline)) {
-    for (int c = 1; c <= nch; c += kAhead) {
-      step(std::integral_constant<int, 1>{}, ck, c);
-      if (c + 1 > nch) break;
-      step(std::integral_constant<int, 2>{}, ck, c + 1);
-      if (c + 2 > nch) break;
-      step(std::integral_constant<int, 0>{}, ck, c + 2);
-    }
-  };
-  if (job.ckpt && a.ckpt)
-    run(std::integral_constant<bool, true>{});
-  else
-    run(std::integral_constant<bool, false>{});
+  for (int c = 1; c <= nch; c += kAhead) {
+    step(std::integral_constant<int, 1>{}, c);
+    if (c + 1 > nch) break;
+    step(std::integral_constant<int, 2>{}, c + 1);
+    if (c + 2 > nch) break;
+    step(std::integral_constant<int, 0>{}, c + 2);
+  }
   if (job.s_final) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
