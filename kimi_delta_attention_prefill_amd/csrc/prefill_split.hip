@@ -127,8 +127,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   __shared__ __align__(16) float Al[CH][36];   // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
   __shared__ __align__(16) float Tl[CH][36];   // (I + A)^{-1}, lower triangle
   __shared__ __align__(16) float bl[CH];
+  __shared__ __align__(16) f16x8 xh_park[8][64];   // (b Kg)^T hi fragments, see below
   const int H = a.num_heads, N = a.num_seqs, T = a.total_tokens;
-  const int slot = blockIdx.x, h = blockIdx.y;
+  // XCD-aware order: consecutive block indices go to the eight XCDs in turn,
+  // so block b takes work item (b % 8) * per + b / 8 (items ordered head-major,
+  // then chunk slot).  Each XCD then walks a contiguous run of chunks of one
+  // head, and chunk c's re-read of chunk c-1's keys and gates (loaded by the
+  // previous block on the same XCD moments earlier) can hit its L2.
+  const int64_t slots = (int64_t)N + T / CH + 1;
+  const int64_t per = (slots * H + 7) / 8;
+  const int64_t item = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (item >= slots * H) return;
+  const int h = (int)(item / slots), slot = (int)(item % slots);
   const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
   const float C = a.anchor_log2;
 
@@ -191,10 +201,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   f32x4 acc[6] = {z, z, z, z, z, z};   // Mqk^T tiles (0,0) (0,1) (1,1), Akk^T tiles likewise
-  // (b Kg)^T A fragments per 16-channel tile (hi, lo) wait for T in the
-  // record's -M and U0 areas, which are written last: each lane reads back
-  // only what it wrote.
-  uint8_t* const xh_park = rec + kRecOffMneg;
+  // (b Kg)^T A fragments per 16-channel tile wait for T: the hi parts in LDS,
+  // the lo parts in the record's U0 area, which is written last (each lane
+  // reads back only what it wrote).  Both in LDS would not fit eight waves
+  // per compute unit.
   uint8_t* const xl_park = rec + kRecOffU0;
 
 #pragma unroll
@@ -322,7 +332,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
         xl[i] = (_Float16)w0[i];  xl[4 + i] = (_Float16)w1[i];
       }
       *reinterpret_cast<f16x8*>(rec + kRecOffKrT + ((2 * p + e) * 64 + lane) * 16) = kt;
-      *reinterpret_cast<f16x8*>(xh_park + ((2 * p + e) * 64 + lane) * 16) = xh;
+      xh_park[2 * p + e][lane] = xh;
       *reinterpret_cast<f16x8*>(xl_park + ((2 * p + e) * 64 + lane) * 16) = xl;
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -359,7 +369,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   f16x8 Xh[8], Xl[8];
 #pragma unroll
   for (int mc = 0; mc < 8; ++mc) {
-    Xh[mc] = *reinterpret_cast<const f16x8*>(xh_park + (mc * 64 + lane) * 16);
+    Xh[mc] = xh_park[mc][lane];
     Xl[mc] = *reinterpret_cast<const f16x8*>(xl_park + (mc * 64 + lane) * 16);
   }
   u32x4 vw[4][2], kpw[4][2], gpw[4][2];
@@ -1030,6 +1040,18 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
         pf[e][p][1] = *reinterpret_cast<const f32x4v*>(r + 16);
       }
   };
+  // B_w of this lane's accumulator entries
+  auto load_b = [&](f32x4& bv, int e, int w) __attribute__((always_inline)) {
+    const float* B = wv.at(n, h, w, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) bv[i] = B[row_of(e, i) * 128 + col];
+  };
+  // P_{w+1} and B_{w+1} are requested while step w computes.
+  f32x4v pf[2][4][2];
+  f32x4 bw[2];
+  load_p(pf, 1);
+  load_b(bw[0], 0, 1);
+  load_b(bw[1], 1, 1);
   {
     const float* e0 = wv.at(n, h, 0, 0);
     float v[8];
@@ -1039,8 +1061,6 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
       for (int i = 0; i < 4; ++i) v[4 * e + i] = e0[row_of(e, i) * 128 + col];
     put_frags(v);
   }
-  f32x4v pf[2][4][2];
-  load_p(pf, 1);
   for (int w = 1; w + 1 < nwin; ++w) {
     __syncthreads();
     f16x8 sh[4], sl[4];
@@ -1049,12 +1069,7 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
       sh[p] = xh[p][lane];
       sl[p] = xl[p][lane];
     }
-    const float* B = wv.at(n, h, w, 0);
-    f32x4 acc[2];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[e][i] = B[row_of(e, i) * 128 + col];
+    f32x4 acc[2] = {bw[0], bw[1]};
 #pragma unroll
     for (int e = 0; e < 2; ++e)
 #pragma unroll
@@ -1071,7 +1086,11 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
         acc[e] = mfma_f16(ph, sl[p], acc[e]);
         acc[e] = mfma_f16(pl, sh[p], acc[e]);
       }
-    if (w + 2 < nwin) load_p(pf, w + 1);
+    if (w + 2 < nwin) {
+      load_p(pf, w + 1);
+      load_b(bw[0], 0, w + 1);
+      load_b(bw[1], 1, w + 1);
+    }
     float* si = wv.at(n, h, w + 1, 2);
     float v[8];
 #pragma unroll
@@ -1110,7 +1129,9 @@ template <int MODE>
 hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
   const int64_t slots = (int64_t)a.num_seqs + a.total_tokens / CH + 1;
-  prefill_split_prep<MODE><<<dim3((unsigned)slots, a.num_heads), 64, 0, s>>>(a, exp2C, ws);
+  const int64_t blocks = 8 * ((slots * a.num_heads + 7) / 8);
+  if (blocks > INT_MAX) return hipErrorInvalidValue;
+  prefill_split_prep<MODE><<<(unsigned)blocks, 64, 0, s>>>(a, exp2C, ws);
   return hipGetLastError();
 }
 
