@@ -216,17 +216,20 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     plan->grid_blocks = units * plan->dv_split;
   } else if (route == KDA_ROUTE_SPLIT) {
     // Chain pass: one block (two state waves, a U wave and an output wave)
-    // per 16-column value tile of each (sequence, head); two blocks fit a CU.
-    plan->dv_split = 8;
+    // per 16 kSplitSubtiles value columns of each (sequence, head); two blocks
+    // fit a CU.
+    plan->dv_split = kda::kSplitChainTiles;
     plan->block_threads = 256;
-    plan->grid_blocks = units * 8;
+    plan->grid_blocks = units * kda::kSplitChainTiles;
     plan->windows = 1;
     // One long sequence whose chain fills a small part of the device: cut it
     // into windows so that phase A (first window + inner windows' maps, 1 +
-    // 2 (W - 2) chains) and phase C (W - 1 chains) each fit two blocks per CU.
+    // 2 (W - 2) chains) and phase C (W - 1 chains) each fit the CUs at
+    // kSplitBlocksPerCU blocks each.
     const int64_t chunks = (total_tokens + 31) / 32;
     if (num_seqs == 1) {
-      const int64_t tiles = units * 8, slots = 2 * (int64_t)num_cus;
+      const int64_t tiles = units * kda::kSplitChainTiles;
+      const int64_t slots = kda::kSplitBlocksPerCU * (int64_t)num_cus;
       int64_t w = 1;
       while (w < 8 && tiles * (1 + 2 * (w + 1 - 2)) <= slots && tiles * w <= slots) ++w;
       w = std::min<int64_t>(w, chunks / 8);   // windows of at least 8 chunks

@@ -9,6 +9,11 @@ namespace kda {
 
 constexpr int kHeadDim = 128;
 constexpr float kLog2e = 1.4426950408889634f;
+// Split-route chain blocks: 16-column value subtiles per block, blocks per
+// (sequence, head), and chain blocks that fit one compute unit at once.
+constexpr int kSplitSubtiles = 1;
+constexpr int kSplitChainTiles = 8 / kSplitSubtiles;
+constexpr int kSplitBlocksPerCU = 2;
 
 struct PrefillArgs {
   const uint16_t* q;      // bf16 [T, H, 128]

@@ -570,19 +570,23 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
 // (sequence, head) unit b % units and tile b / units: with a unit count
 // divisible by 8, all tiles of a unit run on one XCD and share its L2 copy of
 // the records.
-constexpr int kExSb = 0;                                   // fp16 S_c, [kstep 4][lane][8]
-constexpr int kExUh = 4096, kExUl = 5120;                  // U_c hi / lo, [lane][8]
-constexpr int kExP = 6144;                                 // P halves, [half 2][mt 2][lane][4] f32
-constexpr int kExchBytes = 10240;
+constexpr int kNT = kSplitSubtiles;                      // 16-column subtiles per block
+constexpr int kExSb = 0;                                   // fp16 S_c, [kstep 4][t][lane][8]
+constexpr int kExUh = 4096 * kNT;                          // U_c hi, [t][lane][8]
+constexpr int kExUl = kExUh + 1024 * kNT;                  // U_c lo
+constexpr int kExP = kExUl + 1024 * kNT;                   // P halves, [half 2][t][mt 2][lane][4] f32
+constexpr int kExchBytes = kExP + 4096 * kNT;
 constexpr int kDecSlots = 4;                               // chunk decays, 512 B each
 constexpr int kChainLds = 2 * kExchBytes + kDecSlots * 512;
 constexpr int kChainThreads = 256;
 constexpr int kAhead = 3;                                  // register sets per operand stream
+constexpr int kChainTiles = 8 / kNT;                       // blocks per (sequence, head)
 
-// Record fragments, as each wave consumes them.
+// Record fragments, as each wave consumes them.  Everything but U0 is the
+// same for all value columns, so a block with kNT subtiles loads it once.
 struct AOps {            // state half: -M' (its K half) and U0, of chunk c+1
   f16x8 am[2][2];
-  f32x4 u0[2];
+  f32x4 u0[kNT][2];
 };
 struct BOps {            // state half: Kr^T rows of chunk c-1
   f16x8 ak[4];
@@ -596,7 +600,8 @@ struct QOps {            // output wave: Qg and Mqk of chunk c-1
   f16x8 aq[2][4], amq[2];
 };
 
-// One chain run: chunks [cb, ce) of sequence n, head h, 16-column tile.
+// One chain run: chunks [cb, ce) of sequence n, head h, value columns
+// [16 kNT tile, 16 kNT (tile + 1)).
 struct ChainJob {
   int n, h, tile;
   int cb, ce;
@@ -611,10 +616,11 @@ struct ChainJob {
 __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* __restrict__ ws,
                                            unsigned char* lds, const ChainJob job) {
   const int H = a.num_heads;
-  const int n = job.n, h = job.h, tile = job.tile;
+  const int n = job.n, h = job.h;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g4 = lane >> 4;
-  const int col = 16 * tile + (lane & 15);
+  const int sub0 = kNT * job.tile;                      // first 16-column subtile
+  auto colof = [&](int t) __attribute__((always_inline)) { return 16 * (sub0 + t) + (lane & 15); };
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
@@ -676,21 +682,26 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       constexpr int I = decltype(I_const)::value;
       const QOps& o = q[I];
       const uint8_t* ex = exch(c - 1);
-      f16x8 sb[4];
-#pragma unroll
-      for (int p = 0; p < 4; ++p) sb[p] = xfrag(ex + kExSb, p);
-      const f16x8 uh = xfrag(ex + kExUh, 0), ul = xfrag(ex + kExUl, 0);
       // O^T = S^T Qg^T + U^T Mqk^T: the same fragments with A and B swapped;
       // lane (g4, l16) gets value columns 4g4..4g4+3 of token 16mt + l16.
-      f32x4 O[2] = {z, z};
+      f32x4 O[kNT][2];
 #pragma unroll
-      for (int p = 0; p < 4; ++p)
+      for (int t = 0; t < kNT; ++t) {
+        f16x8 sb[4];
 #pragma unroll
-        for (int mt = 0; mt < 2; ++mt) O[mt] = mfma_f16(sb[p], o.aq[mt][p], O[mt]);
+        for (int p = 0; p < 4; ++p) sb[p] = xfrag(ex + kExSb, p * kNT + t);
+        const f16x8 uh = xfrag(ex + kExUh, t), ul = xfrag(ex + kExUl, t);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        O[mt] = mfma_f16(uh, o.amq[mt], O[mt]);
-        O[mt] = mfma_f16(ul, o.amq[mt], O[mt]);
+        for (int mt = 0; mt < 2; ++mt) O[t][mt] = z;
+#pragma unroll
+        for (int p = 0; p < 4; ++p)
+#pragma unroll
+          for (int mt = 0; mt < 2; ++mt) O[t][mt] = mfma_f16(sb[p], o.aq[mt][p], O[t][mt]);
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          O[t][mt] = mfma_f16(uh, o.amq[mt], O[t][mt]);
+          O[t][mt] = mfma_f16(ul, o.amq[mt], O[t][mt]);
+        }
       }
       load_q(q[I], c - 1 + kAhead);
       // rows t >= L of a final partial chunk fall outside the range and are dropped
@@ -699,16 +710,18 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
           a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const int t = 16 * mt + (lane & 15);
-        u32x2 pk;
-        pk[0] = (uint32_t)f32_to_bf16(a.scale * O[mt][0]) |
-                ((uint32_t)f32_to_bf16(a.scale * O[mt][1]) << 16);
-        pk[1] = (uint32_t)f32_to_bf16(a.scale * O[mt][2]) |
-                ((uint32_t)f32_to_bf16(a.scale * O[mt][3]) << 16);
-        __builtin_amdgcn_raw_buffer_store_b64(pk, orsrc,
-                                              (uint32_t)((t * H * D + 16 * tile + 4 * g4) * 2), 0, 0);
-      }
+      for (int t = 0; t < kNT; ++t)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const int tok = 16 * mt + (lane & 15);
+          u32x2 pk;
+          pk[0] = (uint32_t)f32_to_bf16(a.scale * O[t][mt][0]) |
+                  ((uint32_t)f32_to_bf16(a.scale * O[t][mt][1]) << 16);
+          pk[1] = (uint32_t)f32_to_bf16(a.scale * O[t][mt][2]) |
+                  ((uint32_t)f32_to_bf16(a.scale * O[t][mt][3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              pk, orsrc, (uint32_t)((tok * H * D + 16 * (sub0 + t) + 4 * g4) * 2), 0, 0);
+        }
       __syncthreads();
     };
     for (int c = 1; c <= nch; c += kAhead) {
@@ -740,41 +753,51 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
 #pragma unroll
     for (int i = 0; i < kAhead; ++i) load_w(w[i], i);
     put_dec(w[0], 0);                 // decays of chunk 0, used in step 1
-    f16x8 Uh, Ul;
+    f16x8 Uh[kNT], Ul[kNT];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      Uh[j] = static_cast<_Float16>(0.f);
-      Ul[j] = static_cast<_Float16>(0.f);
-    }
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        Uh[t][j] = static_cast<_Float16>(0.f);
+        Ul[t][j] = static_cast<_Float16>(0.f);
+      }
     __syncthreads();   // P_0 published
     // step c: U_c from P_c and U_{c-1}; W_c sits in set c % 3
     auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(I_const)::value;
       const WOps& o = w[I];
       const uint8_t* ex = exch(c - 1);
-      f32x4 U[2];
+      f32x4 U[kNT][2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) U[mt] = xacc(ex + kExP, mt) + xacc(ex + kExP, 2 + mt);
+      for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        U[mt] = mfma_f16(o.wh[mt], Uh, U[mt]);
-        U[mt] = mfma_f16(o.wh[mt], Ul, U[mt]);
-        U[mt] = mfma_f16(o.wl[mt], Uh, U[mt]);
-      }
-      load_w(w[I], c + kAhead);
-      put_dec(w[(I + 1) % kAhead], c + 1);   // used in step c+2
+        for (int mt = 0; mt < 2; ++mt)
+          U[t][mt] = xacc(ex + kExP, t * 2 + mt) + xacc(ex + kExP, (kNT + t) * 2 + mt);
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
+      for (int t = 0; t < kNT; ++t)
 #pragma unroll
-        for (int i2 = 0; i2 < 4; ++i2) {
-          _Float16 hh, ll;
-          split_f16(U[mt][i2], hh, ll);
-          Uh[4 * mt + i2] = hh;
-          Ul[4 * mt + i2] = ll;
+        for (int mt = 0; mt < 2; ++mt) {
+          U[t][mt] = mfma_f16(o.wh[mt], Uh[t], U[t][mt]);
+          U[t][mt] = mfma_f16(o.wh[mt], Ul[t], U[t][mt]);
+          U[t][mt] = mfma_f16(o.wl[mt], Uh[t], U[t][mt]);
         }
+      load_w(w[I], c + kAhead);
+      put_dec(w[(I + 1) % kAhead], c + 1);   // applied at the end of step c+1
       uint8_t* exw = exch(c);
-      *reinterpret_cast<f16x8*>(exw + kExUh + lane * 16) = Uh;
-      *reinterpret_cast<f16x8*>(exw + kExUl + lane * 16) = Ul;
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i2 = 0; i2 < 4; ++i2) {
+            _Float16 hh, ll;
+            split_f16(U[t][mt][i2], hh, ll);
+            Uh[t][4 * mt + i2] = hh;
+            Ul[t][4 * mt + i2] = ll;
+          }
+        *reinterpret_cast<f16x8*>(exw + kExUh + (t * 64 + lane) * 16) = Uh[t];
+        *reinterpret_cast<f16x8*>(exw + kExUl + (t * 64 + lane) * 16) = Ul[t];
+      }
       __syncthreads();
     };
     // steps 0..nch (the last one's U is never read)
@@ -792,14 +815,16 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   // Wave hs owns key rows 64hs..64hs+63: accumulator tiles mt = 4hs..4hs+3,
   // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.
   const int hs = wave;
-  f32x4 S[4];
+  f32x4 S[kNT][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int t = 0; t < kNT; ++t)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = 16 * (4 * hs + m) + 4 * g4 + i;
-      S[m][i] = job.s_init ? job.s_init[row * D + col] : (job.identity && row == col ? 1.f : 0.f);
-    }
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * (4 * hs + m) + 4 * g4 + i, col = colof(t);
+        S[t][m][i] = job.s_init ? job.s_init[row * D + col] : (job.identity && row == col ? 1.f : 0.f);
+      }
   AOps A[kAhead];
   BOps B[kAhead];
   auto load_a = [&](AOps& o, int c) __attribute__((always_inline)) {
@@ -808,7 +833,8 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) o.am[mt][q] = gfrag(r, kRecOffMneg, mt * 4 + 2 * hs + q);
-      o.u0[mt] = gacc(r, kRecOffU0 + tile * 2048, mt);
+#pragma unroll
+      for (int t = 0; t < kNT; ++t) o.u0[t][mt] = gacc(r, kRecOffU0 + (sub0 + t) * 2048, mt);
     }
   };
   auto load_b = [&](BOps& o, int c) __attribute__((always_inline)) {
@@ -816,34 +842,34 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
 #pragma unroll
     for (int m = 0; m < 4; ++m) o.ak[m] = gfrag(r, kRecOffKrT, 4 * hs + m);
   };
-  auto to_f16 = [&](f16x8* Sb) __attribute__((always_inline)) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q)
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) {
-        Sb[q][i2] = static_cast<_Float16>(S[2 * q][i2]);
-        Sb[q][4 + i2] = static_cast<_Float16>(S[2 * q + 1][i2]);
-      }
-  };
   // fp16 S_c to exchange(c) and this half's share of P_{c+1} = U0_{c+1} -
   // M'_{c+1} S_c from the fragments of chunk c+1.
   auto publish = [&](const AOps& o, int c) __attribute__((always_inline)) {
-    f16x8 Sb[2];
-    to_f16(Sb);
     uint8_t* ex = exch(c);
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
-      *reinterpret_cast<f16x8*>(ex + kExSb + ((2 * hs + q) * 64 + lane) * 16) = Sb[q];
-    f32x4 P[2];
+    for (int t = 0; t < kNT; ++t) {
+      f16x8 Sb[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) P[mt] = (hs == 0 && job.with_u0) ? o.u0[mt] : z;
+      for (int q = 0; q < 2; ++q)
 #pragma unroll
-    for (int q = 0; q < 2; ++q)
+        for (int i2 = 0; i2 < 4; ++i2) {
+          Sb[q][i2] = static_cast<_Float16>(S[t][2 * q][i2]);
+          Sb[q][4 + i2] = static_cast<_Float16>(S[t][2 * q + 1][i2]);
+        }
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) P[mt] = mfma_f16(o.am[mt][q], Sb[q], P[mt]);
+      for (int q = 0; q < 2; ++q)
+        *reinterpret_cast<f16x8*>(ex + kExSb + (((2 * hs + q) * kNT + t) * 64 + lane) * 16) = Sb[q];
+      f32x4 P[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
-      *reinterpret_cast<f32x4*>(ex + kExP + ((2 * hs + mt) * 64 + lane) * 16) = P[mt];
+      for (int mt = 0; mt < 2; ++mt) P[mt] = (hs == 0 && job.with_u0) ? o.u0[t][mt] : z;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) P[mt] = mfma_f16(o.am[mt][q], Sb[q], P[mt]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+        *reinterpret_cast<f32x4*>(ex + kExP + (((hs * kNT + t) * 2 + mt) * 64 + lane) * 16) = P[mt];
+    }
   };
   // A set k % 3 holds chunk k's -M', U0 (consumed in step k-1); B set k % 3
   // holds chunk k's Kr^T and decays (consumed in step k+1).
@@ -857,6 +883,27 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   __syncthreads();                 // P_0 published
   publish(A[1], 0);                // step 0: S_0 = S_{-1}; P_1
   load_a(A[1], 1 + kAhead);
+  // The decay of chunk c is applied to S_c once S_c is published (fp16 copy
+  // and P_{c+1} use the undecayed state), so that step c+1 starts with its
+  // MFMAs.  Never after the last step: the final state is undecayed.
+  auto read_decay = [&](f32x4 (&dv)[4], int c) __attribute__((always_inline)) {
+    const float* dc = decs(c);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) dv[m] = *reinterpret_cast<const f32x4*>(dc + 16 * (4 * hs + m) + 4 * g4);
+  };
+  auto decay = [&](const f32x4 (&dv)[4]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i2 = 0; i2 < 4; ++i2) S[t][m][i2] *= dv[m][i2];
+  };
+  if (nch > 0) {
+    f32x4 dv[4];
+    read_decay(dv, 0);
+    decay(dv);
+  }
   __syncthreads();
   // Checkpoints: after step c the state has consumed chunks 0..k-1 of the
   // sequence (k = cb + c); it is stored when k is a multiple of the interval
@@ -867,44 +914,51 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   const int ck_full = (eos - bos) / CH;
   int ck_next = ck_per ? ck_per * ((job.cb + ck_per) / ck_per) : INT_MAX;   // first multiple > cb
   int64_t ck_row = ck_per ? ((int64_t)n + bos / a.ckpt_tokens + ck_next / ck_per - 1) : 0;
-  const uint32_t ck_off = (uint32_t)(((64 * hs + 4 * g4) * D + col) * 4);
-  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1}, then P_{c+1}.
+  const uint32_t ck_off = (uint32_t)(((64 * hs + 4 * g4) * D + colof(0)) * 4);
+  // step c >= 1: S_c = Diag(d_{c-1}) S_{c-1} + Kr_{c-1}^T U_{c-1} (S already
+  // decayed), then P_{c+1}, then the decay of chunk c.
   auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
     constexpr int I = decltype(I_const)::value;   // = c % 3 for the B set of chunk c-1: (I+2)%3
     constexpr int IB = (I + 2) % 3, IA = (I + 1) % 3;
     const BOps& kb = B[IB];
     const uint8_t* ex = exch(c - 1);
-    const f16x8 uh = xfrag(ex + kExUh, 0), ul = xfrag(ex + kExUl, 0);
-    const float* dc = decs(c - 1);
+    f16x8 uh[kNT], ul[kNT];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const f32x4 dv = *reinterpret_cast<const f32x4*>(dc + 16 * (4 * hs + m) + 4 * g4);
-#pragma unroll
-      for (int i2 = 0; i2 < 4; ++i2) S[m][i2] *= dv[i2];
+    for (int t = 0; t < kNT; ++t) {
+      uh[t] = xfrag(ex + kExUh, t);
+      ul[t] = xfrag(ex + kExUl, t);
     }
+    f32x4 dv[4];
+    read_decay(dv, c);                                 // chunk c's decays, used at the end
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      S[m] = mfma_f16(kb.ak[m], uh, S[m]);
-      S[m] = mfma_f16(kb.ak[m], ul, S[m]);
-    }
+    for (int t = 0; t < kNT; ++t)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        S[t][m] = mfma_f16(kb.ak[m], uh[t], S[t][m]);
+        S[t][m] = mfma_f16(kb.ak[m], ul[t], S[t][m]);
+      }
     if (job.cb + c == ck_next) {
       if (ck_next <= ck_full) {
         const __amdgpu_buffer_rsrc_t cr =
             make_buffer(a.ckpt + (ck_row * H + h) * (int64_t)(D * D), (uint32_t)(D * D * 4));
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int t = 0; t < kNT; ++t)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float sv = S[m][i];   // a scalar first: a vector element is not a bit_cast source
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), cr,
-                                                  ck_off + (uint32_t)(i * D * 4), 16 * m * D * 4, 0);
-          }
+          for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float sv = S[t][m][i];   // a scalar first: a vector element is not a bit_cast source
+              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), cr,
+                                                    ck_off + (uint32_t)(i * D * 4 + 64 * t),
+                                                    16 * m * D * 4, 0);
+            }
       }
       ck_next += ck_per;
       ++ck_row;
     }
     load_b(B[IB], c - 1 + kAhead);
     publish(A[IA], c);                                // unused past the end
+    if (c < nch) decay(dv);
     load_a(A[IA], c + 1 + kAhead);
     __syncthreads();
   };
@@ -917,10 +971,12 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   }
   if (job.s_final) {
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int t = 0; t < kNT; ++t)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        job.s_final[(16 * (4 * hs + m) + 4 * g4 + i) * D + col] = S[m][i];
+      for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          job.s_final[(16 * (4 * hs + m) + 4 * g4 + i) * D + colof(t)] = S[t][m][i];
   }
 }
 
@@ -1150,7 +1206,7 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
     static bool done = false;
     hipError_t e = set_lds(&prefill_split_chain, done);
     if (e != hipSuccess) return e;
-    prefill_split_chain<<<dim3((unsigned)(units * 8)), kChainThreads, kChainLds, s>>>(a, ws);
+    prefill_split_chain<<<dim3((unsigned)(units * kChainTiles)), kChainThreads, kChainLds, s>>>(a, ws);
     return hipGetLastError();
   }
   static bool done_a = false, done_c = false;
@@ -1163,9 +1219,9 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
   wv.H = a.num_heads;
   wv.W = a.windows;
   const int jobs = 1 + 2 * (a.windows - 2);
-  prefill_split_window_a<<<dim3((unsigned)(units * jobs * 8)), kChainThreads, kChainLds, s>>>(a, ws, wv);
+  prefill_split_window_a<<<dim3((unsigned)(units * jobs * kChainTiles)), kChainThreads, kChainLds, s>>>(a, ws, wv);
   prefill_split_carry<<<dim3((unsigned)(units * 8)), 256, 0, s>>>(a, wv);
-  prefill_split_window_c<<<dim3((unsigned)(units * (a.windows - 1) * 8)), kChainThreads, kChainLds, s>>>(
+  prefill_split_window_c<<<dim3((unsigned)(units * (a.windows - 1) * kChainTiles)), kChainThreads, kChainLds, s>>>(
       a, ws, wv);
   return hipGetLastError();
 }
@@ -1187,7 +1243,7 @@ hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspac
 
 hipError_t launch_prefill_split(const PrefillArgs& a, int anchor_mode, int dv_split,
                                 void* workspace, hipStream_t s) {
-  if (dv_split != 8) return hipErrorInvalidValue;   // one 16-column tile per chain block
+  if (dv_split != kChainTiles) return hipErrorInvalidValue;   // kNT 16-column subtiles per chain block
   hipError_t e = launch_prefill_split_prepare(a, anchor_mode, workspace, s);
   if (e != hipSuccess) return e;
   return launch_prefill_split_chain(a, workspace, s);
