@@ -71,6 +71,19 @@ def stored_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
+def stored_mfma():
+    """Per-kernel MFMA counters (busy % of SIMDs, executed MFMA TFLOP/s) from a
+    committed rocprofv3 --pmc summary, or {} when missing or stale."""
+    path = os.path.join(ROOT, "profiles", "mfma_prefill_split_T8192_H8_decode_rows4096_f32.json")
+    if not os.path.exists(path):
+        return {}
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != source_digest():
+        return {}
+    return rec.get("kernels", {})
+
+
 def stats(ms):
     a = sorted(ms)
     pick = lambda f: a[min(len(a) - 1, max(0, int(round(f * (len(a) - 1)))))]
@@ -231,6 +244,9 @@ def main():
         windows = plan.windows
         launches = (["prefill_split_window_a", "prefill_split_carry", "prefill_split_window_c"]
                     if windows > 1 else ["prefill_split_chain"])
+        counters = stored_mfma()
+        if "prefill_split_prep" in counters:
+            kernels["prefill_split_prep"]["mfma_counters"] = counters["prefill_split_prep"]
         serial_steps = (2 * plan.window_chunks if windows > 1 else chunks)
         kernels["chain_pass"] = dict(
             k2, launches=launches, bound="mfma", achieved=chain_tf, peak=PEAK_BF16_TFLOPS,
@@ -238,7 +254,8 @@ def main():
             algorithmic_flop_per_call=tokheads * CHAIN_FLOP_PER_TOKHEAD,
             windows=windows, window_chunks=plan.window_chunks,
             serial_chunk_steps=serial_steps,
-            us_per_serial_chunk_step=1e3 * k2["mean_ms"] / serial_steps)
+            us_per_serial_chunk_step=1e3 * k2["mean_ms"] / serial_steps,
+            mfma_counters={k: counters[k] for k in launches if k in counters} or None)
         # The roofline names the longest single kernel that bench times on its own:
         # the preparation (the chain pass is several launches).
         dom = "prefill_split_prep"

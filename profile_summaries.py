@@ -5,6 +5,13 @@
       <stats_dir> holds a `rocprofv3 --kernel-trace --stats --output-format csv`
       run; writes profiles/kernel_trace_<workload>.md (per-kernel calls and
       average / min / max duration).
+  python profile_summaries.py mfma <pmc_dir> <stats_dir> <command...>
+      a `rocprofv3 --pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16` run of the bench
+      command and a kernel-trace run (for durations); writes
+      profiles/mfma_<workload>.json with, per prefill kernel, the counters'
+      MFMA busy percentage of all SIMDs and the executed MFMA FLOP per launch
+      (including hi/lo splits and one-hot transposes) as TFLOP/s against the
+      2.5 PFLOP/s dense fp16/bf16 peak.
   python profile_summaries.py traffic <fetch_dir> <write_dir> <command...>
       the two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the
       same bench command; writes profiles/traffic_<kernel>.json with the HBM
@@ -104,9 +111,41 @@ def traffic(fetch_dir, write_dir, command):
         print(path, f"{(fb + wb) / 1e6:.2f} MB/launch")
 
 
+def mfma(pmc_dir, stats_dir, command):
+    path = one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
+    vals = {}
+    for r in csv.DictReader(open(path)):
+        k = (short(r["Kernel_Name"]), r["Counter_Name"])
+        vals.setdefault(k, {}).setdefault(r["Dispatch_Id"], 0.0)
+        vals[k][r["Dispatch_Id"]] += float(r["Counter_Value"])
+    avg = lambda d: sum(d.values()) / len(d) if d else 0.0
+    dur = {short(r["Name"]): float(r["AverageNs"]) for r in
+           csv.DictReader(open(one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))))}
+    out = {"workload": WORKLOAD, "peak_tflops": 2500.0, "source_digest": source_digest(),
+           "command": command, "kernels": {}}
+    for k in KERNELS:
+        if not k.startswith("prefill") or (k, "MfmaUtil") not in vals:
+            continue
+        flops = avg(vals.get((k, "MfmaFlopsF16"), {})) + avg(vals.get((k, "MfmaFlopsBF16"), {}))
+        ns = dur.get(k)
+        out["kernels"][k] = {
+            "mfma_busy_pct_of_simds": avg(vals[(k, "MfmaUtil")]),
+            "executed_mfma_flop_per_launch": flops,
+            "avg_us": ns / 1e3 if ns else None,
+            "executed_tflops": flops / ns / 1e3 if ns else None,
+            "frac_of_peak": flops / ns / 1e3 / 2500.0 if ns else None}
+    path = os.path.join(ROOT, "profiles", f"mfma_{WORKLOAD}.json")
+    json.dump(out, open(path, "w"), indent=1)
+    print(path)
+    for k, v in out["kernels"].items():
+        print(f"  {k:28s} busy {v['mfma_busy_pct_of_simds']:6.2f}%  {v['executed_tflops'] or 0:8.1f} TFLOP/s")
+
+
 if __name__ == "__main__":
     if len(sys.argv) >= 4 and sys.argv[1] == "trace":
         trace(sys.argv[2], " ".join(sys.argv[3:]))
+    elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
+        mfma(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif len(sys.argv) >= 5 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     else:
