@@ -242,7 +242,7 @@ def main():
             algorithmic_bytes_per_launch=tokheads * PREP_BYTES_PER_TOKHEAD,
             algorithmic_flop_per_launch=tokheads * PREP_FLOP_PER_TOKHEAD, mfma_tflops=prep_tf)
         windows = plan.windows
-        launches = (["prefill_split_window_a", "prefill_split_carry", "prefill_split_window_c"]
+        launches = (["prefill_split_window_a", "prefill_split_window_c"]
                     if windows > 1 else ["prefill_split_chain"])
         counters = stored_mfma()
         if "prefill_split_prep" in counters:

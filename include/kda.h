@@ -185,7 +185,7 @@ size_t kda_prefill_checkpoint_slots(int32_t num_seqs, int64_t total_tokens,
 /* Bytes of workspace kda_prefill needs for these sizes with the route it
  * would choose on the current device (or the forced route): 0 for SERIAL and
  * CHUNK; for SPLIT (N + T_tot / 32 + 1) * H * 49152 bytes of chunk records,
- * plus N * H * windows * 3 * 65536 bytes of window states when the plan cuts
+ * plus N * H * windows * 2 * 65536 bytes of window states when the plan cuts
  * the chain into windows. */
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
                                   int32_t num_heads);

@@ -78,7 +78,7 @@ size_t split_records_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_h
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                              int32_t windows) {
   size_t b = split_records_bytes(num_seqs, total_tokens, num_heads);
-  if (windows > 1) b += (size_t)num_seqs * num_heads * windows * 3 * kStateBytes;
+  if (windows > 1) b += (size_t)num_seqs * num_heads * windows * 2 * kStateBytes;
   return b;
 }
 
@@ -606,6 +606,7 @@ struct ChainJob {
   int n, h, tile;
   int cb, ce;
   const float* s_init;   // [128][128] state entering chunk cb, or null
+  const float* s_init_lds = nullptr;   // or this block's columns of it in LDS, [128][16 kNT]
   bool identity;         // start from the identity instead (a window's map)
   bool with_u0;          // false: drop U0 (the map of a window is linear)
   bool with_out;         // store the outputs of the chunks
@@ -823,7 +824,9 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * (4 * hs + m) + 4 * g4 + i, col = colof(t);
-        S[t][m][i] = job.s_init ? job.s_init[row * D + col] : (job.identity && row == col ? 1.f : 0.f);
+        S[t][m][i] = job.s_init_lds ? job.s_init_lds[row * (16 * kNT) + 16 * t + (lane & 15)]
+                     : job.s_init   ? job.s_init[row * D + col]
+                                    : (job.identity && row == col ? 1.f : 0.f);
       }
   AOps A[kAhead];
   BOps B[kAhead];
@@ -1005,14 +1008,15 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
 //   phase A (all at once): window 0 from the initial state; for every window
 //            w that is neither first nor last, B_w (its chain from zero) and
 //            P_w (its chain from the identity, without U0);
-//   carry:   S_in(1) = end of window 0, S_in(w+1) = P_w S_in(w) + B_w;
-//   phase C (all at once): windows 1.. from S_in(w), with outputs.
+//   phase C (all at once): windows 1.. from S_in(w), with outputs, where
+//            S_in(1) = end of window 0 and S_in(w+1) = P_w S_in(w) + B_w is
+//            composed by each block of window w before its chain.
 // About 2 x window_chunks chain steps instead of the sequence's chunk count.
 struct WinView {
   float* base;
   int H, W;
-  __device__ float* at(int n, int h, int w, int kind) const {   // kind 0 E, 1 P, 2 SI
-    return base + ((((int64_t)n * H + h) * W + w) * 3 + kind) * (128 * 128);
+  __device__ float* at(int n, int h, int w, int kind) const {   // kind 0 E, 1 P
+    return base + ((((int64_t)n * H + h) * W + w) * 2 + kind) * (128 * 128);
   }
 };
 
@@ -1052,23 +1056,23 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillA
   chain_body(a, ws, lds, job);
 }
 
-// S_in(w+1) = P_w S_in(w) + B_w for w = 1 .. nwin-2 (S_in(1) = E_0, read in
-// place by window 1), for one (sequence, head) and 16-column tile.  Wave q
-// owns output row tiles 2q, 2q+1; P as fp16 hi + lo A fragments straight from
-// memory (next step's prefetched), the current S tile as fp16 hi + lo B
-// fragments in LDS (a step's accumulators are the next step's K step q), three
-// products per pair, FP32 accumulation on B_w.
-__global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinView wv) {
-  __shared__ f16x8 xh[4][64], xl[4][64];
-  const int H = a.num_heads, units = a.num_seqs * H, WC = a.window_chunks;
-  const int unit = blockIdx.x % units, tile = blockIdx.x / units;
-  const int n = unit / H, h = unit % H;
-  const int nch = seq_chunks(a, n);
-  const int nwin = max(1, (nch + WC - 1) / WC);
-  if (nwin < 3) return;
+// S_in(wt) = P_{wt-1}( ... (P_1 E_0 + B_1) ... ) + B_{wt-1} for this block's value
+// columns, composed by the window_c block that runs window wt before its chain
+// (a few short steps: a kernel of their own cost more to launch than they
+// take).  Four waves, wave q owning rows 32q..32q+31 of a 16-column subtile;
+// P as fp16 hi + lo A fragments (the next window's requested while a step
+// computes), the current S as fp16 hi + lo B fragments in LDS (a step's
+// accumulators are the next step's K step q), three products per pair, FP32
+// accumulation on B.  The result lands in LDS as FP32 [128][16 kNT] at the
+// first exchange buffer and the fragments use the second; both are free
+// until the chain's first barrier.
+__device__ __forceinline__ void carry_to_lds(const WinView& wv, int n, int h, int tile, int wt,
+                                             unsigned char* lds) {
+  f16x8* const xh = reinterpret_cast<f16x8*>(lds + kExchBytes);   // [kstep 4][lane 64]
+  f16x8* const xl = xh + 4 * 64;
+  float* const sin = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
-  const int col = 16 * tile + l16;
   // rows of this lane's accumulator entries: tile 2q+e, row 16(2q+e) + 4g4 + i
   auto row_of = [&](int e, int i) __attribute__((always_inline)) { return 32 * q + 16 * e + 4 * g4 + i; };
   auto put_frags = [&](const float* v) __attribute__((always_inline)) {
@@ -1080,8 +1084,8 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
       hi[j] = hh;
       lo[j] = ll;
     }
-    xh[q][lane] = hi;
-    xl[q][lane] = lo;
+    xh[q * 64 + lane] = hi;
+    xl[q * 64 + lane] = lo;
   };
   typedef float f32x4v __attribute__((ext_vector_type(4)));
   // P_w fragments of this wave's row tiles: [e][kstep p][half of the K-slots]
@@ -1096,69 +1100,67 @@ __global__ __launch_bounds__(256) void prefill_split_carry(PrefillArgs a, WinVie
         pf[e][p][1] = *reinterpret_cast<const f32x4v*>(r + 16);
       }
   };
-  // B_w of this lane's accumulator entries
-  auto load_b = [&](f32x4& bv, int e, int w) __attribute__((always_inline)) {
-    const float* B = wv.at(n, h, w, 0);
+  for (int t = 0; t < kNT; ++t) {
+    const int col = 16 * (kNT * tile + t) + l16;
+    f32x4v pf[2][4][2];
+    load_p(pf, 1);
+    {
+      const float* e0 = wv.at(n, h, 0, 0);
+      float v[8];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) bv[i] = B[row_of(e, i) * 128 + col];
-  };
-  // P_{w+1} and B_{w+1} are requested while step w computes.
-  f32x4v pf[2][4][2];
-  f32x4 bw[2];
-  load_p(pf, 1);
-  load_b(bw[0], 0, 1);
-  load_b(bw[1], 1, 1);
-  {
-    const float* e0 = wv.at(n, h, 0, 0);
-    float v[8];
+      for (int e = 0; e < 2; ++e)
 #pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) v[4 * e + i] = e0[row_of(e, i) * 128 + col];
-    put_frags(v);
-  }
-  for (int w = 1; w + 1 < nwin; ++w) {
-    __syncthreads();
-    f16x8 sh[4], sl[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      sh[p] = xh[p][lane];
-      sl[p] = xl[p][lane];
+        for (int i = 0; i < 4; ++i) v[4 * e + i] = e0[row_of(e, i) * 128 + col];
+      put_frags(v);
     }
-    f32x4 acc[2] = {bw[0], bw[1]};
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
+    for (int w = 1; w < wt; ++w) {
+      __syncthreads();
+      f16x8 sh[4], sl[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
-        f16x8 ph, pl;
+        sh[p] = xh[p * 64 + lane];
+        sl[p] = xl[p * 64 + lane];
+      }
+      const float* B = wv.at(n, h, w, 0);
+      f32x4 acc[2];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          _Float16 hh, ll;
-          split_f16(pf[e][p][j >> 2][j & 3], hh, ll);
-          ph[j] = hh;
-          pl[j] = ll;
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[e][i] = B[row_of(e, i) * 128 + col];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          f16x8 ph, pl;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            _Float16 hh, ll;
+            split_f16(pf[e][p][j >> 2][j & 3], hh, ll);
+            ph[j] = hh;
+            pl[j] = ll;
+          }
+          acc[e] = mfma_f16(ph, sh[p], acc[e]);
+          acc[e] = mfma_f16(ph, sl[p], acc[e]);
+          acc[e] = mfma_f16(pl, sh[p], acc[e]);
         }
-        acc[e] = mfma_f16(ph, sh[p], acc[e]);
-        acc[e] = mfma_f16(ph, sl[p], acc[e]);
-        acc[e] = mfma_f16(pl, sh[p], acc[e]);
+      if (w + 1 < wt) load_p(pf, w + 1);
+      __syncthreads();   // every wave has read this step's fragments
+      float v[8];
+#pragma unroll
+      for (int e = 0; e < 2; ++e)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * e + i] = acc[e][i];
+      if (w + 1 < wt) {
+        put_frags(v);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sin[row_of(e, i) * (16 * kNT) + 16 * t + l16] = v[4 * e + i];
       }
-    if (w + 2 < nwin) {
-      load_p(pf, w + 1);
-      load_b(bw[0], 0, w + 1);
-      load_b(bw[1], 1, w + 1);
     }
-    float* si = wv.at(n, h, w + 1, 2);
-    float v[8];
-#pragma unroll
-    for (int e = 0; e < 2; ++e)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        v[4 * e + i] = acc[e][i];
-        si[row_of(e, i) * 128 + col] = acc[e][i];
-      }
-    __syncthreads();
-    put_frags(v);
   }
+  __syncthreads();   // the initial state is complete
 }
 
 __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillArgs a,
@@ -1175,7 +1177,12 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillA
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
   job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
-  job.s_init = w == 1 ? wv.at(n, h, 0, 0) : wv.at(n, h, w, 2);
+  job.s_init = w == 1 ? wv.at(n, h, 0, 0) : nullptr;   // window 1 starts from E_0
+  job.s_init_lds = nullptr;
+  if (w >= 2) {
+    carry_to_lds(wv, n, h, tile, w, lds);
+    job.s_init_lds = reinterpret_cast<const float*>(lds);
+  }
   job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
   job.s_final = w == nwin - 1 ? prefill_final_state(a, n, h) : nullptr;
   chain_body(a, ws, lds, job);
@@ -1220,7 +1227,6 @@ hipError_t launch_chain(const PrefillArgs& a, const uint8_t* ws, hipStream_t s) 
   wv.W = a.windows;
   const int jobs = 1 + 2 * (a.windows - 2);
   prefill_split_window_a<<<dim3((unsigned)(units * jobs * kChainTiles)), kChainThreads, kChainLds, s>>>(a, ws, wv);
-  prefill_split_carry<<<dim3((unsigned)(units * 8)), 256, 0, s>>>(a, wv);
   prefill_split_window_c<<<dim3((unsigned)(units * (a.windows - 1) * kChainTiles)), kChainThreads, kChainLds, s>>>(
       a, ws, wv);
   return hipGetLastError();

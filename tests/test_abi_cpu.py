@@ -139,9 +139,9 @@ def test_auto_route_and_workspace():
     assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
     try:
         kda.set_prefill_route(kda.ROUTE_SPLIT)
-        # one long sequence: records plus the window states (E, P, SI per window and head)
+        # one long sequence: records plus the window states (E and P per window and head)
         assert kda.workspace_size(1, 8192, 8) == ((1 + 8192 // 32 + 1) * 8 * 49152
-                                                  + 1 * 8 * 5 * 3 * 65536)
+                                                  + 1 * 8 * 5 * 2 * 65536)
         assert kda.workspace_size(3, 100, 2) == (3 + 3 + 1) * 2 * 49152
         kda.set_prefill_route(kda.ROUTE_CHUNK)
         assert kda.workspace_size(16, 40000, 32) == 0

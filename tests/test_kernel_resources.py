@@ -21,7 +21,6 @@ MIN_WAVES = {
     "prefill_split_chain": 2,
     "prefill_split_window_a": 2,
     "prefill_split_window_c": 2,
-    "prefill_split_carry": 2,
 }
 
 

@@ -251,7 +251,7 @@ def test_two_pass_equals_split_route(dev, which):
                                           (1500, 2, -1.0, None)])
 def test_split_windows(dev, T, H, lb, state):
     """One long sequence on the split route is cut into windows (maps of the inner
-    windows, carry, windows from their true initial states); ragged tails, split-16
+    windows, then each window from its composed initial state); ragged tails, split-16
     anchoring and a missing initial state included."""
     plan = kda.plan(1, T, H, lb, 0, kda.ROUTE_SPLIT)
     assert plan.windows >= 3
