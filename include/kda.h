@@ -29,6 +29,8 @@
  *                   place (flashinfer PR #5551, "Kimi K3 TP12 H=8 fused KDA
  *                   decode": positive unique slots, FP32 and BF16 state,
  *                   64-bit slot offsets).
+ *   kda_decode_ex -- the same with the input front-end (raw gates, beta
+ *                   logits, q/k L2 norm).
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -62,7 +64,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -74,6 +76,29 @@ typedef enum {
 } kda_status;
 
 typedef enum { KDA_STATE_F32 = 0, KDA_STATE_BF16 = 1 } kda_state_dtype;
+
+/* Input front-end: how the gate and beta arrive, and whether q and k are
+ * L2-normalised by the library.  "flashinfer PR #5551: Kimi K3 TP12 H=8 fused
+ * KDA decode" gives the decode kernels a lower-bound switch, the bound and
+ * norm_eps, and tests softplus and lower-bound gates; the PR #5565/#5573
+ * notes feed beta as a sigmoid of logits and run the unbounded softplus gate
+ * of Kimi-Linear.  The formulas (the pages print none) are read as:
+ *   KDA_GATE_LOG          the g tensor is the natural-log decay itself;
+ *   KDA_GATE_LOWER_BOUND  the g tensor holds a, decay = lower_bound * sigmoid(a);
+ *   KDA_GATE_SOFTPLUS     the g tensor holds a, decay = -softplus(a)
+ *                         = -log(1 + e^a) (no lower bound);
+ *   beta_logits != 0      beta is used as sigmoid(beta);
+ *   normalize_qk != 0     q and k of each (token, head) are scaled by
+ *                         1 / sqrt(sum_c x_c^2 + norm_eps) (FP32, before use).
+ * A NULL kda_frontend pointer means {KDA_GATE_LOG, 0, 0, 0, 0}. */
+typedef enum { KDA_GATE_LOG = 0, KDA_GATE_LOWER_BOUND = 1, KDA_GATE_SOFTPLUS = 2 } kda_gate_mode;
+typedef struct {
+  int32_t gate_mode;    /* kda_gate_mode                                        */
+  float lower_bound;    /* KDA_GATE_LOWER_BOUND: the bound (< 0, natural log)   */
+  int32_t beta_logits;
+  int32_t normalize_qk;
+  float norm_eps;       /* >= 0, finite                                          */
+} kda_frontend;
 
 /* Prefill kernels ("routes").  AUTO lets kda_prefill_plan choose. */
 typedef enum {
@@ -276,6 +301,20 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g,
                int64_t num_slots, const int32_t* slot_indices, int32_t rows,
                int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
                float scale, void* out, hipStream_t stream);
+
+/* kda_decode with the input front-end `frontend` (see kda_frontend; NULL =
+ * kda_decode).  With a raw gate, the g tensor holds a and any finite value is
+ * allowed; with beta_logits, beta holds logits.  The q/k normalisation is
+ * folded into the step's reductions (no extra pass over the state).
+ * Errors: KDA_ERR_INVALID_ARGUMENT for an unknown gate mode, a lower bound
+ * that is not negative and finite (KDA_GATE_LOWER_BOUND) or a negative or
+ * non-finite norm_eps; everything else as kda_decode. */
+int kda_decode_ex(const void* q, const void* k, const void* v, const void* g,
+                  const void* beta, void* state_pool, int32_t state_dtype,
+                  int64_t num_slots, const int32_t* slot_indices, int32_t rows,
+                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
+                  float scale, const kda_frontend* frontend, void* out,
+                  hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc -- */
 /* Text describing the last non-OK return on the calling thread ("" if none). */

@@ -48,6 +48,37 @@ class _Plan(ctypes.Structure):
                 ("windows", ctypes.c_int32), ("window_chunks", ctypes.c_int32)]
 
 
+class _FrontEnd(ctypes.Structure):
+    _fields_ = [("gate_mode", ctypes.c_int32), ("lower_bound", ctypes.c_float),
+                ("beta_logits", ctypes.c_int32), ("normalize_qk", ctypes.c_int32),
+                ("norm_eps", ctypes.c_float)]
+
+
+GATE_LOG, GATE_LOWER_BOUND, GATE_SOFTPLUS = 0, 1, 2
+
+
+@dataclass
+class FrontEnd:
+    """Input front-end of kda_decode_ex / kda_prefill_ex (include/kda.h:
+    kda_frontend): gate_mode GATE_LOG (g is the log-decay), GATE_LOWER_BOUND
+    (g holds a; decay lower_bound * sigmoid(a)) or GATE_SOFTPLUS (decay
+    -softplus(a)); beta_logits: beta = sigmoid(beta); normalize_qk: q, k scaled
+    by 1 / sqrt(sum x^2 + norm_eps)."""
+    gate_mode: int = GATE_LOG
+    lower_bound: float = 0.0
+    beta_logits: bool = False
+    normalize_qk: bool = False
+    norm_eps: float = 0.0
+
+    def _c(self):
+        return _FrontEnd(int(self.gate_mode), float(self.lower_bound), int(bool(self.beta_logits)),
+                         int(bool(self.normalize_qk)), float(self.norm_eps))
+
+
+def _fe_ptr(fe):
+    return None if fe is None else ctypes.byref(fe._c())
+
+
 @dataclass
 class Plan:
     route: int
@@ -95,6 +126,9 @@ def load():
     lib.kda_prefill_checkpoint_slots.restype = sz
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
     lib.kda_decode.restype = ctypes.c_int
+    lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32,
+                                  ctypes.POINTER(_FrontEnd), vp, vp]
+    lib.kda_decode_ex.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -294,11 +328,13 @@ def prefill_chain(records, cu_seqlens, num_heads, *, scale, total_tokens, initia
     return out, final_state
 
 
-def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, stream=None):
+def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, stream=None,
+           frontend=None):
     """One T=1 step per row against ``state_pool`` (fp32 or bf16), in place.
 
     q, k, v, g: bf16 [rows, H, 128]; beta: bf16 [rows, H];
     state_pool: [num_slots, H, 128, 128]; slot_indices: int32 [rows].
+    ``frontend``: a :class:`FrontEnd` (kda_decode_ex) or None (kda_decode).
     Returns out (bf16 [rows, H, 128]).
     """
     dev = q.device
@@ -317,7 +353,13 @@ def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, strea
     if out is None:
         out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (R, H, D), dev)
-    _check(load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), sd,
-                             state_pool.shape[0], _ptr(slot_indices), R, H, D, D, float(scale),
-                             _ptr(out), _stream(stream)))
+    if frontend is None:
+        _check(load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
+                                 sd, state_pool.shape[0], _ptr(slot_indices), R, H, D, D,
+                                 float(scale), _ptr(out), _stream(stream)))
+    else:
+        _check(load().kda_decode_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                    _ptr(state_pool), sd, state_pool.shape[0], _ptr(slot_indices),
+                                    R, H, D, D, float(scale), _fe_ptr(frontend), _ptr(out),
+                                    _stream(stream)))
     return out

@@ -17,6 +17,14 @@
 // inside a wave and one LDS exchange across the four waves; the state is
 // read once and written once.  Row counts too small to fill the chip use
 // narrower slices (more blocks per item).
+//
+// Optional input front-end (the decode ABI of that PR carries a lower-bound
+// switch, the bound and norm_eps; its tests use softplus and lower-bound
+// gates): the decay from a raw gate input a, e^{lb sigmoid(a)} or
+// e^{-softplus(a)} = sigmoid(-a); beta from logits; q and k L2-normalised.
+// The normalisation costs no extra pass: w, p and q . k are linear in k and
+// q, so they are reduced from the raw vectors and scaled by 1/|k|, 1/|q| (two
+// more block sums), and 1/|k| is folded into u for the state update.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -73,6 +81,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
 
   __shared__ float sq[kHeadDim], sk[kHeadDim], sd[kHeadDim];
   __shared__ float red[4][TPR][9];
+  __shared__ float nrm[2][2];   // [wave][q, k] partial sums of squares
 
   const int H = a.num_heads;
   const int64_t item = blockIdx.x / SLICES;
@@ -96,11 +105,38 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   for (int i = 0; i < RPT; ++i) s[i] = IO::load(S + (rg + RG * i) * kHeadDim + col0);
 
   if (tid < kHeadDim) {
-    sq[tid] = bf16_to_f32(a.q[rh * kHeadDim + tid]);
-    sk[tid] = bf16_to_f32(a.k[rh * kHeadDim + tid]);
-    sd[tid] = fast_exp2(bf16_to_f32(a.g[rh * kHeadDim + tid]) * kLog2e);
+    const float qv = bf16_to_f32(a.q[rh * kHeadDim + tid]);
+    const float kv = bf16_to_f32(a.k[rh * kHeadDim + tid]);
+    const float gv = bf16_to_f32(a.g[rh * kHeadDim + tid]);
+    sq[tid] = qv;
+    sk[tid] = kv;
+    float d;
+    if (a.fe.gate_mode == 1)
+      d = fast_exp2(a.fe.lower_bound * kLog2e / (1.f + fast_exp2(-gv * kLog2e)));
+    else if (a.fe.gate_mode == 2)
+      d = 1.f / (1.f + fast_exp2(gv * kLog2e));     // e^{-softplus(a)} = sigmoid(-a)
+    else
+      d = fast_exp2(gv * kLog2e);
+    sd[tid] = d;
+    if (a.fe.normalize_qk) {   // waves 0 and 1 hold the 128 channels
+      float sq2 = qv * qv, sk2 = kv * kv;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) {
+        sq2 += __shfl_xor(sq2, off);
+        sk2 += __shfl_xor(sk2, off);
+      }
+      if (lane == 0) {
+        nrm[wave][0] = sq2;
+        nrm[wave][1] = sk2;
+      }
+    }
   }
   __syncthreads();
+  float rq = 1.f, rk = 1.f;
+  if (a.fe.normalize_qk) {
+    rq = 1.f / __builtin_sqrtf(nrm[0][0] + nrm[1][0] + a.fe.norm_eps);
+    rk = 1.f / __builtin_sqrtf(nrm[0][1] + nrm[1][1] + a.fe.norm_eps);
+  }
 
   float w[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;
 #pragma unroll
@@ -151,8 +187,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
       qk = acc;
   }
   (void)RG_PER_WAVE;
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    w[m] *= rk;
+    p[m] *= rq;
+  }
+  qk *= rq * rk;
 
-  const float b = bf16_to_f32(a.beta[rh]);
+  float b = bf16_to_f32(a.beta[rh]);
+  if (a.fe.beta_logits) b = 1.f / (1.f + fast_exp2(-b * kLog2e));
   const uint2 vw = *reinterpret_cast<const uint2*>(a.v + rh * kHeadDim + col0);
   float u[4];
   u[0] = b * (bf16lo(vw.x) - w[0]);
@@ -160,13 +203,15 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   u[2] = b * (bf16lo(vw.y) - w[2]);
   u[3] = b * (bf16hi(vw.y) - w[3]);
 
+  // the update adds k_n u^T = k (u / |k|)^T; the output keeps u
+  const float uk[4] = {u[0] * rk, u[1] * rk, u[2] * rk, u[3] * rk};
 #pragma unroll
   for (int i = 0; i < RPT; ++i) {
     const float kc = sk[rg + RG * i];
-    s[i].x = fmaf(kc, u[0], s[i].x);
-    s[i].y = fmaf(kc, u[1], s[i].y);
-    s[i].z = fmaf(kc, u[2], s[i].z);
-    s[i].w = fmaf(kc, u[3], s[i].w);
+    s[i].x = fmaf(kc, uk[0], s[i].x);
+    s[i].y = fmaf(kc, uk[1], s[i].y);
+    s[i].z = fmaf(kc, uk[2], s[i].z);
+    s[i].w = fmaf(kc, uk[3], s[i].w);
     IO::store(S + (rg + RG * i) * kHeadDim + col0, s[i]);
   }
   if (rg == 0) {

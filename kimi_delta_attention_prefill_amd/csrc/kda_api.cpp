@@ -31,6 +31,27 @@ int ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+// Validates a kda_frontend (NULL = defaults) into *out; KDA_OK or the error.
+int frontend_args(const kda_frontend* f, const char* fn, kda::FrontEnd* out) {
+  *out = kda::FrontEnd{};
+  if (!f) return KDA_OK;
+  if (f->gate_mode != KDA_GATE_LOG && f->gate_mode != KDA_GATE_LOWER_BOUND &&
+      f->gate_mode != KDA_GATE_SOFTPLUS)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown gate mode %d", fn, f->gate_mode);
+  if (f->gate_mode == KDA_GATE_LOWER_BOUND && !(std::isfinite(f->lower_bound) && f->lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: the lower-bound gate needs a finite bound < 0 (got %g)",
+                fn, (double)f->lower_bound);
+  if (!(std::isfinite(f->norm_eps) && f->norm_eps >= 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: norm_eps must be finite and >= 0 (got %g)", fn,
+                (double)f->norm_eps);
+  out->gate_mode = f->gate_mode;
+  out->lower_bound = f->lower_bound;
+  out->beta_logits = f->beta_logits != 0;
+  out->normalize_qk = f->normalize_qk != 0;
+  out->norm_eps = f->norm_eps;
+  return KDA_OK;
+}
+
 // Compute-unit count of the current device, cached per device id.
 int current_device_cus() {
   static std::atomic<int> cache[64];
@@ -429,10 +450,13 @@ int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
   return ok();
 }
 
-int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
-               void* state_pool, int32_t state_dtype, int64_t num_slots,
-               const int32_t* slot_indices, int32_t rows, int32_t num_heads, int32_t head_dim_k,
-               int32_t head_dim_v, float scale, void* out, hipStream_t stream) {
+int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                  void* state_pool, int32_t state_dtype, int64_t num_slots,
+                  const int32_t* slot_indices, int32_t rows, int32_t num_heads,
+                  int32_t head_dim_k, int32_t head_dim_v, float scale,
+                  const kda_frontend* frontend, void* out, hipStream_t stream) {
+  kda::FrontEnd fe;
+  if (const int st = frontend_args(frontend, "kda_decode", &fe)) return st;
   if (head_dim_k != KDA_HEAD_DIM || head_dim_v != KDA_HEAD_DIM)
     return fail(KDA_ERR_UNSUPPORTED, "kda_decode: head dims must be 128 (got dk=%d, dv=%d)",
                 head_dim_k, head_dim_v);
@@ -470,6 +494,7 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g, const
   a.num_heads = num_heads;
   a.scale = scale;
   a.out = static_cast<uint16_t*>(out);
+  a.fe = fe;
 
   // Narrow value-column slices when there are too few items to fill the chip.
   int cus = current_device_cus();
@@ -480,6 +505,14 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g, const
   if (e != hipSuccess)
     return fail(KDA_ERR_HIP, "kda_decode: launch failed: %s", hipGetErrorString(e));
   return ok();
+}
+
+int kda_decode(const void* q, const void* k, const void* v, const void* g, const void* beta,
+               void* state_pool, int32_t state_dtype, int64_t num_slots,
+               const int32_t* slot_indices, int32_t rows, int32_t num_heads, int32_t head_dim_k,
+               int32_t head_dim_v, float scale, void* out, hipStream_t stream) {
+  return kda_decode_ex(q, k, v, g, beta, state_pool, state_dtype, num_slots, slot_indices, rows,
+                       num_heads, head_dim_k, head_dim_v, scale, nullptr, out, stream);
 }
 
 }  // extern "C"

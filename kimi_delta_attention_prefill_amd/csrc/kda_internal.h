@@ -46,6 +46,18 @@ struct PrefillArgs {
   int32_t ckpt_tokens;
 };
 
+// Input front-end: gate_mode 0 = g is the natural-log decay, 1 = g holds a
+// and the decay is lower_bound * sigmoid(a), 2 = g holds a and the decay is
+// -softplus(a); beta_logits: beta = sigmoid(beta); normalize_qk: q, k scaled
+// by 1 / sqrt(sum x^2 + norm_eps) per (token, head).
+struct FrontEnd {
+  int32_t gate_mode = 0;
+  float lower_bound = 0.f;
+  int32_t beta_logits = 0;
+  int32_t normalize_qk = 0;
+  float norm_eps = 0.f;
+};
+
 struct DecodeArgs {
   const uint16_t* q;
   const uint16_t* k;
@@ -59,6 +71,7 @@ struct DecodeArgs {
   int32_t num_heads;
   float scale;
   uint16_t* out;          // bf16 [rows, H, 128]
+  FrontEnd fe;            // how g and beta are given, q/k normalisation
 };
 
 // Token-serial FP32 prefill; `waves` value-column tiles of 16 per block.

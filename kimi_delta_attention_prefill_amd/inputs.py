@@ -171,6 +171,25 @@ def make_decode_case(rows, num_heads=8, num_slots=4096, state_dtype=torch.float3
     return DecodeCase(q, k, v, g, beta, pool, slots, SCALE, int(seed), name)
 
 
+def make_decode_raw_case(rows, num_heads=8, num_slots=4096, seed=BASE_SEED + 5,
+                         qk_std=3.0) -> DecodeCase:
+    """Decode inputs as a model hands them over before the input front-end:
+    q, k ~ qk_std N(0, 1) (not normalised), v ~ N(0, 1), the gate tensor holds
+    raw a ~ N(0, 1), beta holds logits ~ N(0, 1); all bf16.  Same draw order
+    as make_decode_case; no pool is drawn."""
+    gen = torch.Generator().manual_seed(int(seed))
+    R, H = int(rows), int(num_heads)
+    if R > num_slots:
+        raise ValueError("rows exceed the pool size (slots must be unique)")
+    q = (float(qk_std) * torch.randn(R, H, HEAD_DIM, generator=gen)).to(torch.bfloat16)
+    k = (float(qk_std) * torch.randn(R, H, HEAD_DIM, generator=gen)).to(torch.bfloat16)
+    v = torch.randn(R, H, HEAD_DIM, generator=gen).to(torch.bfloat16)
+    a = torch.randn(R, H, HEAD_DIM, generator=gen).to(torch.bfloat16)
+    b = torch.randn(R, H, generator=gen).to(torch.bfloat16)
+    slots = torch.randperm(int(num_slots), generator=gen)[:R].to(torch.int32)
+    return DecodeCase(q, k, v, a, b, None, slots, SCALE, int(seed), "raw")
+
+
 def make_decode_pool(num_slots, num_heads, state_dtype=torch.float32, init_std=0.02,
                      gen=None, dk=HEAD_DIM, dv=HEAD_DIM) -> torch.Tensor:
     """State pool [num_slots, H, dk, dv]: init_std * N(0, 1) in fp32 (bf16: rounded)."""

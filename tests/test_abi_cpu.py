@@ -131,6 +131,29 @@ def test_decode_host_validation():
     assert _decode_raw(rows=0, q=None, pool=None, idx=None, out=None) == 0
 
 
+def test_decode_frontend_host_validation():
+    lib = kda.load()
+    E = _lib.KDA_ERR_INVALID_ARGUMENT
+    P = ctypes.c_void_p
+
+    def call(fe):
+        ref = None if fe is None else ctypes.byref(fe._c())
+        return lib.kda_decode_ex(P(16), P(16), P(16), P(16), P(16), P(16), 0, 4, P(16), 0, 8, 128,
+                                 128, 1.0, ref, P(16), None)
+
+    assert call(None) == 0                                       # rows = 0: a no-op
+    assert call(kda.FrontEnd()) == 0
+    assert call(kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True, normalize_qk=True,
+                             norm_eps=1e-6)) == 0
+    assert call(kda.FrontEnd(gate_mode=3)) == E
+    assert "gate mode" in kda.last_error()
+    assert call(kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=0.0)) == E
+    assert call(kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=float("-inf"))) == E
+    assert call(kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-5.0)) == 0
+    assert call(kda.FrontEnd(normalize_qk=True, norm_eps=-1e-6)) == E
+    assert call(kda.FrontEnd(normalize_qk=True, norm_eps=float("nan"))) == E
+
+
 def test_auto_route_and_workspace():
     # few (sequence, head) units: two-pass split route; many: fused chunk route
     assert kda.plan(1, 8192, 8, -5.0, 256).route == kda.ROUTE_SPLIT

@@ -1,0 +1,95 @@
+"""GPU parity of the input front-end (raw gates, beta logits, q/k L2 norm)
+against the FP64 oracle's front-end followed by the oracle step, through the C
+ABI (kda_decode_ex).  The oracle applies oracle/frontend.py to the same bf16
+raw inputs in double precision, then runs the token recurrence."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_prefill_amd as kda
+import oracle
+from oracle import frontend as ofe
+from kimi_delta_attention_prefill_amd.inputs import make_decode_pool, make_decode_raw_case
+from _checks import check_bf16_state, check_out, check_state
+
+pytestmark = pytest.mark.gpu
+
+H = 8
+NUM_SLOTS = 512
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    kda.load()
+    return torch.device("cuda:0")
+
+
+FRONTENDS = {
+    "log": kda.FrontEnd(),
+    "lower_bound": kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-5.0,
+                                beta_logits=True, normalize_qk=True, norm_eps=1e-6),
+    "softplus": kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True, normalize_qk=True,
+                             norm_eps=1e-6),
+    "softplus_eps": kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=False,
+                                 normalize_qk=True, norm_eps=4.0),
+}
+
+
+def _f64(t):
+    return t.double().numpy()
+
+
+@pytest.mark.parametrize("name", list(FRONTENDS))
+@pytest.mark.parametrize("state", ["f32", "bf16"])
+@pytest.mark.parametrize("rows", [3, 300])
+def test_decode_frontend(dev, name, state, rows):
+    fe = FRONTENDS[name]
+    case = make_decode_raw_case(rows, H, NUM_SLOTS, seed=900 + rows)
+    beta = case.beta
+    if not fe.beta_logits:   # beta must be in [0, 1] when it is used as given
+        beta = torch.sigmoid(case.beta.float()).to(torch.bfloat16)
+    if fe.gate_mode == kda.GATE_LOG:   # a log-decay must be <= 0
+        case.g = (-case.g.float().abs()).to(torch.bfloat16)
+    dt = torch.float32 if state == "f32" else torch.bfloat16
+    P = make_decode_pool(NUM_SLOTS, H, dt, 0.02, 77).to(dev)
+    sl = case.slots.to(dev)
+    pre = P[sl.long()].clone()
+    _say(f"[gpu] decode_ex {name} {state} rows={rows}")
+    to = lambda t: t.to(dev)
+    out = kda.decode(to(case.q), to(case.k), to(case.v), to(case.g), to(beta), P, sl,
+                     scale=case.scale, frontend=fe)
+    torch.cuda.synchronize()
+    q, k, g, b = ofe.apply(_f64(case.q), _f64(case.k), _f64(case.g), _f64(beta),
+                           gate_mode=fe.gate_mode,
+                           lower_bound=fe.lower_bound, beta_logits=fe.beta_logits,
+                           normalize_qk=fe.normalize_qk, norm_eps=fe.norm_eps)
+    ref_out, ref_post = oracle.decode(q, k, case.v, g, b, pre.cpu(), np.arange(rows), case.scale)
+    r1 = check_out(out.cpu(), ref_out)
+    post = P[sl.long()].cpu()
+    r2 = check_state(post, ref_post) if state == "f32" else check_bf16_state(post, ref_post)
+    _say(f"   out {r1} state {r2}")
+
+
+def test_decode_frontend_default_equals_plain(dev):
+    """A default front-end (log gate, beta as given, no norm) is bitwise kda_decode."""
+    case = make_decode_raw_case(64, H, NUM_SLOTS, seed=5)
+    g = (-case.g.float().abs()).to(torch.bfloat16)
+    beta = torch.sigmoid(case.beta.float()).to(torch.bfloat16)
+    outs, pools = [], []
+    for fe in (None, kda.FrontEnd()):
+        P = make_decode_pool(NUM_SLOTS, H, torch.float32, 0.02, 78).to(dev)
+        to = lambda t: t.to(dev)
+        outs.append(kda.decode(to(case.q), to(case.k), to(case.v), to(g), to(beta), P,
+                               to(case.slots), scale=case.scale, frontend=fe))
+        pools.append(P)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(pools[0], pools[1])

@@ -319,3 +319,77 @@ def test_snapshots_equal_truncated_prefills():
             assert np.array_equal(snaps[n][j - 1], f[0])
         if L % I == 0 and L > 0:
             assert np.array_equal(snaps[n][-1], fin[n])
+
+
+# ---------------------------------------------------------------- front-end
+from oracle import frontend as fe  # noqa: E402
+
+
+def test_frontend_sigmoid_softplus_closed_forms():
+    # sigmoid(0) = 1/2; softplus(0) = ln 2; exact asymptotes far from 0
+    assert fe.sigmoid(0.0) == 0.5
+    assert fe.softplus(0.0) == math.log(2.0)
+    assert fe.softplus(60.0) == 60.0                        # log(1 + e^60) = 60 + O(e^-60)
+    assert fe.softplus(-40.0) == pytest.approx(math.exp(-40.0), rel=1e-15)
+    with np.errstate(over="raise", invalid="raise"):             # no overflow either way
+        assert fe.sigmoid(-700.0) == pytest.approx(math.exp(-700.0), rel=1e-15)
+        assert fe.sigmoid(-800.0) == 0.0 and fe.sigmoid(800.0) == 1.0
+        assert fe.softplus(800.0) == 800.0 and fe.softplus(-800.0) == 0.0
+    # sigmoid(x) + sigmoid(-x) = 1 and softplus(x) - softplus(-x) = x, both signs
+    x = np.linspace(-30.0, 30.0, 241)
+    np.testing.assert_allclose(fe.sigmoid(x) + fe.sigmoid(-x), 1.0, rtol=0, atol=4.5e-16)   # 2 ulp
+    np.testing.assert_allclose(fe.softplus(x) - fe.softplus(-x), x, rtol=0, atol=1e-13)
+    # sigmoid(x) = exp(-softplus(-x)): two independent formulas of the same function
+    np.testing.assert_allclose(fe.sigmoid(x), np.exp(-fe.softplus(-x)), rtol=1e-14)
+    # the derivative of softplus is sigmoid (central difference)
+    h = 1e-6
+    np.testing.assert_allclose((fe.softplus(x + h) - fe.softplus(x - h)) / (2 * h), fe.sigmoid(x),
+                               rtol=0, atol=1e-8)
+
+
+def test_frontend_gates():
+    a = np.array([-50.0, -1.0, 0.0, 1.0, 50.0])
+    # lower-bound gate: in (lb, 0), lb / 2 at a = 0, -> 0 and -> lb at the ends
+    g = fe.gate(a, fe.GATE_LOWER_BOUND, -5.0)
+    assert g[2] == -2.5 and g[0] > -1e-20 and g[-1] == -5.0
+    assert np.all(np.diff(g) < 0)
+    # softplus gate: -ln 2 at 0, -a for large a, unbounded below
+    g = fe.gate(a, fe.GATE_SOFTPLUS)
+    assert g[2] == -math.log(2.0) and g[-1] == -50.0 and g[0] < 0.0
+    # log mode passes the value through
+    np.testing.assert_array_equal(fe.gate(a, fe.GATE_LOG), a)
+    with pytest.raises(ValueError):
+        fe.gate(a, 7)
+
+
+def test_frontend_l2_norm_axis_and_eps():
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((3, 4, 128)) * np.arange(1, 13).reshape(3, 4, 1)
+    y = fe.l2_normalize(x, 0.0)
+    # unit length over the 128 channels of every (token, head), direction kept
+    np.testing.assert_allclose(np.linalg.norm(y, axis=-1), 1.0, rtol=1e-15)
+    np.testing.assert_allclose(y * np.linalg.norm(x, axis=-1, keepdims=True), x, rtol=1e-14)
+    # eps: squared length s / (s + eps); a zero vector stays zero
+    s = np.sum(x * x, axis=-1)
+    np.testing.assert_allclose(np.sum(fe.l2_normalize(x, 1e-2) ** 2, axis=-1), s / (s + 1e-2),
+                               rtol=1e-14)
+    assert np.all(fe.l2_normalize(np.zeros((2, 128)), 1e-6) == 0.0)
+    # a basis vector scaled by c normalises to the basis vector exactly
+    e = np.zeros(128)
+    e[17] = 3.0
+    np.testing.assert_array_equal(fe.l2_normalize(e, 0.0), np.eye(128)[17])
+
+
+def test_frontend_apply_composes():
+    rng = np.random.default_rng(6)
+    q, k, a = (rng.standard_normal((5, 2, 128)) for _ in range(3))
+    b = rng.standard_normal((5, 2))
+    q1, k1, g1, b1 = fe.apply(q, k, a, b, gate_mode=fe.GATE_SOFTPLUS, beta_logits=True,
+                              normalize_qk=True, norm_eps=1e-6)
+    np.testing.assert_allclose(np.linalg.norm(q1, axis=-1), 1.0, atol=1e-6)
+    np.testing.assert_allclose(np.linalg.norm(k1, axis=-1), 1.0, atol=1e-6)
+    assert np.all(g1 < 0) and np.all((b1 > 0) & (b1 < 1))
+    # identity settings change nothing
+    q2, k2, g2, b2 = fe.apply(q, k, a, b)
+    for u, w in ((q2, q), (k2, k), (g2, a), (b2, b)):
+        np.testing.assert_array_equal(u, w)
