@@ -30,7 +30,8 @@
  *                   decode": positive unique slots, FP32 and BF16 state,
  *                   64-bit slot offsets).
  *   kda_decode_ex -- the same with the input front-end (raw gates, beta
- *                   logits, q/k L2 norm).
+ *                   logits, q/k L2 norm); kda_prefill_ex and
+ *                   kda_prefill_pool_ex likewise for prefill.
  *
  * Conventions shared by every entry point
  * ---------------------------------------
@@ -47,7 +48,8 @@
  *   kernel surface, as usual in HIP, at the caller's next synchronisation.
  * - Device-side preconditions that are NOT checked (they would need a
  *   device read): cu_seqlens non-decreasing with cu_seqlens[0] = 0 and
- *   cu_seqlens[N] = total_tokens; lower_bound <= g <= 0 for prefill;
+ *   cu_seqlens[N] = total_tokens; lower_bound <= g <= 0 for prefill (any
+ *   g <= 0 with lower_bound = -INFINITY);
  *   beta in [0, 1]; decode slot indices unique among the non-negative ones.
  *   Kernels clamp every index they read so that a violated precondition
  *   gives wrong numbers, never an out-of-bounds access.
@@ -119,8 +121,16 @@ typedef enum {
   KDA_ANCHOR_FIXED = 0,  /* one anchor C = 16 * lower_bound * log2(e) per chunk:
                             operand exponents stay within 16|lb|log2e <= 126,
                             i.e. usable for lower_bound >= -5.45            */
-  KDA_ANCHOR_SPLIT16 = 1 /* per 16-token half anchors ("ordinary SafeGate"
+  KDA_ANCHOR_SPLIT16 = 1, /* per 16-token half anchors ("ordinary SafeGate"
                             16-token blocks), for wider bounds             */
+  KDA_ANCHOR_DATA = 2    /* no bound (lower_bound = -inf, or the softplus gate):
+                            each 16-token half of each chunk is anchored, per
+                            channel, at the midpoint of its gate-prefix range
+                            (a data-dependent range strategy).  Exact to the
+                            usual rounding while no half of a chunk decays a
+                            channel by more than e^-174 (sum of |g| over 16
+                            tokens <= 174); beyond that the anchored factors
+                            are clamped (finite, less accurate)            */
 } kda_anchor_mode;
 
 /* What kda_prefill will launch for a problem (a pure host function of the
@@ -152,7 +162,8 @@ typedef struct {
  *  num_heads   H >= 1.
  *  head_dim_k, head_dim_v   must both be 128 (else KDA_ERR_UNSUPPORTED).
  *  scale       output scale (finite), e.g. 1/sqrt(128).
- *  lower_bound finite, < 0: the bound g >= lower_bound that fixes the anchor.
+ *  lower_bound < 0: the bound g >= lower_bound that fixes the anchor, or
+ *              -INFINITY for an unbounded gate (KDA_ANCHOR_DATA).
  *  initial_state  fp32 [N, H, 128, 128] (dv contiguous) or NULL for zeros.
  *  final_state    fp32 [N, H, 128, 128] or NULL (not stored).  May equal
  *              initial_state (each sequence-head reads its slice before it
@@ -171,6 +182,23 @@ int kda_prefill(const void* q, const void* k, const void* v, const void* g,
                 int32_t head_dim_v, float scale, float lower_bound,
                 const float* initial_state, float* final_state, void* out,
                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* kda_prefill with the input front-end `frontend` (kda_frontend; NULL =
+ * kda_prefill).  The gate mode decides the bound the chunk routes rely on:
+ * KDA_GATE_LOG uses `lower_bound` as kda_prefill does; KDA_GATE_LOWER_BOUND
+ * uses frontend->lower_bound (g lies in (lower_bound, 0)) and ignores the
+ * argument; KDA_GATE_SOFTPLUS is unbounded (KDA_ANCHOR_DATA) and ignores it.
+ * The transforms run inside the prefill kernels on the bf16 inputs, in FP32
+ * (the gate before its prefix sum; q, k scaled per token before any
+ * product); nothing is written back.  A zero q or k vector with norm_eps = 0
+ * stays zero. */
+int kda_prefill_ex(const void* q, const void* k, const void* v, const void* g,
+                   const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                   int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                   int32_t head_dim_v, float scale, float lower_bound,
+                   const kda_frontend* frontend, const float* initial_state,
+                   float* final_state, void* out, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
 
 /* --------------------------------------------------- pooled prefill --
  * kda_prefill with the states of a serving engine: each sequence starts from
@@ -201,6 +229,16 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
                      int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
                      int32_t checkpoint_tokens, void* out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
+
+/* kda_prefill_pool with the input front-end (as kda_prefill_ex). */
+int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                        int32_t head_dim_v, float scale, float lower_bound,
+                        const kda_frontend* frontend, float* state_pool, int64_t num_slots,
+                        const int32_t* slot_indices, float* checkpoints,
+                        int32_t checkpoint_tokens, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream);
 
 /* N + T_tot / checkpoint_tokens + 1: the [H, 128, 128] slots a checkpoint
  * buffer of kda_prefill_pool must hold (0 for invalid arguments). */

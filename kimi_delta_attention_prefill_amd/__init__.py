@@ -5,7 +5,7 @@ of ``include/kda.h``); this package is its Python binding.  Importing the
 package does not load the library; the first call does, and raises if the
 library has not been built.
 """
-from ._lib import (ANCHOR_FIXED, ANCHOR_SPLIT16, GATE_LOG, GATE_LOWER_BOUND, GATE_SOFTPLUS, ROUTE_AUTO,
+from ._lib import (ANCHOR_DATA, ANCHOR_FIXED, ANCHOR_SPLIT16, GATE_LOG, GATE_LOWER_BOUND, GATE_SOFTPLUS, ROUTE_AUTO,
                    ROUTE_CHUNK, ROUTE_SERIAL, ROUTE_SPLIT, FrontEnd, KdaError, Plan, checkpoint_slots,
                    decode, last_error, load, plan, prefill, prefill_chain, prefill_pool, prefill_prepare,
                    records_size, set_prefill_route, workspace_size)
@@ -14,5 +14,5 @@ __all__ = ["prefill", "prefill_pool", "checkpoint_slots", "prefill_prepare", "pr
            "records_size", "decode", "plan",
            "set_prefill_route", "workspace_size", "last_error",
            "load", "KdaError", "Plan", "ROUTE_AUTO", "ROUTE_SERIAL", "ROUTE_CHUNK", "ROUTE_SPLIT",
-           "ANCHOR_FIXED", "ANCHOR_SPLIT16", "FrontEnd", "GATE_LOG", "GATE_LOWER_BOUND",
+           "ANCHOR_FIXED", "ANCHOR_SPLIT16", "ANCHOR_DATA", "FrontEnd", "GATE_LOG", "GATE_LOWER_BOUND",
            "GATE_SOFTPLUS"]

@@ -28,6 +28,7 @@ ROUTE_SPLIT = 2
 
 ANCHOR_FIXED = 0
 ANCHOR_SPLIT16 = 1
+ANCHOR_DATA = 2
 
 STATE_F32 = 0
 STATE_BF16 = 1
@@ -106,6 +107,9 @@ def load():
     lib.kda_prefill.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32, vp, vp,
                                 vp, vp, sz, vp]
     lib.kda_prefill.restype = ctypes.c_int
+    lib.kda_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
+                                   ctypes.POINTER(_FrontEnd), vp, vp, vp, vp, sz, vp]
+    lib.kda_prefill_ex.restype = ctypes.c_int
     lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32]
     lib.kda_prefill_workspace_size.restype = sz
     lib.kda_prefill_plan.argtypes = [i32, i64, i32, f32, i32, i32, ctypes.POINTER(_Plan)]
@@ -122,6 +126,10 @@ def load():
     lib.kda_prefill_pool.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32, vp,
                                      i64, vp, vp, i32, vp, vp, sz, vp]
     lib.kda_prefill_pool.restype = ctypes.c_int
+    lib.kda_prefill_pool_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
+                                        ctypes.POINTER(_FrontEnd), vp, i64, vp, vp, i32, vp, vp,
+                                        sz, vp]
+    lib.kda_prefill_pool_ex.restype = ctypes.c_int
     lib.kda_prefill_checkpoint_slots.argtypes = [i32, i64, i32]
     lib.kda_prefill_checkpoint_slots.restype = sz
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
@@ -187,8 +195,12 @@ def set_prefill_route(route: int) -> None:
 
 
 def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=None,
-            final_state=None, out=None, workspace=None, stream=None):
+            final_state=None, out=None, workspace=None, stream=None, frontend=None):
     """Packed varlen KDA prefill on the GPU.
+
+    ``lower_bound``: the gate bound (< 0), or ``float("-inf")`` for an
+    unbounded gate.  ``frontend``: a :class:`FrontEnd` (kda_prefill_ex) or
+    None (kda_prefill).
 
     ``workspace``: a device uint8 tensor of at least ``workspace_size(N, T, H)``
     bytes (allocated here when None and the chosen route needs one).
@@ -221,10 +233,17 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
         if need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
-                              N, T, H, D, D, float(scale), float(lower_bound), _ptr(initial_state),
-                              _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
-                              _stream(stream)))
+    if frontend is None:
+        _check(load().kda_prefill(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                  N, T, H, D, D, float(scale), float(lower_bound),
+                                  _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
+                                  ws_bytes, _stream(stream)))
+    else:
+        _check(load().kda_prefill_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                     _ptr(cu_seqlens), N, T, H, D, D, float(scale),
+                                     float(lower_bound), _fe_ptr(frontend), _ptr(initial_state),
+                                     _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
+                                     _stream(stream)))
     return out, final_state
 
 
@@ -234,7 +253,8 @@ def checkpoint_slots(num_seqs: int, total_tokens: int, checkpoint_tokens: int) -
 
 
 def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scale, lower_bound,
-                 checkpoints=None, checkpoint_tokens=64, out=None, workspace=None, stream=None):
+                 checkpoints=None, checkpoint_tokens=64, out=None, workspace=None, stream=None,
+                 frontend=None):
     """Packed varlen prefill whose states live in ``state_pool`` (fp32
     [num_slots, H, 128, 128], updated in place; None: zero start, nothing
     stored), one ``slot_indices`` entry (int32, device) per sequence.
@@ -269,12 +289,12 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
         if need > 0:
             workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    _check(load().kda_prefill_pool(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                   _ptr(cu_seqlens), N, T, H, D, D, float(scale),
-                                   float(lower_bound), _ptr(state_pool), num_slots,
-                                   _ptr(slot_indices), _ptr(checkpoints),
-                                   int(checkpoint_tokens) if checkpoints is not None else 0,
-                                   _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
+    _check(load().kda_prefill_pool_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), N, T, H, D, D, float(scale),
+                                      float(lower_bound), _fe_ptr(frontend), _ptr(state_pool),
+                                      num_slots, _ptr(slot_indices), _ptr(checkpoints),
+                                      int(checkpoint_tokens) if checkpoints is not None else 0,
+                                      _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, checkpoints
 
 

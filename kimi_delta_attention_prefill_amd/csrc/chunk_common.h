@@ -59,6 +59,7 @@ struct PrepSmem {
   float EL[D];                 // fixed anchor: 2^{G_L - C}
   float dec[D];                // 2^{G_L}: chunk decay of each key row
   float beta[CH];
+  float rq[CH], rk[CH];        // q/k L2-norm scales per token (1 without the front-end norm)
   float part[4][6][64][4];     // split-K partials of the six Mqk/Akk tiles
   float A[CH][CH + 1];         // Diag(b) stril(Akk), FP32
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
@@ -92,18 +93,49 @@ __device__ __forceinline__ void load_chunk(PrepSmem<DVS>& sm, const PrefillArgs&
       wv = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + c8);
     *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = wv;
   }
-  if (tid < CH) sm.beta[tid] = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
+  if (tid < CH)
+    sm.beta[tid] = tid < L ? frontend_beta(a.fe, bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h])) : 0.f;
+}
+
+// Step 1b (input front-end): 1 / sqrt(sum_c x_c^2 + norm_eps) of q and k per
+// token of the staged chunk; eight threads per token, 16 channels each.
+// Needs 256 threads; runs in the same phase as gate_prefix.
+template <int DVS>
+__device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const PrefillArgs& a, int tid) {
+  const int t = tid >> 3, part = tid & 7;
+  float sq2 = 0.f, sk2 = 0.f;
+  if (a.fe.normalize_qk) {
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      const float qv = bf16_to_f32(sm.qraw[t][16 * part + c]);
+      const float kv = bf16_to_f32(sm.kraw[t][16 * part + c]);
+      sq2 = fmaf(qv, qv, sq2);
+      sk2 = fmaf(kv, kv, sk2);
+    }
+#pragma unroll
+    for (int off = 1; off < 8; off <<= 1) {
+      sq2 += __shfl_xor(sq2, off);
+      sk2 += __shfl_xor(sk2, off);
+    }
+  }
+  if (part == 0) {
+    sm.rq[t] = a.fe.normalize_qk ? inv_norm(sq2 + a.fe.norm_eps) : 1.f;
+    sm.rk[t] = a.fe.normalize_qk ? inv_norm(sk2 + a.fe.norm_eps) : 1.f;
+  }
 }
 
 // Step 2: inclusive gate prefix per channel (threads 0..127), chunk decay,
 // and for the fixed anchor 2^{G_L - C}.
+// Padding tokens (t >= L) add nothing: a transformed gate of their zero input
+// would not be zero.
 template <int MODE, int DVS>
-__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, float C, int tid) {
+__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const FrontEnd& fe, float C, int L,
+                                            int tid) {
   if (tid < D) {
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-      acc += bf16_to_f32(sm.graw[t][tid]);
+      if (t < L) acc += frontend_gate(fe, bf16_to_f32(sm.graw[t][tid]));
       sm.G[t][tid] = acc * kLog2e;
     }
     const float GL = acc * kLog2e;
@@ -140,12 +172,16 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
     const f32x4 G1 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl + 4]);
     const uint4 qw = *reinterpret_cast<const uint4*>(&sm.qraw[t][cb + cl]);
     const uint4 kw = *reinterpret_cast<const uint4*>(&sm.kraw[t][cb + cl]);
-    f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1;
-    if (MODE == 1) {
+    f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1;
+    const float rq = sm.rq[t], rk = sm.rk[t];
+    if (MODE >= 1) {
       Gs0 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl]);
       Gs1 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl + 4]);
       GL0 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl]);
       GL1 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl + 4]);
+      // MODE 2: G at the half's first token (0 or 16) for the midpoint anchor
+      Gf0 = *reinterpret_cast<const f32x4*>(&sm.G[16 * half][cb + cl]);
+      Gf1 = *reinterpret_cast<const f32x4*>(&sm.G[16 * half][cb + cl + 4]);
     } else {
       EL0 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl]);
       EL1 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl + 4]);
@@ -156,8 +192,8 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float Gv = j < 4 ? G0[j] : G1[j - 4];
-      const float qf = (j & 1) ? bf16hi(qu[j >> 1]) : bf16lo(qu[j >> 1]);
-      const float kf = (j & 1) ? bf16hi(ku[j >> 1]) : bf16lo(ku[j >> 1]);
+      const float qf = rq * ((j & 1) ? bf16hi(qu[j >> 1]) : bf16lo(qu[j >> 1]));
+      const float kf = rk * ((j & 1) ? bf16hi(ku[j >> 1]) : bf16lo(ku[j >> 1]));
       float ep, em, P, R, fo = 0.f;
       if (MODE == 0) {
         ep = fast_exp2(Gv - C);                       // 2^{G-C}, |exponent| <= 16|b|
@@ -167,9 +203,18 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
       } else {
         const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
         const float gl = j < 4 ? GL0[j] : GL1[j - 4];
-        const float Ch = (half ? g15 : 0.f) + a.half_anchor_log2;
-        ep = fast_exp2(Gv - Ch);
-        em = fast_exp2(Ch - Gv);
+        if (MODE == 1) {
+          const float Ch = (half ? g15 : 0.f) + a.half_anchor_log2;
+          ep = fast_exp2(Gv - Ch);
+          em = fast_exp2(Ch - Gv);
+        } else {
+          // midpoint of this half's actual range; exponents clamped so that a
+          // half that decays a channel past 2^-252 stays finite
+          const float gf = j < 4 ? Gf0[j] : Gf1[j - 4];
+          const float Ch = 0.5f * (gf + (half ? gl : g15));
+          ep = fast_exp2(__builtin_fminf(Gv - Ch, 126.f));
+          em = fast_exp2(__builtin_fminf(Ch - Gv, 126.f));
+        }
         fo = half ? fast_exp2(Gv - g15) : fast_exp2(g15 - Gv);  // both <= 1
         P = fast_exp2(Gv);
         R = fast_exp2(gl - Gv);

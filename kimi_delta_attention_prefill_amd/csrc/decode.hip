@@ -134,8 +134,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   float rq = 1.f, rk = 1.f;
   if (a.fe.normalize_qk) {
-    rq = 1.f / __builtin_sqrtf(nrm[0][0] + nrm[1][0] + a.fe.norm_eps);
-    rk = 1.f / __builtin_sqrtf(nrm[0][1] + nrm[1][1] + a.fe.norm_eps);
+    rq = inv_norm(nrm[0][0] + nrm[1][0] + a.fe.norm_eps);
+    rk = inv_norm(nrm[0][1] + nrm[1][1] + a.fe.norm_eps);
   }
 
   float w[4] = {0.f, 0.f, 0.f, 0.f}, p[4] = {0.f, 0.f, 0.f, 0.f}, qk = 0.f;

@@ -90,11 +90,25 @@ int check_sizes(const char* fn, int32_t num_seqs, int64_t total_tokens, int32_t 
   return KDA_OK;
 }
 
+// lower_bound: finite and < 0, or -infinity for an unbounded gate.
+bool bound_ok(float lower_bound) {
+  return lower_bound < 0.f && (std::isfinite(lower_bound) || std::isinf(lower_bound));
+}
+
 int check_bound(const char* fn, float lower_bound) {
-  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
-    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: lower_bound must be finite and < 0 (got %g)", fn,
-                (double)lower_bound);
+  if (!bound_ok(lower_bound))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: lower_bound must be < 0, finite or -inf (got %g)",
+                fn, (double)lower_bound);
   return KDA_OK;
+}
+
+// The bound the chunk routes may rely on for the front-end's gate mode: the
+// caller's bound for a log-decay gate, the sigmoid's scale for the
+// lower-bound gate, none (-inf) for the softplus gate.
+float effective_bound(const kda::FrontEnd& fe, float lower_bound) {
+  if (fe.gate_mode == KDA_GATE_LOWER_BOUND) return fe.lower_bound;
+  if (fe.gate_mode == KDA_GATE_SOFTPLUS) return -INFINITY;
+  return lower_bound;
 }
 
 int check_inputs(const char* fn, const void* q, const void* k, const void* v, const void* g,
@@ -156,8 +170,10 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.total_tokens = (int32_t)total_tokens;
   a.num_heads = num_heads;
   a.scale = scale;
-  a.anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
-  a.half_anchor_log2 = (float)(8.0 * (double)lower_bound * 1.4426950408889634);
+  // an unbounded gate (-inf) uses data-dependent anchors; the constants are unused
+  const double lb = std::isfinite(lower_bound) ? (double)lower_bound : 0.0;
+  a.anchor_log2 = (float)(16.0 * lb * 1.4426950408889634);
+  a.half_anchor_log2 = (float)(8.0 * lb * 1.4426950408889634);
   a.s0 = initial_state;
   a.s1 = final_state;
   a.out = static_cast<uint16_t*>(out);
@@ -207,9 +223,9 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
   if (num_seqs < 0 || total_tokens < 0 || num_heads < 1)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: bad sizes (N=%d, T=%lld, H=%d)",
                 num_seqs, (long long)total_tokens, num_heads);
-  if (!std::isfinite(lower_bound) || !(lower_bound < 0.f))
+  if (!bound_ok(lower_bound))
     return fail(KDA_ERR_INVALID_ARGUMENT,
-                "kda_prefill_plan: lower_bound must be finite and < 0 (got %g)",
+                "kda_prefill_plan: lower_bound must be < 0, finite or -inf (got %g)",
                 (double)lower_bound);
   if (num_cus <= 0) num_cus = current_device_cus();
   if (num_cus <= 0) num_cus = 256;
@@ -225,8 +241,11 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
   std::memset(plan, 0, sizeof(*plan));
   plan->route = route;
   plan->windows = 1;
-  plan->anchor_mode = fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED : KDA_ANCHOR_SPLIT16;
-  plan->anchor_log2 = (float)(16.0 * (double)lower_bound * 1.4426950408889634);
+  plan->anchor_mode = !std::isfinite(lower_bound)       ? KDA_ANCHOR_DATA
+                      : fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED
+                                                       : KDA_ANCHOR_SPLIT16;
+  plan->anchor_log2 = std::isfinite(lower_bound)
+                          ? (float)(16.0 * (double)lower_bound * 1.4426950408889634) : 0.f;
   if (route == KDA_ROUTE_SERIAL) {
     // 16 value columns per wave; fewer waves per block (more blocks) when
     // there are few (sequence, head) units to spread over the compute units.
@@ -265,6 +284,7 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     // halve the per-block chain work at the cost of duplicated chunk
     // preparation; worth it only while every block still gets its own CU.
     plan->dv_split = 2 * units <= (int64_t)num_cus ? 2 : 1;
+    if (plan->anchor_mode == KDA_ANCHOR_DATA) plan->dv_split = 2;   // 64-column blocks only
     plan->block_threads = 256;
     plan->grid_blocks = units * plan->dv_split;
   }
@@ -307,39 +327,59 @@ int run_prefill(const char* fn, kda::PrefillArgs a, float lower_bound, void* wor
 
 extern "C" {
 
-int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
-                const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
-                int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
-                float lower_bound, const float* initial_state, float* final_state, void* out,
-                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int kda_prefill_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                   const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                   int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
+                   float lower_bound, const kda_frontend* frontend,
+                   const float* initial_state, float* final_state, void* out,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "kda_prefill";
-  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v);
+  kda::FrontEnd fe;
+  int rc = frontend_args(frontend, fn, &fe);
   if (rc != KDA_OK) return rc;
+  if ((rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v)) != KDA_OK)
+    return rc;
   if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
-  if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  if (fe.gate_mode == KDA_GATE_LOG && (rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  lower_bound = effective_bound(fe, lower_bound);
   if (num_seqs == 0) return ok();
   if ((rc = check_inputs(fn, q, k, v, g, beta, cu_seqlens, total_tokens)) != KDA_OK) return rc;
   if ((rc = check_outputs(fn, initial_state, final_state, out, num_seqs, num_heads,
                           total_tokens)) != KDA_OK)
     return rc;
-  return run_prefill(fn,
-                     make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
-                               scale, lower_bound, initial_state, final_state, out),
-                     lower_bound, workspace, workspace_bytes, stream);
+  kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                                 scale, lower_bound, initial_state, final_state, out);
+  a.fe = fe;
+  return run_prefill(fn, a, lower_bound, workspace, workspace_bytes, stream);
 }
 
-int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
-                     const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
-                     int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
-                     int32_t head_dim_v, float scale, float lower_bound, float* state_pool,
-                     int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
-                     int32_t checkpoint_tokens, void* out, void* workspace,
-                     size_t workspace_bytes, hipStream_t stream) {
+int kda_prefill(const void* q, const void* k, const void* v, const void* g, const void* beta,
+                const int32_t* cu_seqlens, int32_t num_seqs, int64_t total_tokens,
+                int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
+                float lower_bound, const float* initial_state, float* final_state, void* out,
+                void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return kda_prefill_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                        head_dim_k, head_dim_v, scale, lower_bound, nullptr, initial_state,
+                        final_state, out, workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                        int32_t head_dim_v, float scale, float lower_bound,
+                        const kda_frontend* frontend, float* state_pool, int64_t num_slots,
+                        const int32_t* slot_indices, float* checkpoints,
+                        int32_t checkpoint_tokens, void* out, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "kda_prefill_pool";
-  int rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v);
+  kda::FrontEnd fe;
+  int rc = frontend_args(frontend, fn, &fe);
   if (rc != KDA_OK) return rc;
+  if ((rc = check_sizes(fn, num_seqs, total_tokens, num_heads, head_dim_k, head_dim_v)) != KDA_OK)
+    return rc;
   if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
-  if ((rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  if (fe.gate_mode == KDA_GATE_LOG && (rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
+  lower_bound = effective_bound(fe, lower_bound);
   if (state_pool) {
     if (num_slots < 1)
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_slots=%lld", fn, (long long)num_slots);
@@ -367,7 +407,21 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
   a.num_slots = num_slots;
   a.ckpt = checkpoints;
   a.ckpt_tokens = checkpoints ? checkpoint_tokens : 0;
+  a.fe = fe;
   return run_prefill(fn, a, lower_bound, workspace, workspace_bytes, stream);
+}
+
+int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
+                     const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                     int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                     int32_t head_dim_v, float scale, float lower_bound, float* state_pool,
+                     int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
+                     int32_t checkpoint_tokens, void* out, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream) {
+  return kda_prefill_pool_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
+                             head_dim_k, head_dim_v, scale, lower_bound, nullptr, state_pool,
+                             num_slots, slot_indices, checkpoints, checkpoint_tokens, out,
+                             workspace, workspace_bytes, stream);
 }
 
 size_t kda_prefill_checkpoint_slots(int32_t num_seqs, int64_t total_tokens,

@@ -25,6 +25,23 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float x) {
 // 2^x on the hardware exponential unit (v_exp_f32).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Input front-end (FrontEnd): the natural-log decay g from the gate tensor's
+// value x, and beta from the beta tensor's value.
+__device__ __forceinline__ float frontend_gate(const FrontEnd& fe, float x) {
+  if (fe.gate_mode == 1) return fe.lower_bound / (1.f + fast_exp2(-x * kLog2e));   // lb sigmoid(x)
+  if (fe.gate_mode == 2) {   // -softplus(x) = -(max(x, 0) + ln(1 + e^-|x|))
+    const float e = fast_exp2(-__builtin_fabsf(x) * kLog2e);
+    return -(__builtin_fmaxf(x, 0.f) + __builtin_amdgcn_logf(1.f + e) * 0.6931471805599453f);
+  }
+  return x;
+}
+// 1 / sqrt(x) for a front-end L2 norm (x = sum of squares + eps); a zero
+// vector (x == 0, e.g. a padding token) is left at zero instead of 0 * inf.
+__device__ __forceinline__ float inv_norm(float x) { return x > 0.f ? 1.f / __builtin_sqrtf(x) : 0.f; }
+__device__ __forceinline__ float frontend_beta(const FrontEnd& fe, float b) {
+  return fe.beta_logits ? 1.f / (1.f + fast_exp2(-b * kLog2e)) : b;
+}
+
 // Raw buffer resource over [base, base + bytes): buffer loads outside return
 // 0 and buffer stores outside are dropped by the hardware (gfx9 word 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_buffer(const void* base, uint32_t bytes) {

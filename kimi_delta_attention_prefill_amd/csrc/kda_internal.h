@@ -15,6 +15,18 @@ constexpr int kSplitSubtiles = 1;
 constexpr int kSplitChainTiles = 8 / kSplitSubtiles;
 constexpr int kSplitBlocksPerCU = 2;
 
+// Input front-end: gate_mode 0 = g is the natural-log decay, 1 = g holds a
+// and the decay is lower_bound * sigmoid(a), 2 = g holds a and the decay is
+// -softplus(a); beta_logits: beta = sigmoid(beta); normalize_qk: q, k scaled
+// by 1 / sqrt(sum x^2 + norm_eps) per (token, head).
+struct FrontEnd {
+  int32_t gate_mode = 0;
+  float lower_bound = 0.f;
+  int32_t beta_logits = 0;
+  int32_t normalize_qk = 0;
+  float norm_eps = 0.f;
+};
+
 struct PrefillArgs {
   const uint16_t* q;      // bf16 [T, H, 128]
   const uint16_t* k;      // bf16 [T, H, 128]
@@ -44,18 +56,7 @@ struct PrefillArgs {
   // n + floor(cu[n] / ckpt_tokens) + j - 1 of ckpt [., H, 128, 128].
   float* ckpt;            // fp32 or null
   int32_t ckpt_tokens;
-};
-
-// Input front-end: gate_mode 0 = g is the natural-log decay, 1 = g holds a
-// and the decay is lower_bound * sigmoid(a), 2 = g holds a and the decay is
-// -softplus(a); beta_logits: beta = sigmoid(beta); normalize_qk: q, k scaled
-// by 1 / sqrt(sum x^2 + norm_eps) per (token, head).
-struct FrontEnd {
-  int32_t gate_mode = 0;
-  float lower_bound = 0.f;
-  int32_t beta_logits = 0;
-  int32_t normalize_qk = 0;
-  float norm_eps = 0.f;
+  FrontEnd fe;            // how g and beta are given, q/k normalisation
 };
 
 struct DecodeArgs {

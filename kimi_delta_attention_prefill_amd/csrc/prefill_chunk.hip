@@ -108,7 +108,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
     __syncthreads();  // the previous chunk's chain is done with the LDS operands
     load_chunk(ps, a, t0, L, h, col_base, tid, 256);
     __syncthreads();
-    gate_prefix<MODE>(ps, C, tid);
+    gate_prefix<MODE>(ps, a.fe, C, L, tid);
+    qk_norms(ps, a, tid);
     __syncthreads();
     pair_products<MODE>(ps, a, C, exp2C, wave, lane,
                         [&](int t, int c0, const float* kv, const float* qv, const float* P,
@@ -274,6 +275,9 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
   const int nt = dv_split == 1 ? 2 : 1;
   if (anchor_mode == 0)
     return nt == 2 ? launch_variant<0, 2>(a, s) : launch_variant<0, 1>(a, s);
+  // data-dependent anchors: 64-column blocks only (the 128-column variant
+  // would exceed the register file)
+  if (anchor_mode == 2) return dv_split == 2 ? launch_variant<2, 1>(a, s) : hipErrorInvalidValue;
   return nt == 2 ? launch_variant<1, 2>(a, s) : launch_variant<1, 1>(a, s);
 }
 

@@ -71,8 +71,8 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
         sq[t][c8 + 2 * m + 1] = bf16hi(uq[m]);
         sk[t][c8 + 2 * m] = bf16lo(uk[m]);
         sk[t][c8 + 2 * m + 1] = bf16hi(uk[m]);
-        sd[t][c8 + 2 * m] = fast_exp2(bf16lo(ug[m]) * kLog2e);
-        sd[t][c8 + 2 * m + 1] = fast_exp2(bf16hi(ug[m]) * kLog2e);
+        sd[t][c8 + 2 * m] = fast_exp2(frontend_gate(a.fe, bf16lo(ug[m])) * kLog2e);
+        sd[t][c8 + 2 * m + 1] = fast_exp2(frontend_gate(a.fe, bf16hi(ug[m])) * kLog2e);
       }
     }
     for (int e = tid; e < kStage * 16 * W; e += 64 * W) {
@@ -82,11 +82,11 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
                         : 0.f;
     }
     if (tid < kStage)
-      sb[tid] = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
+      sb[tid] = tid < L ? frontend_beta(a.fe, bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h])) : 0.f;
     __syncthreads();
 
     for (int t = 0; t < L; ++t) {
-      float w = 0.f, p = 0.f, qk = 0.f;
+      float w = 0.f, p = 0.f, qk = 0.f, qq = 0.f, kk = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
         const int c = 4 * i + rg;
@@ -101,9 +101,30 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
       p += __shfl_xor(p, 32);
       qk += __shfl_xor(qk, 16);
       qk += __shfl_xor(qk, 32);
-      const float u = sb[t] * (sv[t][wave * 16 + jl] - w);
+      // q/k L2 norm: w, p, q.k are linear in k and q, so they are scaled
+      // afterwards; the update adds k (u / |k|)^T.
+      float rk = 1.f;
+      if (a.fe.normalize_qk) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) S[i] = fmaf(sk[t][4 * i + rg], u, S[i]);
+        for (int i = 0; i < 32; ++i) {
+          const int c = 4 * i + rg;
+          qq = fmaf(sq[t][c], sq[t][c], qq);
+          kk = fmaf(sk[t][c], sk[t][c], kk);
+        }
+        qq += __shfl_xor(qq, 16);
+        qq += __shfl_xor(qq, 32);
+        kk += __shfl_xor(kk, 16);
+        kk += __shfl_xor(kk, 32);
+        const float rq = inv_norm(qq + a.fe.norm_eps);
+        rk = inv_norm(kk + a.fe.norm_eps);
+        w *= rk;
+        p *= rq;
+        qk *= rq * rk;
+      }
+      const float u = sb[t] * (sv[t][wave * 16 + jl] - w);
+      const float uk = u * rk;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) S[i] = fmaf(sk[t][4 * i + rg], uk, S[i]);
       if (rg == 0)
         a.out[((int64_t)(t0 + t) * H + h) * kHeadDim + col] = f32_to_bf16(a.scale * fmaf(qk, u, p));
       if (float* cp = prefill_checkpoint(a, n, h, bos, t0 + t + 1 - bos)) {

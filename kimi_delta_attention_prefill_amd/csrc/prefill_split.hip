@@ -176,15 +176,44 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
   const __amdgpu_buffer_rsrc_t rgp = make_buffer(a.g + base_prev, prev_bytes);
   const uint32_t tok_bytes = (uint32_t)H * D * 2;
+  // Tokens past the sequence end (a final partial chunk) read as zero; their
+  // transformed gate and beta are forced to zero as well.
+  const bool live[2] = {l16 < L, l16 + 16 < L};
   const float beta[2] = {
-      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0)),
-      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((l16 + 16) * H * 2), 0, 0))};
+      live[0] ? frontend_beta(a.fe, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0))) : 0.f,
+      live[1] ? frontend_beta(a.fe, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((l16 + 16) * H * 2), 0, 0))) : 0.f};
   auto load8 = [&](__amdgpu_buffer_rsrc_t r, int hf, int p) __attribute__((always_inline)) {
     const uint32_t off = (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 4 * g4) * 2;
     const u32x2 x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
     const u32x2 x1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off + 32, 0, 0));
     return u32x4{x0[0], x0[1], x1[0], x1[1]};
   };
+  // Input front-end q/k L2 norm: 1 / sqrt(sum x^2 + eps) of this lane's two
+  // tokens (a pass over the chunk's q and k before the main loop; the four
+  // lanes g4 of a token hold its 128 channels).
+  float nq[2] = {1.f, 1.f}, nk[2] = {1.f, 1.f};
+  if (a.fe.normalize_qk) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float s2q = 0.f, s2k = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        const u32x4 qw = load8(rq, hf, p), kw = load8(rk, hf, p);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float qv = bf16_elem(qw, j), kv = bf16_elem(kw, j);
+          s2q = fmaf(qv, qv, s2q);
+          s2k = fmaf(kv, kv, s2k);
+        }
+      }
+      s2q += __shfl_xor(s2q, 16);
+      s2q += __shfl_xor(s2q, 32);
+      s2k += __shfl_xor(s2k, 16);
+      s2k += __shfl_xor(s2k, 32);
+      nq[hf] = inv_norm(s2q + a.fe.norm_eps);
+      nk[hf] = inv_norm(s2k + a.fe.norm_eps);
+    }
+  }
 
   // One-hot transposers.  E[e] selects, for output column l16, the K-slot of
   // channel 16e + l16 of a 32-channel step in K-slot order; Ev[e] the same
@@ -217,16 +246,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
       gw[hf] = load8(rg, hf, p);
     }
     // gate prefix (log2 domain) of both halves, and G at tokens 15 and 31
-    float G[2][8], G15[8], GL[8];
+    float G[2][8], G15[8], GL[8], Gf[2][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s0 = row_scan16(bf16_elem(gw[0], j));
+      const float s0 = row_scan16(live[0] ? frontend_gate(a.fe, bf16_elem(gw[0], j)) : 0.f);
       const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(bf16_elem(gw[1], j)) + b0;
+      const float s1 = row_scan16(live[1] ? frontend_gate(a.fe, bf16_elem(gw[1], j)) : 0.f) + b0;
       G[0][j] = s0 * kLog2e;
       G[1][j] = s1 * kLog2e;
       G15[j] = b0 * kLog2e;
       GL[j] = __shfl(s1, 15, 16) * kLog2e;
+      if (MODE == 2) {   // G at the first token of each half
+        Gf[0][j] = __shfl(s0, 0, 16) * kLog2e;
+        Gf[1][j] = __shfl(s1, 0, 16) * kLog2e;
+      }
     }
     if (l16 == 0) {
       f32x4 d0, d1;
@@ -251,7 +284,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     for (int hf = 0; hf < 2; ++hf)
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float qf = bf16_elem(qw[hf], j), kf = bf16_elem(kw[hf], j);
+        const float qf = nq[hf] * bf16_elem(qw[hf], j), kf = nk[hf] * bf16_elem(kw[hf], j);
         const float Gv = G[hf][j];
         float ep, em, P, R, fo = 0.f;
         if (MODE == 0) {
@@ -260,9 +293,17 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
           P = ep * exp2C;                         // 2^G
           R = EL[j] * em;                         // 2^{G_L - G}
         } else {
-          const float Ch = (hf ? G15[j] : 0.f) + a.half_anchor_log2;
-          ep = fast_exp2(Gv - Ch);
-          em = fast_exp2(Ch - Gv);
+          if (MODE == 1) {
+            const float Ch = (hf ? G15[j] : 0.f) + a.half_anchor_log2;
+            ep = fast_exp2(Gv - Ch);
+            em = fast_exp2(Ch - Gv);
+          } else {
+            // midpoint of this half's actual range; exponents clamped so that
+            // a half that decays a channel past 2^-252 stays finite
+            const float Ch = 0.5f * (Gf[hf][j] + (hf ? GL[j] : G15[j]));
+            ep = fast_exp2(__builtin_fminf(Gv - Ch, 126.f));
+            em = fast_exp2(__builtin_fminf(Ch - Gv, 126.f));
+          }
           fo = hf ? fast_exp2(Gv - G15[j]) : fast_exp2(G15[j] - Gv);   // both <= 1
           P = fast_exp2(Gv);
           R = fast_exp2(GL[j] - Gv);
@@ -274,7 +315,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
         qah[hf][j] = h1; qal[hf][j] = l1;
         kah[hf][j] = h2; kal[hf][j] = l2;
         kbh[hf][j] = h3; kbl[hf][j] = l3;
-        if (MODE == 1) {
+        if (MODE >= 1) {
           if (hf == 1) {
             split_bf16(qf * fo, h1, l1);
             split_bf16(kf * fo, h2, l2);
@@ -482,19 +523,37 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // W^T = Kr_p M^T (M as fp16 hi + lo), whose accumulators (rows = previous
   // tokens s, column = token t) are the W A fragments.
   f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
+  float nkp[2] = {1.f, 1.f};               // front-end norm of the previous chunk's keys
+  if (a.fe.normalize_qk) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      float s2 = 0.f;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float kv = bf16_elem(kpw[p][hf], j);
+          s2 = fmaf(kv, kv, s2);
+        }
+      s2 += __shfl_xor(s2, 16);
+      s2 += __shfl_xor(s2, 32);
+      nkp[hf] = inv_norm(s2 + a.fe.norm_eps);
+    }
+  }
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     float dp[8];
     f16x8 krp[2];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s0 = row_scan16(bf16_elem(gpw[p][0], j));
+      // no previous chunk (an empty range): zero gates, so d_p = 1 and M' = M
+      const float s0 = row_scan16(has_prev ? frontend_gate(a.fe, bf16_elem(gpw[p][0], j)) : 0.f);
       const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(bf16_elem(gpw[p][1], j)) + b0;
+      const float s1 = row_scan16(has_prev ? frontend_gate(a.fe, bf16_elem(gpw[p][1], j)) : 0.f) + b0;
       const float gl = __shfl(s1, 15, 16) * kLog2e;
       dp[j] = fast_exp2(gl);
-      krp[0][j] = static_cast<_Float16>(bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
-      krp[1][j] = static_cast<_Float16>(bf16_elem(kpw[p][1], j) * fast_exp2(gl - s1 * kLog2e));
+      krp[0][j] = static_cast<_Float16>(nkp[0] * bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
+      krp[1][j] = static_cast<_Float16>(nkp[1] * bf16_elem(kpw[p][1], j) * fast_exp2(gl - s1 * kLog2e));
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -1238,6 +1297,7 @@ hipError_t launch_prefill_split_prepare(const PrefillArgs& a, int anchor_mode, v
                                         hipStream_t s) {
   if (a.num_seqs <= 0) return hipSuccess;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
+  if (anchor_mode == 2) return launch_prep<2>(a, ws, s);
   return anchor_mode == 0 ? launch_prep<0>(a, ws, s) : launch_prep<1>(a, ws, s);
 }
 

@@ -112,6 +112,32 @@ def make_prefill_case(lengths, num_heads, lower_bound, init_std=None, seed=BASE_
                        {"lengths": lengths})
 
 
+def make_prefill_raw_case(lengths, num_heads, init_std=0.02, seed=BASE_SEED + 6, qk_std=3.0,
+                          gate_mean=0.0, gate_std=1.0, name="raw") -> PrefillCase:
+    """Prefill inputs as a model hands them over before the input front-end:
+    q, k ~ qk_std N(0, 1) (not normalised), v ~ N(0, 1), the gate tensor holds
+    raw a ~ gate_mean + gate_std N(0, 1), beta holds logits ~ N(0, 1); all
+    bf16.  ``lower_bound`` is -inf (the case carries no bound)."""
+    gen = torch.Generator().manual_seed(int(seed))
+    lengths = [int(x) for x in lengths]
+    T = sum(lengths)
+    H = int(num_heads)
+    q = (float(qk_std) * torch.randn(T, H, HEAD_DIM, generator=gen)).to(torch.bfloat16)
+    k = (float(qk_std) * torch.randn(T, H, HEAD_DIM, generator=gen)).to(torch.bfloat16)
+    v = torch.randn(T, H, HEAD_DIM, generator=gen).to(torch.bfloat16)
+    a = (float(gate_mean) + float(gate_std) * torch.randn(T, H, HEAD_DIM, generator=gen)
+         ).to(torch.bfloat16)
+    b = torch.randn(T, H, generator=gen).to(torch.bfloat16)
+    s0 = None
+    if init_std is not None:
+        s0 = float(init_std) * torch.randn(len(lengths), H, HEAD_DIM, HEAD_DIM, generator=gen)
+    cu = torch.zeros(len(lengths) + 1, dtype=torch.int32)
+    if lengths:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    return PrefillCase(q, k, v, a, b, cu, s0, float("-inf"), SCALE, int(seed), name,
+                       {"lengths": lengths})
+
+
 # The five workloads: prefill configurations 0-3 and the decode sweep 4.
 PREFILL_CONFIGS = {
     0: dict(name="prefill_T64_H2", num_heads=2, lower_bound=-5.0, init_std=None),

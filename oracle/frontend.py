@@ -13,7 +13,7 @@ formulas for them):
 * softplus gate:    g = -softplus(a) = -log(1 + exp(a)) (unbounded below),
 * beta from logits: beta = sigmoid(b),
 * q, k L2 norm:     x / sqrt(sum_c x_c^2 + norm_eps) over the 128 channels of
-  one (token, head).
+  one (token, head); a zero vector with norm_eps = 0 stays zero.
 
 Each function is the plain definition in double precision, written in a form
 that neither overflows nor cancels (so that tests can use extreme inputs).
@@ -52,9 +52,11 @@ def gate(a, mode: int, lower_bound: float = 0.0) -> np.ndarray:
 
 
 def l2_normalize(x, eps: float) -> np.ndarray:
-    """x / sqrt(sum x^2 + eps) along the last axis (the 128 channels)."""
+    """x / sqrt(sum x^2 + eps) along the last axis (the 128 channels); a zero
+    vector with eps = 0 stays zero (reading: no 0/0)."""
     x = np.asarray(x, dtype=np.float64)
-    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + float(eps))
+    d = np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + float(eps))
+    return np.divide(x, d, out=np.zeros_like(x), where=d > 0)
 
 
 def apply(q, k, g_in, beta_in, *, gate_mode=GATE_LOG, lower_bound=0.0, beta_logits=False,

@@ -56,13 +56,24 @@ def test_plan_grid_covers_every_unit(route):
 
 def test_plan_rejects_bad_inputs():
     for args in ((-1, 0, 1, -5.0), (1, -1, 1, -5.0), (1, 0, 0, -5.0), (1, 0, 1, 0.0),
-                 (1, 0, 1, float("nan")), (1, 0, 1, float("-inf")), (1, 0, 1, 1.0)):
+                 (1, 0, 1, float("nan")), (1, 0, 1, float("inf")), (1, 0, 1, 1.0)):
         with pytest.raises(kda.KdaError) as e:
             kda.plan(*args, num_cus=256)
         assert e.value.code == _lib.KDA_ERR_INVALID_ARGUMENT
         assert kda.last_error()
     with pytest.raises(kda.KdaError):
         kda.plan(1, 0, 1, -5.0, 256, route=7)
+
+
+def test_plan_unbounded_gate_uses_data_anchors():
+    # lower_bound = -inf: no bound, each 16-token half anchored at its own range
+    for route in (kda.ROUTE_CHUNK, kda.ROUTE_SPLIT):
+        p = kda.plan(2, 3000, 4, float("-inf"), 256, route)
+        assert p.anchor_mode == kda.ANCHOR_DATA and p.anchor_log2 == 0.0
+    # the fused route runs data anchors on 64-column blocks only
+    assert kda.plan(16, 35000, 32, float("-inf"), 256, kda.ROUTE_CHUNK).dv_split == 2
+    assert kda.plan(16, 35000, 32, -5.0, 256, kda.ROUTE_CHUNK).dv_split == 1
+    assert kda.plan(1, 64, 2, -5.0, 256).anchor_mode == kda.ANCHOR_FIXED
 
 
 def test_set_route_validates():

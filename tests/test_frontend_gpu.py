@@ -93,3 +93,104 @@ def test_decode_frontend_default_equals_plain(dev):
         pools.append(P)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1]) and torch.equal(pools[0], pools[1])
+
+
+# ---------------------------------------------------------------- prefill
+from kimi_delta_attention_prefill_amd.inputs import make_prefill_raw_case  # noqa: E402
+
+ROUTES = {"serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK, "split": kda.ROUTE_SPLIT}
+PREFILL_FE = {
+    "lower_bound": (kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-5.0,
+                                 beta_logits=True, normalize_qk=True, norm_eps=1e-6), {}),
+    "lower_bound_wide": (kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-9.0,
+                                      beta_logits=True, normalize_qk=True, norm_eps=1e-6), {}),
+    "softplus": (kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True, normalize_qk=True,
+                              norm_eps=1e-6), {}),
+    # strong decays: softplus(4 + 2 N(0,1)) ~ 4 per token, ~64 over a 16-token half
+    "softplus_strong": (kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True,
+                                     normalize_qk=True, norm_eps=1e-6),
+                        dict(gate_mean=4.0, gate_std=2.0)),
+}
+
+
+def _run_prefill_case(dev, route, fe, case, pool=False):
+    to = lambda t: None if t is None else t.to(dev)
+    kda.set_prefill_route(ROUTES[route])
+    try:
+        if pool:
+            N, H = case.cu_seqlens.numel() - 1, case.q.shape[1]
+            P = torch.zeros((N + 3, H, 128, 128), dtype=torch.float32, device=dev)
+            slots = torch.arange(N, dtype=torch.int32, device=dev) + 2
+            if case.initial_state is not None:
+                P[2:2 + N] = case.initial_state.to(dev)
+            out, _ = kda.prefill_pool(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                                      to(case.cu_seqlens), slots, P, scale=case.scale,
+                                      lower_bound=-5.0, frontend=fe)
+            torch.cuda.synchronize()
+            return out.cpu(), P[2:2 + N].cpu()
+        out, fin = kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                               to(case.cu_seqlens), scale=case.scale, lower_bound=-5.0,
+                               initial_state=to(case.initial_state), final_state=True, frontend=fe)
+        torch.cuda.synchronize()
+        return out.cpu(), fin.cpu()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+
+
+def _prefill_oracle(case, fe):
+    q, k, g, b = ofe.apply(_f64(case.q), _f64(case.k), _f64(case.g), _f64(case.beta),
+                           gate_mode=fe.gate_mode, lower_bound=fe.lower_bound,
+                           beta_logits=fe.beta_logits, normalize_qk=fe.normalize_qk,
+                           norm_eps=fe.norm_eps)
+    return oracle.prefill(q, k, case.v, g, b, case.cu_seqlens, case.scale, case.initial_state)
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
+@pytest.mark.parametrize("name", list(PREFILL_FE))
+def test_prefill_frontend(dev, route, name):
+    fe, gen = PREFILL_FE[name]
+    case = make_prefill_raw_case([100, 333, 64], 2, seed=70 + len(name), **gen)
+    _say(f"[gpu] prefill_ex {route} {name}")
+    out, fin = _run_prefill_case(dev, route, fe, case)
+    ref_out, ref_fin = _prefill_oracle(case, fe)
+    _say(f"   out {check_out(out, ref_out)} state {check_state(fin, ref_fin)}")
+
+
+@pytest.mark.parametrize("name", ["softplus", "softplus_strong"])
+def test_prefill_frontend_windows_and_pool(dev, name):
+    """One long sequence on the split route (windows) and the pooled entry point."""
+    fe, gen = PREFILL_FE[name]
+    case = make_prefill_raw_case([2000], 3, seed=81, **gen)
+    assert kda.plan(1, 2000, 3, float("-inf"), 0, kda.ROUTE_SPLIT).windows >= 3
+    ref_out, ref_fin = _prefill_oracle(case, fe)
+    for pool in (False, True):
+        _say(f"[gpu] prefill_ex windows {name} pool={pool}")
+        out, fin = _run_prefill_case(dev, "split", fe, case, pool=pool)
+        _say(f"   out {check_out(out, ref_out)} state {check_state(fin, ref_fin)}")
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_prefill_unbounded_log_gate(dev, route):
+    """kda_prefill with lower_bound = -inf: the gate tensor is the log-decay
+    itself, unbounded below (data-dependent anchors on the chunk routes)."""
+    case = make_prefill_raw_case([300, 45], 2, seed=91, gate_mean=3.0, gate_std=2.0, qk_std=1.0)
+    g = -torch.nn.functional.softplus(case.g.float())     # generator-side draw: log-decay <= 0
+    case.g = g.to(torch.bfloat16)
+    q = case.q.float()
+    case.q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    k = case.k.float()
+    case.k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    case.beta = torch.sigmoid(case.beta.float()).to(torch.bfloat16)
+    to = lambda t: None if t is None else t.to(dev)
+    kda.set_prefill_route(ROUTES[route])
+    try:
+        out, fin = kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                               to(case.cu_seqlens), scale=case.scale, lower_bound=float("-inf"),
+                               initial_state=to(case.initial_state), final_state=True)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    ref_out, ref_fin = oracle.prefill(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens,
+                                      case.scale, case.initial_state)
+    _say(f"[gpu] prefill lb=-inf {route}: out {check_out(out.cpu(), ref_out)} "
+         f"state {check_state(fin.cpu(), ref_fin)}")

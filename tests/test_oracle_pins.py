@@ -374,6 +374,7 @@ def test_frontend_l2_norm_axis_and_eps():
     np.testing.assert_allclose(np.sum(fe.l2_normalize(x, 1e-2) ** 2, axis=-1), s / (s + 1e-2),
                                rtol=1e-14)
     assert np.all(fe.l2_normalize(np.zeros((2, 128)), 1e-6) == 0.0)
+    assert np.all(fe.l2_normalize(np.zeros((2, 128)), 0.0) == 0.0)   # no 0/0
     # a basis vector scaled by c normalises to the basis vector exactly
     e = np.zeros(128)
     e[17] = 3.0
