@@ -69,7 +69,7 @@ struct PrepSmem {
 
 // Step 1: stage the chunk [t0, t0 + L) of (sequence, head h): q, k, g rows,
 // the value columns [col0, col0 + DVS) and beta.  Tokens >= L are zero.
-template <int DVS>
+template <int DVS, bool FE>
 __device__ __forceinline__ void load_chunk(PrepSmem<DVS>& sm, const PrefillArgs& a, int t0, int L,
                                            int h, int col0, int tid, int nthreads) {
   const int H = a.num_heads;
@@ -93,8 +93,10 @@ __device__ __forceinline__ void load_chunk(PrepSmem<DVS>& sm, const PrefillArgs&
       wv = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + c8);
     *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = wv;
   }
-  if (tid < CH)
-    sm.beta[tid] = tid < L ? frontend_beta(a.fe, bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h])) : 0.f;
+  if (tid < CH) {
+    const float b = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
+    sm.beta[tid] = FE && tid < L ? frontend_beta(a.fe, b) : b;
+  }
 }
 
 // Step 1b (input front-end): 1 / sqrt(sum_c x_c^2 + norm_eps) of q and k per
@@ -128,14 +130,18 @@ __device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const PrefillArgs& a
 // and for the fixed anchor 2^{G_L - C}.
 // Padding tokens (t >= L) add nothing: a transformed gate of their zero input
 // would not be zero.
-template <int MODE, int DVS>
+template <int MODE, int DVS, bool FE>
 __device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const FrontEnd& fe, float C, int L,
                                             int tid) {
   if (tid < D) {
     float acc = 0.f;
 #pragma unroll
     for (int t = 0; t < CH; ++t) {
-      if (t < L) acc += frontend_gate(fe, bf16_to_f32(sm.graw[t][tid]));
+      if (FE) {
+        if (t < L) acc += frontend_gate(fe, bf16_to_f32(sm.graw[t][tid]));
+      } else {
+        acc += bf16_to_f32(sm.graw[t][tid]);
+      }
       sm.G[t][tid] = acc * kLog2e;
     }
     const float GL = acc * kLog2e;
@@ -159,7 +165,7 @@ struct PairOps {
 // P, R) receives the raw k and q values, P = 2^{G_t} and R = 2^{G_L - G_t}
 // (both <= 1) so the caller can form Kg, Qg and Kr.  The six lower tiles of
 // Mqk and Akk (as partial sums over this wave's channels) go to sm.part.
-template <int MODE, int DVS, class Emit>
+template <int MODE, int DVS, bool FE, class Emit>
 __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillArgs& a, float C,
                                               float exp2C, int wave, int lane, Emit&& emit) {
   const int l16 = lane & 15, g4 = lane >> 4;
@@ -173,7 +179,7 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
     const uint4 qw = *reinterpret_cast<const uint4*>(&sm.qraw[t][cb + cl]);
     const uint4 kw = *reinterpret_cast<const uint4*>(&sm.kraw[t][cb + cl]);
     f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1;
-    const float rq = sm.rq[t], rk = sm.rk[t];
+    const float rq = FE ? sm.rq[t] : 1.f, rk = FE ? sm.rk[t] : 1.f;
     if (MODE >= 1) {
       Gs0 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl]);
       Gs1 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl + 4]);

@@ -27,6 +27,12 @@ struct FrontEnd {
   float norm_eps = 0.f;
 };
 
+// Whether any front-end transform is requested (kernels without it are
+// compiled separately so the plain path carries none of its code).
+inline __host__ __device__ bool frontend_active(const FrontEnd& fe) {
+  return fe.gate_mode != 0 || fe.beta_logits != 0 || fe.normalize_qk != 0;
+}
+
 struct PrefillArgs {
   const uint16_t* q;      // bf16 [T, H, 128]
   const uint16_t* k;      // bf16 [T, H, 128]

@@ -64,7 +64,7 @@ struct FusedSmem {
   _Float16 Mqk[CH][TP];        // causal Mqk       [token][token, permuted]
 };
 
-template <int MODE, int NT>
+template <int MODE, int NT, bool FE>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float exp2C) {
   constexpr int DVS = 64 * NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
@@ -106,12 +106,12 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
   for (int t0 = bos; t0 < eos; t0 += CH) {
     const int L = min(CH, eos - t0);
     __syncthreads();  // the previous chunk's chain is done with the LDS operands
-    load_chunk(ps, a, t0, L, h, col_base, tid, 256);
+    load_chunk<64 * NT, FE>(ps, a, t0, L, h, col_base, tid, 256);
     __syncthreads();
-    gate_prefix<MODE>(ps, a.fe, C, L, tid);
-    qk_norms(ps, a, tid);
+    gate_prefix<MODE, 64 * NT, FE>(ps, a.fe, C, L, tid);
+    if (FE) qk_norms(ps, a, tid);
     __syncthreads();
-    pair_products<MODE>(ps, a, C, exp2C, wave, lane,
+    pair_products<MODE, 64 * NT, FE>(ps, a, C, exp2C, wave, lane,
                         [&](int t, int c0, const float* kv, const float* qv, const float* P,
                             const float* R) {
                           const int cb = c0 & ~31, cl = c0 & 31;
@@ -250,18 +250,18 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
   if (float* s1 = prefill_final_state(a, n, h)) store_state(s1);
 }
 
-template <int MODE, int NT>
+template <int MODE, int NT, bool FE>
 hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
   constexpr size_t bytes = sizeof(FusedSmem<64 * NT>);
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_chunk_kernel<MODE, NT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_chunk_kernel<MODE, NT, FE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
-  prefill_chunk_kernel<MODE, NT>
+  prefill_chunk_kernel<MODE, NT, FE>
       <<<dim3(2 / NT, a.num_heads, a.num_seqs), 256, bytes, s>>>(a, exp2C);
   return hipGetLastError();
 }
@@ -273,12 +273,17 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
   if (a.num_seqs <= 0) return hipSuccess;
   if (dv_split != 1 && dv_split != 2) return hipErrorInvalidValue;
   const int nt = dv_split == 1 ? 2 : 1;
-  if (anchor_mode == 0)
-    return nt == 2 ? launch_variant<0, 2>(a, s) : launch_variant<0, 1>(a, s);
   // data-dependent anchors: 64-column blocks only (the 128-column variant
   // would exceed the register file)
-  if (anchor_mode == 2) return dv_split == 2 ? launch_variant<2, 1>(a, s) : hipErrorInvalidValue;
-  return nt == 2 ? launch_variant<1, 2>(a, s) : launch_variant<1, 1>(a, s);
+  if (anchor_mode == 2 && dv_split != 2) return hipErrorInvalidValue;
+  if (frontend_active(a.fe)) {
+    if (anchor_mode == 0) return nt == 2 ? launch_variant<0, 2, true>(a, s) : launch_variant<0, 1, true>(a, s);
+    if (anchor_mode == 2) return launch_variant<2, 1, true>(a, s);
+    return nt == 2 ? launch_variant<1, 2, true>(a, s) : launch_variant<1, 1, true>(a, s);
+  }
+  if (anchor_mode == 0) return nt == 2 ? launch_variant<0, 2, false>(a, s) : launch_variant<0, 1, false>(a, s);
+  if (anchor_mode == 2) return launch_variant<2, 1, false>(a, s);
+  return nt == 2 ? launch_variant<1, 2, false>(a, s) : launch_variant<1, 1, false>(a, s);
 }
 
 }  // namespace kda

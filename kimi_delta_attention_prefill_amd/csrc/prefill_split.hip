@@ -121,7 +121,7 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
 //    an MFMA against a one-hot matrix (exact: one nonzero product per output);
 //    the transposed b Kg then gives M^T = (b Kg)^T T^T whose accumulators are
 //    the -M A fragments.
-template <int MODE>
+template <int MODE, bool FE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_split_prep(PrefillArgs a, float exp2C,
                                                           uint8_t* __restrict__ ws) {
   __shared__ __align__(16) float Al[CH][36];   // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
@@ -179,9 +179,18 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // Tokens past the sequence end (a final partial chunk) read as zero; their
   // transformed gate and beta are forced to zero as well.
   const bool live[2] = {l16 < L, l16 + 16 < L};
-  const float beta[2] = {
-      live[0] ? frontend_beta(a.fe, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0))) : 0.f,
-      live[1] ? frontend_beta(a.fe, bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((l16 + 16) * H * 2), 0, 0))) : 0.f};
+  float beta[2] = {
+      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)(l16 * H * 2), 0, 0)),
+      bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(rb, (uint32_t)((l16 + 16) * H * 2), 0, 0))};
+  if (FE) {
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) beta[hf] = live[hf] ? frontend_beta(a.fe, beta[hf]) : 0.f;
+  }
+  // the gate tensor's value x of a live token as the log-decay (no transform
+  // without the front-end, where a padding token's zero is already exact)
+  auto gate = [&](float x, bool ok) __attribute__((always_inline)) {
+    return FE ? (ok ? frontend_gate(a.fe, x) : 0.f) : x;
+  };
   auto load8 = [&](__amdgpu_buffer_rsrc_t r, int hf, int p) __attribute__((always_inline)) {
     const uint32_t off = (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 4 * g4) * 2;
     const u32x2 x0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
@@ -192,7 +201,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // tokens (a pass over the chunk's q and k before the main loop; the four
   // lanes g4 of a token hold its 128 channels).
   float nq[2] = {1.f, 1.f}, nk[2] = {1.f, 1.f};
-  if (a.fe.normalize_qk) {
+  if (FE && a.fe.normalize_qk) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float s2q = 0.f, s2k = 0.f;
@@ -249,9 +258,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     float G[2][8], G15[8], GL[8], Gf[2][8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float s0 = row_scan16(live[0] ? frontend_gate(a.fe, bf16_elem(gw[0], j)) : 0.f);
+      const float s0 = row_scan16(gate(bf16_elem(gw[0], j), live[0]));
       const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(live[1] ? frontend_gate(a.fe, bf16_elem(gw[1], j)) : 0.f) + b0;
+      const float s1 = row_scan16(gate(bf16_elem(gw[1], j), live[1])) + b0;
       G[0][j] = s0 * kLog2e;
       G[1][j] = s1 * kLog2e;
       G15[j] = b0 * kLog2e;
@@ -524,7 +533,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // tokens s, column = token t) are the W A fragments.
   f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
   float nkp[2] = {1.f, 1.f};               // front-end norm of the previous chunk's keys
-  if (a.fe.normalize_qk) {
+  if (FE && a.fe.normalize_qk) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float s2 = 0.f;
@@ -547,9 +556,9 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       // no previous chunk (an empty range): zero gates, so d_p = 1 and M' = M
-      const float s0 = row_scan16(has_prev ? frontend_gate(a.fe, bf16_elem(gpw[p][0], j)) : 0.f);
+      const float s0 = row_scan16(gate(bf16_elem(gpw[p][0], j), has_prev));
       const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(has_prev ? frontend_gate(a.fe, bf16_elem(gpw[p][1], j)) : 0.f) + b0;
+      const float s1 = row_scan16(gate(bf16_elem(gpw[p][1], j), has_prev)) + b0;
       const float gl = __shfl(s1, 15, 16) * kLog2e;
       dp[j] = fast_exp2(gl);
       krp[0][j] = static_cast<_Float16>(nkp[0] * bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
@@ -1247,13 +1256,13 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillA
   chain_body(a, ws, lds, job);
 }
 
-template <int MODE>
+template <int MODE, bool FE>
 hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
   const int64_t slots = (int64_t)a.num_seqs + a.total_tokens / CH + 1;
   const int64_t blocks = 8 * ((slots * a.num_heads + 7) / 8);
   if (blocks > INT_MAX) return hipErrorInvalidValue;
-  prefill_split_prep<MODE><<<(unsigned)blocks, 64, 0, s>>>(a, exp2C, ws);
+  prefill_split_prep<MODE, FE><<<(unsigned)blocks, 64, 0, s>>>(a, exp2C, ws);
   return hipGetLastError();
 }
 
@@ -1297,8 +1306,12 @@ hipError_t launch_prefill_split_prepare(const PrefillArgs& a, int anchor_mode, v
                                         hipStream_t s) {
   if (a.num_seqs <= 0) return hipSuccess;
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  if (anchor_mode == 2) return launch_prep<2>(a, ws, s);
-  return anchor_mode == 0 ? launch_prep<0>(a, ws, s) : launch_prep<1>(a, ws, s);
+  if (frontend_active(a.fe)) {
+    if (anchor_mode == 2) return launch_prep<2, true>(a, ws, s);
+    return anchor_mode == 0 ? launch_prep<0, true>(a, ws, s) : launch_prep<1, true>(a, ws, s);
+  }
+  if (anchor_mode == 2) return launch_prep<2, false>(a, ws, s);
+  return anchor_mode == 0 ? launch_prep<0, false>(a, ws, s) : launch_prep<1, false>(a, ws, s);
 }
 
 hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspace,
