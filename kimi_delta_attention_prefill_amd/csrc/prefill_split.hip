@@ -882,8 +882,10 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
 
   // --------------------------------------------------------- state halves
   // Wave hs owns key rows 64hs..64hs+63: accumulator tiles mt = 4hs..4hs+3,
-  // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.
-  const int hs = wave;
+  // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.  The two halves are
+  // separate code (hs a constant): only half 0 adds U0, so only it loads U0.
+  auto state_half = [&](auto hs_const) __attribute__((always_inline)) {
+  constexpr int hs = decltype(hs_const)::value;
   f32x4 S[kNT][4];
 #pragma unroll
   for (int t = 0; t < kNT; ++t)
@@ -904,8 +906,10 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) o.am[mt][q] = gfrag(r, kRecOffMneg, mt * 4 + 2 * hs + q);
+      if (hs == 0) {
 #pragma unroll
-      for (int t = 0; t < kNT; ++t) o.u0[t][mt] = gacc(r, kRecOffU0 + (sub0 + t) * 2048, mt);
+        for (int t = 0; t < kNT; ++t) o.u0[t][mt] = gacc(r, kRecOffU0 + (sub0 + t) * 2048, mt);
+      }
     }
   };
   auto load_b = [&](BOps& o, int c) __attribute__((always_inline)) {
@@ -932,7 +936,11 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
         *reinterpret_cast<f16x8*>(ex + kExSb + (((2 * hs + q) * kNT + t) * 64 + lane) * 16) = Sb[q];
       f32x4 P[2];
 #pragma unroll
-      for (int mt = 0; mt < 2; ++mt) P[mt] = (hs == 0 && job.with_u0) ? o.u0[t][mt] : z;
+      for (int mt = 0; mt < 2; ++mt) P[mt] = z;
+      if (hs == 0 && job.with_u0) {
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) P[mt] = o.u0[t][mt];
+      }
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -1049,6 +1057,11 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
         for (int i = 0; i < 4; ++i)
           job.s_final[(16 * (4 * hs + m) + 4 * g4 + i) * D + colof(t)] = S[t][m][i];
   }
+  };
+  if (wave == 0)
+    state_half(std::integral_constant<int, 0>{});
+  else
+    state_half(std::integral_constant<int, 1>{});
 }
 
 __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs a,
