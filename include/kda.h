@@ -230,13 +230,19 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
                      int32_t checkpoint_tokens, void* out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
-/* kda_prefill_pool with the input front-end (as kda_prefill_ex). */
+/* kda_prefill_pool with the input front-end (as kda_prefill_ex) and a pool
+ * of either state type: `state_dtype` KDA_STATE_F32 (as kda_prefill_pool) or
+ * KDA_STATE_BF16 (a bf16 [num_slots, H, 128, 128] pool; a sequence's state is
+ * widened to FP32 on entry, carried in FP32 and rounded to nearest-even when
+ * stored back; checkpoints stay FP32).  "FP32/BF16 pool with state indices"
+ * of the pages' serving rows (the composite-schedule rows include a BF16
+ * pool).  Unknown dtypes: KDA_ERR_INVALID_ARGUMENT. */
 int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void* g,
                         const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
                         int32_t head_dim_v, float scale, float lower_bound,
-                        const kda_frontend* frontend, float* state_pool, int64_t num_slots,
-                        const int32_t* slot_indices, float* checkpoints,
+                        const kda_frontend* frontend, void* state_pool, int32_t state_dtype,
+                        int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
                         int32_t checkpoint_tokens, void* out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream);
 

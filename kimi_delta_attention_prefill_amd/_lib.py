@@ -127,8 +127,8 @@ def load():
                                      i64, vp, vp, i32, vp, vp, sz, vp]
     lib.kda_prefill_pool.restype = ctypes.c_int
     lib.kda_prefill_pool_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
-                                        ctypes.POINTER(_FrontEnd), vp, i64, vp, vp, i32, vp, vp,
-                                        sz, vp]
+                                        ctypes.POINTER(_FrontEnd), vp, i32, i64, vp, vp, i32, vp,
+                                        vp, sz, vp]
     lib.kda_prefill_pool_ex.restype = ctypes.c_int
     lib.kda_prefill_checkpoint_slots.argtypes = [i32, i64, i32]
     lib.kda_prefill_checkpoint_slots.restype = sz
@@ -255,9 +255,9 @@ def checkpoint_slots(num_seqs: int, total_tokens: int, checkpoint_tokens: int) -
 def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scale, lower_bound,
                  checkpoints=None, checkpoint_tokens=64, out=None, workspace=None, stream=None,
                  frontend=None):
-    """Packed varlen prefill whose states live in ``state_pool`` (fp32
-    [num_slots, H, 128, 128], updated in place; None: zero start, nothing
-    stored), one ``slot_indices`` entry (int32, device) per sequence.
+    """Packed varlen prefill whose states live in ``state_pool`` (fp32 or
+    bf16 [num_slots, H, 128, 128], updated in place; None: zero start,
+    nothing stored), one ``slot_indices`` entry (int32, device) per sequence.
 
     ``checkpoints``: an fp32 [checkpoint_slots(N, T, checkpoint_tokens), H, 128, 128]
     tensor to fill, True to allocate one (zero-filled), or None for none.
@@ -271,9 +271,13 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
     _need(beta, "beta", torch.bfloat16, (T, H), dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     _need(slot_indices, "slot_indices", torch.int32, (N,), dev)
-    num_slots = 0
+    num_slots, sd = 0, STATE_F32
     if state_pool is not None:
-        _need(state_pool, "state_pool", torch.float32, (state_pool.shape[0], H, D, D), dev)
+        if state_pool.dtype == torch.bfloat16:
+            sd = STATE_BF16
+        elif state_pool.dtype != torch.float32:
+            raise TypeError("state_pool must be float32 or bfloat16")
+        _need(state_pool, "state_pool", state_pool.dtype, (state_pool.shape[0], H, D, D), dev)
         num_slots = state_pool.shape[0]
     if checkpoints is True:
         checkpoints = torch.zeros((checkpoint_slots(N, T, checkpoint_tokens), H, D, D),
@@ -291,7 +295,7 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check(load().kda_prefill_pool_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                       _ptr(cu_seqlens), N, T, H, D, D, float(scale),
-                                      float(lower_bound), _fe_ptr(frontend), _ptr(state_pool),
+                                      float(lower_bound), _fe_ptr(frontend), _ptr(state_pool), sd,
                                       num_slots, _ptr(slot_indices), _ptr(checkpoints),
                                       int(checkpoint_tokens) if checkpoints is not None else 0,
                                       _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))

@@ -180,6 +180,7 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.windows = 1;
   a.window_chunks = 0;
   a.pool = nullptr;
+  a.pool_bf16 = 0;
   a.slots = nullptr;
   a.num_slots = 0;
   a.ckpt = nullptr;
@@ -367,8 +368,8 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
                         const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
                         int32_t head_dim_v, float scale, float lower_bound,
-                        const kda_frontend* frontend, float* state_pool, int64_t num_slots,
-                        const int32_t* slot_indices, float* checkpoints,
+                        const kda_frontend* frontend, void* state_pool, int32_t state_dtype,
+                        int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
                         int32_t checkpoint_tokens, void* out, void* workspace,
                         size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "kda_prefill_pool";
@@ -380,6 +381,8 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
   if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "%s: scale is not finite", fn);
   if (fe.gate_mode == KDA_GATE_LOG && (rc = check_bound(fn, lower_bound)) != KDA_OK) return rc;
   lower_bound = effective_bound(fe, lower_bound);
+  if (state_dtype != KDA_STATE_F32 && state_dtype != KDA_STATE_BF16)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "%s: unknown state dtype %d", fn, state_dtype);
   if (state_pool) {
     if (num_slots < 1)
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_slots=%lld", fn, (long long)num_slots);
@@ -403,6 +406,7 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
   kda::PrefillArgs a = make_args(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                                  scale, lower_bound, nullptr, nullptr, out);
   a.pool = state_pool;
+  a.pool_bf16 = state_dtype == KDA_STATE_BF16;
   a.slots = slot_indices;
   a.num_slots = num_slots;
   a.ckpt = checkpoints;
@@ -420,7 +424,7 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, hipStream_t stream) {
   return kda_prefill_pool_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                              head_dim_k, head_dim_v, scale, lower_bound, nullptr, state_pool,
-                             num_slots, slot_indices, checkpoints, checkpoint_tokens, out,
+                             KDA_STATE_F32, num_slots, slot_indices, checkpoints, checkpoint_tokens, out,
                              workspace, workspace_bytes, stream);
 }
 

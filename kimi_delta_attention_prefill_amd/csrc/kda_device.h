@@ -60,18 +60,45 @@ __device__ __forceinline__ int clamp_offset(int x, int total) {
 
 // The [128][128] FP32 state a prefill of (sequence n, head h) starts from
 // (null: zeros) and the one it ends in (null: not stored).
-__device__ __forceinline__ float* prefill_pool_state(const PrefillArgs& a, int n, int h) {
+// One [128][128] state of a sequence-head: FP32, or BF16 in a bf16 state pool
+// (widened on load, rounded to nearest-even on store), or none.
+struct StateRef {
+  void* p = nullptr;
+  bool bf16 = false;
+  __device__ __forceinline__ explicit operator bool() const { return p != nullptr; }
+  __device__ __forceinline__ float load(int i) const {
+    return bf16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i]) : static_cast<const float*>(p)[i];
+  }
+  __device__ __forceinline__ void store(int i, float v) const {
+    if (bf16)
+      static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+    else
+      static_cast<float*>(p)[i] = v;
+  }
+};
+__device__ __forceinline__ StateRef fp32_state(const float* p) {
+  StateRef r;
+  r.p = const_cast<float*>(p);
+  return r;
+}
+__device__ __forceinline__ StateRef prefill_pool_state(const PrefillArgs& a, int n, int h) {
   const int64_t s = a.slots[n];
-  return (s >= 0 && s < a.num_slots) ? a.pool + (s * a.num_heads + h) * (int64_t)(kHeadDim * kHeadDim)
-                                     : nullptr;
+  StateRef r;
+  if (s >= 0 && s < a.num_slots) {
+    const int64_t off = (s * a.num_heads + h) * (int64_t)(kHeadDim * kHeadDim);
+    r.bf16 = a.pool_bf16 != 0;
+    r.p = r.bf16 ? static_cast<void*>(static_cast<uint16_t*>(a.pool) + off)
+                 : static_cast<void*>(static_cast<float*>(a.pool) + off);
+  }
+  return r;
 }
-__device__ __forceinline__ const float* prefill_initial_state(const PrefillArgs& a, int n, int h) {
+__device__ __forceinline__ StateRef prefill_initial_state(const PrefillArgs& a, int n, int h) {
   if (a.pool) return prefill_pool_state(a, n, h);
-  return a.s0 ? a.s0 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr;
+  return fp32_state(a.s0 ? a.s0 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr);
 }
-__device__ __forceinline__ float* prefill_final_state(const PrefillArgs& a, int n, int h) {
+__device__ __forceinline__ StateRef prefill_final_state(const PrefillArgs& a, int n, int h) {
   if (a.pool) return prefill_pool_state(a, n, h);
-  return a.s1 ? a.s1 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr;
+  return fp32_state(a.s1 ? a.s1 + ((int64_t)n * a.num_heads + h) * (kHeadDim * kHeadDim) : nullptr);
 }
 // Where the state after `done` tokens of sequence n (starting at token bos)
 // is checkpointed, or null when checkpoints are off or `done` is not a

@@ -54,7 +54,8 @@ struct PrefillArgs {
   // State pool addressing (kda_prefill_pool): when `pool` is set, s0/s1 are
   // unused and sequence n starts from and ends in pool slot slots[n] (a slot
   // outside [0, num_slots) starts from zeros and is not stored).
-  float* pool;            // fp32 [num_slots, H, 128, 128] or null
+  void* pool;             // fp32 or bf16 [num_slots, H, 128, 128] or null
+  int32_t pool_bf16;      // the pool holds bf16 states (read widened, written RNE)
   const int32_t* slots;   // int32 [N]
   int64_t num_slots;
   // Checkpoints: the state after every `ckpt_tokens` tokens (a multiple of

@@ -81,18 +81,27 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const float* s0 = prefill_initial_state(a, n, h);
+  const StateRef s0 = prefill_initial_state(a, n, h);
 
   // State accumulators: tile (mt, nt) holds rows 16 mt + 4 g4 + i and column
   // col_base + colw + 16 nt + l16.
   f32x4 S[8][NT];
+  auto init_state = [&](auto load) __attribute__((always_inline)) {
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+      for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        S[mt][nt][i] = s0 ? s0[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] : 0.f;
+        for (int i = 0; i < 4; ++i)
+          S[mt][nt][i] = load((16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16);
+  };
+  // one branch on the state's type, outside the element loops
+  if (!s0)
+    init_state([](int) { return 0.f; });
+  else if (s0.bf16)
+    init_state([&](int e) { return bf16_to_f32(static_cast<const uint16_t*>(s0.p)[e]); });
+  else
+    init_state([&](int e) { return static_cast<const float*>(s0.p)[e]; });
   auto store_state = [&](float* dst) __attribute__((always_inline)) {
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
@@ -247,7 +256,20 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
     if (float* cp = prefill_checkpoint(a, n, h, bos, t0 + L - bos)) store_state(cp);
   }
 
-  if (float* s1 = prefill_final_state(a, n, h)) store_state(s1);
+  if (const StateRef s1 = prefill_final_state(a, n, h)) {
+    if (!s1.bf16) {
+      store_state(static_cast<float*>(s1.p));
+    } else {
+      uint16_t* dst = static_cast<uint16_t*>(s1.p);
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = f32_to_bf16(S[mt][nt][i]);
+    }
+  }
 }
 
 template <int MODE, int NT, bool FE>

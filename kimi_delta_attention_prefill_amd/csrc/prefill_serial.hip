@@ -43,11 +43,11 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const float* s0 = prefill_initial_state(a, n, h);
+  const StateRef s0 = prefill_initial_state(a, n, h);
 
   float S[32];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) S[i] = s0 ? s0[(4 * i + rg) * kHeadDim + col] : 0.f;
+  for (int i = 0; i < 32; ++i) S[i] = s0 ? s0.load((4 * i + rg) * kHeadDim + col) : 0.f;
 
   for (int t0 = bos; t0 < eos; t0 += kStage) {
     const int L = min(kStage, eos - t0);
@@ -133,9 +133,9 @@ __global__ __launch_bounds__(64 * W) void prefill_serial_kernel(PrefillArgs a) {
       }
     }
   }
-  if (float* s1 = prefill_final_state(a, n, h)) {
+  if (const StateRef s1 = prefill_final_state(a, n, h)) {
 #pragma unroll
-    for (int i = 0; i < 32; ++i) s1[(4 * i + rg) * kHeadDim + col] = S[i];
+    for (int i = 0; i < 32; ++i) s1.store((4 * i + rg) * kHeadDim + col, S[i]);
   }
 }
 

@@ -673,13 +673,13 @@ struct QOps {            // output wave: Qg and Mqk of chunk c-1
 struct ChainJob {
   int n, h, tile;
   int cb, ce;
-  const float* s_init;   // [128][128] state entering chunk cb, or null
+  StateRef s_init;       // [128][128] state entering chunk cb, or none
   const float* s_init_lds = nullptr;   // or this block's columns of it in LDS, [128][16 kNT]
   bool identity;         // start from the identity instead (a window's map)
   bool with_u0;          // false: drop U0 (the map of a window is linear)
   bool with_out;         // store the outputs of the chunks
   bool ckpt;             // store checkpoints (runs of the true state only)
-  float* s_final;        // [128][128] state after chunk ce-1, or null
+  StateRef s_final;      // [128][128] state after chunk ce-1, or none
 };
 
 __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* __restrict__ ws,
@@ -895,7 +895,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       for (int i = 0; i < 4; ++i) {
         const int row = 16 * (4 * hs + m) + 4 * g4 + i, col = colof(t);
         S[t][m][i] = job.s_init_lds ? job.s_init_lds[row * (16 * kNT) + 16 * t + (lane & 15)]
-                     : job.s_init   ? job.s_init[row * D + col]
+                     : job.s_init   ? job.s_init.load(row * D + col)
                                     : (job.identity && row == col ? 1.f : 0.f);
       }
   AOps A[kAhead];
@@ -1055,7 +1055,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       for (int m = 0; m < 4; ++m)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          job.s_final[(16 * (4 * hs + m) + 4 * g4 + i) * D + colof(t)] = S[t][m][i];
+          job.s_final.store((16 * (4 * hs + m) + 4 * g4 + i) * D + colof(t), S[t][m][i]);
   }
   };
   if (wave == 0)
@@ -1124,15 +1124,15 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillA
     job.cb = 0; job.ce = min(WC, nch);
     job.s_init = prefill_initial_state(a, n, h);
     job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
-    job.s_final = nwin <= 1 ? prefill_final_state(a, n, h) : wv.at(n, h, 0, 0);
+    job.s_final = nwin <= 1 ? prefill_final_state(a, n, h) : fp32_state(wv.at(n, h, 0, 0));
   } else {
     const bool map = j > W - 2;
     const int w = map ? j - (W - 2) : j;
     if (w >= nwin - 1) return;            // the last window needs neither
     job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
-    job.s_init = nullptr;
+    job.s_init = StateRef{};
     job.identity = map; job.with_u0 = !map; job.with_out = false; job.ckpt = false;
-    job.s_final = wv.at(n, h, w, map ? 1 : 0);
+    job.s_final = fp32_state(wv.at(n, h, w, map ? 1 : 0));
   }
   chain_body(a, ws, lds, job);
 }
@@ -1258,14 +1258,14 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillA
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
   job.cb = w * WC; job.ce = min(nch, (w + 1) * WC);
-  job.s_init = w == 1 ? wv.at(n, h, 0, 0) : nullptr;   // window 1 starts from E_0
+  job.s_init = fp32_state(w == 1 ? wv.at(n, h, 0, 0) : nullptr);   // window 1 starts from E_0
   job.s_init_lds = nullptr;
   if (w >= 2) {
     carry_to_lds(wv, n, h, tile, w, lds);
     job.s_init_lds = reinterpret_cast<const float*>(lds);
   }
   job.identity = false; job.with_u0 = true; job.with_out = true; job.ckpt = true;
-  job.s_final = w == nwin - 1 ? prefill_final_state(a, n, h) : nullptr;
+  job.s_final = w == nwin - 1 ? prefill_final_state(a, n, h) : StateRef{};
   chain_body(a, ws, lds, job);
 }
 

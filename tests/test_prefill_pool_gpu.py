@@ -7,7 +7,7 @@ import torch
 import kimi_delta_attention_prefill_amd as kda
 import oracle
 from kimi_delta_attention_prefill_amd.inputs import make_prefill_case
-from _checks import check_out, check_state
+from _checks import check_bf16_state, check_out, check_state
 
 pytestmark = pytest.mark.gpu
 
@@ -22,16 +22,19 @@ def dev():
     return torch.device("cuda:0")
 
 
-def run_case(dev, route, lengths, H, lb, slots, num_slots, ck_tokens, seed, windows=False):
+def run_case(dev, route, lengths, H, lb, slots, num_slots, ck_tokens, seed, windows=False,
+             bf16_pool=False):
     case = make_prefill_case(lengths, H, lb, None, seed=seed, name=f"pool_{route}")
     N, T = case.num_seqs, case.total_tokens
     g = torch.Generator().manual_seed(seed + 1)
     pool0 = (0.02 * torch.randn((num_slots, H, 128, 128), generator=g)).float()
+    if bf16_pool:   # the states the oracle starts from are the bf16 values, read exactly
+        pool0 = pool0.to(torch.bfloat16)
     slots_t = torch.tensor(slots, dtype=torch.int32)
     to = lambda t: t.to(dev)
     pool = to(pool0.clone())
-    print(f"[gpu] prefill_pool route={route} N={N} T={T} H={H} slots={slots} every={ck_tokens}",
-          flush=True)
+    print(f"[gpu] prefill_pool route={route} N={N} T={T} H={H} slots={slots} every={ck_tokens} "
+          f"pool={pool0.dtype}", flush=True)
     kda.set_prefill_route(route)
     try:
         if windows:
@@ -55,7 +58,10 @@ def run_case(dev, route, lengths, H, lb, slots, num_slots, ck_tokens, seed, wind
     for n, (s, ok) in enumerate(zip(slots, valid)):
         if ok:
             touched.add(s)
-            check_state(pool_cpu[s:s + 1], ref_f[n:n + 1])
+            if bf16_pool:   # the prefill state bound on top of the stored value's bf16 rounding
+                check_bf16_state(pool_cpu[s:s + 1], ref_f[n:n + 1], tol=1e-2)
+            else:
+                check_state(pool_cpu[s:s + 1], ref_f[n:n + 1])
     for s in range(num_slots):
         if s not in touched:
             assert torch.equal(pool_cpu[s], pool0[s]), f"pool slot {s} was modified"
@@ -88,3 +94,15 @@ def test_checkpoints_every_chunk_split16(dev, route):
 def test_pool_checkpoints_windows(dev):
     # one long sequence on the windowed split route; checkpoints cross window boundaries
     run_case(dev, kda.ROUTE_SPLIT, [3000], 3, -5.0, [1], 3, 96, seed=47, windows=True)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_bf16_pool(dev, route):
+    """A bf16 state pool: states widened on entry, stored back rounded (checkpoints FP32)."""
+    run_case(dev, route, [45, 0, 200, 96], 3, -5.0, [4, 1, -1, 6], 8, 64, seed=611,
+             bf16_pool=True)
+
+
+def test_bf16_pool_windows(dev):
+    run_case(dev, kda.ROUTE_SPLIT, [2000], 3, -8.0, [2], 4, 96, seed=612, windows=True,
+             bf16_pool=True)
