@@ -279,3 +279,40 @@ def test_pool_prefill_host_validation():
     assert kda.checkpoint_slots(3, 1000, 64) == 3 + 1000 // 64 + 1
     assert kda.checkpoint_slots(1, 8192, 64) == 1 + 128 + 1
     assert kda.checkpoint_slots(1, 10, 0) == 0
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/kda.h compiles as C11 and a C program links against libkda.so and
+    calls it (host-only entry points: no device is touched)."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not available")
+    src = tmp_path / "use_kda.c"
+    src.write_text(r'''
+#include <stdio.h>
+#include "kda.h"
+int main(void) {
+  kda_frontend fe = {KDA_GATE_SOFTPLUS, 0.0f, 1, 1, 1e-6f};
+  kda_prefill_plan_t plan;
+  if (kda_abi_version() != KDA_ABI_VERSION) return 1;
+  if (kda_prefill_plan(1, 8192, 8, -5.0f, 256, KDA_ROUTE_AUTO, &plan) != KDA_OK) return 2;
+  if (plan.route != KDA_ROUTE_SPLIT || plan.windows < 3) return 3;
+  /* invalid arguments are rejected on the host, before any device work */
+  if (kda_decode_ex(0, 0, 0, 0, 0, 0, KDA_STATE_F32, 1, 0, 1, 8, 128, 128, 1.0f, &fe, 0, 0)
+      != KDA_ERR_INVALID_ARGUMENT) return 4;
+  if (kda_last_error()[0] == '\0') return 5;
+  printf("ok %d\n", (int)plan.windows);
+  return 0;
+}
+''')
+    lib_dir = os.path.dirname(kda.load()._name)
+    exe = tmp_path / "use_kda"
+    r = subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-D__HIP_PLATFORM_AMD__",
+                        "-I/opt/rocm/include", f"-I{os.path.join(ROOT, 'include')}", str(src),
+                        f"-L{lib_dir}", "-lkda", f"-Wl,-rpath,{lib_dir}", "-o", str(exe)],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr[-3000:]
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert r.returncode == 0 and r.stdout.startswith("ok"), (r.returncode, r.stdout, r.stderr[-2000:])
