@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -230,21 +230,29 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
                      int32_t checkpoint_tokens, void* out, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
-/* kda_prefill_pool with the input front-end (as kda_prefill_ex) and a pool
- * of either state type: `state_dtype` KDA_STATE_F32 (as kda_prefill_pool) or
- * KDA_STATE_BF16 (a bf16 [num_slots, H, 128, 128] pool; a sequence's state is
- * widened to FP32 on entry, carried in FP32 and rounded to nearest-even when
- * stored back; checkpoints stay FP32).  "FP32/BF16 pool with state indices"
- * of the pages' serving rows (the composite-schedule rows include a BF16
- * pool).  Unknown dtypes: KDA_ERR_INVALID_ARGUMENT. */
+/* kda_prefill_pool with the input front-end (as kda_prefill_ex), a pool of
+ * either state type and a pool slot stride:
+ *  state_dtype  KDA_STATE_F32 (as kda_prefill_pool) or KDA_STATE_BF16 (a
+ *               bf16 pool; a sequence's state is widened to FP32 on entry,
+ *               carried in FP32 and rounded to nearest-even when stored
+ *               back; checkpoints stay FP32).  "FP32/BF16 pool with state
+ *               indices" of the pages' serving rows (the composite-schedule
+ *               rows include a BF16 pool).
+ *  slot_stride  elements from the start of one slot to the next: 0 = the
+ *               dense ("page") layout, num_heads * 128 * 128; otherwise the
+ *               padded layout, >= that and a multiple of 16 bytes, e.g. one
+ *               layer's view of a pool that keeps every layer's states of a
+ *               slot together.  Within a slot the [H, 128, 128] state stays
+ *               dense.
+ * Unknown dtypes, bad strides: KDA_ERR_INVALID_ARGUMENT. */
 int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void* g,
                         const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                         int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
                         int32_t head_dim_v, float scale, float lower_bound,
                         const kda_frontend* frontend, void* state_pool, int32_t state_dtype,
-                        int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
-                        int32_t checkpoint_tokens, void* out, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream);
+                        int64_t num_slots, int64_t slot_stride, const int32_t* slot_indices,
+                        float* checkpoints, int32_t checkpoint_tokens, void* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* N + T_tot / checkpoint_tokens + 1: the [H, 128, 128] slots a checkpoint
  * buffer of kda_prefill_pool must hold (0 for invalid arguments). */
@@ -347,18 +355,21 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g,
                float scale, void* out, hipStream_t stream);
 
 /* kda_decode with the input front-end `frontend` (see kda_frontend; NULL =
- * kda_decode).  With a raw gate, the g tensor holds a and any finite value is
- * allowed; with beta_logits, beta holds logits.  The q/k normalisation is
- * folded into the step's reductions (no extra pass over the state).
+ * kda_decode) and a pool slot stride (`slot_stride`, as kda_prefill_pool_ex:
+ * 0 = dense [num_slots, H, 128, 128], else the elements from one slot to the
+ * next, >= num_heads * 128 * 128 and a multiple of 16 bytes).  With a raw
+ * gate, the g tensor holds a and any finite value is allowed; with
+ * beta_logits, beta holds logits.  The q/k normalisation is folded into the
+ * step's reductions (no extra pass over the state).
  * Errors: KDA_ERR_INVALID_ARGUMENT for an unknown gate mode, a lower bound
- * that is not negative and finite (KDA_GATE_LOWER_BOUND) or a negative or
- * non-finite norm_eps; everything else as kda_decode. */
+ * that is not negative and finite (KDA_GATE_LOWER_BOUND), a negative or
+ * non-finite norm_eps or a bad slot stride; everything else as kda_decode. */
 int kda_decode_ex(const void* q, const void* k, const void* v, const void* g,
                   const void* beta, void* state_pool, int32_t state_dtype,
-                  int64_t num_slots, const int32_t* slot_indices, int32_t rows,
-                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v,
-                  float scale, const kda_frontend* frontend, void* out,
-                  hipStream_t stream);
+                  int64_t num_slots, int64_t slot_stride, const int32_t* slot_indices,
+                  int32_t rows, int32_t num_heads, int32_t head_dim_k,
+                  int32_t head_dim_v, float scale, const kda_frontend* frontend,
+                  void* out, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc -- */
 /* Text describing the last non-OK return on the calling thread ("" if none). */

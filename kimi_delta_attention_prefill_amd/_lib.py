@@ -127,15 +127,15 @@ def load():
                                      i64, vp, vp, i32, vp, vp, sz, vp]
     lib.kda_prefill_pool.restype = ctypes.c_int
     lib.kda_prefill_pool_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
-                                        ctypes.POINTER(_FrontEnd), vp, i32, i64, vp, vp, i32, vp,
-                                        vp, sz, vp]
+                                        ctypes.POINTER(_FrontEnd), vp, i32, i64, i64, vp, vp, i32,
+                                        vp, vp, sz, vp]
     lib.kda_prefill_pool_ex.restype = ctypes.c_int
     lib.kda_prefill_checkpoint_slots.argtypes = [i32, i64, i32]
     lib.kda_prefill_checkpoint_slots.restype = sz
     lib.kda_decode.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32, vp, vp]
     lib.kda_decode.restype = ctypes.c_int
-    lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, vp, i32, i32, i32, i32, f32,
-                                  ctypes.POINTER(_FrontEnd), vp, vp]
+    lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, vp, i32, i32, i32, i32,
+                                  f32, ctypes.POINTER(_FrontEnd), vp, vp]
     lib.kda_decode_ex.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -173,6 +173,31 @@ def _need(t, name, dtype, shape, device):
         raise ValueError(f"{name}: expected device {device}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name}: must be contiguous")
+
+
+def _pool_layout(pool, H, D, device):
+    """(state dtype code, slot stride) of a [num_slots, H, D, D] state pool.
+
+    Each slot's [H, D, D] block must be dense; the slots themselves may sit
+    at a larger stride (the padded layout, e.g. one layer's view of a pool
+    [num_slots, layers, H, D, D]).  Stride 0 means dense."""
+    if pool.dtype == torch.float32:
+        sd = STATE_F32
+    elif pool.dtype == torch.bfloat16:
+        sd = STATE_BF16
+    else:
+        raise TypeError("state_pool must be float32 or bfloat16")
+    if tuple(pool.shape[1:]) != (H, D, D) or pool.dim() != 4:
+        raise ValueError(f"state_pool: expected shape (num_slots, {H}, {D}, {D}), "
+                         f"got {tuple(pool.shape)}")
+    if pool.device != device:
+        raise ValueError(f"state_pool: expected device {device}, got {pool.device}")
+    dense = H * D * D
+    if pool.stride()[1:] != (D * D, D, 1) or (pool.shape[0] > 1 and pool.stride(0) < dense):
+        raise ValueError("state_pool: each slot's [H, D, D] block must be dense and slots "
+                         "must not overlap")
+    stride = pool.stride(0) if pool.shape[0] > 1 else dense
+    return sd, (0 if stride == dense else stride)
 
 
 def workspace_size(num_seqs: int, total_tokens: int, num_heads: int) -> int:
@@ -256,8 +281,9 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
                  checkpoints=None, checkpoint_tokens=64, out=None, workspace=None, stream=None,
                  frontend=None):
     """Packed varlen prefill whose states live in ``state_pool`` (fp32 or
-    bf16 [num_slots, H, 128, 128], updated in place; None: zero start,
-    nothing stored), one ``slot_indices`` entry (int32, device) per sequence.
+    bf16 [num_slots, H, 128, 128], updated in place; each slot dense, the
+    slots dense or at a larger stride (a view); None: zero start, nothing
+    stored), one ``slot_indices`` entry (int32, device) per sequence.
 
     ``checkpoints``: an fp32 [checkpoint_slots(N, T, checkpoint_tokens), H, 128, 128]
     tensor to fill, True to allocate one (zero-filled), or None for none.
@@ -271,13 +297,9 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
     _need(beta, "beta", torch.bfloat16, (T, H), dev)
     _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
     _need(slot_indices, "slot_indices", torch.int32, (N,), dev)
-    num_slots, sd = 0, STATE_F32
+    num_slots, sd, stride = 0, STATE_F32, 0
     if state_pool is not None:
-        if state_pool.dtype == torch.bfloat16:
-            sd = STATE_BF16
-        elif state_pool.dtype != torch.float32:
-            raise TypeError("state_pool must be float32 or bfloat16")
-        _need(state_pool, "state_pool", state_pool.dtype, (state_pool.shape[0], H, D, D), dev)
+        sd, stride = _pool_layout(state_pool, H, D, dev)
         num_slots = state_pool.shape[0]
     if checkpoints is True:
         checkpoints = torch.zeros((checkpoint_slots(N, T, checkpoint_tokens), H, D, D),
@@ -296,7 +318,7 @@ def prefill_pool(q, k, v, g, beta, cu_seqlens, slot_indices, state_pool, *, scal
     _check(load().kda_prefill_pool_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                       _ptr(cu_seqlens), N, T, H, D, D, float(scale),
                                       float(lower_bound), _fe_ptr(frontend), _ptr(state_pool), sd,
-                                      num_slots, _ptr(slot_indices), _ptr(checkpoints),
+                                      num_slots, stride, _ptr(slot_indices), _ptr(checkpoints),
                                       int(checkpoint_tokens) if checkpoints is not None else 0,
                                       _ptr(out), _ptr(workspace), ws_bytes, _stream(stream)))
     return out, checkpoints
@@ -357,7 +379,8 @@ def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, strea
     """One T=1 step per row against ``state_pool`` (fp32 or bf16), in place.
 
     q, k, v, g: bf16 [rows, H, 128]; beta: bf16 [rows, H];
-    state_pool: [num_slots, H, 128, 128]; slot_indices: int32 [rows].
+    state_pool: [num_slots, H, 128, 128], each slot dense, slots dense or at a
+    larger stride (a view); slot_indices: int32 [rows].
     ``frontend``: a :class:`FrontEnd` (kda_decode_ex) or None (kda_decode).
     Returns out (bf16 [rows, H, 128]).
     """
@@ -367,23 +390,18 @@ def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, strea
         _need(t, name, torch.bfloat16, (R, H, D), dev)
     _need(beta, "beta", torch.bfloat16, (R, H), dev)
     _need(slot_indices, "slot_indices", torch.int32, (R,), dev)
-    if state_pool.dtype == torch.float32:
-        sd = STATE_F32
-    elif state_pool.dtype == torch.bfloat16:
-        sd = STATE_BF16
-    else:
-        raise TypeError("state_pool must be float32 or bfloat16")
-    _need(state_pool, "state_pool", state_pool.dtype, (state_pool.shape[0], H, D, D), dev)
+    sd, stride = _pool_layout(state_pool, H, D, dev)
     if out is None:
         out = torch.empty((R, H, D), dtype=torch.bfloat16, device=dev)
     _need(out, "out", torch.bfloat16, (R, H, D), dev)
-    if frontend is None:
+    if frontend is None and stride == 0:
         _check(load().kda_decode(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool),
                                  sd, state_pool.shape[0], _ptr(slot_indices), R, H, D, D,
                                  float(scale), _ptr(out), _stream(stream)))
     else:
         _check(load().kda_decode_ex(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-                                    _ptr(state_pool), sd, state_pool.shape[0], _ptr(slot_indices),
-                                    R, H, D, D, float(scale), _fe_ptr(frontend), _ptr(out),
+                                    _ptr(state_pool), sd, state_pool.shape[0], stride,
+                                    _ptr(slot_indices), R, H, D, D, float(scale),
+                                    _fe_ptr(frontend), _ptr(out),
                                     _stream(stream)))
     return out

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(DecodeArgs a) {
     if (tid < COLS) a.out[rh * kHeadDim + slice * COLS + tid] = 0;
     return;
   }
-  elem* S = reinterpret_cast<elem*>(a.pool) + (slot * H + h) * (int64_t)(kHeadDim * kHeadDim);
+  elem* S = reinterpret_cast<elem*>(a.pool) + slot * a.slot_stride + h * (kHeadDim * kHeadDim);
 
   // Issue the state loads first; they are independent of q/k/g.
   float4 s[RPT];

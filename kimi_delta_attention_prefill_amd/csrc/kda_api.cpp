@@ -90,6 +90,25 @@ int check_sizes(const char* fn, int32_t num_seqs, int64_t total_tokens, int32_t 
   return KDA_OK;
 }
 
+// Pool slot stride in elements: 0 selects the dense layout (H * 128 * 128);
+// otherwise slots must not overlap and every slot must start 16-byte
+// aligned, as the pool does.  Rewrites 0 to the dense stride.
+int check_slot_stride(const char* fn, int32_t num_heads, int32_t state_dtype,
+                      int64_t* slot_stride) {
+  const int64_t dense = (int64_t)num_heads * KDA_HEAD_DIM * KDA_HEAD_DIM;
+  if (*slot_stride == 0) {
+    *slot_stride = dense;
+    return KDA_OK;
+  }
+  const int64_t elem = state_dtype == KDA_STATE_BF16 ? 2 : 4;
+  if (*slot_stride < dense || (*slot_stride * elem) % 16 != 0)
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "%s: slot_stride=%lld must be 0 or >= num_heads * 128 * 128 = %lld and a "
+                "multiple of 16 bytes",
+                fn, (long long)*slot_stride, (long long)dense);
+  return KDA_OK;
+}
+
 // lower_bound: finite and < 0, or -infinity for an unbounded gate.
 bool bound_ok(float lower_bound) {
   return lower_bound < 0.f && (std::isfinite(lower_bound) || std::isinf(lower_bound));
@@ -183,6 +202,7 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.pool_bf16 = 0;
   a.slots = nullptr;
   a.num_slots = 0;
+  a.slot_stride = 0;
   a.ckpt = nullptr;
   a.ckpt_tokens = 0;
   return a;
@@ -369,9 +389,9 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
                         int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
                         int32_t head_dim_v, float scale, float lower_bound,
                         const kda_frontend* frontend, void* state_pool, int32_t state_dtype,
-                        int64_t num_slots, const int32_t* slot_indices, float* checkpoints,
-                        int32_t checkpoint_tokens, void* out, void* workspace,
-                        size_t workspace_bytes, hipStream_t stream) {
+                        int64_t num_slots, int64_t slot_stride, const int32_t* slot_indices,
+                        float* checkpoints, int32_t checkpoint_tokens, void* out,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   const char* fn = "kda_prefill_pool";
   kda::FrontEnd fe;
   int rc = frontend_args(frontend, fn, &fe);
@@ -388,6 +408,7 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s: num_slots=%lld", fn, (long long)num_slots);
     if (!aligned(state_pool, 16))
       return fail(KDA_ERR_INVALID_ARGUMENT, "%s: state_pool is not 16-byte aligned", fn);
+    if ((rc = check_slot_stride(fn, num_heads, state_dtype, &slot_stride)) != KDA_OK) return rc;
   }
   if (checkpoints) {
     if (checkpoint_tokens <= 0 || checkpoint_tokens % 32 != 0)
@@ -409,6 +430,7 @@ int kda_prefill_pool_ex(const void* q, const void* k, const void* v, const void*
   a.pool_bf16 = state_dtype == KDA_STATE_BF16;
   a.slots = slot_indices;
   a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
   a.ckpt = checkpoints;
   a.ckpt_tokens = checkpoints ? checkpoint_tokens : 0;
   a.fe = fe;
@@ -424,8 +446,8 @@ int kda_prefill_pool(const void* q, const void* k, const void* v, const void* g,
                      size_t workspace_bytes, hipStream_t stream) {
   return kda_prefill_pool_ex(q, k, v, g, beta, cu_seqlens, num_seqs, total_tokens, num_heads,
                              head_dim_k, head_dim_v, scale, lower_bound, nullptr, state_pool,
-                             KDA_STATE_F32, num_slots, slot_indices, checkpoints, checkpoint_tokens, out,
-                             workspace, workspace_bytes, stream);
+                             KDA_STATE_F32, num_slots, 0, slot_indices, checkpoints,
+                             checkpoint_tokens, out, workspace, workspace_bytes, stream);
 }
 
 size_t kda_prefill_checkpoint_slots(int32_t num_seqs, int64_t total_tokens,
@@ -510,8 +532,8 @@ int kda_prefill_chain(const int32_t* cu_seqlens, int32_t num_seqs, int64_t total
 
 int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, const void* beta,
                   void* state_pool, int32_t state_dtype, int64_t num_slots,
-                  const int32_t* slot_indices, int32_t rows, int32_t num_heads,
-                  int32_t head_dim_k, int32_t head_dim_v, float scale,
+                  int64_t slot_stride, const int32_t* slot_indices, int32_t rows,
+                  int32_t num_heads, int32_t head_dim_k, int32_t head_dim_v, float scale,
                   const kda_frontend* frontend, void* out, hipStream_t stream) {
   kda::FrontEnd fe;
   if (const int st = frontend_args(frontend, "kda_decode", &fe)) return st;
@@ -524,6 +546,8 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, co
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: rows=%d num_heads=%d num_slots=%lld",
                 rows, num_heads, (long long)num_slots);
   if (!std::isfinite(scale)) return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: scale not finite");
+  if (const int st = check_slot_stride("kda_decode", num_heads, state_dtype, &slot_stride))
+    return st;
   if ((int64_t)rows * num_heads * 4 > (int64_t)UINT32_MAX)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_decode: rows * num_heads too large");
   if (rows == 0) return ok();
@@ -548,6 +572,7 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, co
   a.pool = state_pool;
   a.slots = slot_indices;
   a.num_slots = num_slots;
+  a.slot_stride = slot_stride;
   a.rows = rows;
   a.num_heads = num_heads;
   a.scale = scale;
@@ -569,8 +594,8 @@ int kda_decode(const void* q, const void* k, const void* v, const void* g, const
                void* state_pool, int32_t state_dtype, int64_t num_slots,
                const int32_t* slot_indices, int32_t rows, int32_t num_heads, int32_t head_dim_k,
                int32_t head_dim_v, float scale, void* out, hipStream_t stream) {
-  return kda_decode_ex(q, k, v, g, beta, state_pool, state_dtype, num_slots, slot_indices, rows,
-                       num_heads, head_dim_k, head_dim_v, scale, nullptr, out, stream);
+  return kda_decode_ex(q, k, v, g, beta, state_pool, state_dtype, num_slots, 0, slot_indices,
+                       rows, num_heads, head_dim_k, head_dim_v, scale, nullptr, out, stream);
 }
 
 }  // extern "C"

@@ -85,7 +85,7 @@ __device__ __forceinline__ StateRef prefill_pool_state(const PrefillArgs& a, int
   const int64_t s = a.slots[n];
   StateRef r;
   if (s >= 0 && s < a.num_slots) {
-    const int64_t off = (s * a.num_heads + h) * (int64_t)(kHeadDim * kHeadDim);
+    const int64_t off = s * a.slot_stride + h * (kHeadDim * kHeadDim);
     r.bf16 = a.pool_bf16 != 0;
     r.p = r.bf16 ? static_cast<void*>(static_cast<uint16_t*>(a.pool) + off)
                  : static_cast<void*>(static_cast<float*>(a.pool) + off);

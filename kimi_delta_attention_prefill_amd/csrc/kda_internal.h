@@ -58,6 +58,7 @@ struct PrefillArgs {
   int32_t pool_bf16;      // the pool holds bf16 states (read widened, written RNE)
   const int32_t* slots;   // int32 [N]
   int64_t num_slots;
+  int64_t slot_stride;    // elements from one slot to the next (>= H * 128 * 128)
   // Checkpoints: the state after every `ckpt_tokens` tokens (a multiple of
   // 32) of each sequence; the j-th (j >= 1) of sequence n goes to slot
   // n + floor(cu[n] / ckpt_tokens) + j - 1 of ckpt [., H, 128, 128].
@@ -75,6 +76,7 @@ struct DecodeArgs {
   void* pool;             // fp32 or bf16 [num_slots, H, 128, 128]
   const int32_t* slots;   // int32 [rows]
   int64_t num_slots;
+  int64_t slot_stride;    // elements from one slot to the next (>= H * 128 * 128)
   int32_t rows;
   int32_t num_heads;
   float scale;

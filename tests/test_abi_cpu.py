@@ -147,10 +147,10 @@ def test_decode_frontend_host_validation():
     E = _lib.KDA_ERR_INVALID_ARGUMENT
     P = ctypes.c_void_p
 
-    def call(fe):
+    def call(fe, stride=0, dtype=0):
         ref = None if fe is None else ctypes.byref(fe._c())
-        return lib.kda_decode_ex(P(16), P(16), P(16), P(16), P(16), P(16), 0, 4, P(16), 0, 8, 128,
-                                 128, 1.0, ref, P(16), None)
+        return lib.kda_decode_ex(P(16), P(16), P(16), P(16), P(16), P(16), dtype, 4, stride, P(16),
+                                 0, 8, 128, 128, 1.0, ref, P(16), None)
 
     assert call(None) == 0                                       # rows = 0: a no-op
     assert call(kda.FrontEnd()) == 0
@@ -163,6 +163,15 @@ def test_decode_frontend_host_validation():
     assert call(kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-5.0)) == 0
     assert call(kda.FrontEnd(normalize_qk=True, norm_eps=-1e-6)) == E
     assert call(kda.FrontEnd(normalize_qk=True, norm_eps=float("nan"))) == E
+    # slot stride: 0 (dense) or >= H * 128 * 128 elements and a multiple of 16 bytes
+    dense = 8 * 128 * 128
+    assert call(None, stride=dense) == 0 and call(None, stride=3 * dense) == 0
+    assert call(None, stride=dense + 4) == 0                     # fp32: 16 bytes
+    assert call(None, stride=dense + 4, dtype=1) == E            # bf16: 8 bytes
+    assert "slot_stride" in kda.last_error()
+    assert call(None, stride=dense + 8, dtype=1) == 0
+    assert call(None, stride=dense - 4) == E                     # overlapping slots
+    assert call(None, stride=-dense) == E
 
 
 def test_auto_route_and_workspace():
@@ -276,6 +285,17 @@ def test_pool_prefill_host_validation():
     assert call(ck=0x20008, ckt=64) == E
     assert call(out=None) == E
     assert call(N=0, q=None, cu=None, idx=None, out=None) == 0
+
+    def call_ex(stride, dtype=0, N=0):
+        return lib.kda_prefill_pool_ex(P(16), P(16), P(16), P(16), P(16), P(16), N, 4, 1, 128,
+                                       128, 1.0, -5.0, None, P(0x10000), dtype, 4, stride,
+                                       P(16), None, 0, P(16), None, 0, None)
+
+    dense = 128 * 128
+    assert call_ex(0) == 0 and call_ex(dense) == 0 and call_ex(2 * dense + 4) == 0
+    assert call_ex(dense + 4, dtype=1) == E and "slot_stride" in kda.last_error()
+    assert call_ex(dense - 8) == E and call_ex(-1) == E
+    assert call_ex(0, dtype=2) == E
     assert kda.checkpoint_slots(3, 1000, 64) == 3 + 1000 // 64 + 1
     assert kda.checkpoint_slots(1, 8192, 64) == 1 + 128 + 1
     assert kda.checkpoint_slots(1, 10, 0) == 0
@@ -300,7 +320,7 @@ int main(void) {
   if (kda_prefill_plan(1, 8192, 8, -5.0f, 256, KDA_ROUTE_AUTO, &plan) != KDA_OK) return 2;
   if (plan.route != KDA_ROUTE_SPLIT || plan.windows < 3) return 3;
   /* invalid arguments are rejected on the host, before any device work */
-  if (kda_decode_ex(0, 0, 0, 0, 0, 0, KDA_STATE_F32, 1, 0, 1, 8, 128, 128, 1.0f, &fe, 0, 0)
+  if (kda_decode_ex(0, 0, 0, 0, 0, 0, KDA_STATE_F32, 1, 0, 0, 1, 8, 128, 128, 1.0f, &fe, 0, 0)
       != KDA_ERR_INVALID_ARGUMENT) return 4;
   if (kda_last_error()[0] == '\0') return 5;
   printf("ok %d\n", (int)plan.windows);
