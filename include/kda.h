@@ -134,7 +134,9 @@ typedef enum {
 } kda_anchor_mode;
 
 /* What kda_prefill will launch for a problem (a pure host function of the
- * sizes, the bound and the device's compute-unit count). */
+ * sizes, the bound and the device's compute-unit count).  With the input
+ * front-end (the _ex entry points) the CHUNK route always runs two 64-column
+ * slices per (sequence, head), whatever dv_split says. */
 typedef struct {
   int32_t route;       /* kda_prefill_route actually used                  */
   int32_t anchor_mode; /* kda_anchor_mode (chunk route only)               */

@@ -65,37 +65,81 @@ struct PrepSmem {
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
   float X[16][17];             // A21 T11
   float Mq[CH][CH + 1];        // causal Mqk, FP32 (masked)
+  // the next chunk's q, k, g rows and value columns as fetched straight from
+  // global memory (16-byte slots, row-major, unpadded)
+  uint4 stage[3 * CH * 16 + CH * DVS / 8];
 };
 
-// Step 1: stage the chunk [t0, t0 + L) of (sequence, head h): q, k, g rows,
-// the value columns [col0, col0 + DVS) and beta.  Tokens >= L are zero.
-template <int DVS, bool FE>
-__device__ __forceinline__ void load_chunk(PrepSmem<DVS>& sm, const PrefillArgs& a, int t0, int L,
-                                           int h, int col0, int tid, int nthreads) {
-  const int H = a.num_heads;
-  for (int e = tid; e < CH * 16; e += nthreads) {
-    const int t = e >> 4, c8 = (e & 15) * 8;
-    uint4 wq = {0, 0, 0, 0}, wk = {0, 0, 0, 0}, wg = {0, 0, 0, 0};
-    if (t < L) {
-      const int64_t off = ((int64_t)(t0 + t) * H + h) * D + c8;
-      wq = *reinterpret_cast<const uint4*>(a.q + off);
-      wk = *reinterpret_cast<const uint4*>(a.k + off);
-      wg = *reinterpret_cast<const uint4*>(a.g + off);
-    }
-    *reinterpret_cast<uint4*>(&sm.qraw[t][c8]) = wq;
-    *reinterpret_cast<uint4*>(&sm.kraw[t][c8]) = wk;
-    *reinterpret_cast<uint4*>(&sm.graw[t][c8]) = wg;
+// Step 1: the chunk [t0, t0 + L) of (sequence, head h) -- q, k, g rows, the
+// value columns [col0, col0 + DVS) and beta -- in two halves, so that a block
+// can fetch the next chunk while it works on the current one.  fetch_chunk
+// issues direct global-to-LDS loads into sm.stage (no registers are held; a
+// wave's 16-byte load fills 64 consecutive slots, lane i the i-th) and the
+// chunk's beta into a register; stage_chunk, after every wave's loads have
+// landed, moves them into the padded arrays the later steps read, with tokens
+// >= L as zeros.  256 threads.
+typedef __attribute__((address_space(3))) void lds_void;
+
+template <int DVS>
+__device__ __forceinline__ void fetch_chunk(PrepSmem<DVS>& sm, uint16_t& beta_raw,
+                                            const PrefillArgs& a, int t0, int L, int h,
+                                            int col0, int tid) {
+  const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int slot0 = 64 * wave + 256 * i, e = slot0 + lane;
+    const int t = min(e >> 4, L - 1);   // rows past the end repeat the last one; zeroed when staged
+    const int64_t off = ((int64_t)(t0 + t) * H + h) * D + (e & 15) * 8;
+    __builtin_amdgcn_global_load_lds(a.q + off, (lds_void*)&sm.stage[slot0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.k + off, (lds_void*)&sm.stage[CH * 16 + slot0], 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(a.g + off, (lds_void*)&sm.stage[2 * CH * 16 + slot0], 16, 0,
+                                     0);
   }
-  for (int e = tid; e < CH * (DVS / 8); e += nthreads) {
-    const int t = e / (DVS / 8), c8 = (e % (DVS / 8)) * 8;
-    uint4 wv = {0, 0, 0, 0};
-    if (t < L)
-      wv = *reinterpret_cast<const uint4*>(a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + c8);
-    *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = wv;
+#pragma unroll
+  for (int i = 0; i < DVS / 64; ++i) {
+    const int slot0 = 64 * wave + 256 * i, e = slot0 + lane;
+    const int t = min(e / (DVS / 8), L - 1);
+    const uint16_t* gp = a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + (e % (DVS / 8)) * 8;
+    __builtin_amdgcn_global_load_lds(gp, (lds_void*)&sm.stage[3 * CH * 16 + slot0], 16, 0, 0);
+  }
+  beta_raw = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
+}
+
+// Wait for this wave's direct loads; the caller's next barrier makes every
+// wave's visible.
+__device__ __forceinline__ void fetch_wait() {
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited for
+}
+
+// x with every word cleared unless `keep` (a mask, not a select of sources)
+__device__ __forceinline__ uint4 keep_if(uint4 x, bool keep) {
+  const uint32_t m = keep ? 0xffffffffu : 0u;
+  x.x &= m;
+  x.y &= m;
+  x.z &= m;
+  x.w &= m;
+  return x;
+}
+
+template <int DVS, bool FE>
+__device__ __forceinline__ void stage_chunk(PrepSmem<DVS>& sm, uint16_t beta_raw,
+                                            const FrontEnd& fe, int L, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i, t = e >> 4, c8 = (e & 15) * 8;
+    const bool live = t < L;
+    *reinterpret_cast<uint4*>(&sm.qraw[t][c8]) = keep_if(sm.stage[e], live);
+    *reinterpret_cast<uint4*>(&sm.kraw[t][c8]) = keep_if(sm.stage[CH * 16 + e], live);
+    *reinterpret_cast<uint4*>(&sm.graw[t][c8]) = keep_if(sm.stage[2 * CH * 16 + e], live);
+  }
+#pragma unroll
+  for (int i = 0; i < DVS / 64; ++i) {
+    const int e = tid + 256 * i, t = e / (DVS / 8), c8 = (e % (DVS / 8)) * 8;
+    *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = keep_if(sm.stage[3 * CH * 16 + e], t < L);
   }
   if (tid < CH) {
-    const float b = tid < L ? bf16_to_f32(a.beta[(int64_t)(t0 + tid) * H + h]) : 0.f;
-    sm.beta[tid] = FE && tid < L ? frontend_beta(a.fe, b) : b;
+    const float b = tid < L ? bf16_to_f32(beta_raw) : 0.f;
+    sm.beta[tid] = FE && tid < L ? frontend_beta(fe, b) : b;
   }
 }
 
@@ -286,25 +330,22 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
 // Mqk entry (zero above the diagonal).  256 threads.
 template <int DVS, class EmitMqk>
 __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk&& emit_mqk) {
-  for (int e = tid; e < 8 * 256; e += 256) {
-    const int tile = e >> 8, q4 = tile & 3;
-    const int ln = (e >> 2) & 63, i = e & 3;
+  const int ln = tid >> 2, i = tid & 3;
+  auto sum4 = [&](int p) __attribute__((always_inline)) {
+    return ((sm.part[0][p][ln][i] + sm.part[1][p][ln][i]) + sm.part[2][p][ln][i]) +
+           sm.part[3][p][ln][i];
+  };
+#pragma unroll
+  for (int q4 = 0; q4 < 4; ++q4) {   // 16x16 quadrants (0,0) (1,0) (1,1) (0,1); the last is zero
     const int mt = (q4 == 1 || q4 == 2) ? 1 : 0;
     const int nt = (q4 == 2 || q4 == 3) ? 1 : 0;
     const int r = 16 * mt + 4 * (ln >> 4) + i, s = 16 * nt + (ln & 15);
-    float val = 0.f;
-    if (q4 != 3) {
-      const int p = (tile < 4 ? 0 : 3) + q4;
-      val = ((sm.part[0][p][ln][i] + sm.part[1][p][ln][i]) + sm.part[2][p][ln][i]) +
-            sm.part[3][p][ln][i];
-    }
-    if (tile < 4) {
-      const float m = s <= r ? val : 0.f;
-      sm.Mq[r][s] = m;
-      emit_mqk(r, s, m);
-    } else {
-      sm.A[r][s] = s < r ? sm.beta[r] * val : 0.f;
-    }
+    const float mq = q4 == 3 ? 0.f : sum4(q4);       // Mqk partial tiles 0..2
+    const float ak = q4 == 3 ? 0.f : sum4(3 + q4);   // Akk partial tiles 3..5
+    const float m = s <= r ? mq : 0.f;
+    sm.Mq[r][s] = m;
+    emit_mqk(r, s, m);
+    sm.A[r][s] = s < r ? sm.beta[r] * ak : 0.f;
   }
 }
 

@@ -336,8 +336,9 @@ int run_prefill(const char* fn, kda::PrefillArgs a, float lower_bound, void* wor
     e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
   else if (plan.route == KDA_ROUTE_SPLIT)
     e = kda::launch_prefill_split(a, plan.anchor_mode, plan.dv_split, workspace, stream);
-  else
-    e = kda::launch_prefill_chunk(a, plan.anchor_mode, plan.dv_split, stream);
+  else   // with the input front-end the fused route runs 64-column blocks only
+    e = kda::launch_prefill_chunk(a, plan.anchor_mode,
+                                  kda::frontend_active(a.fe) ? 2 : plan.dv_split, stream);
   if (e == hipErrorNotSupported)
     return fail(KDA_ERR_UNSUPPORTED, "%s: route %d is not available", fn, plan.route);
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: launch failed: %s", fn, hipGetErrorString(e));

@@ -112,11 +112,19 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
           dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = S[mt][nt][i];
   };
 
+  // The next chunk's inputs are fetched (straight into LDS) while the current
+  // one is prepared and consumed, so their load latency is off the per-chunk
+  // path.
+  uint16_t beta_raw = 0;
+  if (bos < eos) fetch_chunk(ps, beta_raw, a, bos, min(CH, eos - bos), h, col_base, tid);
   for (int t0 = bos; t0 < eos; t0 += CH) {
     const int L = min(CH, eos - t0);
-    __syncthreads();  // the previous chunk's chain is done with the LDS operands
-    load_chunk<64 * NT, FE>(ps, a, t0, L, h, col_base, tid, 256);
+    fetch_wait();
+    __syncthreads();  // the chunk has landed; the previous chain is done with the LDS operands
+    stage_chunk<DVS, FE>(ps, beta_raw, a.fe, L, tid);
     __syncthreads();
+    if (t0 + CH < eos)
+      fetch_chunk(ps, beta_raw, a, t0 + CH, min(CH, eos - t0 - CH), h, col_base, tid);
     gate_prefix<MODE, 64 * NT, FE>(ps, a.fe, C, L, tid);
     if (FE) qk_norms(ps, a, tid);
     __syncthreads();
@@ -295,13 +303,13 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
   if (a.num_seqs <= 0) return hipSuccess;
   if (dv_split != 1 && dv_split != 2) return hipErrorInvalidValue;
   const int nt = dv_split == 1 ? 2 : 1;
-  // data-dependent anchors: 64-column blocks only (the 128-column variant
-  // would exceed the register file)
-  if (anchor_mode == 2 && dv_split != 2) return hipErrorInvalidValue;
+  // data-dependent anchors and the input front-end: 64-column blocks only
+  // (their 128-column variants would exceed the register file)
+  if ((anchor_mode == 2 || frontend_active(a.fe)) && dv_split != 2) return hipErrorInvalidValue;
   if (frontend_active(a.fe)) {
-    if (anchor_mode == 0) return nt == 2 ? launch_variant<0, 2, true>(a, s) : launch_variant<0, 1, true>(a, s);
+    if (anchor_mode == 0) return launch_variant<0, 1, true>(a, s);
     if (anchor_mode == 2) return launch_variant<2, 1, true>(a, s);
-    return nt == 2 ? launch_variant<1, 2, true>(a, s) : launch_variant<1, 1, true>(a, s);
+    return launch_variant<1, 1, true>(a, s);
   }
   if (anchor_mode == 0) return nt == 2 ? launch_variant<0, 2, false>(a, s) : launch_variant<0, 1, false>(a, s);
   if (anchor_mode == 2) return launch_variant<2, 1, false>(a, s);
