@@ -170,27 +170,34 @@ __device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const PrefillArgs& a
   }
 }
 
-// Step 2: inclusive gate prefix per channel (threads 0..127), chunk decay,
-// and for the fixed anchor 2^{G_L - C}.
+// Step 2: inclusive gate prefix per channel, chunk decay, and for the fixed
+// anchor 2^{G_L - C}.  256 threads: wave w takes channels 32w..32w+31, lane l
+// channel 32w + l%32 over tokens 16(l/32)..+15; the second half adds the first
+// half's total (a cross-lane read), so each lane's serial sum is 16 long.
 // Padding tokens (t >= L) add nothing: a transformed gate of their zero input
 // would not be zero.
 template <int MODE, int DVS, bool FE>
 __device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const FrontEnd& fe, float C, int L,
                                             int tid) {
-  if (tid < D) {
-    float acc = 0.f;
+  const int lane = tid & 63, c = 32 * (tid >> 6) + (lane & 31), hf = lane >> 5;
+  float pre[16];
+  float acc = 0.f;
 #pragma unroll
-    for (int t = 0; t < CH; ++t) {
-      if (FE) {
-        if (t < L) acc += frontend_gate(fe, bf16_to_f32(sm.graw[t][tid]));
-      } else {
-        acc += bf16_to_f32(sm.graw[t][tid]);
-      }
-      sm.G[t][tid] = acc * kLog2e;
-    }
-    const float GL = acc * kLog2e;
-    sm.dec[tid] = fast_exp2(GL);
-    sm.EL[tid] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
+  for (int j = 0; j < 16; ++j) {
+    const int t = 16 * hf + j;
+    float x = bf16_to_f32(sm.graw[t][c]);
+    if (FE) x = t < L ? frontend_gate(fe, x) : 0.f;
+    acc += x;
+    pre[j] = acc;
+  }
+  const float other = __shfl_xor(acc, 32);   // the first half's total, seen by the second half
+  const float base = hf ? other : 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sm.G[16 * hf + j][c] = (base + pre[j]) * kLog2e;
+  if (hf) {
+    const float GL = (base + acc) * kLog2e;
+    sm.dec[c] = fast_exp2(GL);
+    sm.EL[c] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
   }
 }
 

@@ -150,6 +150,53 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
                           *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
                         });
     __syncthreads();
+    // ---- the state chain, first part (this wave's 16 * NT value columns):
+    // W = Kg S and O = Qg S need only the operands written so far, so their
+    // MFMAs run here, beside the latency-bound reduction and inverse.
+    f16x8 Sb[4][NT];
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          Sb[p][nt][i] = static_cast<_Float16>(S[2 * p][nt][i]);
+          Sb[p][nt][4 + i] = static_cast<_Float16>(S[2 * p + 1][nt][i]);
+        }
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+    f32x4 W[2][NT], O[2][NT];
+#pragma unroll
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) { W[mt][nt] = z; O[mt][nt] = z; }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) {
+        const f16x8 akg = *reinterpret_cast<const f16x8*>(&sm.Kg[16 * mt + l16][32 * p + 8 * g4]);
+        const f16x8 aqg = *reinterpret_cast<const f16x8*>(&sm.Qg[16 * mt + l16][32 * p + 8 * g4]);
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) {
+          W[mt][nt] = mfma_f16(akg, Sb[p][nt], W[mt][nt]);
+          O[mt][nt] = mfma_f16(aqg, Sb[p][nt], O[mt][nt]);
+        }
+      }
+    // V' = b (V - W) as hi + lo fp16 B operands (K = token, permuted)
+    f16x8 Vh[NT], Vl[NT];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = 16 * mt + 4 * g4 + i;
+          const float vp =
+              ps.beta[t] * (bf16_to_f32(ps.vraw[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
+          _Float16 hh, ll;
+          split_f16(vp, hh, ll);
+          Vh[nt][4 * mt + i] = hh;
+          Vl[nt][4 * mt + i] = ll;
+        }
     reduce_pairs(ps, tid, [&](int r, int s, float m) {
       sm.Mqk[r][kslot(s)] = static_cast<_Float16>(m);
     });
@@ -162,52 +209,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
     }
     __syncthreads();
 
-    // ---- the state chain on this wave's 16 * NT value columns
+    // ---- the rest of the state chain on this wave's 16 * NT value columns
     {
-      f16x8 Sb[4][NT];
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            Sb[p][nt][i] = static_cast<_Float16>(S[2 * p][nt][i]);
-            Sb[p][nt][4 + i] = static_cast<_Float16>(S[2 * p + 1][nt][i]);
-          }
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-      f32x4 W[2][NT], O[2][NT];
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) { W[mt][nt] = z; O[mt][nt] = z; }
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) {
-          const f16x8 akg = *reinterpret_cast<const f16x8*>(&sm.Kg[16 * mt + l16][32 * p + 8 * g4]);
-          const f16x8 aqg = *reinterpret_cast<const f16x8*>(&sm.Qg[16 * mt + l16][32 * p + 8 * g4]);
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) {
-            W[mt][nt] = mfma_f16(akg, Sb[p][nt], W[mt][nt]);
-            O[mt][nt] = mfma_f16(aqg, Sb[p][nt], O[mt][nt]);
-          }
-        }
-      // V' = b (V - W) as hi + lo fp16 B operands (K = token, permuted)
-      f16x8 Vh[NT], Vl[NT];
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * mt + 4 * g4 + i;
-            const float vp =
-                ps.beta[t] * (bf16_to_f32(ps.vraw[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
-            _Float16 hh, ll;
-            split_f16(vp, hh, ll);
-            Vh[nt][4 * mt + i] = hh;
-            Vl[nt][4 * mt + i] = ll;
-          }
       f32x4 U[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
