@@ -61,7 +61,7 @@ struct PrepSmem {
   float beta[CH];
   float rq[CH], rk[CH];        // q/k L2-norm scales per token (1 without the front-end norm)
   float part[4][6][64][4];     // split-K partials of the six Mqk/Akk tiles
-  float A[CH][CH + 1];         // Diag(b) stril(Akk), FP32
+  float At[CH][CH + 4];        // (Diag(b) stril(Akk))^T, FP32; rows 16-byte aligned
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
   float X[16][17];             // A21 T11
   float Mq[CH][CH + 1];        // causal Mqk, FP32 (masked)
@@ -333,8 +333,8 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
 
 // Step 3b: sum the four split-K partials in a fixed order, mask the causal
 // triangles by select (masked anchored entries may be inf or NaN) and scale
-// Akk by beta.  Writes sm.Mq (FP32) and sm.A; emit_mqk(r, s, value) sees every
-// Mqk entry (zero above the diagonal).  256 threads.
+// Akk by beta.  Writes sm.Mq (FP32) and sm.At (A transposed); emit_mqk(r, s,
+// value) sees every Mqk entry (zero above the diagonal).  256 threads.
 template <int DVS, class EmitMqk>
 __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk&& emit_mqk) {
   const int ln = tid >> 2, i = tid & 3;
@@ -352,15 +352,17 @@ __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk
     const float m = s <= r ? mq : 0.f;
     sm.Mq[r][s] = m;
     emit_mqk(r, s, m);
-    sm.A[r][s] = s < r ? sm.beta[r] * ak : 0.f;
+    sm.At[s][r] = s < r ? sm.beta[r] * ak : 0.f;
   }
 }
 
-// Steps 4a-4c: T = (I + A)^{-1} in FP32 into sm.Tf.  The 16x16 diagonal
-// blocks by forward substitution (wave 0, one column per lane), then
-// T21 = -T22 A21 T11 and T12 = 0.  256 threads; contains barriers.
-template <int DVS>
-__device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid) {
+// Steps 4a-4c: T = (I + A)^{-1}.  The 16x16 diagonal blocks in FP32 by
+// forward substitution (wave 0, one column per lane), then T21 = -T22 A21 T11
+// and T12 = 0; the last step hands every entry (i, m) of each quadrant to
+// emit_t(row, col, value) (the caller stores the MFMA operand).  256 threads;
+// contains barriers.
+template <int DVS, class EmitT>
+__device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid, EmitT&& emit_t) {
   const int wave = tid >> 6, lane = tid & 63;
   if (wave == 0 && lane < 32) {
     const int base = 16 * (lane >> 4), m = lane & 15;
@@ -368,9 +370,14 @@ __device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j)
+    for (int j = 0; j < 16; ++j) {
+      // column j of the block below the diagonal: row j of At, four 16-byte reads
+      f32x4 c[4];
 #pragma unroll
-      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-sm.A[base + i][base + j], x[j], x[i]);
+      for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(&sm.At[base + j][base + 4 * q]);
+#pragma unroll
+      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[i >> 2][i & 3], x[j], x[i]);
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i) sm.Tf[base + i][base + m] = x[i];
   }
@@ -379,7 +386,7 @@ __device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid) {
     const int i = tid >> 4, m = tid & 15;
     float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc = fmaf(sm.A[16 + i][j], sm.Tf[j][m], acc);
+    for (int j = 0; j < 16; ++j) acc = fmaf(sm.At[j][16 + i], sm.Tf[j][m], acc);
     sm.X[i][m] = acc;
   }
   __syncthreads();
@@ -388,8 +395,10 @@ __device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid) {
     float acc = 0.f;
 #pragma unroll
     for (int j = 0; j < 16; ++j) acc = fmaf(sm.Tf[16 + i][16 + j], sm.X[j][m], acc);
-    sm.Tf[16 + i][m] = -acc;
-    sm.Tf[i][16 + m] = 0.f;
+    emit_t(i, m, sm.Tf[i][m]);
+    emit_t(16 + i, 16 + m, sm.Tf[16 + i][16 + m]);
+    emit_t(16 + i, m, -acc);
+    emit_t(i, 16 + m, 0.f);
   }
 }
 

@@ -201,12 +201,9 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
       sm.Mqk[r][kslot(s)] = static_cast<_Float16>(m);
     });
     __syncthreads();
-    invert_unit_lower(ps, tid);
-    __syncthreads();
-    for (int e = tid; e < CH * CH; e += 256) {
-      const int r = e >> 5, s = e & 31;
-      sm.T[r][kslot(s)] = static_cast<_Float16>(ps.Tf[r][s]);
-    }
+    invert_unit_lower(ps, tid, [&](int r, int s, float t) {
+      sm.T[r][kslot(s)] = static_cast<_Float16>(t);
+    });
     __syncthreads();
 
     // ---- the rest of the state chain on this wave's 16 * NT value columns
