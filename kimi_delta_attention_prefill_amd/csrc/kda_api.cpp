@@ -254,8 +254,11 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
   if (route == KDA_ROUTE_AUTO) {
     // Few recurrences: one block per (sequence, head) would idle most of the
     // chip and serialise chunk preparation, so prepare all chunks in
-    // parallel first.  Many recurrences: keep everything in one pass.
-    route = 8 * units <= (int64_t)num_cus ? KDA_ROUTE_SPLIT : KDA_ROUTE_CHUNK;
+    // parallel first.  Many recurrences: keep everything in one pass.  The
+    // split chain runs 8 blocks per recurrence, two per CU; measured on 256
+    // CUs it wins up to 1.5 such rounds (96 units: 1.29 vs 1.50 ms at T=8192)
+    // and loses from 2 (128 units: 1.78 vs 1.52 ms).
+    route = 8 * units <= 3 * (int64_t)num_cus ? KDA_ROUTE_SPLIT : KDA_ROUTE_CHUNK;
   }
   if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
