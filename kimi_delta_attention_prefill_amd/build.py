@@ -35,10 +35,11 @@ def _flags():
             f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
-# Per-source extra flags.  The split-route chain keeps its FP32 state in the
-# MFMA accumulators for the whole sequence and also updates it with VALU
+# Per-source extra flags.  The chunk-route kernels keep their FP32 state in
+# the MFMA accumulators for the whole sequence and also update it with VALU
 # ops; accumulators in AGPRs would cost two register moves per touch.
-_EXTRA = {"prefill_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+_EXTRA = {"prefill_split.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+          "prefill_chunk.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str) -> str:

@@ -64,7 +64,6 @@ struct PrepSmem {
   float At[CH][CH + 4];        // (Diag(b) stril(Akk))^T, FP32; rows 16-byte aligned
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
   float X[16][17];             // A21 T11
-  float Mq[CH][CH + 1];        // causal Mqk, FP32 (masked)
   // the next chunk's q, k, g rows and value columns as fetched straight from
   // global memory (16-byte slots, row-major, unpadded)
   uint4 stage[3 * CH * 16 + CH * DVS / 8];
@@ -333,8 +332,8 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
 
 // Step 3b: sum the four split-K partials in a fixed order, mask the causal
 // triangles by select (masked anchored entries may be inf or NaN) and scale
-// Akk by beta.  Writes sm.Mq (FP32) and sm.At (A transposed); emit_mqk(r, s,
-// value) sees every Mqk entry (zero above the diagonal).  256 threads.
+// Akk by beta.  Writes sm.At (A transposed); emit_mqk(r, s, value) sees every
+// Mqk entry (zero above the diagonal).  256 threads.
 template <int DVS, class EmitMqk>
 __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk&& emit_mqk) {
   const int ln = tid >> 2, i = tid & 3;
@@ -350,7 +349,6 @@ __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk
     const float mq = q4 == 3 ? 0.f : sum4(q4);       // Mqk partial tiles 0..2
     const float ak = q4 == 3 ? 0.f : sum4(3 + q4);   // Akk partial tiles 3..5
     const float m = s <= r ? mq : 0.f;
-    sm.Mq[r][s] = m;
     emit_mqk(r, s, m);
     sm.At[s][r] = s < r ? sm.beta[r] * ak : 0.f;
   }
