@@ -269,7 +269,9 @@ def main():
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
                 "unit": d["unit"], "frac": d["frac"], "traffic": d["traffic"],
-                "avg_launch_ms": d["mean_ms"], "median_launch_ms": d["median_ms"]}
+                "avg_launch_ms": d["mean_ms"], "median_launch_ms": d["median_ms"],
+                "scope": ("prefill, the headline metric (longest single prefill kernel); the "
+                          "decode kernel, the step's longest, is under decode.roofline")}
     for key in ("algorithmic_flop_per_launch", "algorithmic_bytes_per_launch", "mfma_tflops"):
         if key in d:
             roofline[key] = d[key]
