@@ -71,10 +71,10 @@ def stored_traffic(kernel: str):
     return rec.get("bytes_per_launch")
 
 
-def stored_mfma():
+def stored_mfma(workload: str):
     """Per-kernel MFMA counters (busy % of SIMDs, executed MFMA TFLOP/s) from a
     committed rocprofv3 --pmc summary, or {} when missing or stale."""
-    path = os.path.join(ROOT, "profiles", "mfma_prefill_split_T8192_H8_decode_rows4096_f32.json")
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
     if not os.path.exists(path):
         return {}
     with open(path) as f:
@@ -108,13 +108,13 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / t / 1e9
 
 
-def cpu_baseline(min_seconds=10.0, max_runs=50):
+def cpu_baseline(config=1, min_seconds=10.0, max_runs=50):
     """The FP64 oracle on the whole prefill workload, repeated until about
     `min_seconds` of wall time have passed; reports the mean rate."""
     import oracle
     from kimi_delta_attention_prefill_amd.inputs import prefill_config
 
-    c = prefill_config(1)
+    c = prefill_config(config)
     threads = min(oracle.default_threads(), c.num_seqs * c.num_heads)
     runs, t0 = 0, time.perf_counter()
     while runs < max_runs and (runs == 0 or time.perf_counter() - t0 < min_seconds):
@@ -124,8 +124,8 @@ def cpu_baseline(min_seconds=10.0, max_runs=50):
     dt = (time.perf_counter() - t0) / runs
     return {"value": c.total_tokens * c.num_heads / dt, "unit": "tokens*heads/s",
             "cores": threads, "kind": "oracle",
-            "sample": (f"whole prefill workload ({c.num_seqs} x {c.total_tokens} tokens x "
-                       f"{c.num_heads} heads), FP64 token recurrence, {runs} runs, "
+            "sample": (f"whole prefill workload ({c.num_seqs} sequence(s), {c.total_tokens} "
+                       f"tokens in all, {c.num_heads} heads), FP64 token recurrence, {runs} runs, "
                        f"{dt:.3f} s wall each on {threads} threads")}
 
 
@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--prefill-config", type=int, choices=[0, 1, 2, 3], default=1,
+                    help="prefill workload: 1 (default) = 1 x 8192 x H=8, the headline; "
+                         "0 = 1 x 64 x H=2; 2 = 16 varlen x H=32; 3 = 4 x 8192 x H=64, lb=-8")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the KDA path needs no cross-GPU exchange and "
@@ -157,12 +160,13 @@ def main():
     kda.set_prefill_route(route)
 
     log("[bench] generating inputs")
-    pc = prefill_config(1)
+    pc = prefill_config(args.prefill_config)
+    tag = f"T{pc.total_tokens}_H{pc.num_heads}"
     to = lambda t: None if t is None else t.to(dev)
     P = dict(q=to(pc.q), k=to(pc.k), v=to(pc.v), g=to(pc.g), beta=to(pc.beta),
              cu=to(pc.cu_seqlens), s0=to(pc.initial_state))
     p_out = torch.empty_like(P["q"])
-    p_fin = torch.empty_like(P["s0"])
+    p_fin = torch.empty((pc.num_seqs, pc.num_heads, 128, 128), dtype=torch.float32, device=dev)
     dt = torch.float32 if args.decode_state == "f32" else torch.bfloat16
     dc = decode_config(args.decode_rows, dt)
     D = dict(q=to(dc.q), k=to(dc.k), v=to(dc.v), g=to(dc.g), beta=to(dc.beta),
@@ -238,13 +242,14 @@ def main():
         chain_tf = tokheads * CHAIN_FLOP_PER_TOKHEAD / (k2["mean_ms"] * 1e-3) / 1e12
         kernels["prefill_split_prep"] = dict(
             k1, bound="hbm", achieved=prep_gbs, peak=PEAK_HBM_GBPS, unit="GB/s",
-            frac=prep_gbs / PEAK_HBM_GBPS, traffic=stored_traffic("prefill_split_prep_T8192_H8"),
+            frac=prep_gbs / PEAK_HBM_GBPS, traffic=stored_traffic(f"prefill_split_prep_{tag}"),
             algorithmic_bytes_per_launch=tokheads * PREP_BYTES_PER_TOKHEAD,
             algorithmic_flop_per_launch=tokheads * PREP_FLOP_PER_TOKHEAD, mfma_tflops=prep_tf)
         windows = plan.windows
         launches = (["prefill_split_window_a", "prefill_split_window_c"]
                     if windows > 1 else ["prefill_split_chain"])
-        counters = stored_mfma()
+        counters = stored_mfma(
+            f"prefill_split_{tag}_decode_rows{args.decode_rows}_{args.decode_state}")
         if "prefill_split_prep" in counters:
             kernels["prefill_split_prep"]["mfma_counters"] = counters["prefill_split_prep"]
         serial_steps = (2 * plan.window_chunks if windows > 1 else chunks)
@@ -264,7 +269,7 @@ def main():
         tf = flops / (pre["mean_ms"] * 1e-3) / 1e12
         kernels[dom] = dict(pre, bound="mfma", achieved=tf, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                             frac=tf / PEAK_BF16_TFLOPS,
-                            traffic=stored_traffic(f"{dom}_T8192_H8"),
+                            traffic=stored_traffic(f"{dom}_{tag}"),
                             algorithmic_flop_per_launch=flops)
     d = kernels[dom]
     roofline = {"kernel": dom, "bound": d["bound"], "achieved": d["achieved"], "peak": d["peak"],
@@ -290,7 +295,9 @@ def main():
         "dtype": "bf16",
         "data": "synthetic",
         "config": {
-            "workload": (f"prefill 1x8192 tokens H=8 dk=dv=128 lb=-5 fp32 S0 + decode H=8 "
+            "workload": (f"prefill {pc.num_seqs} sequence(s), {pc.total_tokens} tokens, "
+                         f"H={pc.num_heads}, dk=dv=128, lb={pc.lower_bound:g}, "
+                         f"{'fp32' if pc.initial_state is not None else 'zero'} S0 + decode H=8 "
                          f"rows={args.decode_rows} {args.decode_state} state 4096-slot pool"),
             "prefill": {"num_seqs": pc.num_seqs, "seq_len": pc.total_tokens,
                         "num_heads": pc.num_heads, "lower_bound": pc.lower_bound,
@@ -321,7 +328,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         log("[bench] timing the FP64 oracle on the host")
-        result["cpu_baseline"] = cpu_baseline()
+        result["cpu_baseline"] = cpu_baseline(args.prefill_config)
     kda.set_prefill_route(kda.ROUTE_AUTO)
     print(json.dumps(result), flush=True)
 

@@ -5,6 +5,8 @@
       <stats_dir> holds a `rocprofv3 --kernel-trace --stats --output-format csv`
       run; writes profiles/kernel_trace_<workload>.md (per-kernel calls and
       average / min / max duration).
+  python profile_summaries.py trace-as <workload> <stats_dir> <command...>
+      the same for a bench run of another workload (bench.py --prefill-config).
   python profile_summaries.py mfma <pmc_dir> <stats_dir> <command...>
       a `rocprofv3 --pmc MfmaUtil MfmaFlopsF16 MfmaFlopsBF16` run of the bench
       command and a kernel-trace run (for durations); writes
@@ -60,9 +62,10 @@ def one(pattern):
     return hits[0]
 
 
-def trace(stats_dir, command):
+def trace(stats_dir, command, workload=WORKLOAD):
     rows = list(csv.DictReader(open(one(os.path.join(stats_dir, "**", "*kernel_stats.csv")))))
-    out = [f"# Kernel trace: bench.py default workload ({WORKLOAD})", "",
+    what = "default workload" if workload == WORKLOAD else "workload"
+    out = [f"# Kernel trace: bench.py {what} ({workload})", "",
            "Command:", "", "```", command, "```", "",
            "| kernel | calls | average us | min us | max us | share % |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -70,7 +73,7 @@ def trace(stats_dir, command):
                    f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
                    f"{float(r['Percentage']):.2f} |")
     out += ["", f"Kernel sources digest: `{source_digest()}`", ""]
-    path = os.path.join(ROOT, "profiles", f"kernel_trace_{WORKLOAD}.md")
+    path = os.path.join(ROOT, "profiles", f"kernel_trace_{workload}.md")
     open(path, "w").write("\n".join(out))
     print(path)
 
@@ -143,6 +146,8 @@ def mfma(pmc_dir, stats_dir, command):
 if __name__ == "__main__":
     if len(sys.argv) >= 4 and sys.argv[1] == "trace":
         trace(sys.argv[2], " ".join(sys.argv[3:]))
+    elif len(sys.argv) >= 5 and sys.argv[1] == "trace-as":
+        trace(sys.argv[3], " ".join(sys.argv[4:]), workload=sys.argv[2])
     elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
         mfma(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
     elif len(sys.argv) >= 5 and sys.argv[1] == "traffic":
