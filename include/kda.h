@@ -112,7 +112,9 @@ typedef enum {
   KDA_ROUTE_SPLIT = 2   /* same chunk math in two passes: all chunks are
                            prepared in parallel into the workspace, then a
                            short serial chain per (sequence, head) consumes
-                           them (few units, long sequences)                */
+                           them (few units: AUTO picks it up to 3/8 of the
+                           device's compute units in (sequence, head)
+                           units, 96 on MI355X)                            */
 } kda_prefill_route;
 
 /* Exponent handling of the chunk route's pairwise (Mqk, Akk) products,
