@@ -124,10 +124,13 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
 template <int MODE, bool FE>
 __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_split_prep(PrefillArgs a, float exp2C,
                                                           uint8_t* __restrict__ ws) {
-  __shared__ __align__(16) float Al[CH][36];   // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
-  __shared__ __align__(16) float Tl[CH][36];   // (I + A)^{-1}, lower triangle
+  // (b Kg)^T hi fragments [0, 8) and lo fragments [8, 16), parked until T is
+  // known; once they are back in registers the same bytes hold the FP32
+  // system and its inverse, so eight waves per compute unit still fit.
+  __shared__ __align__(16) f16x8 park[16][64];
   __shared__ __align__(16) float bl[CH];
-  __shared__ __align__(16) f16x8 xh_park[8][64];   // (b Kg)^T hi fragments, see below
+  float (*const Al)[36] = reinterpret_cast<float (*)[36]>(&park[0][0]);  // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
+  float (*const Tl)[36] = Al + CH;                                        // (I + A)^{-1}, lower triangle
   const int H = a.num_heads, N = a.num_seqs, T = a.total_tokens;
   // XCD-aware order: consecutive block indices go to the eight XCDs in turn,
   // so block b takes work item (b % 8) * per + b / 8 (items ordered head-major,
@@ -239,11 +242,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
 
   f32x4 acc[6] = {z, z, z, z, z, z};   // Mqk^T tiles (0,0) (0,1) (1,1), Akk^T tiles likewise
-  // (b Kg)^T A fragments per 16-channel tile wait for T: the hi parts in LDS,
-  // the lo parts in the record's U0 area, which is written last (each lane
-  // reads back only what it wrote).  Both in LDS would not fit eight waves
-  // per compute unit.
-  uint8_t* const xl_park = rec + kRecOffU0;
+  // (b Kg)^T A fragments per 16-channel tile wait for T in LDS (park).
 
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -382,14 +381,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
         xl[i] = (_Float16)w0[i];  xl[4 + i] = (_Float16)w1[i];
       }
       *reinterpret_cast<f16x8*>(rec + kRecOffKrT + ((2 * p + e) * 64 + lane) * 16) = kt;
-      xh_park[2 * p + e][lane] = xh;
-      *reinterpret_cast<f16x8*>(xl_park + ((2 * p + e) * 64 + lane) * 16) = xl;
+      park[2 * p + e][lane] = xh;
+      park[8 + 2 * p + e][lane] = xl;
     }
     __builtin_amdgcn_sched_barrier(0);
   }
 
   // Mqk fragments straight from the Mqk^T accumulators (rows s = 16a + 4g4 + i,
-  // column r = 16b + l16), causal mask by select; A = Diag(b) stril(Akk) to LDS.
+  // column r = 16b + l16), causal mask by select.
   {
     f16x8 m0, m1;
 #pragma unroll
@@ -399,9 +398,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
       m0[4 + i] = (_Float16)0.f;
       m1[i] = (_Float16)acc[1][i];
       m1[4 + i] = (_Float16)(s <= l16 ? acc[2][i] : 0.f);
-      Al[l16][s] = s < l16 ? beta[0] * acc[3][i] : 0.f;
-      Al[16 + l16][s] = beta[1] * acc[4][i];
-      Al[16 + l16][16 + s] = s < l16 ? beta[1] * acc[5][i] : 0.f;
     }
     *reinterpret_cast<f16x8*>(rec + kRecOffMqk + lane * 16) = m0;
     *reinterpret_cast<f16x8*>(rec + kRecOffMqk + (64 + lane) * 16) = m1;
@@ -410,18 +406,26 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
       bl[16 + l16] = beta[1];
     }
   }
-  // Everything the rest reads from memory is requested now, so that the
-  // inverse hides the latency: the parked (b Kg)^T fragments (once this
-  // wave's stores have completed: each lane reads back what it wrote), the
-  // value rows, and the previous chunk's keys and gates.
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
+  // The parked (b Kg)^T fragments back into registers; the barrier orders
+  // these reads before the system overwrites their bytes.
   f16x8 Xh[8], Xl[8];
 #pragma unroll
   for (int mc = 0; mc < 8; ++mc) {
-    Xh[mc] = xh_park[mc][lane];
-    Xl[mc] = *reinterpret_cast<const f16x8*>(xl_park + (mc * 64 + lane) * 16);
+    Xh[mc] = park[mc][lane];
+    Xl[mc] = park[8 + mc][lane];
   }
+  __syncthreads();
+  // A = Diag(b) stril(Akk) to LDS.
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int s = 4 * g4 + i;
+    Al[l16][s] = s < l16 ? beta[0] * acc[3][i] : 0.f;
+    Al[16 + l16][s] = beta[1] * acc[4][i];
+    Al[16 + l16][16 + s] = s < l16 ? beta[1] * acc[5][i] : 0.f;
+  }
+  // Everything the rest reads from memory is requested now, so that the
+  // inverse hides the latency: the value rows, and the previous chunk's keys
+  // and gates.
   u32x4 vw[4][2], kpw[4][2], gpw[4][2];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
@@ -499,9 +503,6 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     }
   }
 
-  // The parked fragments must have arrived before their areas are overwritten.
-  __builtin_amdgcn_s_waitcnt(0x0f70);   // vmcnt(0)
-  __builtin_amdgcn_sched_barrier(0);
 
   // U0 = T Diag(b) V per 16-column tile: V transposed by the one-hot product.
 #pragma unroll
