@@ -794,13 +794,18 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
         }
       __syncthreads();
     };
-    for (int c = 1; c <= nch; c += kAhead) {
+    // Whole triples, then the rest after the loop: a break inside the
+    // unrolled triple would give the loop a second way back to its header,
+    // and the wait counts for the first step's fragments would then assume
+    // they were loaded one step earlier instead of three.
+    int c = 1;
+    for (; c + 2 <= nch; c += kAhead) {
       step(std::integral_constant<int, 0>{}, c);
-      if (c + 1 > nch) break;
       step(std::integral_constant<int, 1>{}, c + 1);
-      if (c + 2 > nch) break;
       step(std::integral_constant<int, 2>{}, c + 2);
     }
+    if (c <= nch) step(std::integral_constant<int, 0>{}, c);
+    if (c + 1 <= nch) step(std::integral_constant<int, 1>{}, c + 1);
     return;
   }
 
@@ -871,13 +876,15 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       __syncthreads();
     };
     // steps 0..nch (the last one's U is never read)
-    for (int c = 0; c <= nch; c += kAhead) {
+    // whole triples, then the rest (as in the output wave)
+    int c = 0;
+    for (; c + 2 <= nch; c += kAhead) {
       step(std::integral_constant<int, 0>{}, c);
-      if (c + 1 > nch) break;
       step(std::integral_constant<int, 1>{}, c + 1);
-      if (c + 2 > nch) break;
       step(std::integral_constant<int, 2>{}, c + 2);
     }
+    if (c <= nch) step(std::integral_constant<int, 0>{}, c);
+    if (c + 1 <= nch) step(std::integral_constant<int, 1>{}, c + 1);
     return;
   }
 
@@ -1042,13 +1049,15 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
     load_a(A[IA], c + 1 + kAhead);
     __syncthreads();
   };
-  for (int c = 1; c <= nch; c += kAhead) {
+  // whole triples, then the rest (as in the output wave)
+  int c = 1;
+  for (; c + 2 <= nch; c += kAhead) {
     step(std::integral_constant<int, 1>{}, c);
-    if (c + 1 > nch) break;
     step(std::integral_constant<int, 2>{}, c + 1);
-    if (c + 2 > nch) break;
     step(std::integral_constant<int, 0>{}, c + 2);
   }
+  if (c <= nch) step(std::integral_constant<int, 1>{}, c);
+  if (c + 1 <= nch) step(std::integral_constant<int, 2>{}, c + 1);
   if (job.s_final) {
 #pragma unroll
     for (int t = 0; t < kNT; ++t)
