@@ -711,11 +711,25 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   auto xacc = [&](const uint8_t* base, int idx) __attribute__((always_inline)) {
     return *reinterpret_cast<const f32x4*>(base + (idx * 64 + lane) * 16);
   };
-  // Record of chunk c (an empty range for c outside [0, nch)).
-  auto rec = [&](int c) __attribute__((always_inline)) {
-    const bool in = c >= 0 && c < nch;
-    return make_buffer(ws + ((slot0 + (in ? c : 0)) * H + h) * kRecBytes,
-                       in ? (uint32_t)kRecBytes : 0u);
+  // Each operand stream of a wave reads the records in chunk order, one
+  // chunk per load, so it keeps a running address and advances it by the
+  // chunk stride: recomputing ((slot0 + c) H + h) kRecBytes per load costs
+  // about 20 scalar instructions (64-bit multiplies), and a chain step is
+  // bound by instruction issue.  A chunk past the run is an empty range (its
+  // loads return zeros without touching memory).
+  struct RecStream {
+    const uint8_t* p;
+    int c;
+  };
+  const int64_t rec_stride = (int64_t)H * kRecBytes;
+  auto rec_stream = [&]() __attribute__((always_inline)) {
+    return RecStream{ws + (slot0 * H + h) * kRecBytes, 0};
+  };
+  auto next_rec = [&](RecStream& st) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = make_buffer(st.p, st.c < nch ? (uint32_t)kRecBytes : 0u);
+    st.p += rec_stride;
+    ++st.c;
+    return r;
   };
   auto ld16 = [&](__amdgpu_buffer_rsrc_t r, int off) __attribute__((always_inline)) {
     return __builtin_amdgcn_raw_buffer_load_b128(r, (uint32_t)off, 0, 0);
@@ -734,8 +748,9 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       return;
     }
     QOps q[kAhead];
-    auto load_q = [&](QOps& o, int c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t r = rec(c);
+    RecStream qs = rec_stream();
+    auto load_q = [&](QOps& o) __attribute__((always_inline)) {   // the stream's next chunk
+      const __amdgpu_buffer_rsrc_t r = next_rec(qs);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -744,9 +759,12 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       }
     };
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) load_q(q[i], i);
+    for (int i = 0; i < kAhead; ++i) load_q(q[i]);   // chunks 0 .. kAhead-1
     __syncthreads();   // P_0 published
     __syncthreads();   // step 0
+    // output rows of chunk c-1 at step c, advanced by one chunk per step
+    const uint16_t* optr = a.out + ((int64_t)tok0 * H + h) * D;
+    int ot0 = tok0;
     // step c >= 1: O_{c-1}, whose fragments sit in set (c-1) % 3
     auto step = [&](auto I_const, int c) __attribute__((always_inline)) {
       constexpr int I = decltype(I_const)::value;
@@ -773,12 +791,12 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
           O[t][mt] = mfma_f16(ul, o.amq[mt], O[t][mt]);
         }
       }
-      load_q(q[I], c - 1 + kAhead);
+      load_q(q[I]);   // chunk c - 1 + kAhead
       // rows t >= L of a final partial chunk fall outside the range and are dropped
-      const int t0 = tok0 + CH * (c - 1);
-      const int L = min(CH, eos - t0);
-      const __amdgpu_buffer_rsrc_t orsrc = make_buffer(
-          a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
+      const int L = min(CH, eos - ot0);
+      const __amdgpu_buffer_rsrc_t orsrc = make_buffer(optr, (uint32_t)(((L - 1) * H + 1) * D * 2));
+      optr += (int64_t)CH * H * D;
+      ot0 += CH;
 #pragma unroll
       for (int t = 0; t < kNT; ++t)
 #pragma unroll
@@ -812,8 +830,9 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   if (wave == 2) {
     // ------------------------------------------------------------------ U
     WOps w[kAhead];
-    auto load_w = [&](WOps& o, int c) __attribute__((always_inline)) {
-      const __amdgpu_buffer_rsrc_t r = rec(c);
+    RecStream wst = rec_stream();
+    auto load_w = [&](WOps& o) __attribute__((always_inline)) {   // the stream's next chunk
+      const __amdgpu_buffer_rsrc_t r = next_rec(wst);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
         o.wh[mt] = gfrag(r, kRecOffWh, mt);
@@ -826,7 +845,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       *reinterpret_cast<f32x2*>(decs(c) + 2 * lane) = o.dec;
     };
 #pragma unroll
-    for (int i = 0; i < kAhead; ++i) load_w(w[i], i);
+    for (int i = 0; i < kAhead; ++i) load_w(w[i]);   // chunks 0 .. kAhead-1
     put_dec(w[0], 0);                 // decays of chunk 0, used in step 1
     f16x8 Uh[kNT], Ul[kNT];
 #pragma unroll
@@ -856,7 +875,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
           U[t][mt] = mfma_f16(o.wh[mt], Ul[t], U[t][mt]);
           U[t][mt] = mfma_f16(o.wl[mt], Uh[t], U[t][mt]);
         }
-      load_w(w[I], c + kAhead);
+      load_w(w[I]);   // chunk c + kAhead
       put_dec(w[(I + 1) % kAhead], c + 1);   // applied at the end of step c+1
       uint8_t* exw = exch(c);
 #pragma unroll
@@ -908,8 +927,9 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       }
   AOps A[kAhead];
   BOps B[kAhead];
-  auto load_a = [&](AOps& o, int c) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = rec(c);
+  RecStream ast = rec_stream(), bst = rec_stream();
+  auto load_a = [&](AOps& o) __attribute__((always_inline)) {   // the A stream's next chunk
+    const __amdgpu_buffer_rsrc_t r = next_rec(ast);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
@@ -920,8 +940,8 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       }
     }
   };
-  auto load_b = [&](BOps& o, int c) __attribute__((always_inline)) {
-    const __amdgpu_buffer_rsrc_t r = rec(c);
+  auto load_b = [&](BOps& o) __attribute__((always_inline)) {   // the B stream's next chunk
+    const __amdgpu_buffer_rsrc_t r = next_rec(bst);
 #pragma unroll
     for (int m = 0; m < 4; ++m) o.ak[m] = gfrag(r, kRecOffKrT, 4 * hs + m);
   };
@@ -962,14 +982,14 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   // holds chunk k's Kr^T and decays (consumed in step k+1).
 #pragma unroll
   for (int i = 0; i < kAhead; ++i) {
-    load_a(A[i], i);
-    load_b(B[i], i);
+    load_a(A[i]);   // chunks 0 .. kAhead-1 of both streams
+    load_b(B[i]);
   }
   publish(A[0], -1);               // fp16 S_{-1} (unused) and P_0 from the initial state
-  load_a(A[0], kAhead);
+  load_a(A[0]);                    // chunk kAhead
   __syncthreads();                 // P_0 published
   publish(A[1], 0);                // step 0: S_0 = S_{-1}; P_1
-  load_a(A[1], 1 + kAhead);
+  load_a(A[1]);                    // chunk 1 + kAhead
   // The decay of chunk c is applied to S_c once S_c is published (fp16 copy
   // and P_{c+1} use the undecayed state), so that step c+1 starts with its
   // MFMAs.  Never after the last step: the final state is undecayed.
@@ -1043,10 +1063,10 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       ck_next += ck_per;
       ++ck_row;
     }
-    load_b(B[IB], c - 1 + kAhead);
+    load_b(B[IB]);                                    // chunk c - 1 + kAhead
     publish(A[IA], c);                                // unused past the end
     if (c < nch) decay(dv);
-    load_a(A[IA], c + 1 + kAhead);
+    load_a(A[IA]);                                    // chunk c + 1 + kAhead
     __syncthreads();
   };
   // whole triples, then the rest (as in the output wave)
