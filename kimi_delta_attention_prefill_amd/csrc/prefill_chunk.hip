@@ -64,6 +64,38 @@ struct FusedSmem {
   _Float16 Mqk[CH][TP];        // causal Mqk       [token][token, permuted]
 };
 
+// Blocks start in index order as compute units free up, and a block holds a
+// compute unit for its whole sequence, so the sequence a block works on is
+// taken in longest-first order (ties by index): in a varlen batch a long
+// sequence otherwise may only start in the last round of blocks and end
+// alone.  Returns the sequence of rank r by (length descending, index
+// ascending); `tmp` is LDS scratch of at least N + 1 ints, free on entry and
+// on return.  256 threads; contains barriers.
+constexpr int kLongestFirstMaxSeqs = 256;
+
+__device__ __forceinline__ int longest_first_sequence(const PrefillArgs& a, int r, int* tmp,
+                                                      int tid) {
+  const int N = a.num_seqs;
+  for (int i = tid; i < N; i += 256) {
+    const int b = clamp_offset(a.cu_seqlens[i], a.total_tokens);
+    tmp[i] = max(b, clamp_offset(a.cu_seqlens[i + 1], a.total_tokens)) - b;
+  }
+  __syncthreads();
+  for (int i = tid; i < N; i += 256) {
+    const int li = tmp[i];
+    int rank = 0;
+    for (int m = 0; m < N; ++m) {
+      const int lm = tmp[m];
+      rank += (lm > li || (lm == li && m < i)) ? 1 : 0;
+    }
+    if (rank == r) tmp[N] = i;   // the ranks are a permutation: exactly one i
+  }
+  __syncthreads();
+  const int n = tmp[N];
+  __syncthreads();
+  return n;
+}
+
 template <int MODE, int NT, bool FE>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float exp2C) {
   constexpr int DVS = 64 * NT;
@@ -72,8 +104,14 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
   PrepSmem<DVS>& ps = sm.p;
 
   const int H = a.num_heads;
-  const int slice = blockIdx.x, h = blockIdx.y, n = blockIdx.z;
+  const int slice = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the sequence of rank blockIdx.z, longest first (the split-K partials'
+  // area is not in use yet)
+  int* const rank_tmp = reinterpret_cast<int*>(&ps.part[0][0][0][0]);
+  const int n = (a.num_seqs > 1 && a.num_seqs <= kLongestFirstMaxSeqs)
+                    ? longest_first_sequence(a, blockIdx.z, rank_tmp, tid)
+                    : (int)blockIdx.z;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int col_base = slice * DVS;
   const int colw = wave * 16 * NT;          // first column of this wave, within the slice

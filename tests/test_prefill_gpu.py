@@ -102,6 +102,20 @@ def test_ragged_lengths(dev, route, lb):
     compare(case, o, f)
 
 
+@pytest.mark.parametrize("nseq", [256, 257])
+def test_many_sequences_fused(dev, nseq):
+    """Many short sequences on the fused route.  Up to 256 sequences each
+    block takes its sequence in longest-first order (ties broken by index;
+    most lengths here are shared by many sequences), above that in index
+    order; every sequence's outputs and state must land in its own rows
+    either way, zero-length sequences included."""
+    rng = np.random.default_rng(1000 + nseq)
+    lengths = [int(x) for x in rng.choice([0, 5, 32, 33, 40, 64, 70], size=nseq)]
+    case = make_prefill_case(lengths, 2, -5.0, 0.02, seed=nseq, name=f"many{nseq}")
+    o, f = run_gpu(case, kda.ROUTE_CHUNK, dev)
+    compare(case, o, f)
+
+
 @pytest.mark.parametrize("route", ROUTES)
 def test_config1_full(dev, route):
     case = prefill_config(1)
