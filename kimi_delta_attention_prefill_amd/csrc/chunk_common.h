@@ -48,13 +48,20 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
+// One chunk's bf16 inputs in LDS: q, k, g rows padded to RP, and the value
+// columns [col0, col0 + DVS).  Padding tokens (t >= L) are zero.
+template <int DVS>
+struct ChunkRaw {
+  uint16_t q[CH][RP];
+  uint16_t k[CH][RP];
+  uint16_t g[CH][RP];
+  uint16_t v[CH][DVS];
+};
+
 // LDS used by the preparation steps.  DVS = value columns staged.
 template <int DVS>
 struct PrepSmem {
-  uint16_t qraw[CH][RP];       // bf16 chunk inputs (padding tokens are zero)
-  uint16_t kraw[CH][RP];
-  uint16_t graw[CH][RP];
-  uint16_t vraw[CH][DVS];
+  ChunkRaw<DVS> raw[2];        // the chunk in work and the next one, landing
   float G[CH][GP];             // log2-domain inclusive gate prefix
   float EL[D];                 // fixed anchor: 2^{G_L - C}
   float dec[D];                // 2^{G_L}: chunk decay of each key row
@@ -64,42 +71,46 @@ struct PrepSmem {
   float At[CH][CH + 4];        // (Diag(b) stril(Akk))^T, FP32; rows 16-byte aligned
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
   float X[16][17];             // A21 T11
-  // the next chunk's q, k, g rows and value columns as fetched straight from
-  // global memory (16-byte slots, row-major, unpadded)
-  uint4 stage[3 * CH * 16 + CH * DVS / 8];
 };
 
 // Step 1: the chunk [t0, t0 + L) of (sequence, head h) -- q, k, g rows, the
-// value columns [col0, col0 + DVS) and beta -- in two halves, so that a block
-// can fetch the next chunk while it works on the current one.  fetch_chunk
-// issues direct global-to-LDS loads into sm.stage (no registers are held; a
-// wave's 16-byte load fills 64 consecutive slots, lane i the i-th) and the
-// chunk's beta into a register; stage_chunk, after every wave's loads have
-// landed, moves them into the padded arrays the later steps read, with tokens
-// >= L as zeros.  256 threads.
+// value columns [col0, col0 + DVS) and beta -- so that a block can fetch the
+// next chunk while it works on the current one.  fetch_chunk issues
+// range-checked buffer loads straight into the padded rows of `cr` (no
+// registers are held; a wave's 4-byte load fills 256 consecutive bytes of
+// LDS, lane i the i-th word, i.e. one q/k/g row or 256 / (2 DVS) value rows),
+// and the chunk's beta into a register.  Rows t >= L lie outside the range
+// and land as zeros, so no later pass has to clear them.  256 threads.
 typedef __attribute__((address_space(3))) void lds_void;
 
 template <int DVS>
-__device__ __forceinline__ void fetch_chunk(PrepSmem<DVS>& sm, uint16_t& beta_raw,
+__device__ __forceinline__ void fetch_chunk(ChunkRaw<DVS>& cr, uint16_t& beta_raw,
                                             const PrefillArgs& a, int t0, int L, int h,
                                             int col0, int tid) {
   const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
+  const int64_t base = ((int64_t)t0 * H + h) * D;
+  const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
+  const uint32_t row_bytes = (uint32_t)H * D * 2;
+  const __amdgpu_buffer_rsrc_t rq = make_buffer(a.q + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rk = make_buffer(a.k + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rg = make_buffer(a.g + base, rows_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int slot0 = 64 * wave + 256 * i, e = slot0 + lane;
-    const int t = min(e >> 4, L - 1);   // rows past the end repeat the last one; zeroed when staged
-    const int64_t off = ((int64_t)(t0 + t) * H + h) * D + (e & 15) * 8;
-    __builtin_amdgcn_global_load_lds(a.q + off, (lds_void*)&sm.stage[slot0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a.k + off, (lds_void*)&sm.stage[CH * 16 + slot0], 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(a.g + off, (lds_void*)&sm.stage[2 * CH * 16 + slot0], 16, 0,
-                                     0);
+  for (int i = 0; i < CH / 4; ++i) {   // wave w: rows w, w + 4, ...
+    const int t = wave + 4 * i;
+    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)lane * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)&cr.q[t][0], 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&cr.k[t][0], 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)&cr.g[t][0], 4, off, 0, 0, 0);
   }
+  constexpr int kRowsPerLoad = 128 / DVS;            // value rows per 256-byte load
+  constexpr int kLanesPerRow = 64 / kRowsPerLoad;
 #pragma unroll
-  for (int i = 0; i < DVS / 64; ++i) {
-    const int slot0 = 64 * wave + 256 * i, e = slot0 + lane;
-    const int t = min(e / (DVS / 8), L - 1);
-    const uint16_t* gp = a.v + ((int64_t)(t0 + t) * H + h) * D + col0 + (e % (DVS / 8)) * 8;
-    __builtin_amdgcn_global_load_lds(gp, (lds_void*)&sm.stage[3 * CH * 16 + slot0], 16, 0, 0);
+  for (int i = 0; i < CH / (4 * kRowsPerLoad); ++i) {
+    const int r0 = (wave + 4 * i) * kRowsPerLoad;    // first row of this load
+    const int t = r0 + lane / kLanesPerRow;
+    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)col0 * 2 + (uint32_t)(lane % kLanesPerRow) * 4;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&cr.v[r0][0], 4, off, 0, 0, 0);
   }
   beta_raw = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
 }
@@ -110,32 +121,11 @@ __device__ __forceinline__ void fetch_wait() {
   __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited for
 }
 
-// x with every word cleared unless `keep` (a mask, not a select of sources)
-__device__ __forceinline__ uint4 keep_if(uint4 x, bool keep) {
-  const uint32_t m = keep ? 0xffffffffu : 0u;
-  x.x &= m;
-  x.y &= m;
-  x.z &= m;
-  x.w &= m;
-  return x;
-}
-
+// The chunk's beta (zero for padding tokens), through the front-end's
+// transform when it is compiled in.
 template <int DVS, bool FE>
-__device__ __forceinline__ void stage_chunk(PrepSmem<DVS>& sm, uint16_t beta_raw,
-                                            const FrontEnd& fe, int L, int tid) {
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = tid + 256 * i, t = e >> 4, c8 = (e & 15) * 8;
-    const bool live = t < L;
-    *reinterpret_cast<uint4*>(&sm.qraw[t][c8]) = keep_if(sm.stage[e], live);
-    *reinterpret_cast<uint4*>(&sm.kraw[t][c8]) = keep_if(sm.stage[CH * 16 + e], live);
-    *reinterpret_cast<uint4*>(&sm.graw[t][c8]) = keep_if(sm.stage[2 * CH * 16 + e], live);
-  }
-#pragma unroll
-  for (int i = 0; i < DVS / 64; ++i) {
-    const int e = tid + 256 * i, t = e / (DVS / 8), c8 = (e % (DVS / 8)) * 8;
-    *reinterpret_cast<uint4*>(&sm.vraw[t][c8]) = keep_if(sm.stage[3 * CH * 16 + e], t < L);
-  }
+__device__ __forceinline__ void stage_beta(PrepSmem<DVS>& sm, uint16_t beta_raw,
+                                           const FrontEnd& fe, int L, int tid) {
   if (tid < CH) {
     const float b = tid < L ? bf16_to_f32(beta_raw) : 0.f;
     sm.beta[tid] = FE && tid < L ? frontend_beta(fe, b) : b;
@@ -146,14 +136,15 @@ __device__ __forceinline__ void stage_chunk(PrepSmem<DVS>& sm, uint16_t beta_raw
 // token of the staged chunk; eight threads per token, 16 channels each.
 // Needs 256 threads; runs in the same phase as gate_prefix.
 template <int DVS>
-__device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const PrefillArgs& a, int tid) {
+__device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
+                                         const PrefillArgs& a, int tid) {
   const int t = tid >> 3, part = tid & 7;
   float sq2 = 0.f, sk2 = 0.f;
   if (a.fe.normalize_qk) {
 #pragma unroll
     for (int c = 0; c < 16; ++c) {
-      const float qv = bf16_to_f32(sm.qraw[t][16 * part + c]);
-      const float kv = bf16_to_f32(sm.kraw[t][16 * part + c]);
+      const float qv = bf16_to_f32(cr.q[t][16 * part + c]);
+      const float kv = bf16_to_f32(cr.k[t][16 * part + c]);
       sq2 = fmaf(qv, qv, sq2);
       sk2 = fmaf(kv, kv, sk2);
     }
@@ -176,7 +167,8 @@ __device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const PrefillArgs& a
 // Padding tokens (t >= L) add nothing: a transformed gate of their zero input
 // would not be zero.
 template <int MODE, int DVS, bool FE>
-__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const FrontEnd& fe, float C, int L,
+__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
+                                            const FrontEnd& fe, float C, int L,
                                             int tid) {
   const int lane = tid & 63, c = 32 * (tid >> 6) + (lane & 31), hf = lane >> 5;
   float pre[16];
@@ -184,7 +176,7 @@ __device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const FrontEnd& f
 #pragma unroll
   for (int j = 0; j < 16; ++j) {
     const int t = 16 * hf + j;
-    float x = bf16_to_f32(sm.graw[t][c]);
+    float x = bf16_to_f32(cr.g[t][c]);
     if (FE) x = t < L ? frontend_gate(fe, x) : 0.f;
     acc += x;
     pre[j] = acc;
@@ -216,7 +208,8 @@ struct PairOps {
 // (both <= 1) so the caller can form Kg, Qg and Kr.  The six lower tiles of
 // Mqk and Akk (as partial sums over this wave's channels) go to sm.part.
 template <int MODE, int DVS, bool FE, class Emit>
-__device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillArgs& a, float C,
+__device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
+                                              const PrefillArgs& a, float C,
                                               float exp2C, int wave, int lane, Emit&& emit) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int cb = 32 * wave, cl = 8 * g4;
@@ -226,8 +219,8 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const PrefillAr
     const int t = l16 + 16 * half;
     const f32x4 G0 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl]);
     const f32x4 G1 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl + 4]);
-    const uint4 qw = *reinterpret_cast<const uint4*>(&sm.qraw[t][cb + cl]);
-    const uint4 kw = *reinterpret_cast<const uint4*>(&sm.kraw[t][cb + cl]);
+    const uint4 qw = *reinterpret_cast<const uint4*>(&cr.q[t][cb + cl]);
+    const uint4 kw = *reinterpret_cast<const uint4*>(&cr.k[t][cb + cl]);
     f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1;
     const float rq = FE ? sm.rq[t] : 1.f, rk = FE ? sm.rk[t] : 1.f;
     if (MODE >= 1) {

@@ -150,23 +150,26 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
           dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = S[mt][nt][i];
   };
 
-  // The next chunk's inputs are fetched (straight into LDS) while the current
-  // one is prepared and consumed, so their load latency is off the per-chunk
-  // path.
+  // The next chunk's inputs are fetched (straight into the other of the two
+  // raw buffers) while the current one is prepared and consumed, so their
+  // load latency is off the per-chunk path.
   uint16_t beta_raw = 0;
-  if (bos < eos) fetch_chunk(ps, beta_raw, a, bos, min(CH, eos - bos), h, col_base, tid);
-  for (int t0 = bos; t0 < eos; t0 += CH) {
+  if (bos < eos) fetch_chunk(ps.raw[0], beta_raw, a, bos, min(CH, eos - bos), h, col_base, tid);
+  int buf = 0;
+  for (int t0 = bos; t0 < eos; t0 += CH, buf ^= 1) {
     const int L = min(CH, eos - t0);
+    const ChunkRaw<DVS>& cr = ps.raw[buf];
     fetch_wait();
-    __syncthreads();  // the chunk has landed; the previous chain is done with the LDS operands
-    stage_chunk<DVS, FE>(ps, beta_raw, a.fe, L, tid);
+    // The chunk has landed in raw[buf]; the previous chunk's steps are done
+    // with raw[buf ^ 1] and with the LDS operands.
     __syncthreads();
+    stage_beta<DVS, FE>(ps, beta_raw, a.fe, L, tid);
     if (t0 + CH < eos)
-      fetch_chunk(ps, beta_raw, a, t0 + CH, min(CH, eos - t0 - CH), h, col_base, tid);
-    gate_prefix<MODE, 64 * NT, FE>(ps, a.fe, C, L, tid);
-    if (FE) qk_norms(ps, a, tid);
+      fetch_chunk(ps.raw[buf ^ 1], beta_raw, a, t0 + CH, min(CH, eos - t0 - CH), h, col_base, tid);
+    gate_prefix<MODE, 64 * NT, FE>(ps, cr, a.fe, C, L, tid);
+    if (FE) qk_norms(ps, cr, a, tid);
     __syncthreads();
-    pair_products<MODE, 64 * NT, FE>(ps, a, C, exp2C, wave, lane,
+    pair_products<MODE, 64 * NT, FE>(ps, cr, a, C, exp2C, wave, lane,
                         [&](int t, int c0, const float* kv, const float* qv, const float* P,
                             const float* R) {
                           const int cb = c0 & ~31, cl = c0 & 31;
@@ -229,7 +232,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * mt + 4 * g4 + i;
           const float vp =
-              ps.beta[t] * (bf16_to_f32(ps.vraw[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
+              ps.beta[t] * (bf16_to_f32(cr.v[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
           _Float16 hh, ll;
           split_f16(vp, hh, ll);
           Vh[nt][4 * mt + i] = hh;
@@ -321,6 +324,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
 template <int MODE, int NT, bool FE>
 hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
   constexpr size_t bytes = sizeof(FusedSmem<64 * NT>);
+  static_assert(bytes <= 160 * 1024, "the fused kernel's LDS exceeds a compute unit's 160 KiB");
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_chunk_kernel<MODE, NT, FE>),
