@@ -14,7 +14,10 @@ preparation kernel (the longest single prefill kernel; the chain pass is
 three launches when one long sequence is cut into windows, reported under
 ``prefill.kernels.chain_pass``) against its roofline; ``decode``
 carries the decode kernel's HBM bandwidth against 8 TB/s and against a
-device-to-device copy timed in the same run.  ``cpu_baseline`` times the
+device-to-device copy timed in the same run.  ``prefill.cold_cache`` repeats the
+prefill with a 512 MiB write before each call (outside the timed region), so
+that its inputs start in HBM rather than in the last-level cache.
+``cpu_baseline`` times the
 FP64 oracle (test infrastructure) on the same prefill workload on the host.
 
 Prints one JSON line on stdout; progress goes to stderr.
@@ -42,6 +45,7 @@ CHAIN_FLOP_PER_TOKHEAD = 106496
 PREFILL_BYTES_PER_TOKHEAD = 1282    # q,k,v,g (4 x 256 B) + beta (2 B) + o (256 B)
 PREP_BYTES_PER_TOKHEAD = 1026       # the preparation pass reads q,k,v,g,beta
 STATE_BYTES = 128 * 128 * 4
+COLD_FLUSH_BYTES = 512 << 20        # written before each cold-cache prefill call
 DECODE_IO_BYTES_PER_ITEM = 1282
 
 
@@ -138,6 +142,9 @@ def main():
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold-steps", type=int, default=10,
+                    help="prefill calls timed after a 512 MiB write has flushed the caches "
+                         "(0 = skip)")
     ap.add_argument("--prefill-config", type=int, choices=[0, 1, 2, 3], default=1,
                     help="prefill workload: 1 (default) = 1 x 8192 x H=8, the headline; "
                          "0 = 1 x 64 x H=2; 2 = 16 varlen x H=32; 3 = 4 x 8192 x H=64, lb=-8")
@@ -180,7 +187,7 @@ def main():
     p_ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
     stream = torch.cuda.current_stream()
 
-    def step(ev=None):
+    def prefill_call(ev=None):
         rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
         rec(0)
         if two_pass:
@@ -196,6 +203,10 @@ def main():
                         out=p_out, workspace=p_ws, stream=stream)
             rec(1)
         rec(2)
+
+    def step(ev=None):
+        rec = (lambda i: ev[i].record(stream)) if ev is not None else (lambda i: None)
+        prefill_call(ev)
         kda.decode(D["q"], D["k"], D["v"], D["g"], D["beta"], D["pool"], D["slots"],
                    scale=dc.scale, out=d_out, stream=stream)
         rec(3)
@@ -219,6 +230,24 @@ def main():
     pre, dec = stats(pre_ms), stats(dec_ms)
     log(f"[bench] prefill {pre['mean_ms']:.4f} ms  decode {dec['mean_ms']:.4f} ms  "
         f"wall/step {1e3 * wall / args.steps:.4f} ms")
+    # Cold-cache prefill: a 512 MiB write before each call evicts the inputs
+    # from L2 and the last-level cache (the flush is outside the timed region).
+    cold = None
+    if args.cold_steps > 0:
+        log(f"[bench] timing {args.cold_steps} cold-cache prefill calls")
+        flush = torch.empty(COLD_FLUSH_BYTES, dtype=torch.uint8, device=dev)
+        cev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
+               for _ in range(args.cold_steps)]
+        for i in range(args.cold_steps):
+            flush.fill_(i & 0xFF)
+            prefill_call(cev[i])
+        torch.cuda.synchronize()
+        cold = dict(stats([e[0].elapsed_time(e[2]) for e in cev]),
+                    flush_bytes=COLD_FLUSH_BYTES)
+        if two_pass:
+            cold["kernels"] = {"prefill_split_prep": stats([e[0].elapsed_time(e[1]) for e in cev]),
+                               "chain_pass": stats([e[1].elapsed_time(e[2]) for e in cev])}
+        del flush
     log("[bench] timing a device-to-device copy")
     copy_gbs = copy_bandwidth(torch, dev)
 
@@ -313,7 +342,9 @@ def main():
                         mfma_frac=flops / (pre["mean_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
                         algorithmic_flop_per_call=flops, algorithmic_bytes_per_call=pbytes,
                         hbm_gbps=pbytes / (pre["mean_ms"] * 1e-3) / 1e9,
-                        us_per_chunk=1e3 * pre["mean_ms"] / chunks, kernels=kernels),
+                        us_per_chunk=1e3 * pre["mean_ms"] / chunks, kernels=kernels,
+                        cold_cache=(None if cold is None else dict(
+                            cold, tokheads_per_s=tokheads / (cold["mean_ms"] * 1e-3)))),
         "decode": dict(dec, value=achieved_gbs, unit="GB/s",
                        copy_gbps_same_run=copy_gbs, frac_of_copy=achieved_gbs / copy_gbs,
                        roofline={"bound": "hbm", "achieved": achieved_gbs,
