@@ -1171,27 +1171,29 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillA
 // columns, composed by the window_c block that runs window wt before its chain
 // (a few short steps: a kernel of their own cost more to launch than they
 // take).  Four waves, wave q owning rows 32q..32q+31 of a 16-column subtile;
-// P as fp16 hi + lo A fragments (the next window's requested while a step
-// computes), the current S as fp16 hi + lo B fragments in LDS (a step's
+// P as bf16 hi + lo A fragments (the next window's requested while a step
+// computes), the current S as bf16 hi + lo B fragments in LDS (a step's
 // accumulators are the next step's K step q), three products per pair, FP32
-// accumulation on B.  The result lands in LDS as FP32 [128][16 kNT] at the
+// accumulation on B.  bf16 rather than fp16: a state that has decayed far
+// below fp16's range (no writes over thousands of tokens) keeps its relative
+// precision, at ~16 significand bits per hi + lo pair.  The result lands in LDS as FP32 [128][16 kNT] at the
 // first exchange buffer and the fragments use the second; both are free
 // until the chain's first barrier.
 __device__ __forceinline__ void carry_to_lds(const WinView& wv, int n, int h, int tile, int wt,
                                              unsigned char* lds) {
-  f16x8* const xh = reinterpret_cast<f16x8*>(lds + kExchBytes);   // [kstep 4][lane 64]
-  f16x8* const xl = xh + 4 * 64;
+  bf16x8* const xh = reinterpret_cast<bf16x8*>(lds + kExchBytes);   // [kstep 4][lane 64]
+  bf16x8* const xl = xh + 4 * 64;
   float* const sin = reinterpret_cast<float*>(lds);
   const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   // rows of this lane's accumulator entries: tile 2q+e, row 16(2q+e) + 4g4 + i
   auto row_of = [&](int e, int i) __attribute__((always_inline)) { return 32 * q + 16 * e + 4 * g4 + i; };
   auto put_frags = [&](const float* v) __attribute__((always_inline)) {
-    f16x8 hi, lo;
+    bf16x8 hi, lo;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      _Float16 hh, ll;
-      split_f16(v[j], hh, ll);
+      __bf16 hh, ll;
+      split_bf16(v[j], hh, ll);
       hi[j] = hh;
       lo[j] = ll;
     }
@@ -1226,7 +1228,7 @@ __device__ __forceinline__ void carry_to_lds(const WinView& wv, int n, int h, in
     }
     for (int w = 1; w < wt; ++w) {
       __syncthreads();
-      f16x8 sh[4], sl[4];
+      bf16x8 sh[4], sl[4];
 #pragma unroll
       for (int p = 0; p < 4; ++p) {
         sh[p] = xh[p * 64 + lane];
@@ -1242,17 +1244,17 @@ __device__ __forceinline__ void carry_to_lds(const WinView& wv, int n, int h, in
       for (int e = 0; e < 2; ++e)
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          f16x8 ph, pl;
+          bf16x8 ph, pl;
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
-            _Float16 hh, ll;
-            split_f16(pf[e][p][j >> 2][j & 3], hh, ll);
+            __bf16 hh, ll;
+            split_bf16(pf[e][p][j >> 2][j & 3], hh, ll);
             ph[j] = hh;
             pl[j] = ll;
           }
-          acc[e] = mfma_f16(ph, sh[p], acc[e]);
-          acc[e] = mfma_f16(ph, sl[p], acc[e]);
-          acc[e] = mfma_f16(pl, sh[p], acc[e]);
+          acc[e] = mfma_bf16(ph, sh[p], acc[e]);
+          acc[e] = mfma_bf16(ph, sl[p], acc[e]);
+          acc[e] = mfma_bf16(pl, sh[p], acc[e]);
         }
       if (w + 1 < wt) load_p(pf, w + 1);
       __syncthreads();   // every wave has read this step's fragments

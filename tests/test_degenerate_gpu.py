@@ -1,0 +1,135 @@
+"""GPU parity on the method's degenerate and extreme inputs (through the C ABI).
+
+Every case is compared element by element with the FP64 oracle, whose own
+behaviour on these inputs is pinned by closed forms in the CPU tests:
+
+* beta = 0: no delta-rule write, so the state only decays per channel and
+  the output reads the decayed initial state;
+* g = 0, beta = 1 and one-hot orthonormal keys: each token overwrites the
+  state row its key selects with its value;
+* every gate at the lower bound: the anchored operand exponents reach the
+  ends of their range (16 |lb| log2 e = 115.4 with one anchor per chunk at
+  lb = -5; the 16-token split at lb = -8);
+* nearly identical keys under weak decay: the 32x32 triangular system's
+  entries approach beta, the hardest case for the chunk's FP32 inverse.
+"""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import kimi_delta_attention_prefill_amd as kda
+import oracle
+from kimi_delta_attention_prefill_amd.inputs import make_prefill_case
+from _checks import check_out, check_state
+
+pytestmark = pytest.mark.gpu
+
+ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT]
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+    kda.load()  # the HIP library must be present on a GPU host
+    return torch.device("cuda:0")
+
+
+def _run_and_compare(case, route, dev):
+    to = lambda t: None if t is None else t.to(dev)
+    _say(f"[gpu] degenerate {case.name} route={route} N={case.num_seqs} T={case.total_tokens} "
+         f"H={case.num_heads} lb={case.lower_bound}")
+    kda.set_prefill_route(route)
+    try:
+        o, f = kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                           to(case.cu_seqlens), scale=case.scale, lower_bound=case.lower_bound,
+                           initial_state=to(case.initial_state), final_state=True)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    ref_o, ref_f = oracle.prefill(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens,
+                                  case.scale, case.initial_state)
+    r1 = check_out(o.cpu(), ref_o)
+    r2 = check_state(f.cpu(), ref_f)
+    _say(f"   out {r1}  state {r2}")
+    return f.cpu(), ref_f
+
+
+def _beta_zero(lengths, H, lb, seed):
+    c = make_prefill_case(lengths, H, lb, 0.02, seed=seed, name=f"beta0_lb{lb}")
+    return dataclasses.replace(c, beta=torch.zeros_like(c.beta))
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_beta_zero_is_pure_decay(dev, route):
+    # weak gates, so that the decayed state stays well inside FP32's range
+    case = _beta_zero([200, 77, 32], 2, -0.25, seed=31)
+    f_gpu, _ = _run_and_compare(case, route, dev)
+    # closed form of the final state: S0 scaled per key channel by exp(sum of g)
+    cu = case.cu_seqlens.tolist()
+    for n in range(case.num_seqs):
+        gsum = case.g[cu[n]:cu[n + 1]].double().sum(0)                # [H, 128]
+        expect = torch.exp(gsum)[:, :, None] * case.initial_state[n].double()
+        err = (f_gpu[n].double() - expect).abs().max().item()
+        rms = expect.pow(2).mean().sqrt().item()
+        assert err <= 1e-2 * rms, (n, err, rms)
+
+
+def test_beta_zero_windows(dev):
+    """One long sequence on the split route cut into windows: the window maps
+    compose pure decays."""
+    case = _beta_zero([3000], 1, -0.015625, seed=32)   # the state survives all windows
+    plan = kda.plan(1, 3000, 1, -0.015625, 0, kda.ROUTE_SPLIT)
+    assert plan.windows > 1, plan
+    _run_and_compare(case, kda.ROUTE_SPLIT, dev)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_orthonormal_keys_overwrite_rows(dev, route):
+    T, H = 96, 2
+    base = make_prefill_case([T], H, -5.0, 0.02, seed=33, name="overwrite")
+    rng = np.random.default_rng(33)
+    k = torch.zeros(T, H, 128)
+    rows = np.stack([rng.permutation(128)[:T] for _ in range(H)], axis=1)   # [T, H], unique per head
+    for t in range(T):
+        for h in range(H):
+            k[t, h, rows[t, h]] = 1.0
+    case = dataclasses.replace(base, k=k.to(torch.bfloat16), g=torch.zeros_like(base.g),
+                               beta=torch.ones_like(base.beta))
+    f_gpu, _ = _run_and_compare(case, route, dev)
+    # each written row holds its token's value
+    v = case.v.double()
+    for h in range(H):
+        got = f_gpu[0, h].double()[rows[:, h]]                     # [T, 128]
+        err = (got - v[:, h]).abs().max().item()
+        assert err <= 1e-2 * v.pow(2).mean().sqrt().item(), (h, err)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("lb", [-5.0, -8.0])
+def test_all_gates_at_lower_bound(dev, route, lb):
+    base = make_prefill_case([100, 64], 2, lb, 0.02, seed=34, name=f"gates_at_lb{lb}")
+    case = dataclasses.replace(base, g=torch.full_like(base.g, lb))
+    _run_and_compare(case, route, dev)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+def test_nearly_identical_keys(dev, route):
+    T, H = 130, 2
+    base = make_prefill_case([T], H, -1.0, 0.02, seed=35, name="aligned_keys")
+    gen = torch.Generator().manual_seed(35)
+    k0 = torch.randn(1, H, 128, generator=gen)
+    k = k0 + 0.05 * torch.randn(T, H, 128, generator=gen)
+    k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    g = (-0.05 * torch.sigmoid(torch.randn(T, H, 128, generator=gen))).to(torch.bfloat16)
+    beta = torch.full((T, H), 0.95).to(torch.bfloat16)
+    case = dataclasses.replace(base, k=k, g=g, beta=beta)
+    _run_and_compare(case, route, dev)
