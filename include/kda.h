@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -374,6 +374,39 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g,
                   int32_t rows, int32_t num_heads, int32_t head_dim_k,
                   int32_t head_dim_v, float scale, const kda_frontend* frontend,
                   void* out, hipStream_t stream);
+
+/* -------------------------------------------------------- input checks --
+ * The device-side preconditions that the entry points document but do not
+ * check (a check would need a device read and a synchronisation, which a
+ * call captured into a hipGraph cannot have), tested on the device -- for
+ * tests and debugging, not for the hot path.  Each call enqueues on `stream`
+ * two small kernels that set its flags in `flags` (caller-owned device int32
+ * [KDA_CHECK_COUNT], 4-byte aligned) to 1 when the check fails anywhere and
+ * to 0 otherwise, leaving the other flags alone; the caller synchronises and
+ * reads them.  Host-side validation and return values as for the other entry
+ * points. */
+enum {
+  KDA_CHECK_CU_SEQLENS = 0,    /* cu[0] = 0, cu[n] <= cu[n+1], cu[N] = total_tokens */
+  KDA_CHECK_GATE_RANGE = 1,    /* lower_bound <= g <= 0, g not NaN (any g <= 0 with -inf) */
+  KDA_CHECK_BETA_RANGE = 2,    /* 0 <= beta <= 1 */
+  KDA_CHECK_QKV_FINITE = 3,    /* every q, k, v element finite */
+  KDA_CHECK_SLOTS_UNIQUE = 4,  /* the slot indices in [0, num_slots) pairwise distinct */
+  KDA_CHECK_COUNT = 5
+};
+
+/* kda_prefill's inputs (as kda_prefill takes them, plain gates and beta);
+ * writes flags KDA_CHECK_CU_SEQLENS .. KDA_CHECK_QKV_FINITE.  Pointers may be
+ * NULL only when num_seqs = 0 (cu_seqlens) or total_tokens = 0 (the rest). */
+int kda_check_prefill_inputs(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                             int64_t total_tokens, int32_t num_heads, float lower_bound,
+                             int32_t* flags, hipStream_t stream);
+
+/* Slot indices as kda_decode and kda_prefill_pool take them: negative or
+ * out-of-range entries are skipped rows (allowed), the others must be
+ * distinct.  Writes flag KDA_CHECK_SLOTS_UNIQUE; O(rows^2) comparisons. */
+int kda_check_slots(const int32_t* slot_indices, int32_t rows, int64_t num_slots,
+                    int32_t* flags, hipStream_t stream);
 
 /* ---------------------------------------------------------------- misc -- */
 /* Text describing the last non-OK return on the calling thread ("" if none). */

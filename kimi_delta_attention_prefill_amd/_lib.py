@@ -137,6 +137,10 @@ def load():
     lib.kda_decode_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i64, vp, i32, i32, i32, i32,
                                   f32, ctypes.POINTER(_FrontEnd), vp, vp]
     lib.kda_decode_ex.restype = ctypes.c_int
+    lib.kda_check_prefill_inputs.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, f32, vp, vp]
+    lib.kda_check_prefill_inputs.restype = ctypes.c_int
+    lib.kda_check_slots.argtypes = [vp, i32, i64, vp, vp]
+    lib.kda_check_slots.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_abi_version.argtypes = []
@@ -405,3 +409,32 @@ def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, strea
                                     _fe_ptr(frontend), _ptr(out),
                                     _stream(stream)))
     return out
+
+
+CHECK_NAMES = ("cu_seqlens", "gate_range", "beta_range", "qkv_finite", "slots_unique")
+
+
+def check_prefill_inputs(q, k, v, g, beta, cu_seqlens, *, lower_bound, stream=None):
+    """Device check of kda_prefill's documented preconditions (debugging and
+    tests; synchronises).  Returns {check name: True when it fails}."""
+    dev = q.device
+    T, H, _ = q.shape
+    N = cu_seqlens.numel() - 1
+    flags = torch.full((5,), -1, dtype=torch.int32, device=dev)
+    _check(load().kda_check_prefill_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                           _ptr(cu_seqlens), N, T, H, float(lower_bound),
+                                           _ptr(flags), _stream(stream)))
+    torch.cuda.synchronize(dev)
+    f = flags.cpu().tolist()
+    return {CHECK_NAMES[i]: bool(f[i]) for i in range(4)}
+
+
+def check_slots(slot_indices, num_slots, *, stream=None):
+    """Device check that the slot indices in [0, num_slots) are distinct
+    (debugging and tests; synchronises).  Returns True when they are not."""
+    flags = torch.full((5,), -1, dtype=torch.int32, device=slot_indices.device)
+    _check(load().kda_check_slots(_ptr(slot_indices), slot_indices.numel(), int(num_slots),
+                                  _ptr(flags), _stream(stream)))
+    torch.cuda.synchronize(slot_indices.device)
+    return bool(flags[4].item())
+

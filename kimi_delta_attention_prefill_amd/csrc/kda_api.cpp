@@ -228,6 +228,62 @@ const char* kda_last_error(void) { return g_last_error; }
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
+int kda_check_prefill_inputs(const void* q, const void* k, const void* v, const void* g,
+                             const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                             int64_t total_tokens, int32_t num_heads, float lower_bound,
+                             int32_t* flags, hipStream_t stream) {
+  if (num_seqs < 0 || total_tokens < 0 || num_heads < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT,
+                "kda_check_prefill_inputs: num_seqs=%d total_tokens=%lld num_heads=%d", num_seqs,
+                (long long)total_tokens, num_heads);
+  if (std::isnan(lower_bound) || !(lower_bound < 0.f))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_prefill_inputs: lower_bound must be < 0");
+  if (!flags || !aligned(flags, 4))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_prefill_inputs: flags NULL or misaligned");
+  if (!cu_seqlens || !aligned(cu_seqlens, 4))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_prefill_inputs: cu_seqlens NULL or misaligned");
+  if (total_tokens > 0) {
+    const void* need[] = {q, k, v, g, beta};
+    const char* names[] = {"q", "k", "v", "g", "beta"};
+    for (int i = 0; i < 5; ++i)
+      if (!need[i] || !aligned(need[i], 2))
+        return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_prefill_inputs: %s NULL or misaligned",
+                    names[i]);
+  }
+  kda::CheckPrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.g = static_cast<const uint16_t*>(g);
+  a.beta = static_cast<const uint16_t*>(beta);
+  a.cu_seqlens = cu_seqlens;
+  a.num_seqs = num_seqs;
+  a.total_tokens = total_tokens;
+  a.num_heads = num_heads;
+  a.lower_bound = lower_bound;
+  a.bounded = std::isfinite(lower_bound);
+  a.flags = flags;
+  const hipError_t e = kda::launch_check_prefill(a, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_check_prefill_inputs: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kda_check_slots(const int32_t* slot_indices, int32_t rows, int64_t num_slots,
+                    int32_t* flags, hipStream_t stream) {
+  if (rows < 0 || num_slots < 1)
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_slots: rows=%d num_slots=%lld", rows,
+                (long long)num_slots);
+  if (!flags || !aligned(flags, 4))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_slots: flags NULL or misaligned");
+  if (rows > 0 && (!slot_indices || !aligned(slot_indices, 4)))
+    return fail(KDA_ERR_INVALID_ARGUMENT, "kda_check_slots: slot_indices NULL or misaligned");
+  const hipError_t e = kda::launch_check_slots(slot_indices, rows, num_slots, flags, stream);
+  if (e != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_check_slots: launch failed: %s", hipGetErrorString(e));
+  return ok();
+}
+
 int kda_set_prefill_route(int32_t route) {
   if (route != KDA_ROUTE_AUTO && route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK &&
       route != KDA_ROUTE_SPLIT)

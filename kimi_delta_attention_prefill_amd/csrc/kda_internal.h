@@ -105,4 +105,19 @@ size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num
 // Decode step; `cols` = value columns per block (32, 64 or 128).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
 
+// Device-side precondition checks (debugging and tests).
+struct CheckPrefillArgs {
+  const uint16_t *q, *k, *v, *g, *beta;   // bf16 as kda_prefill takes them
+  const int32_t* cu_seqlens;              // [num_seqs + 1]
+  int32_t num_seqs;
+  int64_t total_tokens;
+  int32_t num_heads;
+  float lower_bound;
+  bool bounded;                           // lower_bound is finite
+  int32_t* flags;                         // [KDA_CHECK_COUNT]
+};
+hipError_t launch_check_prefill(const CheckPrefillArgs& a, hipStream_t s);
+hipError_t launch_check_slots(const int32_t* slots, int32_t rows, int64_t num_slots,
+                              int32_t* flags, hipStream_t s);
+
 }  // namespace kda

@@ -142,6 +142,39 @@ def test_decode_host_validation():
     assert _decode_raw(rows=0, q=None, pool=None, idx=None, out=None) == 0
 
 
+def test_check_entry_points_host_validation():
+    """kda_check_prefill_inputs / kda_check_slots reject bad arguments on the
+    host, before anything is enqueued (the fake pointers are never touched)."""
+    lib = kda.load()
+    E = _lib.KDA_ERR_INVALID_ARGUMENT
+    P = ctypes.c_void_p
+    A = P(0x1000)
+
+    def pre(N=1, T=64, H=2, lb=-5.0, flags=A, cu=A, q=A):
+        return lib.kda_check_prefill_inputs(q, A, A, A, A, cu, N, T, H, lb, flags, None)
+
+    assert pre(N=-1) == E
+    assert pre(T=-1) == E
+    assert pre(H=0) == E
+    assert pre(lb=0.0) == E
+    assert pre(lb=float("nan")) == E
+    assert pre(flags=None) == E
+    assert pre(flags=P(0x1002)) == E
+    assert pre(cu=None) == E
+    assert pre(q=None) == E
+    assert pre(q=P(0x1001)) == E
+    assert "kda_check_prefill_inputs" in kda.last_error()
+
+    def slots(rows=4, n=16, idx=A, flags=A):
+        return lib.kda_check_slots(idx, rows, n, flags, None)
+
+    assert slots(rows=-1) == E
+    assert slots(n=0) == E
+    assert slots(flags=None) == E
+    assert slots(idx=None) == E
+    assert slots(idx=P(0x1002)) == E
+
+
 def test_decode_frontend_host_validation():
     lib = kda.load()
     E = _lib.KDA_ERR_INVALID_ARGUMENT
