@@ -106,3 +106,14 @@ def test_bf16_pool(dev, route):
 def test_bf16_pool_windows(dev):
     run_case(dev, kda.ROUTE_SPLIT, [2000], 3, -8.0, [2], 4, 96, seed=612, windows=True,
              bf16_pool=True)
+
+
+def test_many_sequences_fused_pool(dev):
+    """40 sequences of shared, varied lengths on the fused route, whose blocks take
+    their sequence in longest-first order: every sequence's state must come from
+    and return to its own slot, and its checkpoints land in its own rows."""
+    rng = np.random.default_rng(613)
+    lengths = [int(x) for x in rng.choice([0, 31, 64, 65, 128, 200], size=40)]
+    slots = [int(s) for s in rng.permutation(64)[:40]]
+    slots[7] = -1                                   # one skipped sequence
+    run_case(dev, kda.ROUTE_CHUNK, lengths, 2, -5.0, slots, 64, 64, seed=613)
