@@ -304,3 +304,43 @@ def test_split_windows_graph_replay(dev):
     finally:
         kda.set_prefill_route(kda.ROUTE_AUTO)
     compare(case, ref_o, ref_f)
+
+
+@pytest.mark.parametrize("route", [kda.ROUTE_CHUNK, kda.ROUTE_SPLIT])
+def test_offsets_above_2_31_elements(dev, route):
+    """64 sequences x 4096 tokens x 64 heads: each bf16 tensor holds 2^31
+    elements (4 GiB), so the last sequences' element offsets exceed 2^31.
+    Inputs are drawn on the device from a seeded generator (as the workloads'
+    recipe: unit q/k, lb sigmoid gates, sigmoid beta); sampled units of the
+    first and last sequences are compared with the oracle."""
+    N, L, H, lb = 64, 4096, 64, -5.0
+    T = N * L
+    gen = torch.Generator(device=dev).manual_seed(2031)
+
+    def unit(shape):
+        x = torch.randn(shape, generator=gen, device=dev)
+        return (x / x.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+
+    q, k = unit((T, H, 128)), unit((T, H, 128))
+    v = torch.randn((T, H, 128), generator=gen, device=dev).to(torch.bfloat16)
+    g = (lb * torch.sigmoid(torch.randn((T, H, 128), generator=gen, device=dev))).to(torch.bfloat16)
+    beta = torch.sigmoid(torch.randn((T, H), generator=gen, device=dev)).to(torch.bfloat16)
+    cu = torch.arange(0, T + 1, L, dtype=torch.int32, device=dev)
+    print(f"[gpu] prefill offsets>2^31 route={route} N={N} T={T} H={H}", flush=True)
+    kda.set_prefill_route(route)
+    try:
+        out, fin = kda.prefill(q, k, v, g, beta, cu, scale=128 ** -0.5, lower_bound=lb,
+                               final_state=True)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    for n, heads in ((0, [5]), (N - 1, [0, 63])):
+        rows = slice(n * L, (n + 1) * L)
+        sub = lambda t: t[rows][:, heads].cpu()
+        ref_o, ref_f = oracle.prefill(sub(q), sub(k), sub(v), sub(g), sub(beta), [0, L],
+                                      128 ** -0.5, None)
+        r1 = check_out(out[rows][:, heads].cpu(), ref_o)
+        r2 = check_state(fin[n:n + 1, heads].cpu(), ref_f)
+        _say(f"   seq {n} heads {heads}: out {r1}  state {r2}")
+    del q, k, v, g, beta, out, fin
+    torch.cuda.empty_cache()
