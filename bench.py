@@ -126,8 +126,16 @@ def cpu_baseline(config=1, min_seconds=10.0, max_runs=50):
                        threads=threads)
         runs += 1
     dt = (time.perf_counter() - t0) / runs
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in f
+                              if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": c.total_tokens * c.num_heads / dt, "unit": "tokens*heads/s",
-            "cores": threads, "kind": "oracle",
+            "cores": threads, "host_cpus": len(os.sched_getaffinity(0)), "cpu_model": cpu_model,
+            "kind": "oracle",
             "sample": (f"whole prefill workload ({c.num_seqs} sequence(s), {c.total_tokens} "
                        f"tokens in all, {c.num_heads} heads), FP64 token recurrence, {runs} runs, "
                        f"{dt:.3f} s wall each on {threads} threads")}
