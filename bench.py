@@ -112,6 +112,53 @@ def copy_bandwidth(torch, dev, nbytes=1 << 30, reps=5):
     return 2 * nbytes / t / 1e9
 
 
+def decode_sweep(torch, dev, kda, copy_gbs, steps=30, warmup=5):
+    """kda_decode at H=8 for rows 1, 2, 4, ..., 4096 over a 4096-slot pool, FP32
+    and BF16 states: time per call over `steps` calls replayed from a graph, achieved
+    GB/s (state read + write and the row inputs/outputs) and its fraction of
+    the same run's device copy."""
+    from kimi_delta_attention_prefill_amd.inputs import decode_config, make_decode_case
+
+    out = []
+    for dt, name, state_b in ((torch.float32, "f32", STATE_BYTES),
+                              (torch.bfloat16, "bf16", STATE_BYTES // 2)):
+        pool = decode_config(1, dt).pool.to(dev)       # the 4096-slot pool of the workload
+        rows = 1
+        while rows <= 4096:
+            d = make_decode_case(rows, 8, 4096, dt, seed=20264 + rows, with_pool=False)
+            to = lambda t: t.to(dev)
+            args = (to(d.q), to(d.k), to(d.v), to(d.g), to(d.beta), pool, to(d.slots))
+            o = torch.empty_like(args[0])
+            for _ in range(warmup):
+                kda.decode(*args, scale=d.scale, out=o)
+            # `steps` calls captured in one graph and replayed between one pair
+            # of events, as a serving loop would issue them: an event-bracketed
+            # call of a few microseconds, or calls launched one by one from
+            # Python, mostly time the launches themselves
+            graph = torch.cuda.CUDAGraph()
+            torch.cuda.synchronize()
+            with torch.cuda.graph(graph):
+                for _ in range(steps):
+                    kda.decode(*args, scale=d.scale, out=o)
+            graph.replay()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            del graph
+            gbs = rows * 8 * (2 * state_b + DECODE_IO_BYTES_PER_ITEM) / (ms * 1e-3) / 1e9
+            out.append({"state": name, "rows": rows, "ms_per_call": ms,
+                        "gbps": gbs, "frac_of_peak": gbs / PEAK_HBM_GBPS,
+                        "frac_of_copy": gbs / copy_gbs})
+            log(f"[bench] decode sweep {name} rows={rows} {ms * 1e3:.1f} us {gbs:.0f} GB/s")
+            rows *= 2
+        del pool
+    return out
+
+
 def cpu_baseline(config=1, min_seconds=10.0, max_runs=50):
     """The FP64 oracle on the whole prefill workload, repeated until about
     `min_seconds` of wall time have passed; reports the mean rate."""
@@ -150,6 +197,8 @@ def main():
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--decode-sweep", action="store_true",
+                    help="also time kda_decode at rows 1, 2, ..., 4096 (FP32 and BF16 pools)")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="prefill calls timed after a 512 MiB write has flushed the caches "
                          "(0 = skip)")
@@ -365,6 +414,8 @@ def main():
                     "b200_prefill_speedup_vs_flashkda_geomean": 2.0512},
         "source_digest": source_digest(),
     }
+    if args.decode_sweep:
+        result["decode_sweep"] = decode_sweep(torch, dev, kda, copy_gbs)
     if not args.no_cpu_baseline:
         log("[bench] timing the FP64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(args.prefill_config)
