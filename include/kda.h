@@ -114,7 +114,8 @@ typedef enum {
                            short serial chain per (sequence, head) consumes
                            them (few units: AUTO picks it up to 3/8 of the
                            device's compute units in (sequence, head)
-                           units, 96 on MI355X)                            */
+                           units, 96 on MI355X, and only for batches of
+                           more than 96 tokens)                            */
 } kda_prefill_route;
 
 /* Exponent handling of the chunk route's pairwise (Mqk, Akk) products,

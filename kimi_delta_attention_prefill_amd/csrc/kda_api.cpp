@@ -314,7 +314,12 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     // split chain runs 8 blocks per recurrence, two per CU; measured on 256
     // CUs it wins up to 1.5 such rounds (96 units: 1.29 vs 1.50 ms at T=8192)
     // and loses from 2 (128 units: 1.78 vs 1.52 ms).
-    route = 8 * units <= 3 * (int64_t)num_cus ? KDA_ROUTE_SPLIT : KDA_ROUTE_CHUNK;
+    // At most three chunks in the whole batch (so in every sequence): the
+    // fused kernel's short serial loop beats the two-pass route's second
+    // launch (measured at H=2: 8.8 vs 19.8 us at 32 tokens, 19.6 vs 20.8 us
+    // at 96, 24.8 vs 21.2 us at 128).
+    route = (8 * units <= 3 * (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
+                                                                         : KDA_ROUTE_CHUNK;
   }
   if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);

@@ -210,7 +210,10 @@ def test_decode_frontend_host_validation():
 def test_auto_route_and_workspace():
     # few (sequence, head) units: two-pass split route; many: fused chunk route
     assert kda.plan(1, 8192, 8, -5.0, 256).route == kda.ROUTE_SPLIT
-    assert kda.plan(1, 64, 2, -5.0, 256).route == kda.ROUTE_SPLIT
+    # at most three chunks in the batch: the fused route's serial loop is shorter
+    assert kda.plan(1, 64, 2, -5.0, 256).route == kda.ROUTE_CHUNK
+    assert kda.plan(3, 96, 8, -5.0, 256).route == kda.ROUTE_CHUNK
+    assert kda.plan(1, 97, 2, -5.0, 256).route == kda.ROUTE_SPLIT
     assert kda.plan(16, 35000, 32, -5.0, 256).route == kda.ROUTE_CHUNK
     assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
     # crossover: the split chain's 8 blocks per unit, two per CU, up to 1.5 rounds
