@@ -102,6 +102,18 @@ def test_ragged_lengths(dev, route, lb):
     compare(case, o, f)
 
 
+@pytest.mark.parametrize("lengths,route", [([96], kda.ROUTE_CHUNK), ([97], kda.ROUTE_SPLIT),
+                                            ([5, 40, 51], kda.ROUTE_CHUNK),
+                                            ([5, 40, 52], kda.ROUTE_SPLIT)])
+def test_auto_route_around_short_batch_limit(dev, lengths, route):
+    """The automatic choice on either side of the short-batch limit (96 tokens in the
+    batch): the planner's pick, and the output of the call that takes it."""
+    case = make_prefill_case(lengths, 2, -5.0, 0.02, seed=41, name=f"auto_{sum(lengths)}")
+    assert kda.plan(case.num_seqs, case.total_tokens, 2, -5.0).route == route
+    o, f = run_gpu(case, kda.ROUTE_AUTO, dev)
+    compare(case, o, f)
+
+
 @pytest.mark.parametrize("nseq", [256, 257])
 def test_many_sequences_fused(dev, nseq):
     """Many short sequences on the fused route.  Up to 256 sequences each
