@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -375,6 +375,34 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g,
                   int32_t rows, int32_t num_heads, int32_t head_dim_k,
                   int32_t head_dim_v, float scale, const kda_frontend* frontend,
                   void* out, hipStream_t stream);
+
+/* ------------------------------------------- allocation-free prefill --
+ * kda_prefill for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  It
+ * takes no workspace; the SPLIT route's chunk records and window states live
+ * in a static device array of KDA_NOALLOC_SCRATCH_BYTES bytes inside the
+ * library (one copy per GPU, held from the first call on that GPU until the
+ * process ends).  Nothing is allocated per call, by the library or through
+ * any other library.
+ *
+ * Arguments, routes, results and errors are those of kda_prefill, plus:
+ *  - KDA_ERR_WORKSPACE when kda_prefill_workspace_size(num_seqs,
+ *    total_tokens, num_heads) exceeds KDA_NOALLOC_SCRATCH_BYTES (nothing is
+ *    enqueued);
+ *  - KDA_ERR_HIP when the scratch's device address cannot be resolved.
+ * The first call on each device resolves that address (hipGetSymbolAddress,
+ * no allocation); make it outside graph capture.
+ * Every call on one GPU shares that GPU's scratch, whose contents are left
+ * from the last call (nothing in it needs to start at zero): calls that can
+ * overlap on one GPU (different streams without ordering between them) race
+ * and must not be issued; calls ordered on one stream are fine. */
+#define KDA_NOALLOC_SCRATCH_BYTES 134217728ULL /* 128 MiB */
+int kda_prefill_noalloc(const void* q, const void* k, const void* v, const void* g,
+                        const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
+                        int64_t total_tokens, int32_t num_heads, int32_t head_dim_k,
+                        int32_t head_dim_v, float scale, float lower_bound,
+                        const float* initial_state, float* final_state, void* out,
+                        hipStream_t stream);
 
 /* -------------------------------------------------------- input checks --
  * The device-side preconditions that the entry points document but do not

@@ -110,6 +110,9 @@ def load():
     lib.kda_prefill_ex.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
                                    ctypes.POINTER(_FrontEnd), vp, vp, vp, vp, sz, vp]
     lib.kda_prefill_ex.restype = ctypes.c_int
+    lib.kda_prefill_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i32, i64, i32, i32, i32, f32, f32,
+                                        vp, vp, vp, vp]
+    lib.kda_prefill_noalloc.restype = ctypes.c_int
     lib.kda_prefill_workspace_size.argtypes = [i32, i64, i32]
     lib.kda_prefill_workspace_size.restype = sz
     lib.kda_prefill_plan.argtypes = [i32, i64, i32, f32, i32, i32, ctypes.POINTER(_Plan)]
@@ -274,6 +277,41 @@ def prefill(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=N
                                      _ptr(final_state), _ptr(out), _ptr(workspace), ws_bytes,
                                      _stream(stream)))
     return out, final_state
+
+
+def prefill_noalloc(q, k, v, g, beta, cu_seqlens, *, scale, lower_bound, initial_state=None,
+                    final_state=None, out=None, stream=None):
+    """kda_prefill_noalloc: :func:`prefill` without a workspace; the split
+    route's workspace is the library's static device scratch (raises
+    KdaError with KDA_ERR_WORKSPACE when the problem needs more).  Outputs
+    and the final state as in :func:`prefill` (allocated here when not
+    given).  Returns (out, final_state)."""
+    dev = q.device
+    T, H, D = q.shape
+    N = cu_seqlens.numel() - 1
+    for name, t in (("q", q), ("k", k), ("v", v), ("g", g)):
+        _need(t, name, torch.bfloat16, (T, H, D), dev)
+    _need(beta, "beta", torch.bfloat16, (T, H), dev)
+    _need(cu_seqlens, "cu_seqlens", torch.int32, (N + 1,), dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", torch.float32, (N, H, D, D), dev)
+    if final_state is True:
+        final_state = torch.empty((N, H, D, D), dtype=torch.float32, device=dev)
+    elif final_state is False:
+        final_state = None
+    if final_state is not None:
+        _need(final_state, "final_state", torch.float32, (N, H, D, D), dev)
+    if out is None:
+        out = torch.empty((T, H, D), dtype=torch.bfloat16, device=dev)
+    _need(out, "out", torch.bfloat16, (T, H, D), dev)
+    _check(load().kda_prefill_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), N, T, H, D, D, float(scale),
+                                      float(lower_bound), _ptr(initial_state), _ptr(final_state),
+                                      _ptr(out), _stream(stream)))
+    return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # KDA_NOALLOC_SCRATCH_BYTES
 
 
 def checkpoint_slots(num_seqs: int, total_tokens: int, checkpoint_tokens: int) -> int:

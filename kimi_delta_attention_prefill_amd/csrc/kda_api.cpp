@@ -210,6 +210,16 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
 
 }  // namespace
 
+namespace kda {
+int set_error(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+}  // namespace kda
+
 extern "C" {
 
 size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens, int32_t num_heads) {

@@ -105,6 +105,10 @@ size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num
 // Decode step; `cols` = value columns per block (32, 64 or 128).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
 
+// Records `code` and the formatted text as the calling thread's last error
+// (kda_last_error) and returns `code`.
+int set_error(int code, const char* fmt, ...);
+
 // Device-side precondition checks (debugging and tests).
 struct CheckPrefillArgs {
   const uint16_t *q, *k, *v, *g, *beta;   // bf16 as kda_prefill takes them
