@@ -3,7 +3,10 @@
 // steps 1-3 of "FlashInfer PR #4262: CAKE KDA Prefill Highlights", section 2
 // (gate prefix and anchored operands; causal Mqk and the triangular system;
 // the 32x32 unit-lower-triangular inverse), with the fixed exponent anchor of
-// section 1 or its 16-token split.
+// section 1 or its 16-token split.  The preparation helpers run on the four
+// producer waves of the fused kernel (256 threads, `tid` 0..255, `wave`
+// 0..3 counted within the producers); they contain no barriers, the caller
+// places them between its own.
 #pragma once
 
 #include "kda_device.h"
@@ -48,45 +51,63 @@ __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   lo = static_cast<_Float16>(x - static_cast<float>(hi));
 }
 
-// One chunk's bf16 inputs in LDS: q, k, g rows padded to RP, and the value
-// columns [col0, col0 + DVS).  Padding tokens (t >= L) are zero.
-template <int DVS>
-struct ChunkRaw {
+// One chunk's q, k, g rows in LDS, padded to RP.  Padding tokens (t >= L)
+// are zero.
+struct ChunkQKG {
   uint16_t q[CH][RP];
   uint16_t k[CH][RP];
   uint16_t g[CH][RP];
-  uint16_t v[CH][DVS];
 };
 
-// LDS used by the preparation steps.  DVS = value columns staged.
+// A prepared chunk: everything the state chain of the fused route reads,
+// one ring slot.  DVS = value columns of the block.
 template <int DVS>
-struct PrepSmem {
-  ChunkRaw<DVS> raw[2];        // the chunk in work and the next one, landing
+struct ChunkOps {
+  _Float16 Kg[CH][RP];         // k 2^G      [token][dk, permuted]
+  _Float16 Qg[CH][RP];         // q 2^G      [token][dk, permuted]
+  _Float16 KrT[D][TP];         // (k 2^{G_L-G})^T [dk][token, permuted]
+  _Float16 T[CH][TP];          // (I + A)^{-1}     [token][token, permuted]
+  _Float16 Mqk[CH][TP];        // causal Mqk       [token][token, permuted]
+  float dec[D];                // 2^{G_L}: chunk decay of each key row
+  float beta[CH];              // zero for padding tokens
+  uint16_t v[CH][DVS];         // the block's value columns, bf16
+};
+
+// The producers' working memory for one chunk: the gate prefix, and, over
+// its bytes once the anchored operands are built, the triangular system and
+// its inverse.  The split-K partials of the pairwise products live over the
+// chunk's own q/k/g rows once every producer has built its operands.
+struct PrepWork {
   float G[CH][GP];             // log2-domain inclusive gate prefix
   float EL[D];                 // fixed anchor: 2^{G_L - C}
-  float dec[D];                // 2^{G_L}: chunk decay of each key row
-  float beta[CH];
   float rq[CH], rk[CH];        // q/k L2-norm scales per token (1 without the front-end norm)
-  float part[4][6][64][4];     // split-K partials of the six Mqk/Akk tiles
+};
+typedef float PartTiles[4][6][64][4];   // split-K partials of the six Mqk/Akk tiles
+static_assert(sizeof(PartTiles) <= sizeof(ChunkQKG), "partials must fit over the q/k/g rows");
+struct InvWork {
   float At[CH][CH + 4];        // (Diag(b) stril(Akk))^T, FP32; rows 16-byte aligned
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
   float X[16][17];             // A21 T11
 };
+static_assert(sizeof(InvWork) <= sizeof(float) * CH * GP, "inverse work must fit over G");
 
-// Step 1: the chunk [t0, t0 + L) of (sequence, head h) -- q, k, g rows, the
-// value columns [col0, col0 + DVS) and beta -- so that a block can fetch the
-// next chunk while it works on the current one.  fetch_chunk issues
-// range-checked buffer loads straight into the padded rows of `cr` (no
-// registers are held; a wave's 4-byte load fills 256 consecutive bytes of
-// LDS, lane i the i-th word, i.e. one q/k/g row or 256 / (2 DVS) value rows),
-// and the chunk's beta into a register.  Rows t >= L lie outside the range
-// and land as zeros, so no later pass has to clear them.  256 threads.
+__device__ __forceinline__ PartTiles& part_of(ChunkQKG& cr) {
+  return *reinterpret_cast<PartTiles*>(&cr);
+}
+__device__ __forceinline__ InvWork& inv_of(PrepWork& pw) {
+  return *reinterpret_cast<InvWork*>(&pw.G[0][0]);
+}
+
 typedef __attribute__((address_space(3))) void lds_void;
 
-template <int DVS>
-__device__ __forceinline__ void fetch_chunk(ChunkRaw<DVS>& cr, uint16_t& beta_raw,
-                                            const PrefillArgs& a, int t0, int L, int h,
-                                            int col0, int tid) {
+// Step 1: the q, k, g rows of the chunk [t0, t0 + L) of head h, by
+// range-checked buffer loads straight into the padded rows of `cr` (no
+// registers are held; a wave's 4-byte load fills 256 consecutive bytes of
+// LDS, lane i the i-th word, i.e. one row), and the chunk's beta into a
+// register.  Rows t >= L lie outside the range and land as zeros.  256
+// threads.
+__device__ __forceinline__ void fetch_qkg(ChunkQKG& cr, uint16_t& beta_raw, const PrefillArgs& a,
+                                          int t0, int L, int h, int tid) {
   const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
   const int64_t base = ((int64_t)t0 * H + h) * D;
   const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
@@ -94,7 +115,6 @@ __device__ __forceinline__ void fetch_chunk(ChunkRaw<DVS>& cr, uint16_t& beta_ra
   const __amdgpu_buffer_rsrc_t rq = make_buffer(a.q + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_buffer(a.k + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rg = make_buffer(a.g + base, rows_bytes);
-  const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
 #pragma unroll
   for (int i = 0; i < CH / 4; ++i) {   // wave w: rows w, w + 4, ...
     const int t = wave + 4 * i;
@@ -103,6 +123,19 @@ __device__ __forceinline__ void fetch_chunk(ChunkRaw<DVS>& cr, uint16_t& beta_ra
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&cr.k[t][0], 4, off, 0, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)&cr.g[t][0], 4, off, 0, 0, 0);
   }
+  beta_raw = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
+}
+
+// The value columns [col0, col0 + DVS) of the same chunk into v (unpadded
+// rows; rows t >= L land as zeros).  256 threads.
+template <int DVS>
+__device__ __forceinline__ void fetch_v(uint16_t (&v)[CH][DVS], const PrefillArgs& a, int t0,
+                                        int L, int h, int col0, int tid) {
+  const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
+  const int64_t base = ((int64_t)t0 * H + h) * D;
+  const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
+  const uint32_t row_bytes = (uint32_t)H * D * 2;
+  const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
   constexpr int kRowsPerLoad = 128 / DVS;            // value rows per 256-byte load
   constexpr int kLanesPerRow = 64 / kRowsPerLoad;
 #pragma unroll
@@ -110,9 +143,8 @@ __device__ __forceinline__ void fetch_chunk(ChunkRaw<DVS>& cr, uint16_t& beta_ra
     const int r0 = (wave + 4 * i) * kRowsPerLoad;    // first row of this load
     const int t = r0 + lane / kLanesPerRow;
     const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)col0 * 2 + (uint32_t)(lane % kLanesPerRow) * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&cr.v[r0][0], 4, off, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&v[r0][0], 4, off, 0, 0, 0);
   }
-  beta_raw = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
 }
 
 // Wait for this wave's direct loads; the caller's next barrier makes every
@@ -123,21 +155,20 @@ __device__ __forceinline__ void fetch_wait() {
 
 // The chunk's beta (zero for padding tokens), through the front-end's
 // transform when it is compiled in.
-template <int DVS, bool FE>
-__device__ __forceinline__ void stage_beta(PrepSmem<DVS>& sm, uint16_t beta_raw,
-                                           const FrontEnd& fe, int L, int tid) {
+template <bool FE>
+__device__ __forceinline__ void stage_beta(float* beta, uint16_t beta_raw, const FrontEnd& fe,
+                                           int L, int tid) {
   if (tid < CH) {
     const float b = tid < L ? bf16_to_f32(beta_raw) : 0.f;
-    sm.beta[tid] = FE && tid < L ? frontend_beta(fe, b) : b;
+    beta[tid] = FE && tid < L ? frontend_beta(fe, b) : b;
   }
 }
 
 // Step 1b (input front-end): 1 / sqrt(sum_c x_c^2 + norm_eps) of q and k per
 // token of the staged chunk; eight threads per token, 16 channels each.
 // Needs 256 threads; runs in the same phase as gate_prefix.
-template <int DVS>
-__device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
-                                         const PrefillArgs& a, int tid) {
+__device__ __forceinline__ void qk_norms(PrepWork& pw, const ChunkQKG& cr, const PrefillArgs& a,
+                                         int tid) {
   const int t = tid >> 3, part = tid & 7;
   float sq2 = 0.f, sk2 = 0.f;
   if (a.fe.normalize_qk) {
@@ -155,8 +186,8 @@ __device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const ChunkRaw<DVS>&
     }
   }
   if (part == 0) {
-    sm.rq[t] = a.fe.normalize_qk ? inv_norm(sq2 + a.fe.norm_eps) : 1.f;
-    sm.rk[t] = a.fe.normalize_qk ? inv_norm(sk2 + a.fe.norm_eps) : 1.f;
+    pw.rq[t] = a.fe.normalize_qk ? inv_norm(sq2 + a.fe.norm_eps) : 1.f;
+    pw.rk[t] = a.fe.normalize_qk ? inv_norm(sk2 + a.fe.norm_eps) : 1.f;
   }
 }
 
@@ -166,10 +197,9 @@ __device__ __forceinline__ void qk_norms(PrepSmem<DVS>& sm, const ChunkRaw<DVS>&
 // half's total (a cross-lane read), so each lane's serial sum is 16 long.
 // Padding tokens (t >= L) add nothing: a transformed gate of their zero input
 // would not be zero.
-template <int MODE, int DVS, bool FE>
-__device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
-                                            const FrontEnd& fe, float C, int L,
-                                            int tid) {
+template <int MODE, bool FE>
+__device__ __forceinline__ void gate_prefix(PrepWork& pw, float* dec, const ChunkQKG& cr,
+                                            const FrontEnd& fe, float C, int L, int tid) {
   const int lane = tid & 63, c = 32 * (tid >> 6) + (lane & 31), hf = lane >> 5;
   float pre[16];
   float acc = 0.f;
@@ -184,11 +214,11 @@ __device__ __forceinline__ void gate_prefix(PrepSmem<DVS>& sm, const ChunkRaw<DV
   const float other = __shfl_xor(acc, 32);   // the first half's total, seen by the second half
   const float base = hf ? other : 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) sm.G[16 * hf + j][c] = (base + pre[j]) * kLog2e;
+  for (int j = 0; j < 16; ++j) pw.G[16 * hf + j][c] = (base + pre[j]) * kLog2e;
   if (hf) {
     const float GL = (base + acc) * kLog2e;
-    sm.dec[c] = fast_exp2(GL);
-    sm.EL[c] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
+    dec[c] = fast_exp2(GL);
+    pw.EL[c] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
   }
 }
 
@@ -205,11 +235,12 @@ struct PairOps {
 // owns key channels 32w..32w+31; lane (g4, l16) owns channels 32w+8g4+j and
 // tokens l16, l16+16.  For every (token t, channel c) owned, emit(t, c, kf, qf,
 // P, R) receives the raw k and q values, P = 2^{G_t} and R = 2^{G_L - G_t}
-// (both <= 1) so the caller can form Kg, Qg and Kr.  The six lower tiles of
-// Mqk and Akk (as partial sums over this wave's channels) go to sm.part.
-template <int MODE, int DVS, bool FE, class Emit>
-__device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const ChunkRaw<DVS>& cr,
-                                              const PrefillArgs& a, float C,
+// (both <= 1) so the caller can form Kg, Qg and Kr.  Returns the six lower
+// tiles of Mqk and Akk as partial sums over this wave's channels; the caller
+// stores them (pair_store) once no producer reads the chunk's rows any more.
+template <int MODE, bool FE, class Emit>
+__device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& pw,
+                                              const ChunkQKG& cr, const PrefillArgs& a, float C,
                                               float exp2C, int wave, int lane, Emit&& emit) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int cb = 32 * wave, cl = 8 * g4;
@@ -217,23 +248,23 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const ChunkRaw<
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
     const int t = l16 + 16 * half;
-    const f32x4 G0 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl]);
-    const f32x4 G1 = *reinterpret_cast<const f32x4*>(&sm.G[t][cb + cl + 4]);
+    const f32x4 G0 = *reinterpret_cast<const f32x4*>(&pw.G[t][cb + cl]);
+    const f32x4 G1 = *reinterpret_cast<const f32x4*>(&pw.G[t][cb + cl + 4]);
     const uint4 qw = *reinterpret_cast<const uint4*>(&cr.q[t][cb + cl]);
     const uint4 kw = *reinterpret_cast<const uint4*>(&cr.k[t][cb + cl]);
     f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1;
-    const float rq = FE ? sm.rq[t] : 1.f, rk = FE ? sm.rk[t] : 1.f;
+    const float rq = FE ? pw.rq[t] : 1.f, rk = FE ? pw.rk[t] : 1.f;
     if (MODE >= 1) {
-      Gs0 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl]);
-      Gs1 = *reinterpret_cast<const f32x4*>(&sm.G[15][cb + cl + 4]);
-      GL0 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl]);
-      GL1 = *reinterpret_cast<const f32x4*>(&sm.G[CH - 1][cb + cl + 4]);
+      Gs0 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl]);
+      Gs1 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl + 4]);
+      GL0 = *reinterpret_cast<const f32x4*>(&pw.G[CH - 1][cb + cl]);
+      GL1 = *reinterpret_cast<const f32x4*>(&pw.G[CH - 1][cb + cl + 4]);
       // MODE 2: G at the half's first token (0 or 16) for the midpoint anchor
-      Gf0 = *reinterpret_cast<const f32x4*>(&sm.G[16 * half][cb + cl]);
-      Gf1 = *reinterpret_cast<const f32x4*>(&sm.G[16 * half][cb + cl + 4]);
+      Gf0 = *reinterpret_cast<const f32x4*>(&pw.G[16 * half][cb + cl]);
+      Gf1 = *reinterpret_cast<const f32x4*>(&pw.G[16 * half][cb + cl + 4]);
     } else {
-      EL0 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl]);
-      EL1 = *reinterpret_cast<const f32x4*>(&sm.EL[cb + cl + 4]);
+      EL0 = *reinterpret_cast<const f32x4*>(&pw.EL[cb + cl]);
+      EL1 = *reinterpret_cast<const f32x4*>(&pw.EL[cb + cl + 4]);
     }
     const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
     const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
@@ -300,7 +331,6 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const ChunkRaw<
     emit(t, cb + cl, kv, qv, Pv, Rv);
   }
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-  f32x4 acc[6];
   acc[0] = mfma_bf16(op.q0h, op.b0h, z);
   acc[0] = mfma_bf16(op.q0h, op.b0l, acc[0]);
   acc[0] = mfma_bf16(op.q0l, op.b0h, acc[0]);
@@ -319,20 +349,24 @@ __device__ __forceinline__ void pair_products(PrepSmem<DVS>& sm, const ChunkRaw<
   acc[5] = mfma_bf16(op.k1h, op.b1h, z);
   acc[5] = mfma_bf16(op.k1h, op.b1l, acc[5]);
   acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
+}
+
+__device__ __forceinline__ void pair_store(PartTiles& part, const f32x4 (&acc)[6], int wave,
+                                           int lane) {
 #pragma unroll
-  for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(&sm.part[wave][p][lane][0]) = acc[p];
+  for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(&part[wave][p][lane][0]) = acc[p];
 }
 
 // Step 3b: sum the four split-K partials in a fixed order, mask the causal
 // triangles by select (masked anchored entries may be inf or NaN) and scale
-// Akk by beta.  Writes sm.At (A transposed); emit_mqk(r, s, value) sees every
+// Akk by beta.  Writes iw.At (A transposed); emit_mqk(r, s, value) sees every
 // Mqk entry (zero above the diagonal).  256 threads.
-template <int DVS, class EmitMqk>
-__device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk&& emit_mqk) {
+template <class EmitMqk>
+__device__ __forceinline__ void reduce_pairs(InvWork& iw, const PartTiles& part, const float* beta,
+                                             int tid, EmitMqk&& emit_mqk) {
   const int ln = tid >> 2, i = tid & 3;
   auto sum4 = [&](int p) __attribute__((always_inline)) {
-    return ((sm.part[0][p][ln][i] + sm.part[1][p][ln][i]) + sm.part[2][p][ln][i]) +
-           sm.part[3][p][ln][i];
+    return ((part[0][p][ln][i] + part[1][p][ln][i]) + part[2][p][ln][i]) + part[3][p][ln][i];
   };
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {   // 16x16 quadrants (0,0) (1,0) (1,1) (0,1); the last is zero
@@ -343,17 +377,17 @@ __device__ __forceinline__ void reduce_pairs(PrepSmem<DVS>& sm, int tid, EmitMqk
     const float ak = q4 == 3 ? 0.f : sum4(3 + q4);   // Akk partial tiles 3..5
     const float m = s <= r ? mq : 0.f;
     emit_mqk(r, s, m);
-    sm.At[s][r] = s < r ? sm.beta[r] * ak : 0.f;
+    iw.At[s][r] = s < r ? beta[r] * ak : 0.f;
   }
 }
 
-// Steps 4a-4c: T = (I + A)^{-1}.  The 16x16 diagonal blocks in FP32 by
-// forward substitution (wave 0, one column per lane), then T21 = -T22 A21 T11
-// and T12 = 0; the last step hands every entry (i, m) of each quadrant to
-// emit_t(row, col, value) (the caller stores the MFMA operand).  256 threads;
-// contains barriers.
-template <int DVS, class EmitT>
-__device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid, EmitT&& emit_t) {
+// Steps 4a-4c: T = (I + A)^{-1}, in three phases separated by the caller's
+// barriers.  Phase 1: the 16x16 diagonal blocks in FP32 by forward
+// substitution (producer wave 0, one column per lane).  Phase 2: X = A21 T11.
+// Phase 3: T21 = -T22 X and T12 = 0; every entry (i, m) of each quadrant goes
+// to emit_t(row, col, value) (the caller stores the MFMA operand).  256
+// threads.
+__device__ __forceinline__ void invert_diag(InvWork& iw, int tid) {
   const int wave = tid >> 6, lane = tid & 63;
   if (wave == 0 && lane < 32) {
     const int base = 16 * (lane >> 4), m = lane & 15;
@@ -365,32 +399,31 @@ __device__ __forceinline__ void invert_unit_lower(PrepSmem<DVS>& sm, int tid, Em
       // column j of the block below the diagonal: row j of At, four 16-byte reads
       f32x4 c[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(&sm.At[base + j][base + 4 * q]);
+      for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(&iw.At[base + j][base + 4 * q]);
 #pragma unroll
       for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[i >> 2][i & 3], x[j], x[i]);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sm.Tf[base + i][base + m] = x[i];
+    for (int i = 0; i < 16; ++i) iw.Tf[base + i][base + m] = x[i];
   }
-  __syncthreads();
-  {
-    const int i = tid >> 4, m = tid & 15;
-    float acc = 0.f;
+}
+__device__ __forceinline__ void invert_offdiag_x(InvWork& iw, int tid) {
+  const int i = tid >> 4, m = tid & 15;
+  float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc = fmaf(sm.At[j][16 + i], sm.Tf[j][m], acc);
-    sm.X[i][m] = acc;
-  }
-  __syncthreads();
-  {
-    const int i = tid >> 4, m = tid & 15;
-    float acc = 0.f;
+  for (int j = 0; j < 16; ++j) acc = fmaf(iw.At[j][16 + i], iw.Tf[j][m], acc);
+  iw.X[i][m] = acc;
+}
+template <class EmitT>
+__device__ __forceinline__ void invert_finish(const InvWork& iw, int tid, EmitT&& emit_t) {
+  const int i = tid >> 4, m = tid & 15;
+  float acc = 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) acc = fmaf(sm.Tf[16 + i][16 + j], sm.X[j][m], acc);
-    emit_t(i, m, sm.Tf[i][m]);
-    emit_t(16 + i, 16 + m, sm.Tf[16 + i][16 + m]);
-    emit_t(16 + i, m, -acc);
-    emit_t(i, 16 + m, 0.f);
-  }
+  for (int j = 0; j < 16; ++j) acc = fmaf(iw.Tf[16 + i][16 + j], iw.X[j][m], acc);
+  emit_t(i, m, iw.Tf[i][m]);
+  emit_t(16 + i, 16 + m, iw.Tf[16 + i][16 + m]);
+  emit_t(16 + i, m, -acc);
+  emit_t(i, 16 + m, 0.f);
 }
 
 }  // namespace chunk

@@ -28,14 +28,29 @@
 //   * gate prefix, inverse, decay and all accumulators in FP32.
 // fp16 operands assume |v| < 2^15 and unit-norm keys/queries, as in KDA.
 //
-// Work decomposition.  One block of 4 waves per (sequence, head, value slice
-// of DVS = 64 * NT columns).  Per chunk the four waves first prepare the
-// chunk together (wave w owns key channels 32w..32w+31 of the pairwise
-// products and of the operand preparation, a split-K whose partials are summed
-// in a fixed order, so results are deterministic), then each wave runs the
-// serial state chain on its own 16 * NT value columns: value columns evolve
-// independently, so the chain needs no cross-wave exchange.  The state stays
-// in the MFMA accumulators for the whole sequence.
+// Work decomposition.  One block of 8 waves per (sequence, head, value slice
+// of DVS = 64 * NT columns), organised as the producer/consumer pipeline of
+// the note's sections 3-4 (a ring of prepared chunks between the waves that
+// prepare chunks and the waves that consume them), sized for a CDNA4 compute
+// unit's 160 KiB of LDS:
+//   * waves 4-7 (producers) prepare chunk c+1 -- gate prefix, anchored
+//     operands, Mqk and the triangular system, its inverse -- into ring slot
+//     (c+1) % 2 (wave w owns key channels 32(w-4).. of the pairwise products,
+//     a split-K whose partials are summed in a fixed order, so results are
+//     deterministic), and fetch the raw rows of chunk c+2 and the value rows
+//     of chunk c+1 by direct global-to-LDS loads;
+//   * waves 0-3 (consumers) meanwhile run the serial state chain of chunk c
+//     from slot c % 2 on their own 16 * NT value columns (value columns
+//     evolve independently, so the chain needs no cross-wave exchange); the
+//     FP32 state stays in their MFMA accumulators for the whole sequence.
+// Both sides meet at the same block barriers (a fixed number per chunk), so a
+// chunk costs about the longer of the two sides rather than their sum.  LDS
+// per block (DVS = 128): two raw q/k/g buffers (2 x 25.5 KiB; the split-K
+// partials of a chunk live over its own rows once its operands are built),
+// the producers' gate prefix (16.5 KiB; the triangular system and its
+// inverse live over it once the operands are built), and two ring slots of
+// 40.6 KiB (Kg, Qg, Kr^T, T, Mqk, decays, beta and the value rows): 149.5
+// KiB.
 //
 // Accumulator-to-operand reuse.  An accumulator tile of v_mfma_f32_16x16x32
 // gives lane l the rows 4(l/16)+i (i < 4) of column l%16, while the B operand
@@ -45,6 +60,7 @@
 // the FP32 state, V' and U into the next product's B operand with a register
 // conversion only.  The A operands (Kg, Qg, Kr^T, T, Mqk) are therefore
 // stored in LDS with their K index in that permuted order.
+#include <climits>
 #include <cmath>
 
 #include "chunk_common.h"
@@ -54,15 +70,17 @@ namespace {
 
 using namespace chunk;
 
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
 template <int DVS>
-struct FusedSmem {
-  PrepSmem<DVS> p;
-  _Float16 Kg[CH][RP];         // k 2^G      [token][dk, permuted]
-  _Float16 Qg[CH][RP];         // q 2^G      [token][dk, permuted]
-  _Float16 KrT[D][TP];         // (k 2^{G_L-G})^T [dk][token, permuted]
-  _Float16 T[CH][TP];          // (I + A)^{-1}     [token][token, permuted]
-  _Float16 Mqk[CH][TP];        // causal Mqk       [token][token, permuted]
+struct RingSmem {
+  ChunkQKG raw[2];             // chunk c+1 in preparation, chunk c+2 landing
+  PrepWork pw;                 // gate prefix (then the inverse's work)
+  ChunkOps<DVS> slot[2];       // the ring: chunk c (consumed), chunk c+1 (prepared)
 };
+
+constexpr int kThreads = 512;
+constexpr int kProducerBase = 256;   // first producer thread
 
 // Blocks start in index order as compute units free up, and a block holds a
 // compute unit for its whole sequence, so the sequence a block works on is
@@ -70,18 +88,18 @@ struct FusedSmem {
 // sequence otherwise may only start in the last round of blocks and end
 // alone.  Returns the sequence of rank r by (length descending, index
 // ascending); `tmp` is LDS scratch of at least N + 1 ints, free on entry and
-// on return.  256 threads; contains barriers.
+// on return.  All threads; contains barriers.
 constexpr int kLongestFirstMaxSeqs = 256;
 
 __device__ __forceinline__ int longest_first_sequence(const PrefillArgs& a, int r, int* tmp,
                                                       int tid) {
   const int N = a.num_seqs;
-  for (int i = tid; i < N; i += 256) {
+  for (int i = tid; i < N; i += kThreads) {
     const int b = clamp_offset(a.cu_seqlens[i], a.total_tokens);
     tmp[i] = max(b, clamp_offset(a.cu_seqlens[i + 1], a.total_tokens)) - b;
   }
   __syncthreads();
-  for (int i = tid; i < N; i += 256) {
+  for (int i = tid; i < N; i += kThreads) {
     const int li = tmp[i];
     int rank = 0;
     for (int m = 0; m < N; ++m) {
@@ -97,162 +115,205 @@ __device__ __forceinline__ int longest_first_sequence(const PrefillArgs& a, int 
 }
 
 template <int MODE, int NT, bool FE>
-__global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float exp2C) {
+__global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, float exp2C) {
   constexpr int DVS = 64 * NT;
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  FusedSmem<DVS>& sm = *reinterpret_cast<FusedSmem<DVS>*>(smem_raw);
-  PrepSmem<DVS>& ps = sm.p;
+  RingSmem<DVS>& sm = *reinterpret_cast<RingSmem<DVS>*>(smem_raw);
 
   const int H = a.num_heads;
   const int slice = blockIdx.x, h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // the sequence of rank blockIdx.z, longest first (the split-K partials'
-  // area is not in use yet)
-  int* const rank_tmp = reinterpret_cast<int*>(&ps.part[0][0][0][0]);
+  const bool producer = tid >= kProducerBase;
+  const int ptid = tid - kProducerBase, pwave = wave - 4;   // producer numbering
+  // the sequence of rank blockIdx.z, longest first (the raw buffers are not in use yet)
+  int* const rank_tmp = reinterpret_cast<int*>(&sm.raw[0]);
   const int n = (a.num_seqs > 1 && a.num_seqs <= kLongestFirstMaxSeqs)
                     ? longest_first_sequence(a, blockIdx.z, rank_tmp, tid)
                     : (int)blockIdx.z;
   const int l16 = lane & 15, g4 = lane >> 4;
   const int col_base = slice * DVS;
-  const int colw = wave * 16 * NT;          // first column of this wave, within the slice
   const float C = a.anchor_log2;
 
   const int bos = clamp_offset(a.cu_seqlens[n], a.total_tokens);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens));
-  const StateRef s0 = prefill_initial_state(a, n, h);
+  const int nch = (eos - bos + CH - 1) / CH;
 
-  // State accumulators: tile (mt, nt) holds rows 16 mt + 4 g4 + i and column
+  if (producer) {
+    // ------------------------------------------------------------ producers
+    // The first chunk's rows go to raw[0] before the pipeline starts.
+    uint16_t beta_raw = 0;
+    if (nch > 0) fetch_qkg(sm.raw[0], beta_raw, a, bos, min(CH, eos - bos), h, ptid);
+    // Step s (s = -1 .. nch-1): chunk s+1 is prepared into ring slot (s+1) % 2
+    // while the consumers run the chain of chunk s.  Every wave passes the
+    // same seven barriers per step.
+    for (int s = -1; s < nch; ++s) {
+      const bool prep = s + 1 < nch;
+      ChunkQKG& cr = sm.raw[(s + 1) & 1];          // chunk s+1's rows
+      ChunkOps<DVS>& sn = sm.slot[(s + 1) & 1];    // chunk s+1's ring slot
+      const int tn0 = bos + CH * (s + 1), Ln = min(CH, eos - tn0);
+      fetch_wait();    // chunk s+1's rows and chunk s's values (issued in step s-1)
+      // B0: raw rows of chunk s+1 and slot s (with its values) complete; the
+      // consumers are done with slot s-1, the producers with raw[s & 1].
+      __syncthreads();
+      if (prep) {
+        stage_beta<FE>(sn.beta, beta_raw, a.fe, Ln, ptid);
+        if (s + 2 < nch)
+          fetch_qkg(sm.raw[s & 1], beta_raw, a, tn0 + CH, min(CH, eos - tn0 - CH), h, ptid);
+        fetch_v(sn.v, a, tn0, Ln, h, col_base, ptid);
+        gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, Ln, ptid);
+        if (FE) qk_norms(sm.pw, cr, a, ptid);
+      }
+      __syncthreads();   // B1: gate prefix, beta and decays of chunk s+1 written
+      f32x4 pacc[6];
+      if (prep) {
+        pair_products<MODE, FE>(pacc, sm.pw, cr, a, C, exp2C, pwave, lane,
+                          [&](int t, int c0, const float* kv, const float* qv, const float* P,
+                              const float* R) {
+                            const int cb = c0 & ~31, cl = c0 & 31;
+                            f16x4 kg_lo, kg_hi, qg_lo, qg_hi;
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) {
+                              kg_lo[j] = static_cast<_Float16>(kv[j] * P[j]);
+                              kg_hi[j] = static_cast<_Float16>(kv[4 + j] * P[4 + j]);
+                              qg_lo[j] = static_cast<_Float16>(qv[j] * P[j]);
+                              qg_hi[j] = static_cast<_Float16>(qv[4 + j] * P[4 + j]);
+                            }
+#pragma unroll
+                            for (int j = 0; j < 8; ++j)
+                              sn.KrT[c0 + j][kslot(t)] = static_cast<_Float16>(kv[j] * R[j]);
+                            // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 slots
+                            *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl)]) = kg_lo;
+                            *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
+                            *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl)]) = qg_lo;
+                            *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
+                          });
+      }
+      __syncthreads();   // B2: every producer has built its operands from chunk s+1's rows
+      if (prep) pair_store(part_of(cr), pacc, pwave, lane);
+      __syncthreads();   // B3: split-K partials of chunk s+1 complete
+      if (prep)
+        reduce_pairs(inv_of(sm.pw), part_of(cr), sn.beta, ptid, [&](int r, int c, float m) {
+          sn.Mqk[r][kslot(c)] = static_cast<_Float16>(m);
+        });
+      __syncthreads();   // B4: the triangular system of chunk s+1 is in place
+      if (prep) invert_diag(inv_of(sm.pw), ptid);
+      __syncthreads();   // B5
+      if (prep) invert_offdiag_x(inv_of(sm.pw), ptid);
+      __syncthreads();   // B6
+      if (prep)
+        invert_finish(inv_of(sm.pw), ptid, [&](int r, int c, float t) {
+          sn.T[r][kslot(c)] = static_cast<_Float16>(t);
+        });
+    }
+    return;
+  }
+
+  // -------------------------------------------------------------- consumers
+  // State tile (mt, nt) holds key rows 16 mt + 4 g4 + i and value column
   // col_base + colw + 16 nt + l16.
+  const int colw = wave * 16 * NT;          // first column of this wave, within the slice
   f32x4 S[8][NT];
-  auto init_state = [&](auto load) __attribute__((always_inline)) {
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          S[mt][nt][i] = load((16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16);
+  auto state_elem = [&](int mt, int nt, int i) __attribute__((always_inline)) {
+    return (16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16;
   };
-  // one branch on the state's type, outside the element loops
-  if (!s0)
-    init_state([](int) { return 0.f; });
-  else if (s0.bf16)
-    init_state([&](int e) { return bf16_to_f32(static_cast<const uint16_t*>(s0.p)[e]); });
-  else
-    init_state([&](int e) { return static_cast<const float*>(s0.p)[e]; });
+  // A state store: one buffer resource over the [128][128] state, the lane's
+  // part of each element offset in one register and the rest uniform, so
+  // that no per-element 64-bit address stays live across the chunk loop.
+  const uint32_t lane_elem = (uint32_t)(4 * g4 * D + colw + l16);
   auto store_state = [&](float* dst) __attribute__((always_inline)) {
+    const __amdgpu_buffer_rsrc_t r = make_buffer(dst, (uint32_t)(D * D * 4));
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = S[mt][nt][i];
-  };
-
-  // The next chunk's inputs are fetched (straight into the other of the two
-  // raw buffers) while the current one is prepared and consumed, so their
-  // load latency is off the per-chunk path.
-  uint16_t beta_raw = 0;
-  if (bos < eos) fetch_chunk(ps.raw[0], beta_raw, a, bos, min(CH, eos - bos), h, col_base, tid);
-  int buf = 0;
-  for (int t0 = bos; t0 < eos; t0 += CH, buf ^= 1) {
-    const int L = min(CH, eos - t0);
-    const ChunkRaw<DVS>& cr = ps.raw[buf];
-    fetch_wait();
-    // The chunk has landed in raw[buf]; the previous chunk's steps are done
-    // with raw[buf ^ 1] and with the LDS operands.
-    __syncthreads();
-    stage_beta<DVS, FE>(ps, beta_raw, a.fe, L, tid);
-    if (t0 + CH < eos)
-      fetch_chunk(ps.raw[buf ^ 1], beta_raw, a, t0 + CH, min(CH, eos - t0 - CH), h, col_base, tid);
-    gate_prefix<MODE, 64 * NT, FE>(ps, cr, a.fe, C, L, tid);
-    if (FE) qk_norms(ps, cr, a, tid);
-    __syncthreads();
-    pair_products<MODE, 64 * NT, FE>(ps, cr, a, C, exp2C, wave, lane,
-                        [&](int t, int c0, const float* kv, const float* qv, const float* P,
-                            const float* R) {
-                          const int cb = c0 & ~31, cl = c0 & 31;
-                          f16x4 kg_lo, kg_hi, qg_lo, qg_hi;
-#pragma unroll
-                          for (int j = 0; j < 4; ++j) {
-                            kg_lo[j] = static_cast<_Float16>(kv[j] * P[j]);
-                            kg_hi[j] = static_cast<_Float16>(kv[4 + j] * P[4 + j]);
-                            qg_lo[j] = static_cast<_Float16>(qv[j] * P[j]);
-                            qg_hi[j] = static_cast<_Float16>(qv[4 + j] * P[4 + j]);
-                          }
-#pragma unroll
-                          for (int j = 0; j < 8; ++j)
-                            sm.KrT[c0 + j][kslot(t)] = static_cast<_Float16>(kv[j] * R[j]);
-                          // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 slots
-                          *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl)]) = kg_lo;
-                          *reinterpret_cast<f16x4*>(&sm.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
-                          *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl)]) = qg_lo;
-                          *reinterpret_cast<f16x4*>(&sm.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
-                        });
-    __syncthreads();
-    // ---- the state chain, first part (this wave's 16 * NT value columns):
-    // W = Kg S and O = Qg S need only the operands written so far, so their
-    // MFMAs run here, beside the latency-bound reduction and inverse.
-    f16x8 Sb[4][NT];
-#pragma unroll
-    for (int p = 0; p < 4; ++p)
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          Sb[p][nt][i] = static_cast<_Float16>(S[2 * p][nt][i]);
-          Sb[p][nt][4 + i] = static_cast<_Float16>(S[2 * p + 1][nt][i]);
+          const float sv = S[mt][nt][i];
+          __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, sv), r, lane_elem * 4,
+                                                (int)(((16 * mt + i) * D + col_base + 16 * nt) * 4), 0);
         }
-    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
-    f32x4 W[2][NT], O[2][NT];
+  };
+  {
+    const StateRef s0 = prefill_initial_state(a, n, h);
+    auto init_state = [&](auto load) __attribute__((always_inline)) {
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+      for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) { W[mt][nt] = z; O[mt][nt] = z; }
+        for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt) {
-        const f16x8 akg = *reinterpret_cast<const f16x8*>(&sm.Kg[16 * mt + l16][32 * p + 8 * g4]);
-        const f16x8 aqg = *reinterpret_cast<const f16x8*>(&sm.Qg[16 * mt + l16][32 * p + 8 * g4]);
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          W[mt][nt] = mfma_f16(akg, Sb[p][nt], W[mt][nt]);
-          O[mt][nt] = mfma_f16(aqg, Sb[p][nt], O[mt][nt]);
-        }
-      }
-    // V' = b (V - W) as hi + lo fp16 B operands (K = token, permuted)
-    f16x8 Vh[NT], Vl[NT];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt)
+          for (int i = 0; i < 4; ++i) S[mt][nt][i] = load(state_elem(mt, nt, i));
+    };
+    // one branch on the state's type, outside the element loops
+    if (!s0)
+      init_state([](int) { return 0.f; });
+    else if (s0.bf16)
+      init_state([&](int e) { return bf16_to_f32(static_cast<const uint16_t*>(s0.p)[e]); });
+    else
+      init_state([&](int e) { return static_cast<const float*>(s0.p)[e]; });
+  }
+  // Checkpoints (the state after every ckpt_tokens tokens): chunk count of
+  // the next one and its row of the checkpoint buffer.
+  const int ck_per = a.ckpt ? a.ckpt_tokens / CH : 0;
+  int ck_next = a.ckpt ? ck_per : INT_MAX;
+  int64_t ck_row = a.ckpt ? (int64_t)n + bos / a.ckpt_tokens : 0;
+  for (int s = -1; s < nch; ++s) {
+    const ChunkOps<DVS>& sc = sm.slot[s & 1];    // chunk s's ring slot
+    __syncthreads();   // B0
+    __syncthreads();   // B1
+    if (s >= 0) {
+      // ---- the state chain of chunk s on this wave's 16 * NT value columns
+      const int t0 = bos + CH * s, L = min(CH, eos - t0);
+      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      // W = Kg S (rows = tokens) and O^T = S^T Qg^T (rows = value columns: the
+      // same fragments with A and B swapped, so each lane ends with 4
+      // adjacent columns of one token for the output store)
+      f32x4 W[2][NT], OT[NT][2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * mt + 4 * g4 + i;
-          const float vp =
-              ps.beta[t] * (bf16_to_f32(cr.v[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
-          _Float16 hh, ll;
-          split_f16(vp, hh, ll);
-          Vh[nt][4 * mt + i] = hh;
-          Vl[nt][4 * mt + i] = ll;
+        for (int nt = 0; nt < NT; ++nt) { W[mt][nt] = z; OT[nt][mt] = z; }
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        // fp16 S of K step p (key rows 32p..32p+31) as B (and, transposed, A) operand
+        f16x8 Sb[NT];
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            Sb[nt][i] = static_cast<_Float16>(S[2 * p][nt][i]);
+            Sb[nt][4 + i] = static_cast<_Float16>(S[2 * p + 1][nt][i]);
+          }
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt) {
+          const f16x8 akg = *reinterpret_cast<const f16x8*>(&sc.Kg[16 * mt + l16][32 * p + 8 * g4]);
+          const f16x8 aqg = *reinterpret_cast<const f16x8*>(&sc.Qg[16 * mt + l16][32 * p + 8 * g4]);
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) {
+            W[mt][nt] = mfma_f16(akg, Sb[nt], W[mt][nt]);
+            OT[nt][mt] = mfma_f16(Sb[nt], aqg, OT[nt][mt]);
+          }
         }
-    reduce_pairs(ps, tid, [&](int r, int s, float m) {
-      sm.Mqk[r][kslot(s)] = static_cast<_Float16>(m);
-    });
-    __syncthreads();
-    invert_unit_lower(ps, tid, [&](int r, int s, float t) {
-      sm.T[r][kslot(s)] = static_cast<_Float16>(t);
-    });
-    __syncthreads();
-
-    // ---- the rest of the state chain on this wave's 16 * NT value columns
-    {
+      }
+      // V' = b (V - W) as hi + lo fp16 B operands (K = token, permuted)
+      f16x8 Vh[NT], Vl[NT];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * mt + 4 * g4 + i;
+            const float vp = sc.beta[t] * (bf16_to_f32(sc.v[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
+            _Float16 hh, ll;
+            split_f16(vp, hh, ll);
+            Vh[nt][4 * mt + i] = hh;
+            Vl[nt][4 * mt + i] = ll;
+          }
+      // U = T V'
       f32x4 U[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const f16x8 at = *reinterpret_cast<const f16x8*>(&sm.T[16 * mt + l16][8 * g4]);
+        const f16x8 at = *reinterpret_cast<const f16x8*>(&sc.T[16 * mt + l16][8 * g4]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
           U[mt][nt] = mfma_f16(at, Vh[nt], z);
@@ -274,8 +335,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
       // S = Diag(2^{G_L}) S + Kr^T U
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
-        const f16x8 akr = *reinterpret_cast<const f16x8*>(&sm.KrT[16 * mt + l16][8 * g4]);
-        const f32x4 d = *reinterpret_cast<const f32x4*>(&ps.dec[16 * mt + 4 * g4]);
+        const f16x8 akr = *reinterpret_cast<const f16x8*>(&sc.KrT[16 * mt + l16][8 * g4]);
+        const f32x4 d = *reinterpret_cast<const f32x4*>(&sc.dec[16 * mt + 4 * g4]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
 #pragma unroll
@@ -284,46 +345,63 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(PrefillArgs a, float
           S[mt][nt] = mfma_f16(akr, Ul[nt], S[mt][nt]);
         }
       }
-      // O = scale (O0 + Mqk U)
+      // O^T += U^T Mqk^T, then O = scale O0 stored as 4 adjacent bf16 columns
+      // per lane (rows t >= L of a final partial chunk fall outside the
+      // buffer range and are dropped)
+      const __amdgpu_buffer_rsrc_t orsrc =
+          make_buffer(a.out + ((int64_t)t0 * H + h) * D, (uint32_t)(((L - 1) * H + 1) * D * 2));
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) {
-        const f16x8 am = *reinterpret_cast<const f16x8*>(&sm.Mqk[16 * mt + l16][8 * g4]);
+        const f16x8 am = *reinterpret_cast<const f16x8*>(&sc.Mqk[16 * mt + l16][8 * g4]);
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt) {
-          O[mt][nt] = mfma_f16(am, Uh[nt], O[mt][nt]);
-          O[mt][nt] = mfma_f16(am, Ul[nt], O[mt][nt]);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int t = 16 * mt + 4 * g4 + i;
-            if (t < L)
-              a.out[((int64_t)(t0 + t) * H + h) * D + col_base + colw + 16 * nt + l16] =
-                  f32_to_bf16(a.scale * O[mt][nt][i]);
-          }
+          OT[nt][mt] = mfma_f16(Uh[nt], am, OT[nt][mt]);
+          OT[nt][mt] = mfma_f16(Ul[nt], am, OT[nt][mt]);
+          const int t = 16 * mt + l16;
+          u32x2 pk;
+          pk[0] = (uint32_t)f32_to_bf16(a.scale * OT[nt][mt][0]) |
+                  ((uint32_t)f32_to_bf16(a.scale * OT[nt][mt][1]) << 16);
+          pk[1] = (uint32_t)f32_to_bf16(a.scale * OT[nt][mt][2]) |
+                  ((uint32_t)f32_to_bf16(a.scale * OT[nt][mt][3]) << 16);
+          __builtin_amdgcn_raw_buffer_store_b64(
+              pk, orsrc, (uint32_t)((t * H * D + col_base + colw + 16 * nt + 4 * g4) * 2), 0, 0);
         }
       }
+      // checkpoint after every ck_per full chunks (counters instead of a
+      // division per chunk)
+      if (s + 1 == ck_next) {
+        if (L == CH) store_state(a.ckpt + (ck_row * H + h) * (int64_t)(D * D));
+        ck_next += ck_per;
+        ++ck_row;
+      }
     }
-    if (float* cp = prefill_checkpoint(a, n, h, bos, t0 + L - bos)) store_state(cp);
+    __syncthreads();   // B2
+    __syncthreads();   // B3
+    __syncthreads();   // B4
+    __syncthreads();   // B5
+    __syncthreads();   // B6
   }
 
   if (const StateRef s1 = prefill_final_state(a, n, h)) {
     if (!s1.bf16) {
       store_state(static_cast<float*>(s1.p));
     } else {
-      uint16_t* dst = static_cast<uint16_t*>(s1.p);
+      const __amdgpu_buffer_rsrc_t r = make_buffer(s1.p, (uint32_t)(D * D * 2));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
         for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
           for (int i = 0; i < 4; ++i)
-            dst[(16 * mt + 4 * g4 + i) * D + col_base + colw + 16 * nt + l16] = f32_to_bf16(S[mt][nt][i]);
+            buffer_store_u16(f32_to_bf16(S[mt][nt][i]), r,
+                             lane_elem * 2 + (uint32_t)(((16 * mt + i) * D + col_base + 16 * nt) * 2));
     }
   }
 }
 
 template <int MODE, int NT, bool FE>
 hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
-  constexpr size_t bytes = sizeof(FusedSmem<64 * NT>);
+  constexpr size_t bytes = sizeof(RingSmem<64 * NT>);
   static_assert(bytes <= 160 * 1024, "the fused kernel's LDS exceeds a compute unit's 160 KiB");
   static bool attr_set = false;   // idempotent; a race only repeats the call
   if (!attr_set) {
@@ -334,7 +412,7 @@ hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
   }
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
   prefill_chunk_kernel<MODE, NT, FE>
-      <<<dim3(2 / NT, a.num_heads, a.num_seqs), 256, bytes, s>>>(a, exp2C);
+      <<<dim3(2 / NT, a.num_heads, a.num_seqs), kThreads, bytes, s>>>(a, exp2C);
   return hipGetLastError();
 }
 
@@ -346,7 +424,6 @@ hipError_t launch_prefill_chunk(const PrefillArgs& a, int anchor_mode, int dv_sp
   if (dv_split != 1 && dv_split != 2) return hipErrorInvalidValue;
   const int nt = dv_split == 1 ? 2 : 1;
   // data-dependent anchors and the input front-end: 64-column blocks only
-  // (their 128-column variants would exceed the register file)
   if ((anchor_mode == 2 || frontend_active(a.fe)) && dv_split != 2) return hipErrorInvalidValue;
   if (frontend_active(a.fe)) {
     if (anchor_mode == 0) return launch_variant<0, 1, true>(a, s);
