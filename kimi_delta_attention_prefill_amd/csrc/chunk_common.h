@@ -76,81 +76,123 @@ struct ChunkOps {
 // The producers' working memory for one chunk: the gate prefix, and, over
 // its bytes once the anchored operands are built, the triangular system and
 // its inverse.  The split-K partials of the pairwise products live over the
-// chunk's own q/k/g rows once every producer has built its operands.
+// chunk's own q/k/g rows (part_entry).
 struct PrepWork {
   float G[CH][GP];             // log2-domain inclusive gate prefix
   float EL[D];                 // fixed anchor: 2^{G_L - C}
+  // 16-token anchors (h = 8 lb log2 e, the half anchors h and G_15 + h): per
+  // channel 2^{G_15 + h}, 2^{G_L - h}, 2^{G_L - G_15 - h}, 2^{G_15 - h}, so
+  // that each element needs only its two anchored factors from the
+  // exponential unit and the rest are products with these
+  float K16[4][D];
   float rq[CH], rk[CH];        // q/k L2-norm scales per token (1 without the front-end norm)
 };
-typedef float PartTiles[4][6][64][4];   // split-K partials of the six Mqk/Akk tiles
-static_assert(sizeof(PartTiles) <= sizeof(ChunkQKG), "partials must fit over the q/k/g rows");
+// Split-K partials of the six Mqk/Akk tiles, 16 bytes per (wave w, tile p,
+// lane): entry e = 64 p + lane of wave w lies in the bytes [64 w, 64 w + 64)
+// of the chunk's q, k and g rows -- the key channels 32w..32w+31, which only
+// wave w reads (96 row segments of 64 bytes: array e / 128, row (e / 4) % 32)
+// -- so each wave stores its partials as soon as its own products are done.
+__device__ __forceinline__ float* part_entry(ChunkQKG& cr, int w, int p, int lane) {
+  const int e = 64 * p + lane, seg = e >> 2;
+  unsigned char* base = reinterpret_cast<unsigned char*>(&cr);
+  return reinterpret_cast<float*>(base + (seg >> 5) * (int)sizeof(cr.q) + (seg & 31) * (RP * 2) +
+                                  64 * w + 16 * (e & 3));
+}
 struct InvWork {
   float At[CH][CH + 4];        // (Diag(b) stril(Akk))^T, FP32; rows 16-byte aligned
   float Tf[CH][CH + 1];        // (I + A)^{-1}, FP32
-  float X[16][17];             // A21 T11
+  float X[16][17];             // W = T22 A21
 };
 static_assert(sizeof(InvWork) <= sizeof(float) * CH * GP, "inverse work must fit over G");
 
-__device__ __forceinline__ PartTiles& part_of(ChunkQKG& cr) {
-  return *reinterpret_cast<PartTiles*>(&cr);
-}
 __device__ __forceinline__ InvWork& inv_of(PrepWork& pw) {
   return *reinterpret_cast<InvWork*>(&pw.G[0][0]);
 }
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Step 1: the q, k, g rows of the chunk [t0, t0 + L) of head h, by
-// range-checked buffer loads straight into the padded rows of `cr` (no
-// registers are held; a wave's 4-byte load fills 256 consecutive bytes of
-// LDS, lane i the i-th word, i.e. one row), and the chunk's beta into a
-// register.  Rows t >= L lie outside the range and land as zeros.  256
-// threads.
-__device__ __forceinline__ void fetch_qkg(ChunkQKG& cr, uint16_t& beta_raw, const PrefillArgs& a,
-                                          int t0, int L, int h, int tid) {
-  const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
+// Block barrier that orders LDS accesses only: the LDS writes before it are
+// complete and visible after it, while global loads and stores (and the
+// direct global-to-LDS loads, which their issuer waits for explicitly) stay in
+// flight across it.  __syncthreads() would also wait for every outstanding
+// global access, exposing a prefetch's whole latency at the next barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Ordering of one wave's own LDS accesses (a write, then reads of it by other
+// lanes of the same wave): LDS operations of a wave complete in order, so only
+// the compiler must not move them across this point.
+__device__ __forceinline__ void wave_lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+}
+
+// Step 1: the chunk [t0, t0 + L) of head h -- its q, k, g rows and the value
+// columns [col0, col0 + DVS) -- fetched into registers by 16-byte buffer
+// loads (16 consecutive threads read one 256-byte row: coalesced), so that a
+// block can load the next chunk while it works on the current one and write
+// it to LDS (stage_chunk) at a point of its choosing.  The loads are range
+// checked: rows t >= L read as zeros.  256 threads.
+template <int DVS>
+struct ChunkRegs {
+  static constexpr int kV = DVS / 64;   // 16-byte pieces of the value rows per thread
+  uint4 q[2], k[2], g[2], v[kV];
+  uint16_t beta;
+};
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <int DVS>
+__device__ __forceinline__ void fetch_chunk(ChunkRegs<DVS>& x, const PrefillArgs& a, int t0, int L,
+                                            int h, int col0, int tid) {
+  const int H = a.num_heads;
   const int64_t base = ((int64_t)t0 * H + h) * D;
   const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
   const uint32_t row_bytes = (uint32_t)H * D * 2;
   const __amdgpu_buffer_rsrc_t rq = make_buffer(a.q + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rk = make_buffer(a.k + base, rows_bytes);
   const __amdgpu_buffer_rsrc_t rg = make_buffer(a.g + base, rows_bytes);
-#pragma unroll
-  for (int i = 0; i < CH / 4; ++i) {   // wave w: rows w, w + 4, ...
-    const int t = wave + 4 * i;
-    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)lane * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rq, (lds_void*)&cr.q[t][0], 4, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void*)&cr.k[t][0], 4, off, 0, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rg, (lds_void*)&cr.g[t][0], 4, off, 0, 0, 0);
-  }
-  beta_raw = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
-}
-
-// The value columns [col0, col0 + DVS) of the same chunk into v (unpadded
-// rows; rows t >= L land as zeros).  256 threads.
-template <int DVS>
-__device__ __forceinline__ void fetch_v(uint16_t (&v)[CH][DVS], const PrefillArgs& a, int t0,
-                                        int L, int h, int col0, int tid) {
-  const int H = a.num_heads, wave = tid >> 6, lane = tid & 63;
-  const int64_t base = ((int64_t)t0 * H + h) * D;
-  const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
-  const uint32_t row_bytes = (uint32_t)H * D * 2;
   const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
-  constexpr int kRowsPerLoad = 128 / DVS;            // value rows per 256-byte load
-  constexpr int kLanesPerRow = 64 / kRowsPerLoad;
 #pragma unroll
-  for (int i = 0; i < CH / (4 * kRowsPerLoad); ++i) {
-    const int r0 = (wave + 4 * i) * kRowsPerLoad;    // first row of this load
-    const int t = r0 + lane / kLanesPerRow;
-    const uint32_t off = (uint32_t)t * row_bytes + (uint32_t)col0 * 2 + (uint32_t)(lane % kLanesPerRow) * 4;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void*)&v[r0][0], 4, off, 0, 0, 0);
+  for (int i = 0; i < 2; ++i) {   // piece tid + 256 i: row / 16, 16-byte chunk % 16
+    const int e = tid + 256 * i;
+    const uint32_t off = (uint32_t)(e >> 4) * row_bytes + (uint32_t)(e & 15) * 16;
+    x.q[i] = load16(rq, off);
+    x.k[i] = load16(rk, off);
+    x.g[i] = load16(rg, off);
   }
+  constexpr int kCh = DVS / 8;    // 16-byte chunks per value row
+#pragma unroll
+  for (int i = 0; i < ChunkRegs<DVS>::kV; ++i) {
+    const int e = tid + 256 * i;
+    x.v[i] = load16(rv, (uint32_t)(e / kCh) * row_bytes + (uint32_t)col0 * 2 + (uint32_t)(e % kCh) * 16);
+  }
+  x.beta = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
 }
 
-// Wait for this wave's direct loads; the caller's next barrier makes every
-// wave's visible.
-__device__ __forceinline__ void fetch_wait() {
-  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0); expcnt and lgkmcnt not waited for
+// Writes the fetched rows into the padded q/k/g rows of `cr` and the value
+// rows `v`.  256 threads.
+template <int DVS>
+__device__ __forceinline__ void stage_chunk(ChunkQKG& cr, uint16_t (&v)[CH][DVS],
+                                            const ChunkRegs<DVS>& x, int tid) {
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = tid + 256 * i, t = e >> 4, c = (e & 15) * 8;
+    *reinterpret_cast<uint4*>(&cr.q[t][c]) = x.q[i];
+    *reinterpret_cast<uint4*>(&cr.k[t][c]) = x.k[i];
+    *reinterpret_cast<uint4*>(&cr.g[t][c]) = x.g[i];
+  }
+  constexpr int kCh = DVS / 8;
+#pragma unroll
+  for (int i = 0; i < ChunkRegs<DVS>::kV; ++i) {
+    const int e = tid + 256 * i;
+    *reinterpret_cast<uint4*>(&v[e / kCh][(e % kCh) * 8]) = x.v[i];
+  }
 }
 
 // The chunk's beta (zero for padding tokens), through the front-end's
@@ -199,7 +241,7 @@ __device__ __forceinline__ void qk_norms(PrepWork& pw, const ChunkQKG& cr, const
 // would not be zero.
 template <int MODE, bool FE>
 __device__ __forceinline__ void gate_prefix(PrepWork& pw, float* dec, const ChunkQKG& cr,
-                                            const FrontEnd& fe, float C, int L, int tid) {
+                                            const FrontEnd& fe, float C, float Ch, int L, int tid) {
   const int lane = tid & 63, c = 32 * (tid >> 6) + (lane & 31), hf = lane >> 5;
   float pre[16];
   float acc = 0.f;
@@ -218,7 +260,14 @@ __device__ __forceinline__ void gate_prefix(PrepWork& pw, float* dec, const Chun
   if (hf) {
     const float GL = (base + acc) * kLog2e;
     dec[c] = fast_exp2(GL);
-    pw.EL[c] = MODE == 0 ? fast_exp2(GL - C) : 0.f;
+    if (MODE == 0) pw.EL[c] = fast_exp2(GL - C);
+    if (MODE == 1) {
+      const float G15 = base * kLog2e;
+      pw.K16[0][c] = fast_exp2(G15 + Ch);
+      pw.K16[1][c] = fast_exp2(GL - Ch);
+      pw.K16[2][c] = fast_exp2(GL - G15 - Ch);
+      pw.K16[3][c] = fast_exp2(G15 - Ch);
+    }
   }
 }
 
@@ -252,9 +301,17 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
     const f32x4 G1 = *reinterpret_cast<const f32x4*>(&pw.G[t][cb + cl + 4]);
     const uint4 qw = *reinterpret_cast<const uint4*>(&cr.q[t][cb + cl]);
     const uint4 kw = *reinterpret_cast<const uint4*>(&cr.k[t][cb + cl]);
-    f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1;
+    f32x4 Gs0, Gs1, GL0, GL1, EL0, EL1, Gf0, Gf1, Ka0, Ka1, Kb0, Kb1;
     const float rq = FE ? pw.rq[t] : 1.f, rk = FE ? pw.rk[t] : 1.f;
-    if (MODE >= 1) {
+    if (MODE == 1) {
+      Gs0 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl]);
+      Gs1 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl + 4]);
+      // half 0: the R and fo constants; half 1: the P and R constants
+      Ka0 = *reinterpret_cast<const f32x4*>(&pw.K16[half ? 0 : 1][cb + cl]);
+      Ka1 = *reinterpret_cast<const f32x4*>(&pw.K16[half ? 0 : 1][cb + cl + 4]);
+      Kb0 = *reinterpret_cast<const f32x4*>(&pw.K16[half ? 2 : 3][cb + cl]);
+      Kb1 = *reinterpret_cast<const f32x4*>(&pw.K16[half ? 2 : 3][cb + cl + 4]);
+    } else if (MODE == 2) {
       Gs0 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl]);
       Gs1 = *reinterpret_cast<const f32x4*>(&pw.G[15][cb + cl + 4]);
       GL0 = *reinterpret_cast<const f32x4*>(&pw.G[CH - 1][cb + cl]);
@@ -280,21 +337,32 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         em = fast_exp2(C - Gv);                       // 2^{C-G}
         P = ep * exp2C;                               // 2^G
         R = (j < 4 ? EL0[j] : EL1[j - 4]) * em;       // 2^{G_L - G}
+      } else if (MODE == 1) {
+        // anchor Ch = h (half 0) or G_15 + h (half 1), h = 8 lb log2 e; the
+        // factors below 2^-126 that a constant can lose belong to operands
+        // far below fp16's range (they are zero either way)
+        const float c1 = j < 4 ? Ka0[j] : Ka1[j - 4], c2 = j < 4 ? Kb0[j] : Kb1[j - 4];
+        const float Ch = (half ? (j < 4 ? Gs0[j] : Gs1[j - 4]) : 0.f) + a.half_anchor_log2;
+        ep = fast_exp2(Gv - Ch);
+        em = fast_exp2(Ch - Gv);
+        if (half) {
+          P = ep * c1;                                // 2^{G_15 + h} 2^{G - G_15 - h}
+          R = em * c2;                                // 2^{G_L - G_15 - h} 2^{G_15 + h - G}
+          fo = ep * exp2C;                            // 2^{G - G_15} = 2^{G - Ch} 2^h
+        } else {
+          P = ep * exp2C;                             // 2^h 2^{G - h}
+          R = em * c1;                                // 2^{G_L - h} 2^{h - G}
+          fo = em * c2;                               // 2^{G_15 - h} 2^{h - G}
+        }
       } else {
         const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
         const float gl = j < 4 ? GL0[j] : GL1[j - 4];
-        if (MODE == 1) {
-          const float Ch = (half ? g15 : 0.f) + a.half_anchor_log2;
-          ep = fast_exp2(Gv - Ch);
-          em = fast_exp2(Ch - Gv);
-        } else {
-          // midpoint of this half's actual range; exponents clamped so that a
-          // half that decays a channel past 2^-252 stays finite
-          const float gf = j < 4 ? Gf0[j] : Gf1[j - 4];
-          const float Ch = 0.5f * (gf + (half ? gl : g15));
-          ep = fast_exp2(__builtin_fminf(Gv - Ch, 126.f));
-          em = fast_exp2(__builtin_fminf(Ch - Gv, 126.f));
-        }
+        // midpoint of this half's actual range; exponents clamped so that a
+        // half that decays a channel past 2^-252 stays finite
+        const float gf = j < 4 ? Gf0[j] : Gf1[j - 4];
+        const float Ch = 0.5f * (gf + (half ? gl : g15));
+        ep = fast_exp2(__builtin_fminf(Gv - Ch, 126.f));
+        em = fast_exp2(__builtin_fminf(Ch - Gv, 126.f));
         fo = half ? fast_exp2(Gv - g15) : fast_exp2(g15 - Gv);  // both <= 1
         P = fast_exp2(Gv);
         R = fast_exp2(gl - Gv);
@@ -351,10 +419,11 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
   acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
 }
 
-__device__ __forceinline__ void pair_store(PartTiles& part, const f32x4 (&acc)[6], int wave,
-                                           int lane) {
+// Stores this wave's partials over its own key-channel columns of the rows
+// (part_entry); call after its last read of the rows.
+__device__ __forceinline__ void pair_store(ChunkQKG& cr, const f32x4 (&acc)[6], int wave, int lane) {
 #pragma unroll
-  for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(&part[wave][p][lane][0]) = acc[p];
+  for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(part_entry(cr, wave, p, lane)) = acc[p];
 }
 
 // Step 3b: sum the four split-K partials in a fixed order, mask the causal
@@ -362,11 +431,12 @@ __device__ __forceinline__ void pair_store(PartTiles& part, const f32x4 (&acc)[6
 // Akk by beta.  Writes iw.At (A transposed); emit_mqk(r, s, value) sees every
 // Mqk entry (zero above the diagonal).  256 threads.
 template <class EmitMqk>
-__device__ __forceinline__ void reduce_pairs(InvWork& iw, const PartTiles& part, const float* beta,
-                                             int tid, EmitMqk&& emit_mqk) {
+__device__ __forceinline__ void reduce_pairs(InvWork& iw, ChunkQKG& cr, const float* beta, int tid,
+                                             EmitMqk&& emit_mqk) {
   const int ln = tid >> 2, i = tid & 3;
   auto sum4 = [&](int p) __attribute__((always_inline)) {
-    return ((part[0][p][ln][i] + part[1][p][ln][i]) + part[2][p][ln][i]) + part[3][p][ln][i];
+    return ((part_entry(cr, 0, p, ln)[i] + part_entry(cr, 1, p, ln)[i]) + part_entry(cr, 2, p, ln)[i]) +
+           part_entry(cr, 3, p, ln)[i];
   };
 #pragma unroll
   for (int q4 = 0; q4 < 4; ++q4) {   // 16x16 quadrants (0,0) (1,0) (1,1) (0,1); the last is zero
@@ -381,47 +451,72 @@ __device__ __forceinline__ void reduce_pairs(InvWork& iw, const PartTiles& part,
   }
 }
 
-// Steps 4a-4c: T = (I + A)^{-1}, in three phases separated by the caller's
-// barriers.  Phase 1: the 16x16 diagonal blocks in FP32 by forward
-// substitution (producer wave 0, one column per lane).  Phase 2: X = A21 T11.
-// Phase 3: T21 = -T22 X and T12 = 0; every entry (i, m) of each quadrant goes
-// to emit_t(row, col, value) (the caller stores the MFMA operand).  256
-// threads.
-__device__ __forceinline__ void invert_diag(InvWork& iw, int tid) {
-  const int wave = tid >> 6, lane = tid & 63;
-  if (wave == 0 && lane < 32) {
-    const int base = 16 * (lane >> 4), m = lane & 15;
+// Steps 4a-4c: T = (I + A)^{-1} in two phases separated by the caller's
+// barrier.  With T11, T22 the inverses of the 16x16 diagonal blocks of I + A
+// and A21 its lower-left block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.
+// Phase 1 (producer waves 0 and 1, block b = wave): lanes 0-15 invert the
+// diagonal block by forward substitution in FP32, one column each, with the
+// block's whole strict lower triangle read into registers first so that the
+// 16 dependent steps wait on no LDS read; wave 1 then forms W (lane (iq, m):
+// rows 4 iq..4 iq+3 of column m) from its own T22, its LDS round trip
+// ordered by wave_lds_fence.  Diagonal blocks go to emit_t(row, col, value)
+// (the caller stores the MFMA operand).  Phase 2 (256 threads): T21 = -W T11
+// and T12 = 0, one entry (and its zero twin) per thread.
+template <class EmitT>
+__device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int lane, EmitT&& emit_t) {
+  if (wave > 1) return;
+  const int base = 16 * wave;
+  if (lane < 16) {
+    const int m = lane;
+    // column j of the block below the diagonal = row j of At; quads q >= j / 4
+    // hold rows i > j.  Two rounds of eight columns (28 and 12 quads), so the
+    // registers for the triangle stay within the wave's budget.
     float x[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      // column j of the block below the diagonal: row j of At, four 16-byte reads
-      f32x4 c[4];
+    for (int j0 = 0; j0 < 16; j0 += 8) {
+      f32x4 c[8][4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) c[q] = *reinterpret_cast<const f32x4*>(&iw.At[base + j][base + 4 * q]);
+      for (int j = j0; j < j0 + 8; ++j)
 #pragma unroll
-      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[i >> 2][i & 3], x[j], x[i]);
+        for (int q = j >> 2; q < 4; ++q)
+          c[j - j0][q] = *reinterpret_cast<const f32x4*>(&iw.At[base + j][base + 4 * q]);
+#pragma unroll
+      for (int j = j0; j < j0 + 8; ++j)
+#pragma unroll
+        for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[j - j0][i >> 2][i & 3], x[j], x[i]);
+      __builtin_amdgcn_sched_barrier(0);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) iw.Tf[base + i][base + m] = x[i];
+    for (int i = 0; i < 16; ++i) {
+      iw.Tf[base + i][base + m] = x[i];
+      emit_t(base + i, base + m, x[i]);
+    }
+  }
+  if (wave == 1) {
+    wave_lds_fence();
+    const int iq = lane >> 4, m = lane & 15;
+    // A21[:, m] = row m of At, columns 16..31
+    f32x4 a21[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a21[q] = *reinterpret_cast<const f32x4*>(&iw.At[m][16 + 4 * q]);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int i = 4 * iq + r;
+      float acc = 0.f;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) acc = fmaf(iw.Tf[16 + i][16 + j], a21[j >> 2][j & 3], acc);
+      iw.X[i][m] = acc;
+    }
   }
 }
-__device__ __forceinline__ void invert_offdiag_x(InvWork& iw, int tid) {
-  const int i = tid >> 4, m = tid & 15;
-  float acc = 0.f;
-#pragma unroll
-  for (int j = 0; j < 16; ++j) acc = fmaf(iw.At[j][16 + i], iw.Tf[j][m], acc);
-  iw.X[i][m] = acc;
-}
 template <class EmitT>
-__device__ __forceinline__ void invert_finish(const InvWork& iw, int tid, EmitT&& emit_t) {
+__device__ __forceinline__ void invert_offdiag(const InvWork& iw, int tid, EmitT&& emit_t) {
   const int i = tid >> 4, m = tid & 15;
   float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) acc = fmaf(iw.Tf[16 + i][16 + j], iw.X[j][m], acc);
-  emit_t(i, m, iw.Tf[i][m]);
-  emit_t(16 + i, 16 + m, iw.Tf[16 + i][16 + m]);
+  for (int k = 0; k < 16; ++k) acc = fmaf(iw.X[i][k], iw.Tf[k][m], acc);
   emit_t(16 + i, m, -acc);
   emit_t(i, 16 + m, 0.f);
 }

@@ -43,8 +43,10 @@
 //     from slot c % 2 on their own 16 * NT value columns (value columns
 //     evolve independently, so the chain needs no cross-wave exchange); the
 //     FP32 state stays in their MFMA accumulators for the whole sequence.
-// Both sides meet at the same block barriers (a fixed number per chunk), so a
-// chunk costs about the longer of the two sides rather than their sum.  LDS
+// Both sides meet at the same four block barriers per chunk (barriers that
+// order LDS only, so prefetches and output stores stay in flight across
+// them), so a chunk costs about the longer of the two sides rather than their
+// sum.  LDS
 // per block (DVS = 128): two raw q/k/g buffers (2 x 25.5 KiB; the split-K
 // partials of a chunk live over its own rows once its operands are built),
 // the producers' gate prefix (16.5 KiB; the triangular system and its
@@ -140,32 +142,37 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
 
   if (producer) {
     // ------------------------------------------------------------ producers
-    // The first chunk's rows go to raw[0] before the pipeline starts.
-    uint16_t beta_raw = 0;
-    if (nch > 0) fetch_qkg(sm.raw[0], beta_raw, a, bos, min(CH, eos - bos), h, ptid);
+    // Chunk c's rows are fetched into registers during step c-2 and written
+    // to LDS at that step's end: its q/k/g rows into raw[c % 2] (free since
+    // chunk c-2 was prepared from it) and its value rows into ring slot c % 2
+    // (the consumers finish reading chunk c-2's values before the last phase
+    // of step c-2).  The first chunk is staged before the pipeline starts.
+    ChunkRegs<DVS> x;
+    if (nch > 0) {
+      fetch_chunk(x, a, bos, min(CH, eos - bos), h, col_base, ptid);
+      stage_chunk(sm.raw[0], sm.slot[0].v, x, ptid);
+    }
     // Step s (s = -1 .. nch-1): chunk s+1 is prepared into ring slot (s+1) % 2
     // while the consumers run the chain of chunk s.  Every wave passes the
-    // same seven barriers per step.
+    // same five barriers per step.
     for (int s = -1; s < nch; ++s) {
       const bool prep = s + 1 < nch;
       ChunkQKG& cr = sm.raw[(s + 1) & 1];          // chunk s+1's rows
       ChunkOps<DVS>& sn = sm.slot[(s + 1) & 1];    // chunk s+1's ring slot
       const int tn0 = bos + CH * (s + 1), Ln = min(CH, eos - tn0);
-      fetch_wait();    // chunk s+1's rows and chunk s's values (issued in step s-1)
-      // B0: raw rows of chunk s+1 and slot s (with its values) complete; the
-      // consumers are done with slot s-1, the producers with raw[s & 1].
-      __syncthreads();
+      // B0: chunk s+1's rows and values and chunk s's slot are complete; the
+      // consumers are done with slot s-1 (except its values, already chunk
+      // s+1's), the producers with the inverse's work space.
+      lds_barrier();
       if (prep) {
-        stage_beta<FE>(sn.beta, beta_raw, a.fe, Ln, ptid);
-        if (s + 2 < nch)
-          fetch_qkg(sm.raw[s & 1], beta_raw, a, tn0 + CH, min(CH, eos - tn0 - CH), h, ptid);
-        fetch_v(sn.v, a, tn0, Ln, h, col_base, ptid);
-        gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, Ln, ptid);
+        stage_beta<FE>(sn.beta, x.beta, a.fe, Ln, ptid);
+        if (s + 2 < nch) fetch_chunk(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
+        gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, a.half_anchor_log2, Ln, ptid);
         if (FE) qk_norms(sm.pw, cr, a, ptid);
       }
-      __syncthreads();   // B1: gate prefix, beta and decays of chunk s+1 written
-      f32x4 pacc[6];
+      lds_barrier();   // B1: gate prefix, anchor constants, beta and decays of chunk s+1 written
       if (prep) {
+        f32x4 pacc[6];
         pair_products<MODE, FE>(pacc, sm.pw, cr, a, C, exp2C, pwave, lane,
                           [&](int t, int c0, const float* kv, const float* qv, const float* P,
                               const float* R) {
@@ -187,23 +194,19 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
                             *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl)]) = qg_lo;
                             *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
                           });
+        pair_store(cr, pacc, pwave, lane);   // over this wave's own columns of the rows
       }
-      __syncthreads();   // B2: every producer has built its operands from chunk s+1's rows
-      if (prep) pair_store(part_of(cr), pacc, pwave, lane);
-      __syncthreads();   // B3: split-K partials of chunk s+1 complete
+      lds_barrier();   // B2: split-K partials of chunk s+1 complete
       if (prep)
-        reduce_pairs(inv_of(sm.pw), part_of(cr), sn.beta, ptid, [&](int r, int c, float m) {
+        reduce_pairs(inv_of(sm.pw), cr, sn.beta, ptid, [&](int r, int c, float m) {
           sn.Mqk[r][kslot(c)] = static_cast<_Float16>(m);
         });
-      __syncthreads();   // B4: the triangular system of chunk s+1 is in place
-      if (prep) invert_diag(inv_of(sm.pw), ptid);
-      __syncthreads();   // B5
-      if (prep) invert_offdiag_x(inv_of(sm.pw), ptid);
-      __syncthreads();   // B6
-      if (prep)
-        invert_finish(inv_of(sm.pw), ptid, [&](int r, int c, float t) {
-          sn.T[r][kslot(c)] = static_cast<_Float16>(t);
-        });
+      lds_barrier();   // B3: the triangular system of chunk s+1 is in place
+      auto emit_t = [&](int r, int c, float t) { sn.T[r][kslot(c)] = static_cast<_Float16>(t); };
+      if (prep) invert_diag_blocks(inv_of(sm.pw), pwave, lane, emit_t);
+      lds_barrier();   // B4: T11, T22 and W = T22 A21 in place; the consumers are done with slot s
+      if (prep) invert_offdiag(inv_of(sm.pw), ptid, emit_t);
+      if (s + 2 < nch) stage_chunk(sm.raw[s & 1], sm.slot[s & 1].v, x, ptid);   // chunk s+2
     }
     return;
   }
@@ -258,16 +261,33 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
   int64_t ck_row = a.ckpt ? (int64_t)n + bos / a.ckpt_tokens : 0;
   for (int s = -1; s < nch; ++s) {
     const ChunkOps<DVS>& sc = sm.slot[s & 1];    // chunk s's ring slot
-    __syncthreads();   // B0
-    __syncthreads();   // B1
+    lds_barrier();   // B0
+    lds_barrier();   // B1
+    lds_barrier();   // B2
+    // ---- the state chain of chunk s on this wave's 16 * NT value columns,
+    // beside the producers' reduction (part A) and inverse (part B), the
+    // phases that leave most of the producers' issue slots free
+    f32x4 OT[NT][2];
+    f16x8 Uh[NT], Ul[NT];
+    const int t0 = bos + CH * s, L = min(CH, eos - t0);
     if (s >= 0) {
-      // ---- the state chain of chunk s on this wave's 16 * NT value columns
-      const int t0 = bos + CH * s, L = min(CH, eos - t0);
       const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      // this lane's value entries (tokens 16 mt + 4 g4 + i, column 16 nt +
+      // l16), read before the products so that the reads are in flight together
+      float vv[NT][2][4];
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            vv[nt][mt][i] = sc.beta[16 * mt + 4 * g4 + i] * bf16_to_f32(sc.v[16 * mt + 4 * g4 + i][colw + 16 * nt + l16]);
+      // the value and beta reads as one group ahead of the products
+      __builtin_amdgcn_sched_group_barrier(0x0100, 16 * NT + 8, 0);
       // W = Kg S (rows = tokens) and O^T = S^T Qg^T (rows = value columns: the
       // same fragments with A and B swapped, so each lane ends with 4
       // adjacent columns of one token for the output store)
-      f32x4 W[2][NT], OT[NT][2];
+      f32x4 W[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -303,7 +323,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * mt + 4 * g4 + i;
-            const float vp = sc.beta[t] * (bf16_to_f32(sc.v[t][colw + 16 * nt + l16]) - W[mt][nt][i]);
+            const float vp = vv[nt][mt][i] - sc.beta[t] * W[mt][nt][i];
             _Float16 hh, ll;
             split_f16(vp, hh, ll);
             Vh[nt][4 * mt + i] = hh;
@@ -320,7 +340,6 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
           U[mt][nt] = mfma_f16(at, Vl[nt], U[mt][nt]);
         }
       }
-      f16x8 Uh[NT], Ul[NT];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -332,6 +351,9 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
             Uh[nt][4 * mt + i] = hh;
             Ul[nt][4 * mt + i] = ll;
           }
+    }
+    lds_barrier();   // B3
+    if (s >= 0) {
       // S = Diag(2^{G_L}) S + Kr^T U
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) {
@@ -375,11 +397,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
         ++ck_row;
       }
     }
-    __syncthreads();   // B2
-    __syncthreads();   // B3
-    __syncthreads();   // B4
-    __syncthreads();   // B5
-    __syncthreads();   // B6
+    lds_barrier();   // B4
   }
 
   if (const StateRef s1 = prefill_final_state(a, n, h)) {
@@ -410,7 +428,10 @@ hipError_t launch_variant(const PrefillArgs& a, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
+  // the anchor's power of two: 2^C (one anchor per chunk) or 2^h, h = 8 lb
+  // log2 e (16-token anchors)
+  const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2)
+                                : MODE == 1 ? std::exp2(a.half_anchor_log2) : 0.f;
   prefill_chunk_kernel<MODE, NT, FE>
       <<<dim3(2 / NT, a.num_heads, a.num_seqs), kThreads, bytes, s>>>(a, exp2C);
   return hipGetLastError();
