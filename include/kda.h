@@ -147,9 +147,10 @@ typedef struct {
   int32_t block_threads;
   int64_t grid_blocks;
   float anchor_log2;   /* C = 16 * lower_bound * log2(e), as used on device */
-  int32_t windows;     /* SPLIT route: windows the chain of a single long
-                          sequence is cut into (1 = none); see below       */
-  int32_t window_chunks; /* chunks per window (0 when windows == 1)       */
+  int32_t windows;     /* SPLIT route: windows each sequence's chain is cut
+                          into at most (1 = none); see below               */
+  int32_t window_chunks; /* chunks per window of a sequence as long as the
+                            batch (0 when windows == 1)                    */
 } kda_prefill_plan_t;
 
 /* ------------------------------------------------------------- prefill --
@@ -207,11 +208,14 @@ int kda_prefill_ex(const void* q, const void* k, const void* v, const void* g,
 
 /* --------------------------------------------------- pooled prefill --
  * kda_prefill with the states of a serving engine: each sequence starts from
- * and ends in a slot of an FP32 state pool, updated in place ([SBH]'s "FP32
- * pool with state indices"), and optionally the state after every
- * `checkpoint_tokens` tokens of each sequence is stored ([SBH]'s checkpoint
- * rows, "every 64 tokens").  All other arguments, the routes and the
- * workspace are those of kda_prefill.
+ * and ends in a slot of an FP32 state pool, addressed by a per-sequence slot
+ * index and updated in place, and optionally the state after every
+ * `checkpoint_tokens` tokens of each sequence is stored as a checkpoint row
+ * (flashinfer PR #5551 "Kimi K3 TP12 H=8 fused KDA decode in the Cake
+ * backend on SM100/SM103", embedded PR #5565: section "1. Kernel body" runs
+ * FP32 checkpoint rows at a 64-token interval, and its "Baselines and their
+ * source PRs" rows use a state pool with indices).  All other arguments, the
+ * routes and the workspace are those of kda_prefill.
  *
  *  state_pool   fp32 [num_slots, H, 128, 128] (dv contiguous), 16-byte
  *               aligned, or NULL (zero initial states, final states not
@@ -277,14 +281,18 @@ size_t kda_prefill_workspace_size(int32_t num_seqs, int64_t total_tokens,
  * route (KDA_ROUTE_AUTO to let the planner choose).  Pure host function:
  * it enqueues nothing and touches no device memory.
  *
- * Windows (SPLIT route, one sequence): the chunk recurrence is affine in the
- * state, S_end = P S_in + B over any run of chunks ([SBH]'s affine-composite
- * windows).  When one sequence's chain would occupy only a small part of the
- * device, the plan cuts it into `windows` runs of `window_chunks` chunks: the
- * maps (P, B) of the inner windows are computed concurrently with the first
+ * Windows (SPLIT route): the chunk recurrence is affine in the state, S_end =
+ * P S_in + B over any run of chunks (the affine composite of flashinfer PR
+ * #5551's page, embedded PR #5573, section "1. Composite schedule").  When
+ * the chains of a batch would occupy only a small part of the device, the
+ * plan cuts every sequence into up to `windows` runs of chunks: the maps
+ * (P, B) of the inner windows are computed concurrently with the first
  * window, the true initial state of each window follows by a short carry, and
- * all later windows then run concurrently.  The result equals the unwindowed
- * computation up to rounding. */
+ * all later windows then run concurrently.  Each sequence is cut by its own
+ * length, into runs of max(8, ceil(chunks / windows)) chunks; `window_chunks`
+ * reports that cut for a sequence as long as the whole batch (for one
+ * sequence, its cut).  The result equals the unwindowed computation up to
+ * rounding. */
 int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                      float lower_bound, int32_t num_cus, int32_t route,
                      kda_prefill_plan_t* plan);

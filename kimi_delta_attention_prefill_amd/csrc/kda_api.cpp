@@ -357,21 +357,31 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     plan->block_threads = 256;
     plan->grid_blocks = units * kda::kSplitChainTiles;
     plan->windows = 1;
-    // One long sequence whose chain fills a small part of the device: cut it
-    // into windows so that phase A (first window + inner windows' maps, 1 +
-    // 2 (W - 2) chains) and phase C (W - 1 chains) each fit the CUs at
-    // kSplitBlocksPerCU blocks each.
+    // Chains that fill a small part of the device: cut each sequence into up
+    // to W windows so that phase A (first window + inner windows' maps, 1 +
+    // 2 (W - 2) chains per (sequence, head)) and phase C (W - 1 chains) each
+    // fit the CUs at kSplitBlocksPerCU blocks each.  The device cuts every
+    // sequence by its own length (max(8, ceil(chunks / W)) chunks per
+    // window), so W is sized here from the average sequence (windows of at
+    // least 8 chunks); window_chunks reports the cut of a sequence as long as
+    // the whole batch.
     const int64_t chunks = (total_tokens + 31) / 32;
-    if (num_seqs == 1) {
+    if (num_seqs >= 1) {
       const int64_t tiles = units * kda::kSplitChainTiles;
       const int64_t slots = kda::kSplitBlocksPerCU * (int64_t)num_cus;
       int64_t w = 1;
       while (w < 8 && tiles * (1 + 2 * (w + 1 - 2)) <= slots && tiles * w <= slots) ++w;
-      w = std::min<int64_t>(w, chunks / 8);   // windows of at least 8 chunks
+      w = std::min<int64_t>(w, chunks / num_seqs / 8);   // windows of at least 8 chunks
+      // Three windows shorten a chain to about 2/3 of its steps plus the
+      // carry: measured on 4 x 4096 tokens at H = 4 (128 chunks per sequence)
+      // that no longer pays (116.9 vs 114.5 us), on 2 x 8192 at H = 8 (256
+      // chunks) it does (242 vs 263 us).
+      if (w == 3 && chunks / num_seqs < 192) w = 1;
       if (w >= 3) {
-        const int64_t wc = (chunks + w - 1) / w;
+        const int64_t wc = std::max<int64_t>(8, (chunks + w - 1) / w);
         plan->window_chunks = (int32_t)wc;
-        plan->windows = (int32_t)((chunks + wc - 1) / wc);
+        // one sequence: the windows its cut actually yields
+        plan->windows = num_seqs == 1 ? (int32_t)((chunks + wc - 1) / wc) : (int32_t)w;
       }
     }
   } else {

@@ -86,6 +86,16 @@ namespace {
 
 using namespace chunk;
 
+// Chunks per window of a sequence of `nch` chunks when the chains are cut
+// into a.windows windows (0 when they are not): at least kMinWindowChunks,
+// and at most a.windows windows per sequence, whatever the other sequences'
+// lengths (each sequence is cut by its own length, which only the device
+// knows).
+constexpr int kMinWindowChunks = 8;
+__device__ __forceinline__ int window_chunks_of(const PrefillArgs& a, int nch) {
+  return a.windows <= 1 ? 0 : max(kMinWindowChunks, (nch + a.windows - 1) / a.windows);
+}
+
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -173,7 +183,8 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // The previous chunk of the same sequence (chunk 0, and the first chunk of
   // a window: an empty range, so its keys and gates read as zero, which
   // gives W = 0 and M' = M and lets a chain start there).
-  const bool has_prev = c > 0 && (a.window_chunks <= 0 || c % a.window_chunks != 0);
+  const int wcn = window_chunks_of(a, (eos - bos + CH - 1) / CH);
+  const bool has_prev = c > 0 && (wcn <= 0 || c % wcn != 0);
   const int64_t base_prev = has_prev ? base - (int64_t)CH * H * D : base;
   const uint32_t prev_bytes = has_prev ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
@@ -1113,8 +1124,9 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_chain(PrefillArgs
 }
 
 // ------------------------------------------------------------ windows
-// A long sequence is cut into windows of `window_chunks` chunks whose first
-// chunks carry M' = M and W = 0, so a chain can start at any window.  The
+// A long sequence is cut into windows (window_chunks_of: up to a.windows per
+// sequence, by its own length) whose first chunks carry M' = M and W = 0, so
+// a chain can start at any window.  The
 // state map of a window is affine, S_end = P_w S_in + B_w, which gives
 //   phase A (all at once): window 0 from the initial state; for every window
 //            w that is neither first nor last, B_w (its chain from zero) and
@@ -1141,12 +1153,13 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_a(PrefillA
                                                                         const uint8_t* __restrict__ ws,
                                                                         WinView wv) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows, WC = a.window_chunks;
+  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows;
   const int jobs = 1 + 2 * (W - 2);
   const int tile = blockIdx.x / (units * jobs), r = blockIdx.x % (units * jobs);
   const int unit = r % units, j = r / units;
   const int n = unit / H, h = unit % H;
   const int nch = seq_chunks(a, n);
+  const int WC = max(1, window_chunks_of(a, nch));
   const int nwin = max(1, (nch + WC - 1) / WC);
   ChainJob job;
   job.n = n; job.h = h; job.tile = tile;
@@ -1280,11 +1293,12 @@ __global__ __launch_bounds__(kChainThreads) void prefill_split_window_c(PrefillA
                                                                         const uint8_t* __restrict__ ws,
                                                                         WinView wv) {
   extern __shared__ __align__(16) unsigned char lds[];
-  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows, WC = a.window_chunks;
+  const int H = a.num_heads, units = a.num_seqs * H, W = a.windows;
   const int tile = blockIdx.x / (units * (W - 1)), r = blockIdx.x % (units * (W - 1));
   const int unit = r % units, w = 1 + r / units;
   const int n = unit / H, h = unit % H;
   const int nch = seq_chunks(a, n);
+  const int WC = max(1, window_chunks_of(a, nch));
   const int nwin = max(1, (nch + WC - 1) / WC);
   if (w >= nwin) return;
   ChainJob job;

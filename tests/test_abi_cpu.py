@@ -295,10 +295,25 @@ def test_plan_windows():
     assert (p.windows - 1) * p.window_chunks < 94 <= p.windows * p.window_chunks
     p = kda.plan(1, 1000, 8, -5.0, 256, kda.ROUTE_SPLIT)   # 32 chunks: windows of >= 8 chunks
     assert (p.windows, p.window_chunks) == (4, 8)
-    for args in ((1, 64, 2), (2, 345, 4), (1, 8192, 32), (1, 700, 8)):
+    for args in ((1, 64, 2), (2, 345, 4), (1, 8192, 32), (1, 700, 8), (8, 4000, 4),
+                 (4, 4 * 4096, 4)):
         p = kda.plan(*args, -5.0, 256, kda.ROUTE_SPLIT)
-        assert (p.windows, p.window_chunks) == (1, 0), args   # too short, too many units, or N > 1
+        assert (p.windows, p.window_chunks) == (1, 0), args   # too short or too many units
+    # (4 x 4096 at H = 4 would get three windows of 43 chunks: not worth the carry)
     assert kda.plan(1, 8192, 8, -5.0, 256, kda.ROUTE_CHUNK).windows == 1
+    # several sequences: W from the (sequence, head) count and the average
+    # length; each sequence is cut by its own length on the device, into
+    # max(8, ceil(chunks / W)) chunks per window (reported for a sequence as
+    # long as the batch)
+    p = kda.plan(2, 2 * 8192, 8, -5.0, 256, kda.ROUTE_SPLIT)      # 16 units, 128 chain tiles
+    assert (p.windows, p.window_chunks) == (3, 171)
+    assert 128 * (1 + 2 * (p.windows - 2)) <= 512 and 128 * (p.windows - 1) <= 512
+    p = kda.plan(2, 3000 + 13384, 8, -5.0, 256, kda.ROUTE_SPLIT)
+    assert p.windows == 3
+    p = kda.plan(3, 2000 + 4100 + 777, 2, -8.0, 256, kda.ROUTE_SPLIT)
+    assert p.windows == 6                                          # 6 units: 48 chain tiles
+    assert kda.workspace_size(3, 6877, 2) == (
+        (3 + 6877 // 32 + 1) * 2 * 49152 + 3 * 2 * p.windows * 2 * 65536)
 
 
 def test_pool_prefill_host_validation():

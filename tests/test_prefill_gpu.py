@@ -286,6 +286,32 @@ def test_split_windows(dev, T, H, lb, state):
     compare(case, o, f)
 
 
+@pytest.mark.parametrize("lengths,H,lb,state", [([3000, 2500], 3, -5.0, 0.02),
+                                                ([2000, 4100, 777], 2, -8.0, 0.02),
+                                                ([0, 1500, 31, 4000], 2, -5.0, None)])
+def test_split_windows_several_sequences(dev, lengths, H, lb, state):
+    """A batch of several sequences whose chains fill little of the device:
+    every sequence is cut into windows by its own length (ragged tails, a
+    sequence shorter than one window, a zero-length one and split-16
+    anchoring included)."""
+    T = sum(lengths)
+    plan = kda.plan(len(lengths), T, H, lb, 0, kda.ROUTE_SPLIT)
+    assert plan.windows >= 3, plan
+    case = make_prefill_case(lengths, H, lb, state, seed=29 + T, name=f"windows_{len(lengths)}seq_H{H}")
+    o, f = run_gpu(case, kda.ROUTE_SPLIT, dev)
+    compare(case, o, f)
+
+
+def test_split_windows_two_long_sequences(dev):
+    """2 x 8192 tokens at H = 8 on the automatic route (the split route with
+    windows), sampled heads of both sequences against the oracle."""
+    case = make_prefill_case([8192, 8192], 8, -5.0, 0.02, seed=31, name="windows_2x8192_H8")
+    plan = kda.plan(2, case.total_tokens, 8, -5.0, 0, kda.ROUTE_AUTO)
+    assert plan.route == kda.ROUTE_SPLIT and plan.windows >= 3, plan
+    o, f = run_gpu(case, kda.ROUTE_AUTO, dev)
+    compare(case, o, f, heads=[0, 7])
+
+
 def test_split_windows_graph_replay(dev):
     case = make_prefill_case([1500], 2, -5.0, 0.02, seed=23, name="windows_graph")
     to = lambda t: t.to(dev)
