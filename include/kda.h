@@ -124,16 +124,24 @@ typedef enum {
   KDA_ANCHOR_FIXED = 0,  /* one anchor C = 16 * lower_bound * log2(e) per chunk:
                             operand exponents stay within 16|lb|log2e <= 126,
                             i.e. usable for lower_bound >= -5.45            */
-  KDA_ANCHOR_SPLIT16 = 1, /* per 16-token half anchors ("ordinary SafeGate"
-                            16-token blocks), for wider bounds             */
-  KDA_ANCHOR_DATA = 2    /* no bound (lower_bound = -inf, or the softplus gate):
-                            each 16-token half of each chunk is anchored, per
-                            channel, at the midpoint of its gate-prefix range
-                            (a data-dependent range strategy).  Exact to the
-                            usual rounding while no half of a chunk decays a
-                            channel by more than e^-174 (sum of |g| over 16
-                            tokens <= 174); beyond that the anchored factors
-                            are clamped (finite, less accurate)            */
+  KDA_ANCHOR_SPLIT16 = 1, /* per 16-token half anchors (the note's ordinary
+                            16-token blocks) for bounds down to -10.9: the
+                            factors reach 2^{8 |lb| log2 e}               */
+  KDA_ANCHOR_DATA = 2    /* no bound (lower_bound = -inf, or the softplus
+                            gate), or a bound below -10.9: each 16-token half
+                            of each chunk is anchored, per channel, at the
+                            midpoint of its own gate-prefix range (a
+                            data-dependent range strategy).  Where a half's
+                            prefix falls by more than 2^248 (about 172 nats)
+                            in some channel, its products are formed per
+                            8-token quarter instead (each quarter at its own
+                            midpoint, the cross-quarter block through their
+                            boundary).  Exact to the usual rounding while no
+                            quarter of a chunk falls by more than 2^252 (the
+                            gate summed over the quarter's last seven tokens
+                            >= -174.6 in every channel);
+                            kda_check_prefill_inputs flags inputs beyond
+                            that (KDA_CHECK_GATE_STEEP)                    */
 } kda_anchor_mode;
 
 /* What kda_prefill will launch for a problem (a pure host function of the
@@ -428,12 +436,17 @@ enum {
   KDA_CHECK_BETA_RANGE = 2,    /* 0 <= beta <= 1 */
   KDA_CHECK_QKV_FINITE = 3,    /* every q, k, v element finite */
   KDA_CHECK_SLOTS_UNIQUE = 4,  /* the slot indices in [0, num_slots) pairwise distinct */
-  KDA_CHECK_COUNT = 5
+  KDA_CHECK_GATE_STEEP = 5,    /* set when the gate falls by more than 2^252 (174.6 nats)
+                                  within an 8-token quarter of a chunk (tokens 0-7, 8-15,
+                                  ... of each sequence) in some (head, channel): the
+                                  chunk routes are not exact there */
+  KDA_CHECK_COUNT = 6
 };
 
 /* kda_prefill's inputs (as kda_prefill takes them, plain gates and beta);
- * writes flags KDA_CHECK_CU_SEQLENS .. KDA_CHECK_QKV_FINITE.  Pointers may be
- * NULL only when num_seqs = 0 (cu_seqlens) or total_tokens = 0 (the rest). */
+ * writes flags KDA_CHECK_CU_SEQLENS .. KDA_CHECK_QKV_FINITE and
+ * KDA_CHECK_GATE_STEEP.  Pointers may be NULL only when num_seqs = 0
+ * (cu_seqlens) or total_tokens = 0 (the rest). */
 int kda_check_prefill_inputs(const void* q, const void* k, const void* v, const void* g,
                              const void* beta, const int32_t* cu_seqlens, int32_t num_seqs,
                              int64_t total_tokens, int32_t num_heads, float lower_bound,

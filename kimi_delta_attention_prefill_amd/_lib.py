@@ -449,7 +449,8 @@ def decode(q, k, v, g, beta, state_pool, slot_indices, *, scale, out=None, strea
     return out
 
 
-CHECK_NAMES = ("cu_seqlens", "gate_range", "beta_range", "qkv_finite", "slots_unique")
+CHECK_NAMES = ("cu_seqlens", "gate_range", "beta_range", "qkv_finite", "slots_unique",
+               "gate_steep")
 
 
 def check_prefill_inputs(q, k, v, g, beta, cu_seqlens, *, lower_bound, stream=None):
@@ -458,19 +459,19 @@ def check_prefill_inputs(q, k, v, g, beta, cu_seqlens, *, lower_bound, stream=No
     dev = q.device
     T, H, _ = q.shape
     N = cu_seqlens.numel() - 1
-    flags = torch.full((5,), -1, dtype=torch.int32, device=dev)
+    flags = torch.full((6,), -1, dtype=torch.int32, device=dev)
     _check(load().kda_check_prefill_inputs(_ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
                                            _ptr(cu_seqlens), N, T, H, float(lower_bound),
                                            _ptr(flags), _stream(stream)))
     torch.cuda.synchronize(dev)
     f = flags.cpu().tolist()
-    return {CHECK_NAMES[i]: bool(f[i]) for i in range(4)}
+    return {CHECK_NAMES[i]: bool(f[i]) for i in (0, 1, 2, 3, 5)}
 
 
 def check_slots(slot_indices, num_slots, *, stream=None):
     """Device check that the slot indices in [0, num_slots) are distinct
     (debugging and tests; synchronises).  Returns True when they are not."""
-    flags = torch.full((5,), -1, dtype=torch.int32, device=slot_indices.device)
+    flags = torch.full((6,), -1, dtype=torch.int32, device=slot_indices.device)
     _check(load().kda_check_slots(_ptr(slot_indices), slot_indices.numel(), int(num_slots),
                                   _ptr(flags), _stream(stream)))
     torch.cuda.synchronize(slot_indices.device)

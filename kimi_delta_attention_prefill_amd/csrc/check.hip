@@ -16,12 +16,29 @@ __global__ void clear_flags(int32_t* flags, int first, int count) {
   if ((int)threadIdx.x < count) flags[first + threadIdx.x] = 0;
 }
 
+// The gate's fall over an 8-token quarter of a chunk (its prefix from the
+// quarter's first to its last token, natural log) beyond which the chunk
+// routes' exact quarter products leave the FP32 exponent range: 2^252.
+constexpr float kQuarterFallLimit = 252.f / 1.4426950408889634f;
+
+// Sequence of token t (the largest n with cu[n] <= t), with the offsets
+// clamped as the prefill kernels clamp them.
+__device__ __forceinline__ int sequence_of(const CheckPrefillArgs& a, int64_t t) {
+  int lo = 0, hi = a.num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    const int64_t c = a.cu_seqlens[mid] < 0 ? 0 : a.cu_seqlens[mid];
+    if (c <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
 __device__ __forceinline__ bool bf16_finite(uint16_t x) { return (x & 0x7F80u) != 0x7F80u; }
 
 __global__ __launch_bounds__(kCheckThreads) void check_prefill_kernel(CheckPrefillArgs a) {
   const int64_t tid = (int64_t)blockIdx.x * kCheckThreads + threadIdx.x;
   const int64_t stride = (int64_t)gridDim.x * kCheckThreads;
-  bool bad_cu = false, bad_gate = false, bad_beta = false, bad_qkv = false;
+  bool bad_cu = false, bad_gate = false, bad_beta = false, bad_qkv = false, steep = false;
   // sequence offsets
   for (int64_t i = tid; i <= a.num_seqs; i += stride) {
     const int32_t c = a.cu_seqlens[i];
@@ -36,6 +53,19 @@ __global__ __launch_bounds__(kCheckThreads) void check_prefill_kernel(CheckPrefi
     if (!bf16_finite(a.q[i]) || !bf16_finite(a.k[i]) || !bf16_finite(a.v[i])) bad_qkv = true;
     const float gv = bf16_to_f32(a.g[i]);
     if (!(gv <= 0.f) || (a.bounded && !(gv >= a.lower_bound))) bad_gate = true;
+    // element (t, h, c) that opens an 8-token quarter of a chunk of its sequence
+    const int64_t t = i / ((int64_t)a.num_heads * kHeadDim);
+    if (a.num_seqs > 0) {
+      const int n = sequence_of(a, t);
+      const int64_t bos = a.cu_seqlens[n] < 0 ? 0 : a.cu_seqlens[n];
+      const int64_t eos = a.cu_seqlens[n + 1] > a.total_tokens ? a.total_tokens : a.cu_seqlens[n + 1];
+      if (t >= bos && t < eos && (t - bos) % 8 == 0) {
+        float fall = 0.f;
+        for (int64_t u = t + 1; u < t + 8 && u < eos; ++u)
+          fall -= bf16_to_f32(a.g[i + (u - t) * a.num_heads * kHeadDim]);
+        if (fall > kQuarterFallLimit) steep = true;
+      }
+    }
   }
   const int64_t tokheads = a.total_tokens * a.num_heads;
   for (int64_t i = tid; i < tokheads; i += stride) {
@@ -46,6 +76,7 @@ __global__ __launch_bounds__(kCheckThreads) void check_prefill_kernel(CheckPrefi
   if (bad_gate) a.flags[1] = 1;
   if (bad_beta) a.flags[2] = 1;
   if (bad_qkv) a.flags[3] = 1;
+  if (steep) a.flags[5] = 1;
 }
 
 __global__ __launch_bounds__(kCheckThreads) void check_slots_kernel(const int32_t* slots, int32_t rows,
@@ -71,6 +102,7 @@ unsigned grid_for(int64_t work) {
 
 hipError_t launch_check_prefill(const CheckPrefillArgs& a, hipStream_t s) {
   clear_flags<<<1, 64, 0, s>>>(a.flags, 0, 4);
+  clear_flags<<<1, 64, 0, s>>>(a.flags, 5, 1);
   const int64_t work = a.total_tokens * a.num_heads * kHeadDim;
   check_prefill_kernel<<<grid_for(work > a.num_seqs + 1 ? work : a.num_seqs + 1), kCheckThreads, 0,
                          s>>>(a);

@@ -419,6 +419,132 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
   acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
 }
 
+// Data-dependent anchors (no gate bound): a 16-token half whose gate prefix
+// falls by more than kSteepRange (log2 units, about 172 nats) in some channel
+// cannot be anchored once (its factors would leave the FP32/bf16 exponent
+// range).  steep_wave tells, for the channels of this producer wave, whether
+// any half of the chunk is that steep (wave-uniform).
+constexpr float kSteepRange = 248.f;
+__device__ __forceinline__ bool steep_wave(const PrepWork& pw, int wave, int lane) {
+  bool steep = false;
+  if ((lane & 15) < 2) {          // lane l16 = h checks half h of its row's 8 channels
+    const int h = lane & 1, c0 = 32 * wave + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) steep |= pw.G[16 * h][c0 + j] - pw.G[16 * h + 15][c0 + j] > kSteepRange;
+  }
+  return __builtin_amdgcn_ballot_w64(steep) != 0;
+}
+
+// The pairwise products for a wave whose channels have a steep half
+// (steep_wave), exact to the usual rounding while no 8-token quarter falls by
+// more than 2^252: each diagonal 16x16 tile is the sum of three products over
+// the quarters Q0 (tokens 0-7 of the half) and Q1 (8-15),
+//   Q0 x Q0 anchored at the middle of Q0's range,
+//   Q1 x Q1 anchored at the middle of Q1's range,
+//   Q1 x Q0 through the prefix at the quarters' boundary (factors <= 1),
+// so no factor exceeds half of one quarter's range; the off-diagonal tile
+// goes through the prefix at token 15 as in pair_products.  Lane (g4, l16)
+// supplies row l16 and column l16 of a tile, so one mask per lane (its
+// token's quarter) selects its part of each product.  Same interface as
+// pair_products (MODE 2).
+template <bool FE, class Emit>
+__device__ __forceinline__ void pair_products_steep(f32x4 (&acc)[6], const PrepWork& pw,
+                                                    const ChunkQKG& cr, int wave, int lane,
+                                                    Emit&& emit) {
+  const int l16 = lane & 15, g4 = lane >> 4;
+  const int cb = 32 * wave, cl = 8 * g4;
+  const bool q1 = l16 >= 8;       // this lane's token is in the second quarter of its half
+  const f32x4 z = {0.f, 0.f, 0.f, 0.f};
+  auto mfma3 = [&](const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl,
+                   f32x4 c) __attribute__((always_inline)) {
+    c = mfma_bf16(ah, bh, c);
+    c = mfma_bf16(ah, bl, c);
+    return mfma_bf16(al, bh, c);
+  };
+  bf16x8 boh, bol;   // half 0 column operands of the off-diagonal tile
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int t = l16 + 16 * half, hb = 16 * half;
+    const uint4 qw = *reinterpret_cast<const uint4*>(&cr.q[t][cb + cl]);
+    const uint4 kw = *reinterpret_cast<const uint4*>(&cr.k[t][cb + cl]);
+    const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
+    const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
+    const float rq = FE ? pw.rq[t] : 1.f, rk = FE ? pw.rk[t] : 1.f;
+    auto qf_of = [&](int j) __attribute__((always_inline)) {
+      return rq * ((j & 1) ? bf16hi(qu[j >> 1]) : bf16lo(qu[j >> 1]));
+    };
+    auto kf_of = [&](int j) __attribute__((always_inline)) {
+      return rk * ((j & 1) ? bf16hi(ku[j >> 1]) : bf16lo(ku[j >> 1]));
+    };
+    const int im = half ? 2 : 0, ia = half ? 5 : 3;   // diagonal tiles of Mqk and Akk
+#pragma unroll
+    for (int qq = 0; qq < 2; ++qq) {
+      // Qqq x Qqq anchored at the middle of quarter qq's range; lanes of the
+      // other quarter supply zeros
+      const bool mine = q1 == (qq == 1);
+      bf16x8 qah, qal, kah, kal, bah, bal;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = cb + cl + j;
+        const float Gv = pw.G[t][c];
+        const float Ca = 0.5f * (pw.G[hb + 8 * qq][c] + pw.G[hb + 8 * qq + 7][c]);
+        const float rowA = mine ? fast_exp2(Gv - Ca) : 0.f;
+        const float colA = mine ? fast_exp2(Ca - Gv) : 0.f;
+        __bf16 h, l;
+        split_bf16(qf_of(j) * rowA, h, l); qah[j] = h; qal[j] = l;
+        split_bf16(kf_of(j) * rowA, h, l); kah[j] = h; kal[j] = l;
+        split_bf16(kf_of(j) * colA, h, l); bah[j] = h; bal[j] = l;
+      }
+      acc[im] = mfma3(qah, qal, bah, bal, qq ? acc[im] : z);
+      acc[ia] = mfma3(kah, kal, bah, bal, qq ? acc[ia] : z);
+      __builtin_amdgcn_sched_barrier(0);   // one pass's operands live at a time
+    }
+    {
+      // Q1 x Q0 through the prefix at the quarters' boundary: rows of Q1, columns of Q0
+      bf16x8 q3h, q3l, k3h, k3l, b3h, b3l;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = cb + cl + j;
+        const float Gv = pw.G[t][c], G7 = pw.G[hb + 7][c];
+        const float e3 = fast_exp2(q1 ? Gv - G7 : G7 - Gv);   // <= 1 either way
+        const float qf = qf_of(j), kf = kf_of(j);
+        __bf16 h, l;
+        split_bf16(q1 ? qf * e3 : 0.f, h, l); q3h[j] = h; q3l[j] = l;
+        split_bf16(q1 ? kf * e3 : 0.f, h, l); k3h[j] = h; k3l[j] = l;
+        split_bf16(q1 ? 0.f : kf * e3, h, l); b3h[j] = h; b3l[j] = l;
+      }
+      acc[im] = mfma3(q3h, q3l, b3h, b3l, acc[im]);
+      acc[ia] = mfma3(k3h, k3l, b3h, b3l, acc[ia]);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    {
+      // the off-diagonal tile's operands (through the prefix at token 15) and Kg, Qg, Kr
+      bf16x8 qoh, qol, koh, kol;
+      float kv[8], qv[8], Pv[8], Rv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int c = cb + cl + j;
+        const float Gv = pw.G[t][c], g15 = pw.G[15][c], gl = pw.G[CH - 1][c];
+        const float qf = qf_of(j), kf = kf_of(j);
+        const float fo = half ? fast_exp2(Gv - g15) : fast_exp2(g15 - Gv);
+        __bf16 h, l;
+        if (half == 1) {
+          split_bf16(qf * fo, h, l); qoh[j] = h; qol[j] = l;
+          split_bf16(kf * fo, h, l); koh[j] = h; kol[j] = l;
+        } else {
+          split_bf16(kf * fo, h, l); boh[j] = h; bol[j] = l;
+        }
+        kv[j] = kf; qv[j] = qf; Pv[j] = fast_exp2(Gv); Rv[j] = fast_exp2(gl - Gv);
+      }
+      emit(t, cb + cl, kv, qv, Pv, Rv);
+      if (half == 1) {
+        acc[1] = mfma3(qoh, qol, boh, bol, z);
+        acc[4] = mfma3(koh, kol, boh, bol, z);
+      }
+    }
+  }
+}
+
 // Stores this wave's partials over its own key-channel columns of the rows
 // (part_entry); call after its last read of the rows.
 __device__ __forceinline__ void pair_store(ChunkQKG& cr, const f32x4 (&acc)[6], int wave, int lane) {

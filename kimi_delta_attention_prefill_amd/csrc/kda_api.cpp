@@ -75,6 +75,13 @@ bool fixed_anchor_fits(float lower_bound) {
   return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
 }
 
+// The same for the 16-token anchors: a half's factors reach 2^{8 |lb| log2(e)},
+// so they fit while lower_bound >= -10.9; wider bounds take the
+// data-dependent anchors.
+bool half_anchor_fits(float lower_bound) {
+  return 8.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
+}
+
 // Argument checks shared by the prefill entry points; each returns KDA_OK or
 // records the error and returns its code.
 int check_sizes(const char* fn, int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
@@ -338,7 +345,8 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
   plan->windows = 1;
   plan->anchor_mode = !std::isfinite(lower_bound)       ? KDA_ANCHOR_DATA
                       : fixed_anchor_fits(lower_bound) ? KDA_ANCHOR_FIXED
-                                                       : KDA_ANCHOR_SPLIT16;
+                      : half_anchor_fits(lower_bound)  ? KDA_ANCHOR_SPLIT16
+                                                       : KDA_ANCHOR_DATA;
   plan->anchor_log2 = std::isfinite(lower_bound)
                           ? (float)(16.0 * (double)lower_bound * 1.4426950408889634) : 0.f;
   if (route == KDA_ROUTE_SERIAL) {

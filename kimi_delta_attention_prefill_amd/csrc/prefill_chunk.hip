@@ -173,8 +173,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       lds_barrier();   // B1: gate prefix, anchor constants, beta and decays of chunk s+1 written
       if (prep) {
         f32x4 pacc[6];
-        pair_products<MODE, FE>(pacc, sm.pw, cr, a, C, exp2C, pwave, lane,
-                          [&](int t, int c0, const float* kv, const float* qv, const float* P,
+        auto emit = [&](int t, int c0, const float* kv, const float* qv, const float* P,
                               const float* R) {
                             const int cb = c0 & ~31, cl = c0 & 31;
                             f16x4 kg_lo, kg_hi, qg_lo, qg_hi;
@@ -193,7 +192,11 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
                             *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
                             *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl)]) = qg_lo;
                             *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
-                          });
+                          };
+        if (MODE == 2 && steep_wave(sm.pw, pwave, lane))
+          pair_products_steep<FE>(pacc, sm.pw, cr, pwave, lane, emit);
+        else
+          pair_products<MODE, FE>(pacc, sm.pw, cr, a, C, exp2C, pwave, lane, emit);
         pair_store(cr, pacc, pwave, lane);   // over this wave's own columns of the rows
       }
       lds_barrier();   // B2: split-K partials of chunk s+1 complete

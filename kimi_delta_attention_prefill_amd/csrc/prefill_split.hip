@@ -356,24 +356,80 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
       qoh = qah[1]; qol = qal[1]; koh = kah[1]; kol = kal[1]; boh = kbh[0]; bol = kbl[0];
     }
     // transposed pairwise products, split K over the four steps
-    acc[0] = mfma_bf16(kbh[0], qah[0], acc[0]);
-    acc[0] = mfma_bf16(kbh[0], qal[0], acc[0]);
-    acc[0] = mfma_bf16(kbl[0], qah[0], acc[0]);
-    acc[1] = mfma_bf16(boh, qoh, acc[1]);
-    acc[1] = mfma_bf16(boh, qol, acc[1]);
-    acc[1] = mfma_bf16(bol, qoh, acc[1]);
-    acc[2] = mfma_bf16(kbh[1], qah[1], acc[2]);
-    acc[2] = mfma_bf16(kbh[1], qal[1], acc[2]);
-    acc[2] = mfma_bf16(kbl[1], qah[1], acc[2]);
-    acc[3] = mfma_bf16(kbh[0], kah[0], acc[3]);
-    acc[3] = mfma_bf16(kbh[0], kal[0], acc[3]);
-    acc[3] = mfma_bf16(kbl[0], kah[0], acc[3]);
-    acc[4] = mfma_bf16(boh, koh, acc[4]);
-    acc[4] = mfma_bf16(boh, kol, acc[4]);
-    acc[4] = mfma_bf16(bol, koh, acc[4]);
-    acc[5] = mfma_bf16(kbh[1], kah[1], acc[5]);
-    acc[5] = mfma_bf16(kbh[1], kal[1], acc[5]);
-    acc[5] = mfma_bf16(kbl[1], kah[1], acc[5]);
+    auto mfma3 = [&](const bf16x8& ah, const bf16x8& al, const bf16x8& bh, const bf16x8& bl,
+                     f32x4 c) __attribute__((always_inline)) {
+      c = mfma_bf16(ah, bh, c);
+      c = mfma_bf16(ah, bl, c);
+      return mfma_bf16(al, bh, c);
+    };
+    acc[1] = mfma3(boh, bol, qoh, qol, acc[1]);
+    acc[4] = mfma3(boh, bol, koh, kol, acc[4]);
+    // Unbounded gates: a 16-token half whose prefix falls by more than
+    // kSteepRange in some channel of this K step cannot take one anchor, so
+    // its diagonal tile is formed from the 8-token quarters Q0 (tokens 0-7 of
+    // the half) and Q1 (8-15): Q0 x Q0 and Q1 x Q1 anchored at their own
+    // midpoints, Q1 x Q0 through the prefix at their boundary (factors <= 1);
+    // exact to the usual rounding while no quarter falls by more than 2^252.
+    // The lane of token l16 supplies row and column l16 of a tile, so its
+    // quarter decides which products it takes part in.
+    bool steep = false;
+    if (MODE == 2) {
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        steep |= (Gf[0][j] - G15[j] > kSteepRange) || (Gf[1][j] - GL[j] > kSteepRange);
+      steep = __builtin_amdgcn_ballot_w64(steep) != 0;
+    }
+    if (MODE == 2 && steep) {
+      const bool q1 = l16 >= 8;
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        // the prefix at the quarter boundaries of this half (tokens 16hf + 7, + 8, + 15)
+        float G7[8], G8[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          G7[j] = __shfl(G[hf][j], 7, 16);
+          G8[j] = __shfl(G[hf][j], 8, 16);
+        }
+        const int im = hf ? 2 : 0, ia = hf ? 5 : 3;
+#pragma unroll
+        for (int qq = 0; qq < 2; ++qq) {
+          const bool mine = q1 == (qq == 1);
+          bf16x8 ah, al, bh, bl, ch, cl;   // row side q, row side k, column side k
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float Ca = qq ? 0.5f * (G8[j] + (hf ? GL[j] : G15[j])) : 0.5f * (Gf[hf][j] + G7[j]);
+            const float rowA = mine ? fast_exp2(G[hf][j] - Ca) : 0.f;
+            const float colA = mine ? fast_exp2(Ca - G[hf][j]) : 0.f;
+            const float qf = nq[hf] * bf16_elem(qw[hf], j), kf = nk[hf] * bf16_elem(kw[hf], j);
+            __bf16 h1, l1;
+            split_bf16(qf * rowA, h1, l1); ah[j] = h1; al[j] = l1;
+            split_bf16(kf * rowA, h1, l1); bh[j] = h1; bl[j] = l1;
+            split_bf16(kf * colA, h1, l1); ch[j] = h1; cl[j] = l1;
+          }
+          acc[im] = mfma3(ch, cl, ah, al, acc[im]);
+          acc[ia] = mfma3(ch, cl, bh, bl, acc[ia]);
+        }
+        {
+          bf16x8 ah, al, bh, bl, ch, cl;   // rows of Q1 (q, k), columns of Q0 (k)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float e3 = fast_exp2(q1 ? G[hf][j] - G7[j] : G7[j] - G[hf][j]);   // <= 1
+            const float qf = nq[hf] * bf16_elem(qw[hf], j), kf = nk[hf] * bf16_elem(kw[hf], j);
+            __bf16 h1, l1;
+            split_bf16(q1 ? qf * e3 : 0.f, h1, l1); ah[j] = h1; al[j] = l1;
+            split_bf16(q1 ? kf * e3 : 0.f, h1, l1); bh[j] = h1; bl[j] = l1;
+            split_bf16(q1 ? 0.f : kf * e3, h1, l1); ch[j] = h1; cl[j] = l1;
+          }
+          acc[im] = mfma3(ch, cl, ah, al, acc[im]);
+          acc[ia] = mfma3(ch, cl, bh, bl, acc[ia]);
+        }
+      }
+    } else {
+      acc[0] = mfma3(kbh[0], kbl[0], qah[0], qal[0], acc[0]);
+      acc[2] = mfma3(kbh[1], kbl[1], qah[1], qal[1], acc[2]);
+      acc[3] = mfma3(kbh[0], kbl[0], kah[0], kal[0], acc[3]);
+      acc[5] = mfma3(kbh[1], kbl[1], kah[1], kal[1], acc[5]);
+    }
     // Qg fragments go out as they are
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf)

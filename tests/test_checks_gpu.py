@@ -13,7 +13,8 @@ from kimi_delta_attention_prefill_amd.inputs import make_decode_case, make_prefi
 
 pytestmark = pytest.mark.gpu
 
-NONE = {"cu_seqlens": False, "gate_range": False, "beta_range": False, "qkv_finite": False}
+NONE = {"cu_seqlens": False, "gate_range": False, "beta_range": False, "qkv_finite": False,
+        "gate_steep": False}
 
 
 @pytest.fixture(scope="module")
@@ -70,6 +71,25 @@ def test_each_violation_raises_its_flag(dev):
     q = c.q.clone()
     q[100, 1, 127] = float("inf")
     assert _check(dataclasses.replace(c, q=q, name="q_inf"), dev) == dict(NONE, qkv_finite=True)
+
+
+def test_steep_quarter_flag(dev):
+    """KDA_CHECK_GATE_STEEP: a gate falling by more than 174.6 nats within an
+    8-token quarter of a chunk (tokens 8-15 of the first sequence, 7 x -30)
+    is flagged; the same fall split by a sequence boundary is not."""
+    c = _base()
+    g = c.g.clone()
+    g[9:16, 1, 40] = -30.0                              # quarter 8-15 of sequence 0: 210 nats
+    assert _check(dataclasses.replace(c, g=g, name="steep"), dev,
+                  lower_bound=float("-inf")) == dict(NONE, gate_steep=True)
+    g = c.g.clone()
+    g[66:74, 0, 3] = -30.0                              # 64-69 in sequence 0, 70-73 in sequence 2
+    assert _check(dataclasses.replace(c, g=g, name="steep_split"), dev,
+                  lower_bound=float("-inf")) == NONE
+    g = c.g.clone()
+    g[9:16, 1, 40] = -24.875                            # 7 x 24.875 = 174.1 nats: within the limit
+    assert _check(dataclasses.replace(c, g=g, name="steep_edge"), dev,
+                  lower_bound=float("-inf")) == NONE
 
 
 def test_slot_uniqueness(dev):

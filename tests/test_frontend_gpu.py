@@ -2,6 +2,7 @@
 against the FP64 oracle's front-end followed by the oracle step, through the C
 ABI (kda_decode_ex).  The oracle applies oracle/frontend.py to the same bf16
 raw inputs in double precision, then runs the token recurrence."""
+import dataclasses
 import sys
 
 import numpy as np
@@ -96,7 +97,7 @@ def test_decode_frontend_default_equals_plain(dev):
 
 
 # ---------------------------------------------------------------- prefill
-from kimi_delta_attention_prefill_amd.inputs import make_prefill_raw_case  # noqa: E402
+from kimi_delta_attention_prefill_amd.inputs import make_prefill_case, make_prefill_raw_case  # noqa: E402
 
 ROUTES = {"serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK, "split": kda.ROUTE_SPLIT}
 PREFILL_FE = {
@@ -194,3 +195,91 @@ def test_prefill_unbounded_log_gate(dev, route):
                                       case.scale, case.initial_state)
     _say(f"[gpu] prefill lb=-inf {route}: out {check_out(out.cpu(), ref_out)} "
          f"state {check_state(fin.cpu(), ref_fin)}")
+
+
+def _steep_case(seed, lengths, H, steep_channels=6, mean=14.0):
+    """Unbounded softplus gates whose chosen channels fall by ~14 nats per
+    token (~210 over a 16-token half, beyond a single anchor's 2^248, ~98 per
+    8-token quarter), the rest as usual; q, k unit, beta from N(0,1) logits."""
+    case = make_prefill_raw_case(lengths, H, seed=seed, qk_std=1.0)
+    gen = torch.Generator().manual_seed(seed + 1)
+    a = case.g.float()
+    ch = torch.randperm(128, generator=gen)[:steep_channels]
+    a[:, :, ch] = mean + torch.randn(a.shape[0], H, steep_channels, generator=gen)
+    case.g = a.to(torch.bfloat16)
+    q = case.q.float()
+    case.q = (q / q.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    k = case.k.float()
+    case.k = (k / k.norm(dim=-1, keepdim=True)).to(torch.bfloat16)
+    return case
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_prefill_steep_unbounded_gates(dev, route):
+    """Softplus gates above 200 nats per 16-token half on a few channels, as
+    the log-decay (lower_bound = -inf) and through the front-end's softplus
+    gate: the chunk routes form those halves' products per 8-token quarter."""
+    case = _steep_case(97, [300, 77], 2)
+    fe = kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True)
+    _say(f"[gpu] prefill steep softplus (front-end) {route}")
+    out, fin = _run_prefill_case(dev, route, fe, case)
+    ref_out, ref_fin = _prefill_oracle(case, fe)
+    _say(f"   out {check_out(out, ref_out)} state {check_state(fin, ref_fin)}")
+    # the same gates as a plain log-decay
+    g = -torch.nn.functional.softplus(case.g.float())
+    plain = dataclasses.replace(case, g=g.to(torch.bfloat16),
+                                beta=torch.sigmoid(case.beta.float()).to(torch.bfloat16))
+    to = lambda t: None if t is None else t.to(dev)
+    kda.set_prefill_route(ROUTES[route])
+    try:
+        out, fin = kda.prefill(to(plain.q), to(plain.k), to(plain.v), to(plain.g), to(plain.beta),
+                               to(plain.cu_seqlens), scale=plain.scale, lower_bound=float("-inf"),
+                               initial_state=to(plain.initial_state), final_state=True)
+        torch.cuda.synchronize()
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
+    ref_out, ref_fin = oracle.prefill(plain.q, plain.k, plain.v, plain.g, plain.beta,
+                                      plain.cu_seqlens, plain.scale, plain.initial_state)
+    _say(f"[gpu] prefill steep lb=-inf {route}: out {check_out(out.cpu(), ref_out)} "
+         f"state {check_state(fin.cpu(), ref_fin)}")
+
+
+def test_prefill_steep_gates_windows_and_pool(dev):
+    """Steep softplus gates on one long sequence: the split route with windows
+    and the pooled entry point."""
+    fe = kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True, normalize_qk=True, norm_eps=1e-6)
+    case = _steep_case(99, [2000], 3)
+    assert kda.plan(1, 2000, 3, float("-inf"), 0, kda.ROUTE_SPLIT).windows >= 3
+    ref_out, ref_fin = _prefill_oracle(case, fe)
+    for pool in (False, True):
+        _say(f"[gpu] prefill steep windows pool={pool}")
+        out, fin = _run_prefill_case(dev, "split", fe, case, pool=pool)
+        _say(f"   out {check_out(out, ref_out)} state {check_state(fin, ref_fin)}")
+
+
+@pytest.mark.parametrize("route", list(ROUTES))
+def test_prefill_wide_bound_takes_data_anchors(dev, route):
+    """A bound below -10.9 (here -20: g = -20 sigmoid(a), halves falling by up
+    to ~300 nats) leaves the 16-token anchors' range; the plan takes the
+    data-dependent anchors and the steep halves' quarter products."""
+    assert kda.plan(1, 4096, 2, -20.0, 0, kda.ROUTE_CHUNK).anchor_mode == kda.ANCHOR_DATA
+    assert kda.plan(1, 4096, 2, -10.0, 0, kda.ROUTE_CHUNK).anchor_mode == kda.ANCHOR_SPLIT16
+    case = make_prefill_case([200, 90], 2, -20.0, 0.02, seed=101, name="lb-20")
+    out, fin = _run_lb(dev, route, case)
+    ref_out, ref_fin = oracle.prefill(case.q, case.k, case.v, case.g, case.beta, case.cu_seqlens,
+                                      case.scale, case.initial_state)
+    _say(f"[gpu] prefill lb=-20 {route}: out {check_out(out.cpu(), ref_out)} "
+         f"state {check_state(fin.cpu(), ref_fin)}")
+
+
+def _run_lb(dev, route, case):
+    to = lambda t: None if t is None else t.to(dev)
+    kda.set_prefill_route(ROUTES[route])
+    try:
+        out, fin = kda.prefill(to(case.q), to(case.k), to(case.v), to(case.g), to(case.beta),
+                               to(case.cu_seqlens), scale=case.scale, lower_bound=case.lower_bound,
+                               initial_state=to(case.initial_state), final_state=True)
+        torch.cuda.synchronize()
+        return out, fin
+    finally:
+        kda.set_prefill_route(kda.ROUTE_AUTO)
