@@ -672,12 +672,23 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, co
   a.out = static_cast<uint16_t*>(out);
   a.fe = fe;
 
-  // Narrow value-column slices when there are too few items to fill the chip.
+  // Narrow value-column slices when there are too few items to fill the chip;
+  // with many items, whole-item 512-thread blocks, three resident per CU.
   int cus = current_device_cus();
   if (cus <= 0) cus = 256;
   const int64_t items = (int64_t)rows * num_heads;
-  const int cols = items >= 2LL * cus ? 128 : (items >= cus ? 64 : 32);
-  hipError_t e = kda::launch_decode(a, state_dtype == KDA_STATE_BF16, cols, stream);
+  const bool bf16 = state_dtype == KDA_STATE_BF16;
+  int cols = 128, threads = 512, per_cu = 0;
+  if (items >= 16LL * cus) {
+    per_cu = 3;
+  } else if (items >= 2LL * cus) {
+  } else if (bf16) {
+    cols = 64;
+  } else {
+    cols = items >= cus ? 64 : 32;
+    threads = 256;
+  }
+  hipError_t e = kda::launch_decode(a, bf16, cols, threads, per_cu, stream);
   if (e != hipSuccess)
     return fail(KDA_ERR_HIP, "kda_decode: launch failed: %s", hipGetErrorString(e));
   return ok();

@@ -102,8 +102,11 @@ hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspac
                                       hipStream_t s);
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                              int32_t windows);
-// Decode step; `cols` = value columns per block (32, 64 or 128).
-hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, hipStream_t s);
+// Decode step; `cols` = value columns per block (32, 64 or 128 for FP32
+// state, 64 or 128 for BF16), `threads` per block (256 or 512),
+// `blocks_per_cu` > 0 caps the resident blocks per compute unit (0 = no cap).
+hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, int threads,
+                         int blocks_per_cu, hipStream_t s);
 
 // Records `code` and the formatted text as the calling thread's last error
 // (kda_last_error) and returns `code`.
