@@ -19,6 +19,11 @@ prefill with a 512 MiB write before each call (outside the timed region), so
 that its inputs start in HBM rather than in the last-level cache.
 ``cpu_baseline`` times the
 FP64 oracle (test infrastructure) on the same prefill workload on the host.
+After the timed steps, ``decode_sweep`` times kda_decode at rows 1 ... 4096
+(FP32 and BF16 pools), ``multitoken_decode_sweep`` the T = 2, 4, 8 multi-token
+decode through kda_prefill_pool_ex, and ``configs`` prefill configurations 2
+(16 varlen sequences, H=32) and 3 (4 x 8192, H=64) with their kernel's MFMA
+and HBM fractions.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -159,6 +164,118 @@ def decode_sweep(torch, dev, kda, copy_gbs, steps=30, warmup=5):
     return out
 
 
+def multitoken_sweep(torch, dev, kda, copy_gbs, steps=10, warmup=3):
+    """Multi-token decode (T = 2, 4, 8 new tokens per row) through
+    kda_prefill_pool_ex at H=8 over a 4096-slot pool (FP32 and BF16), rows 1,
+    64 and 4096, with the decode front-end (softplus gates, beta logits,
+    q/k L2 norm): time per call over graph-replayed calls and GB/s of state
+    read + write plus the tokens' inputs and outputs."""
+    from kimi_delta_attention_prefill_amd.inputs import decode_config, make_prefill_raw_case
+
+    fe = kda.FrontEnd(gate_mode=kda.GATE_SOFTPLUS, beta_logits=True, normalize_qk=True,
+                      norm_eps=1e-6)
+    out = []
+    for dt, name, state_b in ((torch.float32, "f32", STATE_BYTES),
+                              (torch.bfloat16, "bf16", STATE_BYTES // 2)):
+        pool = decode_config(1, dt).pool.to(dev)
+        for tokens in (2, 4, 8):
+            for rows in (1, 64, 4096):
+                c = make_prefill_raw_case([tokens] * rows, 8, init_std=None,
+                                          seed=30000 + rows + tokens)
+                gen = torch.Generator().manual_seed(30001 + rows)
+                slots = torch.randperm(4096, generator=gen)[:rows].to(torch.int32).to(dev)
+                x = [t.to(dev) for t in (c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens)]
+                o = torch.empty_like(x[0])
+                ws_bytes = kda.workspace_size(rows, rows * tokens, 8)
+                ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+                call = lambda: kda.prefill_pool(*x, slots, pool, scale=c.scale,
+                                                lower_bound=float("-inf"), out=o, workspace=ws,
+                                                frontend=fe)
+                for _ in range(warmup):
+                    call()
+                graph = torch.cuda.CUDAGraph()
+                torch.cuda.synchronize()
+                with torch.cuda.graph(graph):
+                    for _ in range(steps):
+                        call()
+                graph.replay()
+                torch.cuda.synchronize()
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                graph.replay()
+                e1.record()
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / steps
+                del graph
+                nbytes = rows * 8 * (2 * state_b + tokens * PREFILL_BYTES_PER_TOKHEAD)
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                out.append({"state": name, "tokens": tokens, "rows": rows, "ms_per_call": ms,
+                            "gbps": gbs, "frac_of_peak": gbs / PEAK_HBM_GBPS,
+                            "frac_of_copy": gbs / copy_gbs,
+                            "route": kda.plan(rows, rows * tokens, 8, float("-inf"), 0,
+                                              kda.ROUTE_AUTO).route})
+                log(f"[bench] multi-token decode {name} T={tokens} rows={rows} "
+                    f"{ms * 1e3:.1f} us {gbs:.0f} GB/s")
+        del pool
+    return out
+
+
+def fused_configs(torch, dev, kda, configs=(2, 3), steps=5, warmup=2):
+    """Prefill configurations 2 (16 varlen sequences, H=32) and 3 (4 x 8192,
+    H=64, lb=-8) on the route the planner picks (the fused chunk kernel, one
+    launch per call): event-timed calls, tokens*heads/s, and the kernel's
+    MFMA and HBM fractions from the algorithmic FLOPs and bytes."""
+    from kimi_delta_attention_prefill_amd.inputs import prefill_config
+
+    res = {}
+    stream = torch.cuda.current_stream()
+    for i in configs:
+        log(f"[bench] prefill configuration {i}")
+        c = prefill_config(i)
+        x = [t.to(dev) for t in (c.q, c.k, c.v, c.g, c.beta, c.cu_seqlens)]
+        s0 = None if c.initial_state is None else c.initial_state.to(dev)
+        N, T, H = c.num_seqs, c.total_tokens, c.num_heads
+        plan = kda.plan(N, T, H, c.lower_bound, 0, kda.ROUTE_AUTO)
+        o = torch.empty_like(x[0])
+        fin = torch.empty((N, H, 128, 128), dtype=torch.float32, device=dev)
+        ws_bytes = kda.workspace_size(N, T, H)
+        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev) if ws_bytes else None
+        call = lambda: kda.prefill(*x, scale=c.scale, lower_bound=c.lower_bound,
+                                   initial_state=s0, final_state=fin, out=o, workspace=ws,
+                                   stream=stream)
+        for _ in range(warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(steps)]
+        for e in ev:
+            e[0].record(stream)
+            call()
+            e[1].record(stream)
+        torch.cuda.synchronize()
+        st = stats([e[0].elapsed_time(e[1]) for e in ev])
+        tokheads = T * H
+        t = st["mean_ms"] * 1e-3
+        flops = tokheads * PREFILL_FLOP_PER_TOKHEAD
+        nbytes = tokheads * PREFILL_BYTES_PER_TOKHEAD + (N * H * STATE_BYTES) * (
+            2 if s0 is not None else 1)
+        route = {kda.ROUTE_SERIAL: "serial", kda.ROUTE_CHUNK: "chunk",
+                 kda.ROUTE_SPLIT: "split"}[plan.route]
+        kname = f"prefill_{route}"
+        res[f"config{i}"] = dict(
+            st, workload=(f"prefill {N} sequence(s), {T} tokens, H={H}, dk=dv=128, "
+                          f"lb={c.lower_bound:g}, {'fp32' if s0 is not None else 'zero'} S0"),
+            route=route, tokheads_per_s=tokheads / t,
+            mfma_tflops=flops / t / 1e12, mfma_frac=flops / t / 1e12 / PEAK_BF16_TFLOPS,
+            hbm_gbps=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBPS,
+            algorithmic_flop_per_call=flops, algorithmic_bytes_per_call=nbytes,
+            kernels={kname: dict(st, launches_per_call=1,
+                                 traffic=stored_traffic(f"{kname}_T{T}_H{H}"))})
+        log(f"[bench] configuration {i}: {st['mean_ms']:.3f} ms, "
+            f"{tokheads / t:.3e} tokens*heads/s")
+        del x, s0, o, fin, ws
+    return res
+
+
 def cpu_baseline(config=1, min_seconds=10.0, max_runs=50):
     """The FP64 oracle on the whole prefill workload, repeated until about
     `min_seconds` of wall time have passed; reports the mean rate."""
@@ -197,8 +314,11 @@ def main():
     ap.add_argument("--decode-state", choices=["f32", "bf16"], default="f32")
     ap.add_argument("--route", choices=["auto", "serial", "chunk", "split"], default="auto")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--decode-sweep", action="store_true",
-                    help="also time kda_decode at rows 1, 2, ..., 4096 (FP32 and BF16 pools)")
+    ap.add_argument("--no-decode-sweep", action="store_true",
+                    help="skip the kda_decode sweep over rows 1, 2, ..., 4096 (FP32 and BF16 "
+                         "pools) and the multi-token (T = 2, 4, 8) decode sweep")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip prefill configurations 2 and 3 (reported under 'configs')")
     ap.add_argument("--cold-steps", type=int, default=10,
                     help="prefill calls timed after a 512 MiB write has flushed the caches "
                          "(0 = skip)")
@@ -414,8 +534,13 @@ def main():
                     "b200_prefill_speedup_vs_flashkda_geomean": 2.0512},
         "source_digest": source_digest(),
     }
-    if args.decode_sweep:
+    if not args.no_decode_sweep:
+        del D, d_out
         result["decode_sweep"] = decode_sweep(torch, dev, kda, copy_gbs)
+        result["multitoken_decode_sweep"] = multitoken_sweep(torch, dev, kda, copy_gbs)
+    if not args.no_configs:
+        del P, p_out, p_fin, p_ws
+        result["configs"] = fused_configs(torch, dev, kda)
     if not args.no_cpu_baseline:
         log("[bench] timing the FP64 oracle on the host")
         result["cpu_baseline"] = cpu_baseline(args.prefill_config)

@@ -335,8 +335,17 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     // fused kernel's short serial loop beats the two-pass route's second
     // launch (measured at H=2: 8.8 vs 19.8 us at 32 tokens, 19.6 vs 20.8 us
     // at 96, 24.8 vs 21.2 us at 128).
-    route = (8 * units <= 3 * (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
-                                                                         : KDA_ROUTE_CHUNK;
+    // Many sequences of at most four tokens on average (multi-token
+    // decode): the token-serial kernel streams each state once and runs a
+    // few steps on it, where a fused block sets up its whole chunk pipeline
+    // for one short chunk (4096 rows x H = 8 from a pool: 1.48 vs 2.29 ms at
+    // T = 2, 1.77 vs 2.32 ms at T = 4; at T = 8 the fused kernel wins, 2.40
+    // vs 2.63 ms).
+    if (total_tokens <= 4 * (int64_t)num_seqs)
+      route = KDA_ROUTE_SERIAL;
+    else
+      route = (8 * units <= 3 * (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
+                                                                           : KDA_ROUTE_CHUNK;
   }
   if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);

@@ -210,6 +210,11 @@ def test_decode_frontend_host_validation():
 def test_auto_route_and_workspace():
     # few (sequence, head) units: two-pass split route; many: fused chunk route
     assert kda.plan(1, 8192, 8, -5.0, 256).route == kda.ROUTE_SPLIT
+    # many sequences of at most 4 tokens on average (multi-token decode): serial
+    assert kda.plan(4096, 4 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_SERIAL
+    assert kda.plan(64, 2 * 64, 8, -5.0, 256).route == kda.ROUTE_SERIAL
+    assert kda.plan(4096, 8 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_CHUNK
+    assert kda.plan(1, 5, 2, -5.0, 256).route == kda.ROUTE_CHUNK
     # at most three chunks in the batch: the fused route's serial loop is shorter
     assert kda.plan(1, 64, 2, -5.0, 256).route == kda.ROUTE_CHUNK
     assert kda.plan(3, 96, 8, -5.0, 256).route == kda.ROUTE_CHUNK
