@@ -269,7 +269,9 @@ def fused_configs(torch, dev, kda, configs=(2, 3), steps=5, warmup=2):
             hbm_gbps=nbytes / t / 1e9, hbm_frac=nbytes / t / 1e9 / PEAK_HBM_GBPS,
             algorithmic_flop_per_call=flops, algorithmic_bytes_per_call=nbytes,
             kernels={kname: dict(st, launches_per_call=1,
-                                 traffic=stored_traffic(f"{kname}_T{T}_H{H}"))})
+                                 traffic=stored_traffic(f"{kname}_T{T}_H{H}"),
+                                 mfma_counters=stored_mfma(f"{kname}_T{T}_H{H}").get(
+                                     f"{kname}_kernel"))})
         log(f"[bench] configuration {i}: {st['mean_ms']:.3f} ms, "
             f"{tokheads / t:.3e} tokens*heads/s")
         del x, s0, o, fin, ws

@@ -14,12 +14,18 @@
       MFMA busy percentage of all SIMDs and the executed MFMA FLOP per launch
       (including hi/lo splits and one-hot transposes) as TFLOP/s against the
       2.5 PFLOP/s dense fp16/bf16 peak.
+  python profile_summaries.py mfma-as <tag> <pmc_dir> <stats_dir> <command...>
+      the same for a bench run of another workload, whose fused prefill kernel is
+      summarised as profiles/mfma_prefill_chunk_<tag>.json (tag e.g. T35413_H32).
   python profile_summaries.py traffic <fetch_dir> <write_dir> <command...>
       the two `rocprofv3 --pmc FETCH_SIZE` / `--pmc WRITE_SIZE` runs of the
       same bench command; writes profiles/traffic_<kernel>.json with the HBM
       bytes per launch of each bench kernel.  Both counters are scaled by
       what they read for the bench's 1 GiB device-to-device copy (the
       __amd_rocclr_copyBuffer dispatches: 2^30 bytes read, 2^30 written).
+  python profile_summaries.py traffic-as <tag> <fetch_dir> <write_dir> <command...>
+      the same for a bench run of another workload (bench.py --prefill-config):
+      profiles/traffic_prefill_chunk_<tag>.json for its fused prefill kernel.
 
 The command that produced the run is passed after the directories and stored
 verbatim.  bench.py uses a traffic figure only while its `source_digest`
@@ -88,7 +94,8 @@ def per_kernel(pmc_dir, counter):
     return vals
 
 
-def traffic(fetch_dir, write_dir, command):
+def traffic(fetch_dir, write_dir, command, kernels=None):
+    kernels = KERNELS if kernels is None else kernels
     fetch = per_kernel(fetch_dir, "FETCH_SIZE")
     write = per_kernel(write_dir, "WRITE_SIZE")
     big = lambda xs: [x for x in xs if x > 0.5 * COPY_BYTES]
@@ -98,7 +105,7 @@ def traffic(fetch_dir, write_dir, command):
     f_scale = COPY_BYTES / (sum(f_copy) / len(f_copy))
     w_scale = COPY_BYTES / (sum(w_copy) / len(w_copy))
     digest = source_digest()
-    for k, name in KERNELS.items():
+    for k, name in kernels.items():
         if k not in fetch or k not in write:
             continue
         fb = f_scale * sum(fetch[k]) / len(fetch[k])
@@ -113,7 +120,8 @@ def traffic(fetch_dir, write_dir, command):
         print(path, f"{(fb + wb) / 1e6:.2f} MB/launch")
 
 
-def mfma(pmc_dir, stats_dir, command):
+def mfma(pmc_dir, stats_dir, command, kernels=None, workload=WORKLOAD):
+    kernels = KERNELS if kernels is None else kernels
     path = one(os.path.join(pmc_dir, "**", "*counter_collection.csv"))
     vals = {}
     for r in csv.DictReader(open(path)):
@@ -123,9 +131,9 @@ def mfma(pmc_dir, stats_dir, command):
     avg = lambda d: sum(d.values()) / len(d) if d else 0.0
     dur = {short(r["Name"]): float(r["AverageNs"]) for r in
            csv.DictReader(open(one(os.path.join(stats_dir, "**", "*kernel_stats.csv"))))}
-    out = {"workload": WORKLOAD, "peak_tflops": 2500.0, "source_digest": source_digest(),
+    out = {"workload": workload, "peak_tflops": 2500.0, "source_digest": source_digest(),
            "command": command, "kernels": {}}
-    for k in KERNELS:
+    for k in kernels:
         if not k.startswith("prefill") or (k, "MfmaUtil") not in vals:
             continue
         flops = avg(vals.get((k, "MfmaFlopsF16"), {})) + avg(vals.get((k, "MfmaFlopsBF16"), {}))
@@ -136,7 +144,7 @@ def mfma(pmc_dir, stats_dir, command):
             "avg_us": ns / 1e3 if ns else None,
             "executed_tflops": flops / ns / 1e3 if ns else None,
             "frac_of_peak": flops / ns / 1e3 / 2500.0 if ns else None}
-    path = os.path.join(ROOT, "profiles", f"mfma_{WORKLOAD}.json")
+    path = os.path.join(ROOT, "profiles", f"mfma_{workload}.json")
     json.dump(out, open(path, "w"), indent=1)
     print(path)
     for k, v in out["kernels"].items():
@@ -150,7 +158,16 @@ if __name__ == "__main__":
         trace(sys.argv[3], " ".join(sys.argv[4:]), workload=sys.argv[2])
     elif len(sys.argv) >= 5 and sys.argv[1] == "mfma":
         mfma(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif len(sys.argv) >= 6 and sys.argv[1] == "mfma-as":
+        tag = sys.argv[2]
+        mfma(sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]),
+             kernels={"prefill_chunk_kernel": f"prefill_chunk_{tag}"},
+             workload=f"prefill_chunk_{tag}")
     elif len(sys.argv) >= 5 and sys.argv[1] == "traffic":
         traffic(sys.argv[2], sys.argv[3], " ".join(sys.argv[4:]))
+    elif len(sys.argv) >= 6 and sys.argv[1] == "traffic-as":
+        tag = sys.argv[2]
+        traffic(sys.argv[3], sys.argv[4], " ".join(sys.argv[5:]),
+                kernels={"prefill_chunk_kernel": f"prefill_chunk_{tag}"})
     else:
         sys.exit(__doc__)
