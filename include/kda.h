@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 8
+#define KDA_ABI_VERSION 9
 #define KDA_HEAD_DIM 128
 
 typedef enum {
@@ -109,13 +109,22 @@ typedef enum {
   KDA_ROUTE_CHUNK = 1,  /* 32-token chunks on bf16/fp16 MFMA, each block
                            prepares and consumes its own chunks (many
                            (sequence, head) units)                         */
-  KDA_ROUTE_SPLIT = 2   /* same chunk math in two passes: all chunks are
+  KDA_ROUTE_SPLIT = 2,  /* same chunk math in two passes: all chunks are
                            prepared in parallel into the workspace, then a
                            short serial chain per (sequence, head) consumes
                            them (few units: AUTO picks it up to 3/8 of the
                            device's compute units in (sequence, head)
                            units, 96 on MI355X, and only for batches of
                            more than 96 tokens)                            */
+  KDA_ROUTE_STREAM = 3  /* token recurrence as a decode-style state stream:
+                           one block per (sequence, head, value slice) keeps
+                           the state in registers across the sequence's
+                           tokens, one read and one write of it, a block
+                           reduction per token (AUTO: many short sequences,
+                           e.g. multi-token decode of a few new tokens per
+                           row against a state pool, flashinfer PR #5551
+                           "Kimi K3 TP12 H=8 fused KDA decode", its T > 1
+                           path)                                           */
 } kda_prefill_route;
 
 /* Exponent handling of the chunk route's pairwise (Mqk, Akk) products,

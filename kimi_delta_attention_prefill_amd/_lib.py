@@ -25,6 +25,7 @@ ROUTE_AUTO = -1
 ROUTE_SERIAL = 0
 ROUTE_CHUNK = 1
 ROUTE_SPLIT = 2
+ROUTE_STREAM = 3
 
 ANCHOR_FIXED = 0
 ANCHOR_SPLIT16 = 1

@@ -111,17 +111,6 @@ __device__ __forceinline__ InvWork& inv_of(PrepWork& pw) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Block barrier that orders LDS accesses only: the LDS writes before it are
-// complete and visible after it, while global loads and stores (and the
-// direct global-to-LDS loads, which their issuer waits for explicitly) stay in
-// flight across it.  __syncthreads() would also wait for every outstanding
-// global access, exposing a prefetch's whole latency at the next barrier.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
-  __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
-}
-
 // Ordering of one wave's own LDS accesses (a write, then reads of it by other
 // lanes of the same wave): LDS operations of a wave complete in order, so only
 // the compiler must not move them across this point.

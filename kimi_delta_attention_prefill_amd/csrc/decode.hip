@@ -16,8 +16,10 @@
 // and q . k are finished in registers inside a wave (a DPP butterfly, then
 // lane-swap reduce-scatter steps) and by one LDS fold across the waves; the
 // state is read once and written once.  Row counts too small to fill the
-// chip use narrower slices (more blocks per item); many rows use whole-item
-// 512-thread blocks, three resident per compute unit.
+// chip use narrower slices (more blocks per item).  Many rows go to the token
+// stream below with one token per row: the same step in whole-item 512-thread
+// blocks, two resident per compute unit, which measured faster at thousands
+// of rows.
 //
 // Optional input front-end (the decode ABI of that PR carries a lower-bound
 // switch, the bound and norm_eps; its tests use softplus and lower-bound
@@ -367,49 +369,265 @@ __global__ __launch_bounds__(NT) void decode_kernel(DecodeArgs a) {
   B::run(a, sm);
 }
 
-constexpr int kLdsPerCU = 160 * 1024;
-
-// `per_cu` > 0 caps the blocks resident on a compute unit by reserving
-// unused dynamic LDS: with thousands of items, three 64 KiB state streams
-// per CU keep HBM busier than four (fewer DRAM pages contended at once).
 template <int COLS, bool BF16, int NT>
-hipError_t launch_shape(const DecodeArgs& a, int per_cu, hipStream_t s) {
+hipError_t launch_shape(const DecodeArgs& a, hipStream_t s) {
   const int64_t units = (int64_t)a.rows * a.num_heads * (kHeadDim / COLS);
-  const int smem = (int)sizeof(typename DecodeBlock<COLS, BF16, NT>::Smem);
-  const int reserve = per_cu > 0 ? max(0, kLdsPerCU / per_cu - 1024 - smem) : 0;
-  decode_kernel<COLS, BF16, NT><<<dim3((unsigned)units), NT, reserve, s>>>(a);
+  decode_kernel<COLS, BF16, NT><<<dim3((unsigned)units), NT, 0, s>>>(a);
   return hipGetLastError();
 }
 
 template <bool BF16>
-hipError_t launch_cols(const DecodeArgs& a, int cols, int threads, int per_cu, hipStream_t s) {
+hipError_t launch_cols(const DecodeArgs& a, int cols, int threads, hipStream_t s) {
   if (threads != 256 && threads != 512) return hipErrorInvalidValue;
   const bool wide = threads == 512;
-  const int c = per_cu;
   if constexpr (BF16) {
     if (cols == 128)
-      return wide ? launch_shape<128, true, 512>(a, c, s) : launch_shape<128, true, 256>(a, c, s);
+      return wide ? launch_shape<128, true, 512>(a, s) : launch_shape<128, true, 256>(a, s);
     if (cols == 64)
-      return wide ? launch_shape<64, true, 512>(a, c, s) : launch_shape<64, true, 256>(a, c, s);
+      return wide ? launch_shape<64, true, 512>(a, s) : launch_shape<64, true, 256>(a, s);
   } else {
     if (cols == 128)
-      return wide ? launch_shape<128, false, 512>(a, c, s) : launch_shape<128, false, 256>(a, c, s);
+      return wide ? launch_shape<128, false, 512>(a, s) : launch_shape<128, false, 256>(a, s);
     if (cols == 64)
-      return wide ? launch_shape<64, false, 512>(a, c, s) : launch_shape<64, false, 256>(a, c, s);
+      return wide ? launch_shape<64, false, 512>(a, s) : launch_shape<64, false, 256>(a, s);
     if (cols == 32)
-      return wide ? launch_shape<32, false, 512>(a, c, s) : launch_shape<32, false, 256>(a, c, s);
+      return wide ? launch_shape<32, false, 512>(a, s) : launch_shape<32, false, 256>(a, s);
   }
   return hipErrorInvalidValue;
 }
 
+// ---------------------------------------------------------------------------
+// Token stream: the prefill of many short sequences -- multi-token decode, a
+// few new tokens per row appended to the row's pool state -- as a decode-style
+// streamer.  One block per (sequence, head, value slice) keeps its slice of
+// the FP32 state in registers across the sequence's tokens: one state read and
+// one write (16-byte vectors, as the decode), and per token the decode step's
+// two dk-reductions.  The next token's inputs are loaded while the current one
+// is processed (the barriers order LDS only, so those loads stay in flight).
+// The decay, beta and the q/k norm follow the decode step's front-end.
+template <int COLS, bool BF16, int NT>
+struct StreamBlock {
+  using IO = StateIO<BF16>;
+  using elem = typename IO::elem;
+  using raw = typename IO::raw;
+  static constexpr int CPT = IO::CPT;
+  static constexpr int TPR = COLS / CPT;
+  static constexpr int RG = NT / TPR;
+  static constexpr int RPT = kHeadDim / RG;
+  static constexpr int SLICES = kHeadDim / COLS;
+  static constexpr int WAVES = NT / 64;
+  static constexpr int NRED = 2 * CPT + 1;
+  static_assert(TPR >= 8 && TPR <= 32 && RPT >= 1 && RG * RPT == kHeadDim, "stream tiling");
+
+  struct Smem {
+    float sq[2][kHeadDim], sk[2][kHeadDim], sd[2][kHeadDim];  // by token parity
+    float red[WAVES][TPR][NRED + 1];
+    float tot[TPR][NRED + 1];
+    float nrm[2][2][2];   // [parity][wave][q, k] partial sums of squares
+  };
+
+  // One token's inputs as this thread needs them.
+  struct Tok {
+    uint16_t q, k, g, b;
+    float v[CPT];
+  };
+
+  __device__ __forceinline__ static void fetch(Tok& x, const PrefillArgs& a, int t, int h, int ch,
+                                               int col0) {
+    const int64_t th = (int64_t)t * a.num_heads + h;
+    x.q = a.q[th * kHeadDim + ch];
+    x.k = a.k[th * kHeadDim + ch];
+    x.g = a.g[th * kHeadDim + ch];
+    x.b = a.beta[th];
+    load_bf16_vec<CPT>(a.v + th * kHeadDim + col0, x.v);
+  }
+
+  __device__ __forceinline__ static void run(const PrefillArgs& a, Smem& sm) {
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int jq = tid % TPR, rg = tid / TPR;
+    const int H = a.num_heads;
+    const int slice = (int)(blockIdx.x % SLICES);
+    const int64_t item = blockIdx.x / SLICES;
+    const int h = (int)(item % H), n = (int)(item / H);
+    const int col0 = slice * COLS + jq * CPT;
+    const int ch = tid & (kHeadDim - 1);
+    const int bos = a.cu_seqlens ? clamp_offset(a.cu_seqlens[n], a.total_tokens) : n;
+    const int eos =
+        a.cu_seqlens ? max(bos, clamp_offset(a.cu_seqlens[n + 1], a.total_tokens)) : n + 1;
+
+    // where the state comes from and goes to (uniform over the block)
+    const elem* src = nullptr;
+    elem* dst = nullptr;
+    if (a.pool) {
+      const int64_t slot = a.slots[n];
+      if (slot >= 0 && slot < a.num_slots) {
+        dst = reinterpret_cast<elem*>(a.pool) + slot * a.slot_stride + h * (kHeadDim * kHeadDim);
+        src = dst;
+      } else if (a.skip_null_slots) {   // the decode's skipped row: zero output, pool untouched
+        for (int t = bos; t < eos; ++t)
+          if (tid < COLS) a.out[((int64_t)t * H + h) * kHeadDim + slice * COLS + tid] = 0;
+        return;
+      }
+    } else {
+      const int64_t off = ((int64_t)n * H + h) * (kHeadDim * kHeadDim);
+      if (a.s0) src = reinterpret_cast<const elem*>(a.s0 + off);
+      if (a.s1) dst = reinterpret_cast<elem*>(a.s1 + off);
+    }
+    Tok nxt;
+    if (bos < eos) fetch(nxt, a, bos, h, ch, col0);
+
+    const uint32_t lane_elem = (uint32_t)(rg * kHeadDim + col0);
+    constexpr uint32_t kStep = RG * kHeadDim * sizeof(elem);
+    float s[RPT][CPT];
+    if (src) {
+      const __amdgpu_buffer_rsrc_t rs = make_buffer(src, kHeadDim * kHeadDim * sizeof(elem));
+      raw sr[RPT];
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) sr[i] = IO::load(rs, lane_elem * (uint32_t)sizeof(elem), i * kStep);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) IO::unpack(sr[i], s[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) s[i][m] = 0.f;
+    }
+
+    for (int t = bos; t < eos; ++t) {
+      const int pb = (t - bos) & 1;
+      const Tok cur = nxt;
+      if (t + 1 < eos) fetch(nxt, a, t + 1, h, ch, col0);
+      if (tid < kHeadDim) {   // waves 0 and 1
+        const float qv = bf16_to_f32(cur.q), kv = bf16_to_f32(cur.k), gv = bf16_to_f32(cur.g);
+        sm.sq[pb][tid] = qv;
+        sm.sk[pb][tid] = kv;
+        float d;
+        if (a.fe.gate_mode == 1)
+          d = fast_exp2(a.fe.lower_bound * kLog2e / (1.f + fast_exp2(-gv * kLog2e)));
+        else if (a.fe.gate_mode == 2)
+          d = 1.f / (1.f + fast_exp2(gv * kLog2e));     // e^{-softplus(a)} = sigmoid(-a)
+        else
+          d = fast_exp2(gv * kLog2e);
+        sm.sd[pb][tid] = d;
+        if (a.fe.normalize_qk) {
+          float sq2 = qv * qv, sk2 = kv * kv;
+#pragma unroll
+          for (int off = 1; off < 64; off <<= 1) {
+            sq2 += __shfl_xor(sq2, off);
+            sk2 += __shfl_xor(sk2, off);
+          }
+          if (lane == 0) {
+            sm.nrm[pb][wave][0] = sq2;
+            sm.nrm[pb][wave][1] = sk2;
+          }
+        }
+      }
+      lds_barrier();
+      float rq = 1.f, rk = 1.f;
+      if (a.fe.normalize_qk) {
+        rq = inv_norm(sm.nrm[pb][0][0] + sm.nrm[pb][1][0] + a.fe.norm_eps);
+        rk = inv_norm(sm.nrm[pb][0][1] + sm.nrm[pb][1][1] + a.fe.norm_eps);
+      }
+      float part[NRED];
+#pragma unroll
+      for (int m = 0; m < NRED; ++m) part[m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int c = rg + RG * i;
+        const float d = sm.sd[pb][c], kc = sm.sk[pb][c], qc = sm.sq[pb][c];
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) {
+          s[i][m] *= d;
+          part[m] = fmaf(kc, s[i][m], part[m]);
+          part[CPT + m] = fmaf(qc, s[i][m], part[CPT + m]);
+        }
+        part[2 * CPT] = fmaf(qc, kc, part[2 * CPT]);
+      }
+      wave_reduce_store<TPR, NRED>(part, &sm.red[wave][jq][0], lane);
+      lds_barrier();
+      for (int e = tid; e < TPR * NRED; e += NT) {
+        const int j = e / NRED, m = e % NRED;
+        float acc = sm.red[0][j][m];
+#pragma unroll
+        for (int w = 1; w < WAVES; ++w) acc += sm.red[w][j][m];
+        sm.tot[j][m] = acc;
+      }
+      lds_barrier();
+#pragma unroll
+      for (int m = 0; m < NRED; ++m) part[m] = sm.tot[jq][m];
+      const float qk = part[2 * CPT] * (rq * rk);
+      float b = bf16_to_f32(cur.b);
+      if (a.fe.beta_logits) b = 1.f / (1.f + fast_exp2(-b * kLog2e));
+      float u[CPT], uk[CPT];
+#pragma unroll
+      for (int m = 0; m < CPT; ++m) {
+        u[m] = b * (cur.v[m] - part[m] * rk);
+        uk[m] = u[m] * rk;   // the update adds k_n u^T = k (u / |k|)^T; the output keeps u
+      }
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float kc = sm.sk[pb][rg + RG * i];
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) s[i][m] = fmaf(kc, uk[m], s[i][m]);
+      }
+      if (rg == 0) {
+        float o[CPT];
+#pragma unroll
+        for (int m = 0; m < CPT; ++m) o[m] = a.scale * fmaf(qk, u[m], part[CPT + m] * rq);
+        store_bf16_vec<CPT>(a.out + ((int64_t)t * H + h) * kHeadDim + col0, o);
+      }
+      if (float* cp = prefill_checkpoint(a, n, h, bos, t + 1 - bos)) {   // FP32 rows
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+#pragma unroll
+          for (int m = 0; m < CPT; m += 4)
+            StateIO<false>::store(
+                (__attribute__((address_space(1))) float*)(cp + lane_elem + i * (RG * kHeadDim) + m),
+                s[i] + m);
+      }
+    }
+    if (dst) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        auto* row = (__attribute__((address_space(1))) elem*)(dst + i * (RG * kHeadDim));
+        asm volatile("" : "+s"(row));
+        IO::store(row + lane_elem, s[i]);
+      }
+    }
+  }
+};
+
+template <int COLS, bool BF16, int NT>
+__global__ __launch_bounds__(NT) void stream_kernel(PrefillArgs a) {
+  using B = StreamBlock<COLS, BF16, NT>;
+  __shared__ typename B::Smem sm;
+  B::run(a, sm);
+}
+
+template <int COLS, bool BF16, int NT>
+hipError_t launch_stream_shape(const PrefillArgs& a, hipStream_t s) {
+  const int64_t units = (int64_t)a.num_seqs * a.num_heads * (kHeadDim / COLS);
+  stream_kernel<COLS, BF16, NT><<<dim3((unsigned)units), NT, 0, s>>>(a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
+hipError_t launch_prefill_stream(const PrefillArgs& a, int cols, hipStream_t s) {
+  if (a.num_seqs <= 0) return hipSuccess;
+  const bool bf16 = a.pool && a.pool_bf16;
+  if (cols == 128)
+    return bf16 ? launch_stream_shape<128, true, 512>(a, s) : launch_stream_shape<128, false, 512>(a, s);
+  if (cols == 64)
+    return bf16 ? launch_stream_shape<64, true, 512>(a, s) : launch_stream_shape<64, false, 512>(a, s);
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, int threads,
-                         int blocks_per_cu, hipStream_t s) {
+                         hipStream_t s) {
   if (a.rows <= 0) return hipSuccess;
-  if (blocks_per_cu < 0 || blocks_per_cu > 8) return hipErrorInvalidValue;
-  return bf16_state ? launch_cols<true>(a, cols, threads, blocks_per_cu, s)
-                    : launch_cols<false>(a, cols, threads, blocks_per_cu, s);
+  return bf16_state ? launch_cols<true>(a, cols, threads, s)
+                    : launch_cols<false>(a, cols, threads, s);
 }
 
 }  // namespace kda

@@ -211,6 +211,7 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   a.num_slots = 0;
   a.slot_stride = 0;
   a.ckpt = nullptr;
+  a.skip_null_slots = 0;
   a.ckpt_tokens = 0;
   return a;
 }
@@ -303,7 +304,7 @@ int kda_check_slots(const int32_t* slot_indices, int32_t rows, int64_t num_slots
 
 int kda_set_prefill_route(int32_t route) {
   if (route != KDA_ROUTE_AUTO && route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK &&
-      route != KDA_ROUTE_SPLIT)
+      route != KDA_ROUTE_SPLIT && route != KDA_ROUTE_STREAM)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_set_prefill_route: unknown route %d", route);
   g_forced_route.store(route);
   return ok();
@@ -335,19 +336,23 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     // fused kernel's short serial loop beats the two-pass route's second
     // launch (measured at H=2: 8.8 vs 19.8 us at 32 tokens, 19.6 vs 20.8 us
     // at 96, 24.8 vs 21.2 us at 128).
-    // Many sequences of at most four tokens on average (multi-token
-    // decode): the token-serial kernel streams each state once and runs a
-    // few steps on it, where a fused block sets up its whole chunk pipeline
-    // for one short chunk (4096 rows x H = 8 from a pool: 1.48 vs 2.29 ms at
-    // T = 2, 1.77 vs 2.32 ms at T = 4; at T = 8 the fused kernel wins, 2.40
-    // vs 2.63 ms).
-    if (total_tokens <= 4 * (int64_t)num_seqs)
-      route = KDA_ROUTE_SERIAL;
+    // Many short sequences (multi-token decode): the stream kernel reads and
+    // writes each state once and runs the few token steps on it in
+    // registers, where a fused block sets up its whole chunk pipeline for one
+    // short chunk.  Measured from a 4096-slot FP32 pool at H = 8: 4096 rows
+    // 0.74 / 0.92 / 1.59 / 2.71 ms at T = 2 / 4 / 8 / 16 against the fused
+    // route's 2.30 / 2.33 / 2.41 / 2.56 ms; one row 8.8 vs 10.8 us at T = 4
+    // but 15.0 vs 11.2 us at T = 8 (eight blocks, per-token latency exposed).
+    const int64_t per_seq8 = 8 * (int64_t)num_seqs;
+    if (total_tokens <= 4 * (int64_t)num_seqs ||
+        (total_tokens <= per_seq8 && units >= (int64_t)num_cus))
+      route = KDA_ROUTE_STREAM;
     else
       route = (8 * units <= 3 * (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
                                                                            : KDA_ROUTE_CHUNK;
   }
-  if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT)
+  if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT &&
+      route != KDA_ROUTE_STREAM)
     return fail(KDA_ERR_INVALID_ARGUMENT, "kda_prefill_plan: unknown route %d", route);
   std::memset(plan, 0, sizeof(*plan));
   plan->route = route;
@@ -358,7 +363,13 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                                                        : KDA_ANCHOR_DATA;
   plan->anchor_log2 = std::isfinite(lower_bound)
                           ? (float)(16.0 * (double)lower_bound * 1.4426950408889634) : 0.f;
-  if (route == KDA_ROUTE_SERIAL) {
+  if (route == KDA_ROUTE_STREAM) {
+    // Whole 128-column items (512 threads) once there are enough of them to
+    // fill the device, else two 64-column slices per (sequence, head).
+    plan->dv_split = units >= 2 * (int64_t)num_cus ? 1 : 2;
+    plan->block_threads = 512;
+    plan->grid_blocks = units * plan->dv_split;
+  } else if (route == KDA_ROUTE_SERIAL) {
     // 16 value columns per wave; fewer waves per block (more blocks) when
     // there are few (sequence, head) units to spread over the compute units.
     int waves = 4;
@@ -435,6 +446,8 @@ int run_prefill(const char* fn, kda::PrefillArgs a, float lower_bound, void* wor
   hipError_t e;
   if (plan.route == KDA_ROUTE_SERIAL)
     e = kda::launch_prefill_serial(a, plan.block_threads / 64, stream);
+  else if (plan.route == KDA_ROUTE_STREAM)
+    e = kda::launch_prefill_stream(a, 128 / plan.dv_split, stream);
   else if (plan.route == KDA_ROUTE_SPLIT)
     e = kda::launch_prefill_split(a, plan.anchor_mode, plan.dv_split, workspace, stream);
   else   // with the input front-end the fused route runs 64-column blocks only
@@ -681,23 +694,39 @@ int kda_decode_ex(const void* q, const void* k, const void* v, const void* g, co
   a.out = static_cast<uint16_t*>(out);
   a.fe = fe;
 
-  // Narrow value-column slices when there are too few items to fill the chip;
-  // with many items, whole-item 512-thread blocks, three resident per CU.
+  // Many items: the token-stream kernel with one token per row (whole-item
+  // 512-thread blocks, two resident per CU; 4096 rows x H=8 FP32 0.74 ms
+  // against 0.77-0.81 ms for the decode blocks below; BF16 gains only from
+  // about 2048 rows, 204 vs 207 us).  Fewer: decode blocks, narrow
+  // value-column slices when the items cannot fill the chip.
   int cus = current_device_cus();
   if (cus <= 0) cus = 256;
   const int64_t items = (int64_t)rows * num_heads;
   const bool bf16 = state_dtype == KDA_STATE_BF16;
-  int cols = 128, threads = 512, per_cu = 0;
-  if (items >= 16LL * cus) {
-    per_cu = 3;
-  } else if (items >= 2LL * cus) {
-  } else if (bf16) {
-    cols = 64;
+  hipError_t e;
+  if (items >= (bf16 ? 16LL : 8LL) * cus) {
+    kda::PrefillArgs p = make_args(q, k, v, g, beta, nullptr, rows, rows, num_heads, scale, -1.f,
+                                   nullptr, nullptr, out);
+    p.pool = state_pool;
+    p.pool_bf16 = bf16;
+    p.slots = slot_indices;
+    p.num_slots = num_slots;
+    p.slot_stride = slot_stride;
+    p.fe = fe;
+    p.skip_null_slots = 1;
+    e = kda::launch_prefill_stream(p, 128, stream);
   } else {
-    cols = items >= cus ? 64 : 32;
-    threads = 256;
+    int cols = 128, threads = 512;
+    if (items < 2LL * cus) {
+      if (bf16) {
+        cols = 64;
+      } else {
+        cols = items >= cus ? 64 : 32;
+        threads = 256;
+      }
+    }
+    e = kda::launch_decode(a, bf16, cols, threads, stream);
   }
-  hipError_t e = kda::launch_decode(a, bf16, cols, threads, per_cu, stream);
   if (e != hipSuccess)
     return fail(KDA_ERR_HIP, "kda_decode: launch failed: %s", hipGetErrorString(e));
   return ok();

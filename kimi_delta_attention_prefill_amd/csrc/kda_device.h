@@ -53,6 +53,16 @@ __device__ __forceinline__ void buffer_store_u16(uint16_t v, __amdgpu_buffer_rsr
   __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
 }
 
+// Block barrier that orders LDS accesses only: the LDS writes before it are
+// complete and visible after it, while global loads and stores stay in
+// flight across it.  __syncthreads() would also wait for every outstanding
+// global access, exposing a prefetch's whole latency at the next barrier.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Clamp a device-read sequence offset into [0, total].
 __device__ __forceinline__ int clamp_offset(int x, int total) {
   return x < 0 ? 0 : (x > total ? total : x);

@@ -65,6 +65,11 @@ struct PrefillArgs {
   float* ckpt;            // fp32 or null
   int32_t ckpt_tokens;
   FrontEnd fe;            // how g and beta are given, q/k normalisation
+  // Stream route only: a null cu_seqlens means one token per sequence (token
+  // n of sequence n: the T = 1 decode), and with skip_null_slots a sequence
+  // whose pool slot is out of range gets zero outputs (the decode's
+  // skipped row) instead of a step from the zero state.
+  int32_t skip_null_slots;
 };
 
 struct DecodeArgs {
@@ -102,11 +107,14 @@ hipError_t launch_prefill_split_chain(const PrefillArgs& a, const void* workspac
                                       hipStream_t s);
 size_t split_workspace_bytes(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
                              int32_t windows);
+// Token stream over many short sequences (multi-token decode): the prefill
+// with one block per (sequence, head, `cols` value columns, 128 or 64), the
+// state in registers across the sequence's tokens.
+hipError_t launch_prefill_stream(const PrefillArgs& a, int cols, hipStream_t s);
 // Decode step; `cols` = value columns per block (32, 64 or 128 for FP32
-// state, 64 or 128 for BF16), `threads` per block (256 or 512),
-// `blocks_per_cu` > 0 caps the resident blocks per compute unit (0 = no cap).
+// state, 64 or 128 for BF16), `threads` per block (256 or 512).
 hipError_t launch_decode(const DecodeArgs& a, bool bf16_state, int cols, int threads,
-                         int blocks_per_cu, hipStream_t s);
+                         hipStream_t s);
 
 // Records `code` and the formatted text as the calling thread's last error
 // (kda_last_error) and returns `code`.

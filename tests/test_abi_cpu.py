@@ -44,7 +44,7 @@ def test_plan_anchor_mode_boundary():
     assert abs(p.anchor_log2 - 16 * -5.0 * 1.4426950408889634) < 1e-4
 
 
-@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT])
+@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT, kda.ROUTE_STREAM])
 def test_plan_grid_covers_every_unit(route):
     for N, H, cus in ((1, 8, 256), (16, 32, 256), (4, 64, 256), (1, 1, 256), (3, 5, 80)):
         p = kda.plan(N, 100 * N, H, -5.0, cus, route)
@@ -210,10 +210,14 @@ def test_decode_frontend_host_validation():
 def test_auto_route_and_workspace():
     # few (sequence, head) units: two-pass split route; many: fused chunk route
     assert kda.plan(1, 8192, 8, -5.0, 256).route == kda.ROUTE_SPLIT
-    # many sequences of at most 4 tokens on average (multi-token decode): serial
-    assert kda.plan(4096, 4 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_SERIAL
-    assert kda.plan(64, 2 * 64, 8, -5.0, 256).route == kda.ROUTE_SERIAL
-    assert kda.plan(4096, 8 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_CHUNK
+    # many short sequences (multi-token decode): the stream route, up to 4
+    # tokens per sequence on average, up to 8 with at least one unit per CU
+    assert kda.plan(4096, 4 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_STREAM
+    assert kda.plan(64, 2 * 64, 8, -5.0, 256).route == kda.ROUTE_STREAM
+    assert kda.plan(1, 4, 8, -5.0, 256).route == kda.ROUTE_STREAM
+    assert kda.plan(4096, 8 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_STREAM
+    assert kda.plan(1, 8, 8, -5.0, 256).route == kda.ROUTE_CHUNK          # 8 units only
+    assert kda.plan(4096, 9 * 4096, 8, float("-inf"), 256).route == kda.ROUTE_CHUNK
     assert kda.plan(1, 5, 2, -5.0, 256).route == kda.ROUTE_CHUNK
     # at most three chunks in the batch: the fused route's serial loop is shorter
     assert kda.plan(1, 64, 2, -5.0, 256).route == kda.ROUTE_CHUNK

@@ -216,7 +216,7 @@ def test_prefill_pool_graph_replay(dev):
 
 
 @pytest.mark.parametrize("dtype", [torch.float32, torch.bfloat16], ids=["f32", "bf16"])
-@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT])
+@pytest.mark.parametrize("route", [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT, kda.ROUTE_STREAM])
 def test_prefill_pool_padded_layout(dev, dtype, route):
     """Pooled prefill on layer 1 of a [slots, 3, H, 128, 128] pool: results as
     on a dense pool (checked against the oracle), other layers untouched."""

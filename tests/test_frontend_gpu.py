@@ -99,7 +99,8 @@ def test_decode_frontend_default_equals_plain(dev):
 # ---------------------------------------------------------------- prefill
 from kimi_delta_attention_prefill_amd.inputs import make_prefill_case, make_prefill_raw_case  # noqa: E402
 
-ROUTES = {"serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK, "split": kda.ROUTE_SPLIT}
+ROUTES = {"serial": kda.ROUTE_SERIAL, "chunk": kda.ROUTE_CHUNK, "split": kda.ROUTE_SPLIT,
+          "stream": kda.ROUTE_STREAM}
 PREFILL_FE = {
     "lower_bound": (kda.FrontEnd(gate_mode=kda.GATE_LOWER_BOUND, lower_bound=-5.0,
                                  beta_logits=True, normalize_qk=True, norm_eps=1e-6), {}),

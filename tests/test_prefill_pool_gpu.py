@@ -11,7 +11,7 @@ from _checks import check_bf16_state, check_out, check_state
 
 pytestmark = pytest.mark.gpu
 
-ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT]
+ROUTES = [kda.ROUTE_SERIAL, kda.ROUTE_CHUNK, kda.ROUTE_SPLIT, kda.ROUTE_STREAM]
 
 
 @pytest.fixture(scope="module")
