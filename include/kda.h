@@ -112,9 +112,9 @@ typedef enum {
   KDA_ROUTE_SPLIT = 2,  /* same chunk math in two passes: all chunks are
                            prepared in parallel into the workspace, then a
                            short serial chain per (sequence, head) consumes
-                           them (few units: AUTO picks it up to 3/8 of the
-                           device's compute units in (sequence, head)
-                           units, 96 on MI355X, and only for batches of
+                           them (few units: AUTO picks it up to a quarter of
+                           the device's compute units in (sequence, head)
+                           units, 64 on MI355X, and only for batches of
                            more than 96 tokens)                            */
   KDA_ROUTE_STREAM = 3  /* token recurrence as a decode-style state stream:
                            one block per (sequence, head, value slice) keeps

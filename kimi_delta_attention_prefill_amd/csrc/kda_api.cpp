@@ -330,8 +330,10 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
     // chip and serialise chunk preparation, so prepare all chunks in
     // parallel first.  Many recurrences: keep everything in one pass.  The
     // split chain runs 8 blocks per recurrence, two per CU; measured on 256
-    // CUs it wins up to 1.5 such rounds (96 units: 1.29 vs 1.50 ms at T=8192)
-    // and loses from 2 (128 units: 1.78 vs 1.52 ms).
+    // CUs at T=8192 per sequence against the fused pipeline (1.10-1.15 ms
+    // for up to 128 units): 64 units 0.73 ms, 80 units 1.14 vs 1.12 ms, 96
+    // units 1.28 vs 1.14 ms, so the split route takes up to a quarter of
+    // the CU count in units.
     // At most three chunks in the whole batch (so in every sequence): the
     // fused kernel's short serial loop beats the two-pass route's second
     // launch (measured at H=2: 8.8 vs 19.8 us at 32 tokens, 19.6 vs 20.8 us
@@ -348,8 +350,8 @@ int kda_prefill_plan(int32_t num_seqs, int64_t total_tokens, int32_t num_heads,
         (total_tokens <= per_seq8 && units >= (int64_t)num_cus))
       route = KDA_ROUTE_STREAM;
     else
-      route = (8 * units <= 3 * (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
-                                                                           : KDA_ROUTE_CHUNK;
+      route = (4 * units <= (int64_t)num_cus && total_tokens > 3 * 32) ? KDA_ROUTE_SPLIT
+                                                                       : KDA_ROUTE_CHUNK;
   }
   if (route != KDA_ROUTE_SERIAL && route != KDA_ROUTE_CHUNK && route != KDA_ROUTE_SPLIT &&
       route != KDA_ROUTE_STREAM)

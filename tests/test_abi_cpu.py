@@ -225,9 +225,10 @@ def test_auto_route_and_workspace():
     assert kda.plan(1, 97, 2, -5.0, 256).route == kda.ROUTE_SPLIT
     assert kda.plan(16, 35000, 32, -5.0, 256).route == kda.ROUTE_CHUNK
     assert kda.plan(4, 32768, 64, -8.0, 256).route == kda.ROUTE_CHUNK
-    # crossover: the split chain's 8 blocks per unit, two per CU, up to 1.5 rounds
+    # crossover against the fused pipeline: up to a quarter of the CUs in units
     assert kda.plan(1, 8192, 64, -5.0, 256).route == kda.ROUTE_SPLIT
-    assert kda.plan(4, 16384, 24, -5.0, 256).route == kda.ROUTE_SPLIT     # 96 units
+    assert kda.plan(1, 8192, 65, -5.0, 256).route == kda.ROUTE_CHUNK
+    assert kda.plan(4, 16384, 24, -5.0, 256).route == kda.ROUTE_CHUNK     # 96 units
     assert kda.plan(1, 8192, 97, -5.0, 256).route == kda.ROUTE_CHUNK
     assert kda.plan(2, 16384, 64, -5.0, 256).route == kda.ROUTE_CHUNK
     try:
