@@ -111,14 +111,6 @@ __device__ __forceinline__ InvWork& inv_of(PrepWork& pw) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Ordering of one wave's own LDS accesses (a write, then reads of it by other
-// lanes of the same wave): LDS operations of a wave complete in order, so only
-// the compiler must not move them across this point.
-__device__ __forceinline__ void wave_lds_fence() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
-}
-
 // Step 1: the chunk [t0, t0 + L) of head h -- its q, k, g rows and the value
 // columns [col0, col0 + DVS) -- fetched into registers by 16-byte buffer
 // loads (16 consecutive threads read one 256-byte row: coalesced), so that a
@@ -197,7 +189,7 @@ __device__ __forceinline__ void stage_beta(float* beta, uint16_t beta_raw, const
 
 // Step 1b (input front-end): 1 / sqrt(sum_c x_c^2 + norm_eps) of q and k per
 // token of the staged chunk; eight threads per token, 16 channels each.
-// Needs 256 threads; runs in the same phase as gate_prefix.
+// Needs 256 threads (the producers); runs in the same phase as gate_prefix.
 __device__ __forceinline__ void qk_norms(PrepWork& pw, const ChunkQKG& cr, const PrefillArgs& a,
                                          int tid) {
   const int t = tid >> 3, part = tid & 7;
@@ -222,36 +214,41 @@ __device__ __forceinline__ void qk_norms(PrepWork& pw, const ChunkQKG& cr, const
   }
 }
 
-// Step 2: inclusive gate prefix per channel, chunk decay, and for the fixed
-// anchor 2^{G_L - C}.  256 threads: wave w takes channels 32w..32w+31, lane l
-// channel 32w + l%32 over tokens 16(l/32)..+15; the second half adds the first
-// half's total (a cross-lane read), so each lane's serial sum is 16 long.
-// Padding tokens (t >= L) add nothing: a transformed gate of their zero input
-// would not be zero.
+// Step 2: inclusive gate prefix per channel, chunk decay, and the anchor
+// constants (fixed anchor: 2^{G_L - C}; 16-token anchors: the K16 factors).
+// 512 threads, every wave of the fused block (the consumers' phase is
+// otherwise idle): thread (wave w, lane l) sums 8 tokens, quarter q = l / 16,
+// of key channel 16 w + l % 16, so each serial sum is 8 long; the quarters'
+// totals come from the channel's three other lanes, and the last quarter's
+// thread writes the decay and the constants.  Padding tokens (t >= L) add
+// nothing: a transformed gate of their zero input would not be zero.
 template <int MODE, bool FE>
 __device__ __forceinline__ void gate_prefix(PrepWork& pw, float* dec, const ChunkQKG& cr,
                                             const FrontEnd& fe, float C, float Ch, int L, int tid) {
-  const int lane = tid & 63, c = 32 * (tid >> 6) + (lane & 31), hf = lane >> 5;
-  float pre[16];
+  const int lane = tid & 63, cl = lane & 15, q = lane >> 4;
+  const int c = 16 * (tid >> 6) + cl;
+  float pre[8];
   float acc = 0.f;
 #pragma unroll
-  for (int j = 0; j < 16; ++j) {
-    const int t = 16 * hf + j;
+  for (int j = 0; j < 8; ++j) {
+    const int t = 8 * q + j;
     float x = bf16_to_f32(cr.g[t][c]);
     if (FE) x = t < L ? frontend_gate(fe, x) : 0.f;
     acc += x;
     pre[j] = acc;
   }
-  const float other = __shfl_xor(acc, 32);   // the first half's total, seen by the second half
-  const float base = hf ? other : 0.f;
+  float tq[4];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) pw.G[16 * hf + j][c] = (base + pre[j]) * kLog2e;
-  if (hf) {
+  for (int k = 0; k < 4; ++k) tq[k] = __shfl(acc, cl + 16 * k);
+  const float base = q == 0 ? 0.f : q == 1 ? tq[0] : q == 2 ? tq[0] + tq[1] : (tq[0] + tq[1]) + tq[2];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) pw.G[8 * q + j][c] = (base + pre[j]) * kLog2e;
+  if (q == 3) {
     const float GL = (base + acc) * kLog2e;
     dec[c] = fast_exp2(GL);
     if (MODE == 0) pw.EL[c] = fast_exp2(GL - C);
     if (MODE == 1) {
-      const float G15 = base * kLog2e;
+      const float G15 = (tq[0] + tq[1]) * kLog2e;
       pw.K16[0][c] = fast_exp2(G15 + Ch);
       pw.K16[1][c] = fast_exp2(GL - Ch);
       pw.K16[2][c] = fast_exp2(GL - G15 - Ch);
@@ -569,60 +566,60 @@ __device__ __forceinline__ void reduce_pairs(InvWork& iw, ChunkQKG& cr, const fl
 // Steps 4a-4c: T = (I + A)^{-1} in two phases separated by the caller's
 // barrier.  With T11, T22 the inverses of the 16x16 diagonal blocks of I + A
 // and A21 its lower-left block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.
-// Phase 1 (producer waves 0 and 1, block b = wave): lanes 0-15 invert the
-// diagonal block by forward substitution in FP32, one column each, with the
+// Phase 1 (producer waves 0-2): lanes 0-15 of waves 0 and 1 invert diagonal
+// block b = wave by forward substitution in FP32, one column each, with the
 // block's whole strict lower triangle read into registers first so that the
-// 16 dependent steps wait on no LDS read; wave 1 then forms W (lane (iq, m):
-// rows 4 iq..4 iq+3 of column m) from its own T22, its LDS round trip
-// ordered by wave_lds_fence.  Diagonal blocks go to emit_t(row, col, value)
-// (the caller stores the MFMA operand).  Phase 2 (256 threads): T21 = -W T11
-// and T12 = 0, one entry (and its zero twin) per thread.
+// 16 dependent steps wait on no LDS read; at the same time wave 2 solves
+// (I + A22) W = A21 by the same substitution, so W = T22 A21 needs no wait
+// for T22.  Diagonal blocks go to emit_t(row, col, value) (the caller stores
+// the MFMA operand).  Phase 2 (256 threads): T21 = -W T11 and T12 = 0, one
+// entry (and its zero twin) per thread.
 template <class EmitT>
 __device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int lane, EmitT&& emit_t) {
-  if (wave > 1) return;
-  const int base = 16 * wave;
-  if (lane < 16) {
-    const int m = lane;
-    // column j of the block below the diagonal = row j of At; quads q >= j / 4
-    // hold rows i > j.  Two rounds of eight columns (28 and 12 quads), so the
-    // registers for the triangle stay within the wave's budget.
-    float x[16];
+  if (wave > 2 || lane >= 16) return;
+  // waves 0 and 1: T11, T22, lane m forming column m from e_m; wave 2: W =
+  // T22 A21 = (I + A22)^{-1} A21 by the same substitution on A22, lane m
+  // starting from column m of A21 (row m of At, columns 16..31)
+  const bool w21 = wave == 2;
+  const int base = w21 ? 16 : 16 * wave;
+  const int m = lane;
+  float x[16];
+  if (w21) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const f32x4 a = *reinterpret_cast<const f32x4*>(&iw.At[m][16 + 4 * q]);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) x[4 * q + r] = a[r];
+    }
+  } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) x[i] = i == m ? 1.f : 0.f;
+  }
+  // column j of the block below the diagonal = row j of At; quads q >= j / 4
+  // hold rows i > j.  Two rounds of eight columns (28 and 12 quads), so the
+  // registers for the triangle stay within the wave's budget.
 #pragma unroll
-    for (int j0 = 0; j0 < 16; j0 += 8) {
-      f32x4 c[8][4];
+  for (int j0 = 0; j0 < 16; j0 += 8) {
+    f32x4 c[8][4];
 #pragma unroll
-      for (int j = j0; j < j0 + 8; ++j)
+    for (int j = j0; j < j0 + 8; ++j)
 #pragma unroll
-        for (int q = j >> 2; q < 4; ++q)
-          c[j - j0][q] = *reinterpret_cast<const f32x4*>(&iw.At[base + j][base + 4 * q]);
+      for (int q = j >> 2; q < 4; ++q)
+        c[j - j0][q] = *reinterpret_cast<const f32x4*>(&iw.At[base + j][base + 4 * q]);
 #pragma unroll
-      for (int j = j0; j < j0 + 8; ++j)
+    for (int j = j0; j < j0 + 8; ++j)
 #pragma unroll
-        for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[j - j0][i >> 2][i & 3], x[j], x[i]);
-      __builtin_amdgcn_sched_barrier(0);
-    }
+      for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[j - j0][i >> 2][i & 3], x[j], x[i]);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+  if (w21) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) iw.X[i][m] = x[i];
+  } else {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       iw.Tf[base + i][base + m] = x[i];
       emit_t(base + i, base + m, x[i]);
-    }
-  }
-  if (wave == 1) {
-    wave_lds_fence();
-    const int iq = lane >> 4, m = lane & 15;
-    // A21[:, m] = row m of At, columns 16..31
-    f32x4 a21[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) a21[q] = *reinterpret_cast<const f32x4*>(&iw.At[m][16 + 4 * q]);
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int i = 4 * iq + r;
-      float acc = 0.f;
-#pragma unroll
-      for (int j = 0; j < 16; ++j) acc = fmaf(iw.Tf[16 + i][16 + j], a21[j >> 2][j & 3], acc);
-      iw.X[i][m] = acc;
     }
   }
 }

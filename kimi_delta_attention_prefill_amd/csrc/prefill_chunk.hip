@@ -167,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       if (prep) {
         stage_beta<FE>(sn.beta, x.beta, a.fe, Ln, ptid);
         if (s + 2 < nch) fetch_chunk(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
-        gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, a.half_anchor_log2, Ln, ptid);
+        gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, a.half_anchor_log2, Ln, tid);
         if (FE) qk_norms(sm.pw, cr, a, ptid);
       }
       lds_barrier();   // B1: gate prefix, anchor constants, beta and decays of chunk s+1 written
@@ -265,6 +265,11 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
   for (int s = -1; s < nch; ++s) {
     const ChunkOps<DVS>& sc = sm.slot[s & 1];    // chunk s's ring slot
     lds_barrier();   // B0
+    if (s + 1 < nch) {   // the consumers' share of chunk s+1's gate prefix (channels 0-63)
+      const int tn0 = bos + CH * (s + 1);
+      gate_prefix<MODE, FE>(sm.pw, sm.slot[(s + 1) & 1].dec, sm.raw[(s + 1) & 1], a.fe, C,
+                            a.half_anchor_log2, min(CH, eos - tn0), tid);
+    }
     lds_barrier();   // B1
     lds_barrier();   // B2
     // ---- the state chain of chunk s on this wave's 16 * NT value columns,
