@@ -271,18 +271,19 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
                             a.half_anchor_log2, min(CH, eos - tn0), tid);
     }
     lds_barrier();   // B1
-    lds_barrier();   // B2
-    // ---- the state chain of chunk s on this wave's 16 * NT value columns,
-    // beside the producers' reduction (part A) and inverse (part B), the
-    // phases that leave most of the producers' issue slots free
+    // ---- the state chain of chunk s on this wave's 16 * NT value columns.
+    // Its products with the state (W, O: matrix-core work and little VALU)
+    // run beside the producers' VALU-bound pair products; the rest beside
+    // the producers' reduction (part A) and inverse (part B)
     f32x4 OT[NT][2];
     f16x8 Uh[NT], Ul[NT];
+    f32x4 W[2][NT];
+    float vv[NT][2][4];
     const int t0 = bos + CH * s, L = min(CH, eos - t0);
+    const f32x4 z = {0.f, 0.f, 0.f, 0.f};
     if (s >= 0) {
-      const f32x4 z = {0.f, 0.f, 0.f, 0.f};
       // this lane's value entries (tokens 16 mt + 4 g4 + i, column 16 nt +
       // l16), read before the products so that the reads are in flight together
-      float vv[NT][2][4];
 #pragma unroll
       for (int nt = 0; nt < NT; ++nt)
 #pragma unroll
@@ -295,7 +296,6 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       // W = Kg S (rows = tokens) and O^T = S^T Qg^T (rows = value columns: the
       // same fragments with A and B swapped, so each lane ends with 4
       // adjacent columns of one token for the output store)
-      f32x4 W[2][NT];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -322,6 +322,9 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
           }
         }
       }
+    }
+    lds_barrier();   // B2
+    if (s >= 0) {
       // V' = b (V - W) as hi + lo fp16 B operands (K = token, permuted)
       f16x8 Vh[NT], Vl[NT];
 #pragma unroll
