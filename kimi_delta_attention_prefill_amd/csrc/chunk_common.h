@@ -19,6 +19,8 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int CH = 32;          // chunk length
 constexpr int D = kHeadDim;     // 128
@@ -45,6 +47,17 @@ __device__ __forceinline__ f32x4 mfma_f16(f16x8 a, f16x8 b, f32x4 c) {
 __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo) {
   hi = static_cast<__bf16>(x);
   lo = static_cast<__bf16>(x - static_cast<float>(hi));
+}
+// Two values at once (one packed conversion for both his, one for both los;
+// the same roundings as split_bf16), into elements j, j+1 of hi and lo.
+__device__ __forceinline__ void split_bf16_pair(float a, float b, bf16x8& hi, bf16x8& lo, int j) {
+  const f32x2 x = {a, b};
+  const bf16x2 h = __builtin_convertvector(x, bf16x2);
+  const bf16x2 l = __builtin_convertvector(x - __builtin_convertvector(h, f32x2), bf16x2);
+  hi[j] = h[0];
+  hi[j + 1] = h[1];
+  lo[j] = l[0];
+  lo[j + 1] = l[1];
 }
 __device__ __forceinline__ void split_f16(float x, _Float16& hi, _Float16& lo) {
   hi = static_cast<_Float16>(x);
@@ -312,6 +325,8 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
     const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
     const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
     float kv[8], qv[8], Pv[8], Rv[8];
+    // the anchored operand values, split into bf16 hi/lo pairs after the loop
+    float xq[8], xk[8], xb[8], xqo[8], xko[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
       const float Gv = j < 4 ? G0[j] : G1[j - 4];
@@ -353,34 +368,41 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         P = fast_exp2(Gv);
         R = fast_exp2(gl - Gv);
       }
-      __bf16 h1, l1, h2, l2, h3, l3;
-      split_bf16(qf * ep, h1, l1);
-      split_bf16(kf * ep, h2, l2);
-      split_bf16(kf * em, h3, l3);
+      xq[j] = qf * ep;
+      xk[j] = kf * ep;
+      xb[j] = kf * em;
+      xqo[j] = qf * fo;
+      xko[j] = kf * fo;
+      kv[j] = kf; qv[j] = qf; Pv[j] = P; Rv[j] = R;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; j += 2) {
       if (half == 0) {
-        op.q0h[j] = h1; op.q0l[j] = l1;
-        op.k0h[j] = h2; op.k0l[j] = l2;
-        op.b0h[j] = h3; op.b0l[j] = l3;
+        split_bf16_pair(xq[j], xq[j + 1], op.q0h, op.q0l, j);
+        split_bf16_pair(xk[j], xk[j + 1], op.k0h, op.k0l, j);
+        split_bf16_pair(xb[j], xb[j + 1], op.b0h, op.b0l, j);
       } else {
-        op.q1h[j] = h1; op.q1l[j] = l1;
-        op.k1h[j] = h2; op.k1l[j] = l2;
-        op.b1h[j] = h3; op.b1l[j] = l3;
+        split_bf16_pair(xq[j], xq[j + 1], op.q1h, op.q1l, j);
+        split_bf16_pair(xk[j], xk[j + 1], op.k1h, op.k1l, j);
+        split_bf16_pair(xb[j], xb[j + 1], op.b1h, op.b1l, j);
       }
       if (MODE == 0) {
         // one anchor for the whole chunk: the off-diagonal tile reuses the diagonal operands
-        if (half == 1) { op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2; }
-        else { op.boh[j] = h3; op.bol[j] = l3; }
-      } else {
         if (half == 1) {
-          split_bf16(qf * fo, h1, l1);
-          split_bf16(kf * fo, h2, l2);
-          op.qoh[j] = h1; op.qol[j] = l1; op.koh[j] = h2; op.kol[j] = l2;
+          op.qoh[j] = op.q1h[j]; op.qoh[j + 1] = op.q1h[j + 1];
+          op.qol[j] = op.q1l[j]; op.qol[j + 1] = op.q1l[j + 1];
+          op.koh[j] = op.k1h[j]; op.koh[j + 1] = op.k1h[j + 1];
+          op.kol[j] = op.k1l[j]; op.kol[j + 1] = op.k1l[j + 1];
         } else {
-          split_bf16(kf * fo, h3, l3);
-          op.boh[j] = h3; op.bol[j] = l3;
+          op.boh[j] = op.b0h[j]; op.boh[j + 1] = op.b0h[j + 1];
+          op.bol[j] = op.b0l[j]; op.bol[j + 1] = op.b0l[j + 1];
         }
+      } else if (half == 1) {
+        split_bf16_pair(xqo[j], xqo[j + 1], op.qoh, op.qol, j);
+        split_bf16_pair(xko[j], xko[j + 1], op.koh, op.kol, j);
+      } else {
+        split_bf16_pair(xko[j], xko[j + 1], op.boh, op.bol, j);
       }
-      kv[j] = kf; qv[j] = qf; Pv[j] = P; Rv[j] = R;
     }
     emit(t, cb + cl, kv, qv, Pv, Rv);
   }
