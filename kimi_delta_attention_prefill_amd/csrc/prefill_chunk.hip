@@ -33,25 +33,29 @@
 // the note's sections 3-4 (a ring of prepared chunks between the waves that
 // prepare chunks and the waves that consume them), sized for a CDNA4 compute
 // unit's 160 KiB of LDS:
-//   * waves 4-7 (producers) prepare chunk c+1 -- gate prefix, anchored
-//     operands, Mqk and the triangular system, its inverse -- into ring slot
-//     (c+1) % 2 (wave w owns key channels 32(w-4).. of the pairwise products,
-//     a split-K whose partials are summed in a fixed order, so results are
-//     deterministic), and fetch the raw rows of chunk c+2 and the value rows
-//     of chunk c+1 by direct global-to-LDS loads;
+//   * waves 4-7 (producers) prepare chunk c+1 -- anchored operands, Mqk and
+//     the triangular system, the inverse's diagonal blocks and W = T22 A21 --
+//     into ring slot (c+1) % 2 (wave w owns key channels 32(w-4).. of the
+//     pairwise products, a split-K whose partials are summed in a fixed
+//     order, so results are deterministic), and fetch the rows of chunk c+2
+//     into registers, writing them to LDS at the step's end;
 //   * waves 0-3 (consumers) meanwhile run the serial state chain of chunk c
 //     from slot c % 2 on their own 16 * NT value columns (value columns
 //     evolve independently, so the chain needs no cross-wave exchange); the
 //     FP32 state stays in their MFMA accumulators for the whole sequence.
-// Both sides meet at the same four block barriers per chunk (barriers that
+//     In the phases where the chain has nothing to do they take a share of
+//     the preparation: half of chunk c+1's gate prefix and the inverse's
+//     off-diagonal block T21 = -W T11.
+// Both sides meet at the same five block barriers per chunk (barriers that
 // order LDS only, so prefetches and output stores stay in flight across
-// them), so a chunk costs about the longer of the two sides rather than their
-// sum.  LDS
-// per block (DVS = 128): two raw q/k/g buffers (2 x 25.5 KiB; the split-K
-// partials of a chunk live over its own rows once its operands are built),
-// the producers' gate prefix (16.5 KiB; the triangular system and its
+// them), and the chain's products with the state (matrix-core work) sit in
+// the phase of the producers' VALU-bound pair products, so a chunk costs
+// about the longer of the two sides rather than their sum.  LDS per block
+// (DVS = 128): two raw q/k/g buffers (2 x 25.5 KiB; the split-K partials of
+// a chunk live over its own rows once its operands are built), the gate
+// prefix (19.3 KiB with the anchor constants; the triangular system and its
 // inverse live over it once the operands are built), and two ring slots of
-// 40.6 KiB (Kg, Qg, Kr^T, T, Mqk, decays, beta and the value rows): 149.5
+// 40.6 KiB (Kg, Qg, Kr^T, T, Mqk, decays, beta and the value rows): 151.5
 // KiB.
 //
 // Accumulator-to-operand reuse.  An accumulator tile of v_mfma_f32_16x16x32
@@ -208,7 +212,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       auto emit_t = [&](int r, int c, float t) { sn.T[r][kslot(c)] = static_cast<_Float16>(t); };
       if (prep) invert_diag_blocks(inv_of(sm.pw), pwave, lane, emit_t);
       lds_barrier();   // B4: T11, T22 and W = T22 A21 in place; the consumers are done with slot s
-      if (prep) invert_offdiag(inv_of(sm.pw), ptid, emit_t);
+      // (the consumers form T21 = -W T11 meanwhile)
       if (s + 2 < nch) stage_chunk(sm.raw[s & 1], sm.slot[s & 1].v, x, ptid);   // chunk s+2
     }
     return;
@@ -409,6 +413,10 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       }
     }
     lds_barrier();   // B4
+    if (s + 1 < nch)   // chunk s+1's T21 = -W T11, beside the producers' staging of chunk s+2
+      invert_offdiag(inv_of(sm.pw), tid, [&](int r, int c, float t) {
+        sm.slot[(s + 1) & 1].T[r][kslot(c)] = static_cast<_Float16>(t);
+      });
   }
 
   if (const StateRef s1 = prefill_final_state(a, n, h)) {
