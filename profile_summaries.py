@@ -49,6 +49,7 @@ KERNELS = {  # short kernel name -> summary name (the bench workload's kernels)
     "prefill_split_window_c": "prefill_split_window_c_T8192_H8",
     "prefill_split_chain": "prefill_split_chain_T8192_H8",
     "decode_kernel": "decode_f32_rows4096_H8",
+    "stream_kernel": "decode_f32_rows4096_H8",   # kda_decode's many-row shape
 }
 COPY = "__amd_rocclr_copyBuffer"
 COPY_BYTES = 1 << 30
@@ -57,7 +58,7 @@ COPY_BYTES = 1 << 30
 def short(name):
     m = re.search(r"(prefill_split_prep|prefill_split_chain|prefill_split_window_a|"
                   r"prefill_split_window_c|prefill_chunk_kernel|"
-                  r"prefill_serial_kernel|decode_kernel|__amd_rocclr_\w+)", name)
+                  r"prefill_serial_kernel|decode_kernel|stream_kernel|__amd_rocclr_\w+)", name)
     return m.group(1) if m else name[:60]
 
 
