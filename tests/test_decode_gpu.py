@@ -86,26 +86,36 @@ def test_decode_rows(dev, pool, rows):
         del before
 
 
-def test_decode_negative_and_out_of_range_slots(dev, pool):
+@pytest.mark.parametrize("rows", [6, 1200])
+def test_decode_negative_and_out_of_range_slots(dev, pool, rows):
+    """Skipped rows (negative or out-of-range slot): zero output, pool untouched.
+    At 1200 rows x H=8 both pools take the many-row shape (the token stream
+    with one token per row), at 6 rows the decode blocks."""
     tag, P = pool
-    rows = 6
-    case = make_decode_case(rows, H, NUM_SLOTS, seed=77, with_pool=False)
+    case = make_decode_case(rows, H, NUM_SLOTS, seed=77 + rows, with_pool=False)
     slots = case.slots.clone()
     slots[1] = -1
     slots[4] = NUM_SLOTS + 5   # out of range: treated as a skipped row
-    live = [0, 2, 3, 5]
+    slots[rows - 1] = -7
+    dead = {1, 4, rows - 1}
+    live = [i for i in range(rows) if i not in dead]
+    if len(live) > MAX_ORACLE_ROWS:
+        live = sorted(np.random.default_rng(rows).choice(live, MAX_ORACLE_ROWS, replace=False))
     slots_d = slots.to(dev).long()
     pre = P[slots_d[live]].clone()
     before = P.clone()
     out = _step(case, P, dev, slots=slots)
-    assert torch.all(out[1] == 0) and torch.all(out[4] == 0)
+    for r in dead:
+        assert torch.all(out[r] == 0), f"skipped row {r} has a nonzero output"
     ref_out, ref_post = _oracle_rows(case, pre.cpu(), np.array(live))
     check_out(out.cpu()[live], ref_out)
     post = P[slots_d[live]].cpu()
     (check_state if tag == "f32" else check_bf16_state)(post, ref_post)
+    valid = slots_d[[i for i in range(rows) if i not in dead]]
     mask = torch.ones(NUM_SLOTS, dtype=torch.bool, device=dev)
-    mask[slots_d[live]] = False
+    mask[valid] = False
     assert torch.equal(P[mask], before[mask])
+    del before
 
 
 def test_decode_matches_prefill_T1(dev):
