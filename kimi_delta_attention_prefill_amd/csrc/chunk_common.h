@@ -292,6 +292,13 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
                                               float exp2C, int wave, int lane, Emit&& emit) {
   const int l16 = lane & 15, g4 = lane >> 4;
   const int cb = 32 * wave, cl = 8 * g4;
+  // 16-token anchors: the off-diagonal tile's rows reuse half 1's diagonal
+  // operands (anchored at G_15 + h, h an integer), its half-0 columns carry
+  // 2^{G_15 - G} 2^z, and the tile is scaled back by 2^{h - z} afterwards
+  // (exact powers of two; z = floor(h / 2) keeps the unscaled sums within
+  // 2^{|h|/2} of the products)
+  const int hz = MODE == 1 ? (int)a.half_anchor_log2 : 0, zc = hz >> 1;
+  const float colscale = __builtin_ldexpf(1.f, zc), accscale = __builtin_ldexpf(1.f, hz - zc);
   PairOps op;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -349,11 +356,10 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         if (half) {
           P = ep * c1;                                // 2^{G_15 + h} 2^{G - G_15 - h}
           R = em * c2;                                // 2^{G_L - G_15 - h} 2^{G_15 + h - G}
-          fo = ep * exp2C;                            // 2^{G - G_15} = 2^{G - Ch} 2^h
         } else {
           P = ep * exp2C;                             // 2^h 2^{G - h}
           R = em * c1;                                // 2^{G_L - h} 2^{h - G}
-          fo = em * c2;                               // 2^{G_15 - h} 2^{h - G}
+          fo = (em * c2) * colscale;                  // 2^{G_15 - h} 2^{h - G} 2^z
         }
       } else {
         const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
@@ -398,8 +404,10 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
           op.bol[j] = op.b0l[j]; op.bol[j + 1] = op.b0l[j + 1];
         }
       } else if (half == 1) {
-        split_bf16_pair(xqo[j], xqo[j + 1], op.qoh, op.qol, j);
-        split_bf16_pair(xko[j], xko[j + 1], op.koh, op.kol, j);
+        if (MODE != 1) {   // MODE 1 uses half 1's diagonal operands
+          split_bf16_pair(xqo[j], xqo[j + 1], op.qoh, op.qol, j);
+          split_bf16_pair(xko[j], xko[j + 1], op.koh, op.kol, j);
+        }
       } else {
         split_bf16_pair(xko[j], xko[j + 1], op.boh, op.bol, j);
       }
@@ -410,21 +418,32 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
   acc[0] = mfma_bf16(op.q0h, op.b0h, z);
   acc[0] = mfma_bf16(op.q0h, op.b0l, acc[0]);
   acc[0] = mfma_bf16(op.q0l, op.b0h, acc[0]);
-  acc[1] = mfma_bf16(op.qoh, op.boh, z);
-  acc[1] = mfma_bf16(op.qoh, op.bol, acc[1]);
-  acc[1] = mfma_bf16(op.qol, op.boh, acc[1]);
+  const bf16x8& qoh = MODE == 1 ? op.q1h : op.qoh;
+  const bf16x8& qol = MODE == 1 ? op.q1l : op.qol;
+  const bf16x8& koh = MODE == 1 ? op.k1h : op.koh;
+  const bf16x8& kol = MODE == 1 ? op.k1l : op.kol;
+  acc[1] = mfma_bf16(qoh, op.boh, z);
+  acc[1] = mfma_bf16(qoh, op.bol, acc[1]);
+  acc[1] = mfma_bf16(qol, op.boh, acc[1]);
   acc[2] = mfma_bf16(op.q1h, op.b1h, z);
   acc[2] = mfma_bf16(op.q1h, op.b1l, acc[2]);
   acc[2] = mfma_bf16(op.q1l, op.b1h, acc[2]);
   acc[3] = mfma_bf16(op.k0h, op.b0h, z);
   acc[3] = mfma_bf16(op.k0h, op.b0l, acc[3]);
   acc[3] = mfma_bf16(op.k0l, op.b0h, acc[3]);
-  acc[4] = mfma_bf16(op.koh, op.boh, z);
-  acc[4] = mfma_bf16(op.koh, op.bol, acc[4]);
-  acc[4] = mfma_bf16(op.kol, op.boh, acc[4]);
+  acc[4] = mfma_bf16(koh, op.boh, z);
+  acc[4] = mfma_bf16(koh, op.bol, acc[4]);
+  acc[4] = mfma_bf16(kol, op.boh, acc[4]);
   acc[5] = mfma_bf16(op.k1h, op.b1h, z);
   acc[5] = mfma_bf16(op.k1h, op.b1l, acc[5]);
   acc[5] = mfma_bf16(op.k1l, op.b1h, acc[5]);
+  if (MODE == 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      acc[1][i] *= accscale;
+      acc[4][i] *= accscale;
+    }
+  }
 }
 
 // Data-dependent anchors (no gate bound): a 16-token half whose gate prefix

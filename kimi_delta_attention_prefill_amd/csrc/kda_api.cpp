@@ -75,11 +75,12 @@ bool fixed_anchor_fits(float lower_bound) {
   return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
 }
 
-// The same for the 16-token anchors: a half's factors reach 2^{8 |lb| log2(e)},
-// so they fit while lower_bound >= -10.9; wider bounds take the
-// data-dependent anchors.
+// The same for the 16-token anchors at h' = the integer nearest h = 8 lb
+// log2(e): a half's factors reach 2^{|h'|} and 2^{|2h - h'|}, so they fit
+// while lower_bound >= -10.9; wider bounds take the data-dependent anchors.
 bool half_anchor_fits(float lower_bound) {
-  return 8.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
+  const double h = 8.0 * (double)lower_bound * 1.4426950408889634, hr = std::nearbyint(h);
+  return std::fabs(hr) <= 126.0 && std::fabs(2.0 * h - hr) <= 126.0;
 }
 
 // Argument checks shared by the prefill entry points; each returns KDA_OK or
@@ -199,7 +200,8 @@ kda::PrefillArgs make_args(const void* q, const void* k, const void* v, const vo
   // an unbounded gate (-inf) uses data-dependent anchors; the constants are unused
   const double lb = std::isfinite(lower_bound) ? (double)lower_bound : 0.0;
   a.anchor_log2 = (float)(16.0 * lb * 1.4426950408889634);
-  a.half_anchor_log2 = (float)(8.0 * lb * 1.4426950408889634);
+  // an integer, so that the off-diagonal tile can be rescaled by powers of two
+  a.half_anchor_log2 = (float)std::nearbyint(8.0 * lb * 1.4426950408889634);
   a.s0 = initial_state;
   a.s1 = final_state;
   a.out = static_cast<uint16_t*>(out);

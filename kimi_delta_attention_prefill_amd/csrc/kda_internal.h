@@ -45,7 +45,7 @@ struct PrefillArgs {
   int32_t num_heads;
   float scale;
   float anchor_log2;      // C = 16 * lower_bound * log2(e)  (chunk route)
-  float half_anchor_log2; // 8 * lower_bound * log2(e)     (split-16 mode)
+  float half_anchor_log2; // nearest integer to 8 * lower_bound * log2(e) (split-16 mode)
   const float* s0;        // fp32 [N, H, 128, 128] or null
   float* s1;              // fp32 [N, H, 128, 128] or null
   uint16_t* out;          // bf16 [T, H, 128]

@@ -146,6 +146,12 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
 
   if (producer) {
     // ------------------------------------------------------------ producers
+    // Nothing of this wave's is in flight here.  The compiler may lay the
+    // producers' code after the consumers' and then count the consumers'
+    // state loads as pending in the producers' waits (up to waiting for the
+    // next chunk's prefetch in the middle of a step); an explicit vmcnt(0)
+    // (expcnt, lgkmcnt not waited on) clears that count.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
     // Chunk c's rows are fetched into registers during step c-2 and written
     // to LDS at that step's end: its q/k/g rows into raw[c % 2] (free since
     // chunk c-2 was prepared from it) and its value rows into ring slot c % 2
