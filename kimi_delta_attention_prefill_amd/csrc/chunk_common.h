@@ -613,8 +613,8 @@ __device__ __forceinline__ void reduce_pairs(InvWork& iw, ChunkQKG& cr, const fl
 // 16 dependent steps wait on no LDS read; at the same time wave 2 solves
 // (I + A22) W = A21 by the same substitution, so W = T22 A21 needs no wait
 // for T22.  Diagonal blocks go to emit_t(row, col, value) (the caller stores
-// the MFMA operand).  Phase 2 (256 threads): T21 = -W T11 and T12 = 0, one
-// entry (and its zero twin) per thread.
+// the MFMA operand).  Phase 2 (one wave): T21 = -W T11 on the matrix cores
+// (T12 = 0 is the caller's, once).
 template <class EmitT>
 __device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int lane, EmitT&& emit_t) {
   if (wave > 2 || lane >= 16) return;
@@ -664,14 +664,18 @@ __device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int la
     }
   }
 }
+// T21 = -W T11 as four 16x16x4 FP32 matrix products (K = 16): in step kk
+// lane l supplies W[l % 16][4 kk + l / 16] and T11[4 kk + l / 16][l % 16]
+// and ends with T21[4 (l / 16) + i][l % 16], i < 4.  One wave.
 template <class EmitT>
-__device__ __forceinline__ void invert_offdiag(const InvWork& iw, int tid, EmitT&& emit_t) {
-  const int i = tid >> 4, m = tid & 15;
-  float acc = 0.f;
+__device__ __forceinline__ void invert_offdiag(const InvWork& iw, int lane, EmitT&& emit_t) {
+  const int r = lane & 15, kq = lane >> 4;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int k = 0; k < 16; ++k) acc = fmaf(iw.X[i][k], iw.Tf[k][m], acc);
-  emit_t(16 + i, m, -acc);
-  emit_t(i, 16 + m, 0.f);
+  for (int kk = 0; kk < 4; ++kk)
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(iw.X[r][4 * kk + kq], iw.Tf[4 * kk + kq][r], acc, 0, 0, 0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) emit_t(16 + 4 * kq + i, r, -acc[i]);
 }
 
 }  // namespace chunk

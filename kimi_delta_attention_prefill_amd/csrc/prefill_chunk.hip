@@ -45,7 +45,7 @@
 //     FP32 state stays in their MFMA accumulators for the whole sequence.
 //     In the phases where the chain has nothing to do they take a share of
 //     the preparation: half of chunk c+1's gate prefix and the inverse's
-//     off-diagonal block T21 = -W T11.
+//     off-diagonal block T21 = -W T11 (one wave, four FP32 matrix products).
 // Both sides meet at the same five block barriers per chunk (barriers that
 // order LDS only, so prefetches and output stores stay in flight across
 // them), and the chain's products with the state (matrix-core work) sit in
@@ -267,6 +267,11 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
     else
       init_state([&](int e) { return static_cast<const float*>(s0.p)[e]; });
   }
+  {   // T12 = 0 in both ring slots, once: the inverse writes only T's other blocks
+    const int i = tid >> 4, m = tid & 15;
+#pragma unroll
+    for (int sl = 0; sl < 2; ++sl) sm.slot[sl].T[i][kslot(16 + m)] = static_cast<_Float16>(0.f);
+  }
   // Checkpoints (the state after every ckpt_tokens tokens): chunk count of
   // the next one and its row of the checkpoint buffer.
   const int ck_per = a.ckpt ? a.ckpt_tokens / CH : 0;
@@ -419,8 +424,8 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       }
     }
     lds_barrier();   // B4
-    if (s + 1 < nch)   // chunk s+1's T21 = -W T11, beside the producers' staging of chunk s+2
-      invert_offdiag(inv_of(sm.pw), tid, [&](int r, int c, float t) {
+    if (s + 1 < nch && wave == 0)   // chunk s+1's T21 = -W T11, beside the producers' staging of chunk s+2
+      invert_offdiag(inv_of(sm.pw), lane, [&](int r, int c, float t) {
         sm.slot[(s + 1) & 1].T[r][kslot(c)] = static_cast<_Float16>(t);
       });
   }
