@@ -582,26 +582,31 @@ __device__ __forceinline__ void pair_store(ChunkQKG& cr, const f32x4 (&acc)[6], 
 // Step 3b: sum the four split-K partials in a fixed order, mask the causal
 // triangles by select (masked anchored entries may be inf or NaN) and scale
 // Akk by beta.  Writes iw.At (A transposed); emit_mqk(r, s, value) sees every
-// Mqk entry (zero above the diagonal).  256 threads.
+// Mqk entry (zero above the diagonal).  256 threads: wave q of them takes
+// quadrant q of both matrices ((0,0), (1,0), (1,1), then the zero (0,1)),
+// lane l the entries of MFMA lane l, each partial as one 16-byte read.
 template <class EmitMqk>
 __device__ __forceinline__ void reduce_pairs(InvWork& iw, ChunkQKG& cr, const float* beta, int tid,
                                              EmitMqk&& emit_mqk) {
-  const int ln = tid >> 2, i = tid & 3;
-  auto sum4 = [&](int p) __attribute__((always_inline)) {
-    return ((part_entry(cr, 0, p, ln)[i] + part_entry(cr, 1, p, ln)[i]) + part_entry(cr, 2, p, ln)[i]) +
-           part_entry(cr, 3, p, ln)[i];
-  };
-#pragma unroll
-  for (int q4 = 0; q4 < 4; ++q4) {   // 16x16 quadrants (0,0) (1,0) (1,1) (0,1); the last is zero
-    const int mt = (q4 == 1 || q4 == 2) ? 1 : 0;
-    const int nt = (q4 == 2 || q4 == 3) ? 1 : 0;
-    const int r = 16 * mt + 4 * (ln >> 4) + i, s = 16 * nt + (ln & 15);
-    const float mq = q4 == 3 ? 0.f : sum4(q4);       // Mqk partial tiles 0..2
-    const float ak = q4 == 3 ? 0.f : sum4(3 + q4);   // Akk partial tiles 3..5
-    const float m = s <= r ? mq : 0.f;
-    emit_mqk(r, s, m);
-    iw.At[s][r] = s < r ? beta[r] * ak : 0.f;
+  const int q4 = tid >> 6, ln = tid & 63;
+  const int mt = (q4 == 1 || q4 == 2) ? 1 : 0, nt = (q4 == 2 || q4 == 3) ? 1 : 0;
+  f32x4 mq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
+  if (q4 < 3) {   // Mqk partial tile q4, Akk partial tile 3 + q4
+    auto rd = [&](int w, int p) __attribute__((always_inline)) {
+      return *reinterpret_cast<const f32x4*>(part_entry(cr, w, p, ln));
+    };
+    mq = ((rd(0, q4) + rd(1, q4)) + rd(2, q4)) + rd(3, q4);
+    ak = ((rd(0, 3 + q4) + rd(1, 3 + q4)) + rd(2, 3 + q4)) + rd(3, 3 + q4);
   }
+  const int r0 = 16 * mt + 4 * (ln >> 4), s = 16 * nt + (ln & 15);
+  f32x4 at;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = r0 + i;
+    emit_mqk(r, s, s <= r ? mq[i] : 0.f);
+    at[i] = s < r ? beta[r] * ak[i] : 0.f;
+  }
+  *reinterpret_cast<f32x4*>(&iw.At[s][r0]) = at;
 }
 
 // Steps 4a-4c: T = (I + A)^{-1} in two phases separated by the caller's
