@@ -131,24 +131,26 @@ typedef enum {
  * "FlashInfer PR #4262: CAKE KDA Prefill Highlights", section 1. */
 typedef enum {
   KDA_ANCHOR_FIXED = 0,  /* one anchor C = 16 * lower_bound * log2(e) per chunk:
-                            operand exponents stay within 16|lb|log2e <= 126,
-                            i.e. usable for lower_bound >= -5.45            */
+                            operand exponents reach 16|lb|log2e, kept <= 116
+                            (above it the operands' bf16 low halves lose
+                            their precision before the bf16 range ends at
+                            126), i.e. used for lower_bound >= -5.02       */
   KDA_ANCHOR_SPLIT16 = 1, /* per 16-token half anchors (the note's ordinary
-                            16-token blocks) for bounds down to -10.9: the
-                            factors reach 2^{8 |lb| log2 e}               */
+                            16-token blocks) for bounds down to -10.05: the
+                            factors reach about 2^{8 |lb| log2 e} <= 2^116 */
   KDA_ANCHOR_DATA = 2    /* no bound (lower_bound = -inf, or the softplus
-                            gate), or a bound below -10.9: each 16-token half
-                            of each chunk is anchored, per channel, at the
-                            midpoint of its own gate-prefix range (a
+                            gate), or a bound below -10.05: each 16-token
+                            half of each chunk is anchored, per channel, at
+                            the midpoint of its own gate-prefix range (a
                             data-dependent range strategy).  Where a half's
-                            prefix falls by more than 2^248 (about 172 nats)
-                            in some channel, its products are formed per
-                            8-token quarter instead (each quarter at its own
-                            midpoint, the cross-quarter block through their
-                            boundary).  Exact to the usual rounding while no
-                            quarter of a chunk falls by more than 2^252 (the
-                            gate summed over the quarter's last seven tokens
-                            >= -174.6 in every channel);
+                            prefix falls by more than 2^232 (about 160.8
+                            nats) in some channel, its products are formed
+                            per 8-token quarter instead (each quarter at its
+                            own midpoint, the cross-quarter block through
+                            their boundary).  Exact to the usual rounding
+                            while no quarter of a chunk falls by more than
+                            2^232 (the gate summed over the quarter's last
+                            seven tokens >= -160.8 in every channel);
                             kda_check_prefill_inputs flags inputs beyond
                             that (KDA_CHECK_GATE_STEEP)                    */
 } kda_anchor_mode;
@@ -445,7 +447,7 @@ enum {
   KDA_CHECK_BETA_RANGE = 2,    /* 0 <= beta <= 1 */
   KDA_CHECK_QKV_FINITE = 3,    /* every q, k, v element finite */
   KDA_CHECK_SLOTS_UNIQUE = 4,  /* the slot indices in [0, num_slots) pairwise distinct */
-  KDA_CHECK_GATE_STEEP = 5,    /* set when the gate falls by more than 2^252 (174.6 nats)
+  KDA_CHECK_GATE_STEEP = 5,    /* set when the gate falls by more than 2^232 (160.8 nats)
                                   within an 8-token quarter of a chunk (tokens 0-7, 8-15,
                                   ... of each sequence) in some (head, channel): the
                                   chunk routes are not exact there */

@@ -18,8 +18,10 @@ __global__ void clear_flags(int32_t* flags, int first, int count) {
 
 // The gate's fall over an 8-token quarter of a chunk (its prefix from the
 // quarter's first to its last token, natural log) beyond which the chunk
-// routes' exact quarter products leave the FP32 exponent range: 2^252.
-constexpr float kQuarterFallLimit = 252.f / 1.4426950408889634f;
+// routes' quarter products, anchored at the quarter's midpoint, exceed the
+// 2^116 factor budget within which the operands' bf16 low halves keep their
+// precision: 2^232.
+constexpr float kQuarterFallLimit = 232.f / 1.4426950408889634f;
 
 // Sequence of token t (the largest n with cu[n] <= t), with the offsets
 // clamped as the prefill kernels clamp them.

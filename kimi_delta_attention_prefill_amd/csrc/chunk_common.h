@@ -447,11 +447,13 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
 }
 
 // Data-dependent anchors (no gate bound): a 16-token half whose gate prefix
-// falls by more than kSteepRange (log2 units, about 172 nats) in some channel
-// cannot be anchored once (its factors would leave the FP32/bf16 exponent
-// range).  steep_wave tells, for the channels of this producer wave, whether
-// any half of the chunk is that steep (wave-uniform).
-constexpr float kSteepRange = 248.f;
+// falls by more than kSteepRange (log2 units, about 160.8 nats) in some
+// channel cannot be anchored once (its factors, up to half the fall at the
+// midpoint anchor, would exceed the 2^116 budget within which the operands'
+// bf16 low halves keep their precision).  steep_wave tells, for the channels
+// of this producer wave, whether any half of the chunk is that steep
+// (wave-uniform).
+constexpr float kSteepRange = 232.f;
 __device__ __forceinline__ bool steep_wave(const PrepWork& pw, int wave, int lane) {
   bool steep = false;
   if ((lane & 15) < 2) {          // lane l16 = h checks half h of its row's 8 channels
@@ -464,7 +466,7 @@ __device__ __forceinline__ bool steep_wave(const PrepWork& pw, int wave, int lan
 
 // The pairwise products for a wave whose channels have a steep half
 // (steep_wave), exact to the usual rounding while no 8-token quarter falls by
-// more than 2^252: each diagonal 16x16 tile is the sum of three products over
+// more than 2^232: each diagonal 16x16 tile is the sum of three products over
 // the quarters Q0 (tokens 0-7 of the half) and Q1 (8-15),
 //   Q0 x Q0 anchored at the middle of Q0's range,
 //   Q1 x Q1 anchored at the middle of Q1's range,

@@ -68,19 +68,26 @@ int current_device_cus() {
   return cus;
 }
 
-// Largest |exponent| of an anchored chunk-32 operand factor 2^{G-C} or
+// Largest |exponent| E of an anchored chunk-32 operand factor 2^{G-C} or
 // 2^{C-G} when lower_bound <= g <= 0: 16 |lb| log2(e) (CAKE prefill note,
-// section 1).  bf16/fp32 normals need it <= 126.
+// section 1).  The pairwise products split each operand x into bf16 hi + lo,
+// and lo is about 2^-9 |x|: for an entry of a unit-norm 128-channel row
+// (|x| ~ 2^-3.5) scaled by 2^-E, lo keeps some 4 significant bits at E = 116
+// and falls below bf16's subnormals at E = 126, where such products drop to
+// bf16 precision (every gate at lower_bound = -10.875, E = 126: output errors
+// of 8-12% of RMS).  The budget is therefore E <= 116, not the normal
+// range's 126.
+constexpr double kAnchorExpBudget = 116.0;
 bool fixed_anchor_fits(float lower_bound) {
-  return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= 126.0;
+  return 16.0 * std::fabs((double)lower_bound) * 1.4426950408889634 <= kAnchorExpBudget;
 }
 
 // The same for the 16-token anchors at h' = the integer nearest h = 8 lb
 // log2(e): a half's factors reach 2^{|h'|} and 2^{|2h - h'|}, so they fit
-// while lower_bound >= -10.9; wider bounds take the data-dependent anchors.
+// while lower_bound >= -10.05; wider bounds take the data-dependent anchors.
 bool half_anchor_fits(float lower_bound) {
   const double h = 8.0 * (double)lower_bound * 1.4426950408889634, hr = std::nearbyint(h);
-  return std::fabs(hr) <= 126.0 && std::fabs(2.0 * h - hr) <= 126.0;
+  return std::fabs(hr) <= kAnchorExpBudget && std::fabs(2.0 * h - hr) <= kAnchorExpBudget;
 }
 
 // Argument checks shared by the prefill entry points; each returns KDA_OK or

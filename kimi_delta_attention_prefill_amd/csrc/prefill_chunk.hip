@@ -10,8 +10,8 @@
 //   U   = T Diag(b) (V - W)                                     (residual/beta)
 //   S1  = Diag(2^{G_L}) S0 + Kr^T U,   O = scale (O0 + Mqk U)   (fused update)
 // with Qc = q 2^{G-C}, Kc' = k 2^{G-C}, Kc = k 2^{C-G}, C = 16 lb log2(e),
-// Kg = k 2^G, Qg = q 2^G, Kr[s] = k_s 2^{G_L - G_s}.  When 16|lb|log2(e) > 126
-// the anchored operands would leave the bf16/fp32 exponent range, so the
+// Kg = k 2^G, Qg = q 2^G, Kr[s] = k_s 2^{G_L - G_s}.  When 16|lb|log2(e) > 116
+// the anchored operands' bf16 low halves would lose their precision, so the
 // pairwise products are formed per 16-token half instead (diagonal blocks
 // anchored at the prefix before the half plus 8 lb log2(e), the off-diagonal
 // block factored through the prefix at the split point, whose factors are all

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     // its diagonal tile is formed from the 8-token quarters Q0 (tokens 0-7 of
     // the half) and Q1 (8-15): Q0 x Q0 and Q1 x Q1 anchored at their own
     // midpoints, Q1 x Q0 through the prefix at their boundary (factors <= 1);
-    // exact to the usual rounding while no quarter falls by more than 2^252.
+    // exact to the usual rounding while no quarter falls by more than 2^232.
     // The lane of token l16 supplies row and column l16 of a tile, so its
     // quarter decides which products it takes part in.
     bool steep = false;

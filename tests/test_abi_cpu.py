@@ -35,11 +35,18 @@ def test_abi_version_matches_header():
 
 
 def test_plan_anchor_mode_boundary():
-    # fixed anchor iff 16 |lb| log2(e) <= 126  <=>  |lb| <= 5.4592...
+    # fixed anchor iff 16 |lb| log2(e) <= 116 (the budget that keeps the bf16
+    # low halves of the anchored operands)  <=>  |lb| <= 5.0254...
     assert kda.plan(1, 64, 2, -5.0, 256).anchor_mode == kda.ANCHOR_FIXED
-    assert kda.plan(1, 64, 2, -5.45, 256).anchor_mode == kda.ANCHOR_FIXED
-    assert kda.plan(1, 64, 2, -5.47, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    assert kda.plan(1, 64, 2, -5.02, 256).anchor_mode == kda.ANCHOR_FIXED
+    assert kda.plan(1, 64, 2, -5.03, 256).anchor_mode == kda.ANCHOR_SPLIT16
     assert kda.plan(4, 32768, 64, -8.0, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    # 16-token anchors at the integer h' nearest h = 8 lb log2(e): factors up to
+    # 2^|h'| and 2^|2h - h'|, both <= 116 down to |lb| ~ 10.05
+    assert kda.plan(1, 64, 2, -10.0, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    assert kda.plan(1, 64, 2, -10.05, 256).anchor_mode == kda.ANCHOR_SPLIT16
+    assert kda.plan(1, 64, 2, -10.1, 256).anchor_mode == kda.ANCHOR_DATA
+    assert kda.plan(1, 64, 2, -10.875, 256).anchor_mode == kda.ANCHOR_DATA
     p = kda.plan(1, 64, 2, -5.0, 256)
     assert abs(p.anchor_log2 - 16 * -5.0 * 1.4426950408889634) < 1e-4
 

@@ -74,7 +74,7 @@ def test_each_violation_raises_its_flag(dev):
 
 
 def test_steep_quarter_flag(dev):
-    """KDA_CHECK_GATE_STEEP: a gate falling by more than 174.6 nats within an
+    """KDA_CHECK_GATE_STEEP: a gate falling by more than 160.8 nats within an
     8-token quarter of a chunk (tokens 8-15 of the first sequence, 7 x -30)
     is flagged; the same fall split by a sequence boundary is not."""
     c = _base()
@@ -87,7 +87,7 @@ def test_steep_quarter_flag(dev):
     assert _check(dataclasses.replace(c, g=g, name="steep_split"), dev,
                   lower_bound=float("-inf")) == NONE
     g = c.g.clone()
-    g[9:16, 1, 40] = -24.875                            # 7 x 24.875 = 174.1 nats: within the limit
+    g[9:16, 1, 40] = -22.875                            # 7 x 22.875 = 160.1 nats: within the limit
     assert _check(dataclasses.replace(c, g=g, name="steep_edge"), dev,
                   lower_bound=float("-inf")) == NONE
 

@@ -9,7 +9,9 @@ behaviour on these inputs is pinned by closed forms in the CPU tests:
   state row its key selects with its value;
 * every gate at the lower bound: the anchored operand exponents reach the
   ends of their range (16 |lb| log2 e = 115.4 with one anchor per chunk at
-  lb = -5; the 16-token split at lb = -8);
+  lb = -5; the 16-token split at lb = -8 and at lb = -10, where its factors
+  reach the 2^116 budget; the data-dependent anchors with quarter products at
+  lb = -10.875; random gates at both of the last two bounds as well);
 * nearly identical keys under weak decay: the 32x32 triangular system's
   entries approach beta, the hardest case for the chunk's FP32 inverse.
 """
@@ -114,10 +116,19 @@ def test_orthonormal_keys_overwrite_rows(dev, route):
 
 
 @pytest.mark.parametrize("route", ROUTES)
-@pytest.mark.parametrize("lb", [-5.0, -8.0])
+@pytest.mark.parametrize("lb", [-5.0, -8.0, -10.0, -10.875])
 def test_all_gates_at_lower_bound(dev, route, lb):
     base = make_prefill_case([100, 64], 2, lb, 0.02, seed=34, name=f"gates_at_lb{lb}")
     case = dataclasses.replace(base, g=torch.full_like(base.g, lb))
+    _run_and_compare(case, route, dev)
+
+
+@pytest.mark.parametrize("route", ROUTES)
+@pytest.mark.parametrize("lb", [-10.0, -10.875])
+def test_anchor_budget_edge(dev, route, lb):
+    """Random gates at lower_bound = -10 (the 16-token anchors at their 2^116
+    budget) and -10.875 (beyond it: data-dependent anchors)."""
+    case = make_prefill_case([300, 77], 2, lb, 0.02, seed=36, name=f"gates_lb{lb}")
     _run_and_compare(case, route, dev)
 
 
