@@ -150,7 +150,8 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
     // producers' code after the consumers' and then count the consumers'
     // state loads as pending in the producers' waits (up to waiting for the
     // next chunk's prefetch in the middle of a step); an explicit vmcnt(0)
-    // (expcnt, lgkmcnt not waited on) clears that count.
+    // clears that count.  s_waitcnt fields: vmcnt bits 3:0 (and 15:14) = 0,
+    // expcnt bits 6:4 = 7 and lgkmcnt bits 11:8 = 15, i.e. not waited on.
     __builtin_amdgcn_s_waitcnt(0x0F70);
     // Chunk c's rows are fetched into registers during step c-2 and written
     // to LDS at that step's end: its q/k/g rows into raw[c % 2] (free since
