@@ -93,10 +93,10 @@ struct ChunkOps {
 struct PrepWork {
   float G[CH][GP];             // log2-domain inclusive gate prefix
   float EL[D];                 // fixed anchor: 2^{G_L - C}
-  // 16-token anchors (h = 8 lb log2 e, the half anchors h and G_15 + h): per
-  // channel 2^{G_15 + h}, 2^{G_L - h}, 2^{G_L - G_15 - h}, 2^{G_15 - h}, so
-  // that each element needs only its two anchored factors from the
-  // exponential unit and the rest are products with these
+  // 16-token anchors (h = 8 lb log2 e rounded to an integer, the half anchors
+  // h and G_15 + h): per channel 2^{G_15 + h}, 2^{G_L - h}, 2^{G_L - G_15 - h},
+  // 2^{G_15 - h}, so that each element needs only its two anchored factors
+  // from the exponential unit and the rest are products with these
   float K16[4][D];
   float rq[CH], rk[CH];        // q/k L2-norm scales per token (1 without the front-end norm)
 };
@@ -346,7 +346,7 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         P = ep * exp2C;                               // 2^G
         R = (j < 4 ? EL0[j] : EL1[j - 4]) * em;       // 2^{G_L - G}
       } else if (MODE == 1) {
-        // anchor Ch = h (half 0) or G_15 + h (half 1), h = 8 lb log2 e; the
+        // anchor Ch = h (half 0) or G_15 + h (half 1), h = 8 lb log2 e rounded; the
         // factors below 2^-126 that a constant can lose belong to operands
         // far below fp16's range (they are zero either way)
         const float c1 = j < 4 ? Ka0[j] : Ka1[j - 4], c2 = j < 4 ? Kb0[j] : Kb1[j - 4];

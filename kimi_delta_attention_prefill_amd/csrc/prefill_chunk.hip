@@ -13,9 +13,10 @@
 // Kg = k 2^G, Qg = q 2^G, Kr[s] = k_s 2^{G_L - G_s}.  When 16|lb|log2(e) > 116
 // the anchored operands' bf16 low halves would lose their precision, so the
 // pairwise products are formed per 16-token half instead (diagonal blocks
-// anchored at the prefix before the half plus 8 lb log2(e), the off-diagonal
-// block factored through the prefix at the split point, whose factors are all
-// <= 1): the note's "ordinary SafeGate" 16-token blocks.
+// anchored at the prefix before the half plus 8 lb log2(e) rounded to an
+// integer, the off-diagonal block factored through the prefix at the split
+// point, whose factors are all <= 1): the note's "ordinary SafeGate" 16-token
+// blocks.
 //
 // Number formats (chosen so the FP32-state result stays within 1e-2 RMS of
 // the exact recurrence at the largest state entries; bf16 alone loses up to
