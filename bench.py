@@ -220,7 +220,7 @@ def multitoken_sweep(torch, dev, kda, copy_gbs, steps=10, warmup=3):
     return out
 
 
-def fused_configs(torch, dev, kda, configs=(2, 3), steps=5, warmup=2):
+def fused_configs(torch, dev, kda, configs=(2, 3), steps=10, warmup=3):
     """Prefill configurations 2 (16 varlen sequences, H=32) and 3 (4 x 8192,
     H=64, lb=-8) on the route the planner picks (the fused chunk kernel, one
     launch per call): event-timed calls, tokens*heads/s, and the kernel's
