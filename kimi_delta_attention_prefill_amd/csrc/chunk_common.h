@@ -169,6 +169,36 @@ __device__ __forceinline__ void fetch_chunk(ChunkRegs<DVS>& x, const PrefillArgs
   x.beta = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
 }
 
+// One part of fetch_chunk: PART 0 the q rows and beta, 1 the k rows, 2 the g
+// rows, 3 the value rows, so that the loads can be spread over a step.
+template <int PART, int DVS>
+__device__ __forceinline__ void fetch_chunk_part(ChunkRegs<DVS>& x, const PrefillArgs& a, int t0, int L,
+                                                 int h, int col0, int tid) {
+  const int H = a.num_heads;
+  const int64_t base = ((int64_t)t0 * H + h) * D;
+  const uint32_t rows_bytes = (uint32_t)(((L - 1) * H + 1) * D * 2);
+  const uint32_t row_bytes = (uint32_t)H * D * 2;
+  if constexpr (PART < 3) {
+    const uint16_t* src = PART == 0 ? a.q : PART == 1 ? a.k : a.g;
+    const __amdgpu_buffer_rsrc_t r = make_buffer(src + base, rows_bytes);
+    uint4* dst = PART == 0 ? x.q : PART == 1 ? x.k : x.g;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = tid + 256 * i;
+      dst[i] = load16(r, (uint32_t)(e >> 4) * row_bytes + (uint32_t)(e & 15) * 16);
+    }
+    if (PART == 0) x.beta = a.beta[(int64_t)(t0 + min(tid & (CH - 1), L - 1)) * H + h];
+  } else {
+    constexpr int kCh = DVS / 8;
+    const __amdgpu_buffer_rsrc_t rv = make_buffer(a.v + base, rows_bytes);
+#pragma unroll
+    for (int i = 0; i < ChunkRegs<DVS>::kV; ++i) {
+      const int e = tid + 256 * i;
+      x.v[i] = load16(rv, (uint32_t)(e / kCh) * row_bytes + (uint32_t)col0 * 2 + (uint32_t)(e % kCh) * 16);
+    }
+  }
+}
+
 // Writes the fetched rows into the padded q/k/g rows of `cr` and the value
 // rows `v`.  256 threads.
 template <int DVS>

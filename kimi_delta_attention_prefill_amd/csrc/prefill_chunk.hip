@@ -154,7 +154,10 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
     // clears that count.  s_waitcnt fields: vmcnt bits 3:0 (and 15:14) = 0,
     // expcnt bits 6:4 = 7 and lgkmcnt bits 11:8 = 15, i.e. not waited on.
     __builtin_amdgcn_s_waitcnt(0x0F70);
-    // Chunk c's rows are fetched into registers during step c-2 and written
+    // Chunk c's rows are fetched into registers during step c-2 (the q and k
+    // rows around the gate prefix, the g and value rows around the pair
+    // products, so that the 16-byte loads find the compute unit's address
+    // path free instead of queueing behind each other) and written
     // to LDS at that step's end: its q/k/g rows into raw[c % 2] (free since
     // chunk c-2 was prepared from it) and its value rows into ring slot c % 2
     // (the consumers finish reading chunk c-2's values before the last phase
@@ -178,12 +181,17 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       lds_barrier();
       if (prep) {
         stage_beta<FE>(sn.beta, x.beta, a.fe, Ln, ptid);
-        if (s + 2 < nch) fetch_chunk(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
+        if (s + 2 < nch) fetch_chunk_part<0>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
         gate_prefix<MODE, FE>(sm.pw, sn.dec, cr, a.fe, C, a.half_anchor_log2, Ln, tid);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 2 < nch) fetch_chunk_part<1>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
+        __builtin_amdgcn_sched_barrier(0);
         if (FE) qk_norms(sm.pw, cr, a, ptid);
       }
       lds_barrier();   // B1: gate prefix, anchor constants, beta and decays of chunk s+1 written
       if (prep) {
+        if (s + 2 < nch) fetch_chunk_part<2>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
+        __builtin_amdgcn_sched_barrier(0);
         f32x4 pacc[6];
         auto emit = [&](int t, int c0, const float* kv, const float* qv, const float* P,
                               const float* R) {
@@ -210,6 +218,8 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
         else
           pair_products<MODE, FE>(pacc, sm.pw, cr, a, C, exp2C, pwave, lane, emit);
         pair_store(cr, pacc, pwave, lane);   // over this wave's own columns of the rows
+        __builtin_amdgcn_sched_barrier(0);
+        if (s + 2 < nch) fetch_chunk_part<3>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
       }
       lds_barrier();   // B2: split-K partials of chunk s+1 complete
       if (prep)
