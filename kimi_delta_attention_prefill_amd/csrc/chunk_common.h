@@ -295,7 +295,8 @@ __device__ __forceinline__ void gate_prefix(PrepWork& pw, float* dec, const Chun
       pw.K16[0][c] = fast_exp2(G15 + Ch);
       pw.K16[1][c] = fast_exp2(GL - Ch);
       pw.K16[2][c] = fast_exp2(GL - G15 - Ch);
-      pw.K16[3][c] = fast_exp2(G15 - Ch);
+      // with the off-diagonal tile's column scale 2^z, z = floor(h / 2), folded in
+      pw.K16[3][c] = fast_exp2(G15 - Ch) * __builtin_ldexpf(1.f, (int)Ch >> 1);
     }
   }
 }
@@ -311,9 +312,11 @@ struct PairOps {
 
 // Step 3: anchored operands and the split-K pairwise products.  Wave w (of 4)
 // owns key channels 32w..32w+31; lane (g4, l16) owns channels 32w+8g4+j and
-// tokens l16, l16+16.  For every (token t, channel c) owned, emit(t, c, kf, qf,
-// P, R) receives the raw k and q values, P = 2^{G_t} and R = 2^{G_L - G_t}
-// (both <= 1) so the caller can form Kg, Qg and Kr.  Returns the six lower
+// tokens l16, l16+16.  For the 8 channels c0.. of each owned token t,
+// emit(t, c0, kg, qg, kr) receives Kg = k 2^{G_t}, Qg = q 2^{G_t} and Kr =
+// k 2^{G_L - G_t} in fp16 (from the anchored values times the anchor's
+// remaining factor, or with data-dependent anchors from the raw k and q and
+// their own exponentials), so the caller can store them.  Returns the six lower
 // tiles of Mqk and Akk as partial sums over this wave's channels; the caller
 // stores them (pair_store) once no producer reads the chunk's rows any more.
 template <int MODE, bool FE, class Emit>
@@ -324,11 +327,11 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
   const int cb = 32 * wave, cl = 8 * g4;
   // 16-token anchors: the off-diagonal tile's rows reuse half 1's diagonal
   // operands (anchored at G_15 + h, h an integer), its half-0 columns carry
-  // 2^{G_15 - G} 2^z, and the tile is scaled back by 2^{h - z} afterwards
-  // (exact powers of two; z = floor(h / 2) keeps the unscaled sums within
-  // 2^{|h|/2} of the products)
+  // 2^{G_15 - G} 2^z (the 2^z in the channel constant), and the tile is
+  // scaled back by 2^{h - z} afterwards (exact powers of two; z = floor(h / 2)
+  // keeps the unscaled sums within 2^{|h|/2} of the products)
   const int hz = MODE == 1 ? (int)a.half_anchor_log2 : 0, zc = hz >> 1;
-  const float colscale = __builtin_ldexpf(1.f, zc), accscale = __builtin_ldexpf(1.f, hz - zc);
+  const float accscale = __builtin_ldexpf(1.f, hz - zc);
   PairOps op;
 #pragma unroll
   for (int half = 0; half < 2; ++half) {
@@ -361,7 +364,7 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
     }
     const uint32_t qu[4] = {qw.x, qw.y, qw.z, qw.w};
     const uint32_t ku[4] = {kw.x, kw.y, kw.z, kw.w};
-    float kv[8], qv[8], Pv[8], Rv[8];
+    f16x8 kg, qg, kr;   // Kg, Qg and Kr of the 8 channels
     // the anchored operand values, split into bf16 hi/lo pairs after the loop
     float xq[8], xk[8], xb[8], xqo[8], xko[8];
 #pragma unroll
@@ -373,8 +376,8 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
       if (MODE == 0) {
         ep = fast_exp2(Gv - C);                       // 2^{G-C}, |exponent| <= 16|b|
         em = fast_exp2(C - Gv);                       // 2^{C-G}
-        P = ep * exp2C;                               // 2^G
-        R = (j < 4 ? EL0[j] : EL1[j - 4]) * em;       // 2^{G_L - G}
+        P = exp2C;                                    // Kg = (k 2^{G-C}) 2^C
+        R = (j < 4 ? EL0[j] : EL1[j - 4]);            // Kr = (k 2^{C-G}) 2^{G_L-C}
       } else if (MODE == 1) {
         // anchor Ch = h (half 0) or G_15 + h (half 1), h = 8 lb log2 e rounded; the
         // factors below 2^-126 that a constant can lose belong to operands
@@ -384,12 +387,12 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         ep = fast_exp2(Gv - Ch);
         em = fast_exp2(Ch - Gv);
         if (half) {
-          P = ep * c1;                                // 2^{G_15 + h} 2^{G - G_15 - h}
-          R = em * c2;                                // 2^{G_L - G_15 - h} 2^{G_15 + h - G}
+          P = c1;                                     // 2^{G_15 + h}
+          R = c2;                                     // 2^{G_L - G_15 - h}
         } else {
-          P = ep * exp2C;                             // 2^h 2^{G - h}
-          R = em * c1;                                // 2^{G_L - h} 2^{h - G}
-          fo = (em * c2) * colscale;                  // 2^{G_15 - h} 2^{h - G} 2^z
+          P = exp2C;                                  // 2^h
+          R = c1;                                     // 2^{G_L - h}
+          fo = c2;                                    // 2^{G_15 - h} 2^z
         }
       } else {
         const float g15 = j < 4 ? Gs0[j] : Gs1[j - 4];
@@ -407,9 +410,19 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
       xq[j] = qf * ep;
       xk[j] = kf * ep;
       xb[j] = kf * em;
-      xqo[j] = qf * fo;
-      xko[j] = kf * fo;
-      kv[j] = kf; qv[j] = qf; Pv[j] = P; Rv[j] = R;
+      if (MODE == 2) {
+        xqo[j] = qf * fo;
+        xko[j] = kf * fo;
+        kg[j] = static_cast<_Float16>(kf * P);
+        qg[j] = static_cast<_Float16>(qf * P);
+        kr[j] = static_cast<_Float16>(kf * R);
+      } else {
+        xqo[j] = 0.f;
+        xko[j] = xb[j] * fo;
+        kg[j] = static_cast<_Float16>(xk[j] * P);
+        qg[j] = static_cast<_Float16>(xq[j] * P);
+        kr[j] = static_cast<_Float16>(xb[j] * R);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 8; j += 2) {
@@ -442,7 +455,7 @@ __device__ __forceinline__ void pair_products(f32x4 (&acc)[6], const PrepWork& p
         split_bf16_pair(xko[j], xko[j + 1], op.boh, op.bol, j);
       }
     }
-    emit(t, cb + cl, kv, qv, Pv, Rv);
+    emit(t, cb + cl, kg, qg, kr);
   }
   const f32x4 z = {0.f, 0.f, 0.f, 0.f};
   acc[0] = mfma_bf16(op.q0h, op.b0h, z);
@@ -579,7 +592,7 @@ __device__ __forceinline__ void pair_products_steep(f32x4 (&acc)[6], const PrepW
     {
       // the off-diagonal tile's operands (through the prefix at token 15) and Kg, Qg, Kr
       bf16x8 qoh, qol, koh, kol;
-      float kv[8], qv[8], Pv[8], Rv[8];
+      f16x8 kg, qg, kr;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         const int c = cb + cl + j;
@@ -593,9 +606,12 @@ __device__ __forceinline__ void pair_products_steep(f32x4 (&acc)[6], const PrepW
         } else {
           split_bf16(kf * fo, h, l); boh[j] = h; bol[j] = l;
         }
-        kv[j] = kf; qv[j] = qf; Pv[j] = fast_exp2(Gv); Rv[j] = fast_exp2(gl - Gv);
+        const float P = fast_exp2(Gv), R = fast_exp2(gl - Gv);
+        kg[j] = static_cast<_Float16>(kf * P);
+        qg[j] = static_cast<_Float16>(qf * P);
+        kr[j] = static_cast<_Float16>(kf * R);
       }
-      emit(t, cb + cl, kv, qv, Pv, Rv);
+      emit(t, cb + cl, kg, qg, kr);
       if (half == 1) {
         acc[1] = mfma3(qoh, qol, boh, bol, z);
         acc[4] = mfma3(koh, kol, boh, bol, z);
@@ -611,56 +627,72 @@ __device__ __forceinline__ void pair_store(ChunkQKG& cr, const f32x4 (&acc)[6], 
   for (int p = 0; p < 6; ++p) *reinterpret_cast<f32x4*>(part_entry(cr, wave, p, lane)) = acc[p];
 }
 
-// Step 3b: sum the four split-K partials in a fixed order, mask the causal
-// triangles by select (masked anchored entries may be inf or NaN) and scale
-// Akk by beta.  Writes iw.At (A transposed); emit_mqk(r, s, value) sees every
-// Mqk entry (zero above the diagonal).  256 threads: wave q of them takes
-// quadrant q of both matrices ((0,0), (1,0), (1,1), then the zero (0,1)),
-// lane l the entries of MFMA lane l, each partial as one 16-byte read.
-template <class EmitMqk>
-__device__ __forceinline__ void reduce_pairs(InvWork& iw, ChunkQKG& cr, const float* beta, int tid,
-                                             EmitMqk&& emit_mqk) {
-  const int q4 = tid >> 6, ln = tid & 63;
-  const int mt = (q4 == 1 || q4 == 2) ? 1 : 0, nt = (q4 == 2 || q4 == 3) ? 1 : 0;
-  f32x4 mq = {0.f, 0.f, 0.f, 0.f}, ak = {0.f, 0.f, 0.f, 0.f};
-  if (q4 < 3) {   // Mqk partial tile q4, Akk partial tile 3 + q4
-    auto rd = [&](int w, int p) __attribute__((always_inline)) {
-      return *reinterpret_cast<const f32x4*>(part_entry(cr, w, p, ln));
-    };
-    mq = ((rd(0, q4) + rd(1, q4)) + rd(2, q4)) + rd(3, q4);
-    ak = ((rd(0, 3 + q4) + rd(1, 3 + q4)) + rd(2, 3 + q4)) + rd(3, 3 + q4);
-  }
-  const int r0 = 16 * mt + 4 * (ln >> 4), s = 16 * nt + (ln & 15);
-  f32x4 at;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = r0 + i;
-    emit_mqk(r, s, s <= r ? mq[i] : 0.f);
-    at[i] = s < r ? beta[r] * ak[i] : 0.f;
-  }
-  *reinterpret_cast<f32x4*>(&iw.At[s][r0]) = at;
+// A wave's own LDS accesses in program order: its writes before this point
+// are seen by the reads of any of its lanes after it (one wave's LDS
+// operations are performed in order; the fences keep the compiler from
+// moving accesses across).
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 }
 
-// Steps 4a-4c: T = (I + A)^{-1} in two phases separated by the caller's
-// barrier.  With T11, T22 the inverses of the 16x16 diagonal blocks of I + A
-// and A21 its lower-left block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.
-// Phase 1 (producer waves 0-2): lanes 0-15 of waves 0 and 1 invert diagonal
-// block b = wave by forward substitution in FP32, one column each, with the
-// block's whole strict lower triangle read into registers first so that the
-// 16 dependent steps wait on no LDS read; at the same time wave 2 solves
-// (I + A22) W = A21 by the same substitution, so W = T22 A21 needs no wait
-// for T22.  Diagonal blocks go to emit_t(row, col, value) (the caller stores
-// the MFMA operand).  Phase 2 (one wave): T21 = -W T11 on the matrix cores
-// (T12 = 0 is the caller's, once).
+// Sum of the four split-K partials of tile p, in a fixed order, for MFMA lane
+// `lane` (rows 4 (lane / 16) + i of column lane % 16 of the tile).
+__device__ __forceinline__ f32x4 sum_partials(ChunkQKG& cr, int p, int lane) {
+  auto rd = [&](int w) __attribute__((always_inline)) {
+    return *reinterpret_cast<const f32x4*>(part_entry(cr, w, p, lane));
+  };
+  return ((rd(0) + rd(1)) + rd(2)) + rd(3);
+}
+
+// Step 3b for Mqk: lower tile p (0 = rows/columns 0-15, 1 = rows 16-31 x
+// columns 0-15, 2 = rows/columns 16-31) from its partials, the causal
+// triangle masked by select (masked anchored entries may be inf or NaN);
+// emit_mqk(r, s, value) sees each entry.  Tile 0's wave also emits the zero
+// block (rows 0-15 x columns 16-31).  One wave per tile.
+template <class EmitMqk>
+__device__ __forceinline__ void reduce_mqk(ChunkQKG& cr, int p, int lane, EmitMqk&& emit_mqk) {
+  const f32x4 mq = sum_partials(cr, p, lane);
+  const int r0 = (p == 0 ? 0 : 16) + 4 * (lane >> 4), s = (p == 2 ? 16 : 0) + (lane & 15);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s, s <= r0 + i ? mq[i] : 0.f);
+  if (p == 0) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s + 16, 0.f);
+  }
+}
+
+// Steps 3b-4 for the triangular system, on one wave: the lower blocks of
+// A = Diag(b) stril(Akk) summed from their partials (as Mqk's) into iw.At
+// (A transposed, FP32), then T = (I + A)^{-1} by blocks.  With T11, T22 the
+// inverses of the 16x16 diagonal blocks of I + A and A21 its lower-left
+// block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.  Lanes 0-15 invert
+// I + A11 and lanes 16-31 I + A22, lane m forming column m from e_m, while
+// lanes 32-47 solve (I + A22) W = A21 from column m of A21 (lanes 48-63
+// repeat them and store nothing): forward substitution in FP32 with the
+// block's strict lower triangle read into registers first, so the 16
+// dependent steps wait on no LDS read.  T21 then takes four 16x16x4 FP32
+// matrix products.  The blocks pass between the lanes through LDS in the
+// wave's own order (no block barrier).  emit_t(row, col, value) receives
+// T11, T22 and T21 (T12 = 0 is the caller's, once).
 template <class EmitT>
-__device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int lane, EmitT&& emit_t) {
-  if (wave > 2 || lane >= 16) return;
-  // waves 0 and 1: T11, T22, lane m forming column m from e_m; wave 2: W =
-  // T22 A21 = (I + A22)^{-1} A21 by the same substitution on A22, lane m
-  // starting from column m of A21 (row m of At, columns 16..31)
-  const bool w21 = wave == 2;
-  const int base = w21 ? 16 : 16 * wave;
-  const int m = lane;
+__device__ __forceinline__ void reduce_invert(InvWork& iw, ChunkQKG& cr, const float* beta, int lane,
+                                              EmitT&& emit_t) {
+  // A's tiles 3 + q: (0,0), (1,0), (1,1); At's block (0,1) is never read
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    const f32x4 ak = sum_partials(cr, 3 + q, lane);
+    const int r0 = (q == 0 ? 0 : 16) + 4 * (lane >> 4), s = (q == 2 ? 16 : 0) + (lane & 15);
+    f32x4 at;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) at[i] = s < r0 + i ? beta[r0 + i] * ak[i] : 0.f;
+    *reinterpret_cast<f32x4*>(&iw.At[s][r0]) = at;
+  }
+  wave_lds_sync();
+  const int grp = lane >> 4, m = lane & 15;
+  const bool w21 = grp >= 2;
+  const int base = grp == 0 ? 0 : 16;
   float x[16];
   if (w21) {
 #pragma unroll
@@ -690,29 +722,26 @@ __device__ __forceinline__ void invert_diag_blocks(InvWork& iw, int wave, int la
       for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[j - j0][i >> 2][i & 3], x[j], x[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (w21) {
+  if (grp == 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) iw.X[i][m] = x[i];
-  } else {
+  } else if (grp < 2) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       iw.Tf[base + i][base + m] = x[i];
       emit_t(base + i, base + m, x[i]);
     }
   }
-}
-// T21 = -W T11 as four 16x16x4 FP32 matrix products (K = 16): in step kk
-// lane l supplies W[l % 16][4 kk + l / 16] and T11[4 kk + l / 16][l % 16]
-// and ends with T21[4 (l / 16) + i][l % 16], i < 4.  One wave.
-template <class EmitT>
-__device__ __forceinline__ void invert_offdiag(const InvWork& iw, int lane, EmitT&& emit_t) {
-  const int r = lane & 15, kq = lane >> 4;
+  wave_lds_sync();
+  // T21 = -W T11: in step kk lane l supplies W[l % 16][4 kk + l / 16] and
+  // T11[4 kk + l / 16][l % 16] and ends with T21[4 (l / 16) + i][l % 16]
+  const int kq = lane >> 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(iw.X[r][4 * kk + kq], iw.Tf[4 * kk + kq][r], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(iw.X[m][4 * kk + kq], iw.Tf[4 * kk + kq][m], acc, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) emit_t(16 + 4 * kq + i, r, -acc[i]);
+  for (int i = 0; i < 4; ++i) emit_t(16 + 4 * kq + i, m, -acc[i]);
 }
 
 }  // namespace chunk

@@ -35,19 +35,19 @@
 // prepare chunks and the waves that consume them), sized for a CDNA4 compute
 // unit's 160 KiB of LDS:
 //   * waves 4-7 (producers) prepare chunk c+1 -- anchored operands, Mqk and
-//     the triangular system, the inverse's diagonal blocks and W = T22 A21 --
-//     into ring slot (c+1) % 2 (wave w owns key channels 32(w-4).. of the
-//     pairwise products, a split-K whose partials are summed in a fixed
-//     order, so results are deterministic), and fetch the rows of chunk c+2
-//     into registers, writing them to LDS at the step's end;
+//     the triangular system and its inverse -- into ring slot (c+1) % 2 (wave
+//     w owns key channels 32(w-4).. of the pairwise products, a split-K whose
+//     partials are summed in a fixed order, so results are deterministic;
+//     then one wave sums the system's blocks and inverts it while the others
+//     sum Mqk's), and fetch the rows of chunk c+2 into registers, writing
+//     them to LDS at the step's end;
 //   * waves 0-3 (consumers) meanwhile run the serial state chain of chunk c
 //     from slot c % 2 on their own 16 * NT value columns (value columns
 //     evolve independently, so the chain needs no cross-wave exchange); the
 //     FP32 state stays in their MFMA accumulators for the whole sequence.
-//     In the phases where the chain has nothing to do they take a share of
-//     the preparation: half of chunk c+1's gate prefix and the inverse's
-//     off-diagonal block T21 = -W T11 (one wave, four FP32 matrix products).
-// Both sides meet at the same five block barriers per chunk (barriers that
+//     In the phase where the chain has nothing to do they take half of
+//     chunk c+1's gate prefix.
+// Both sides meet at the same four block barriers per chunk (barriers that
 // order LDS only, so prefetches and output stores stay in flight across
 // them), and the chain's products with the state (matrix-core work) sit in
 // the phase of the producers' VALU-bound pair products, so a chunk costs
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
     }
     // Step s (s = -1 .. nch-1): chunk s+1 is prepared into ring slot (s+1) % 2
     // while the consumers run the chain of chunk s.  Every wave passes the
-    // same five barriers per step.
+    // same four barriers per step.
     for (int s = -1; s < nch; ++s) {
       const bool prep = s + 1 < nch;
       ChunkQKG& cr = sm.raw[(s + 1) & 1];          // chunk s+1's rows
@@ -193,26 +193,18 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
         if (s + 2 < nch) fetch_chunk_part<2>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
         __builtin_amdgcn_sched_barrier(0);
         f32x4 pacc[6];
-        auto emit = [&](int t, int c0, const float* kv, const float* qv, const float* P,
-                              const float* R) {
-                            const int cb = c0 & ~31, cl = c0 & 31;
-                            f16x4 kg_lo, kg_hi, qg_lo, qg_hi;
+        auto emit = [&](int t, int c0, const f16x8& kg, const f16x8& qg, const f16x8& kr) {
+          const int cb = c0 & ~31, cl = c0 & 31;
+          const f16x4 kg_lo = {kg[0], kg[1], kg[2], kg[3]}, kg_hi = {kg[4], kg[5], kg[6], kg[7]};
+          const f16x4 qg_lo = {qg[0], qg[1], qg[2], qg[3]}, qg_hi = {qg[4], qg[5], qg[6], qg[7]};
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) {
-                              kg_lo[j] = static_cast<_Float16>(kv[j] * P[j]);
-                              kg_hi[j] = static_cast<_Float16>(kv[4 + j] * P[4 + j]);
-                              qg_lo[j] = static_cast<_Float16>(qv[j] * P[j]);
-                              qg_hi[j] = static_cast<_Float16>(qv[4 + j] * P[4 + j]);
-                            }
-#pragma unroll
-                            for (int j = 0; j < 8; ++j)
-                              sn.KrT[c0 + j][kslot(t)] = static_cast<_Float16>(kv[j] * R[j]);
-                            // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 slots
-                            *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl)]) = kg_lo;
-                            *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
-                            *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl)]) = qg_lo;
-                            *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
-                          };
+          for (int j = 0; j < 8; ++j) sn.KrT[c0 + j][kslot(t)] = kr[j];
+          // channels cl..cl+3 and cl+4..cl+7 land in two runs of 4 slots
+          *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl)]) = kg_lo;
+          *reinterpret_cast<f16x4*>(&sn.Kg[t][cb + kslot(cl + 4)]) = kg_hi;
+          *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl)]) = qg_lo;
+          *reinterpret_cast<f16x4*>(&sn.Qg[t][cb + kslot(cl + 4)]) = qg_hi;
+        };
         if (MODE == 2 && steep_wave(sm.pw, pwave, lane))
           pair_products_steep<FE>(pacc, sm.pw, cr, pwave, lane, emit);
         else
@@ -222,15 +214,18 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
         if (s + 2 < nch) fetch_chunk_part<3>(x, a, tn0 + CH, min(CH, eos - tn0 - CH), h, col_base, ptid);
       }
       lds_barrier();   // B2: split-K partials of chunk s+1 complete
-      if (prep)
-        reduce_pairs(inv_of(sm.pw), cr, sn.beta, ptid, [&](int r, int c, float m) {
-          sn.Mqk[r][kslot(c)] = static_cast<_Float16>(m);
-        });
-      lds_barrier();   // B3: the triangular system of chunk s+1 is in place
-      auto emit_t = [&](int r, int c, float t) { sn.T[r][kslot(c)] = static_cast<_Float16>(t); };
-      if (prep) invert_diag_blocks(inv_of(sm.pw), pwave, lane, emit_t);
-      lds_barrier();   // B4: T11, T22 and W = T22 A21 in place; the consumers are done with slot s
-      // (the consumers form T21 = -W T11 meanwhile)
+      if (prep) {
+        // the triangular system and its inverse on one wave, Mqk's tiles on the others
+        if (pwave == 0)
+          reduce_invert(inv_of(sm.pw), cr, sn.beta, lane, [&](int r, int c, float t) {
+            sn.T[r][kslot(c)] = static_cast<_Float16>(t);
+          });
+        else
+          reduce_mqk(cr, pwave - 1, lane, [&](int r, int c, float m) {
+            sn.Mqk[r][kslot(c)] = static_cast<_Float16>(m);
+          });
+      }
+      lds_barrier();   // B3: chunk s+1's ring slot complete; the consumers are done with slot s
       if (s + 2 < nch) stage_chunk(sm.raw[s & 1], sm.slot[s & 1].v, x, ptid);   // chunk s+2
     }
     return;
@@ -301,7 +296,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
     // ---- the state chain of chunk s on this wave's 16 * NT value columns.
     // Its products with the state (W, O: matrix-core work and little VALU)
     // run beside the producers' VALU-bound pair products; the rest beside
-    // the producers' reduction (part A) and inverse (part B)
+    // the producers' reduction and inverse
     f32x4 OT[NT][2];
     f16x8 Uh[NT], Ul[NT];
     f32x4 W[2][NT];
@@ -390,7 +385,6 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
             Ul[nt][4 * mt + i] = ll;
           }
     }
-    lds_barrier();   // B3
     if (s >= 0) {
       // S = Diag(2^{G_L}) S + Kr^T U
 #pragma unroll
@@ -435,11 +429,7 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
         ++ck_row;
       }
     }
-    lds_barrier();   // B4
-    if (s + 1 < nch && wave == 0)   // chunk s+1's T21 = -W T11, beside the producers' staging of chunk s+2
-      invert_offdiag(inv_of(sm.pw), lane, [&](int r, int c, float t) {
-        sm.slot[(s + 1) & 1].T[r][kslot(c)] = static_cast<_Float16>(t);
-      });
+    lds_barrier();   // B3
   }
 
   if (const StateRef s1 = prefill_final_state(a, n, h)) {
