@@ -646,42 +646,49 @@ __device__ __forceinline__ f32x4 sum_partials(ChunkQKG& cr, int p, int lane) {
   return ((rd(0) + rd(1)) + rd(2)) + rd(3);
 }
 
-// Step 3b for Mqk: lower tile p (0 = rows/columns 0-15, 1 = rows 16-31 x
-// columns 0-15, 2 = rows/columns 16-31) from its partials, the causal
-// triangle masked by select (masked anchored entries may be inf or NaN);
-// emit_mqk(r, s, value) sees each entry.  Tile 0's wave also emits the zero
-// block (rows 0-15 x columns 16-31).  One wave per tile.
+// Step 3b for Mqk on two waves: wave 0 sums the diagonal tiles (rows/columns
+// 0-15 and 16-31) from their partials and emits the zero block (rows 0-15 x
+// columns 16-31), wave 1 the tile of rows 16-31 x columns 0-15; the causal
+// triangle is masked by select (masked anchored entries may be inf or NaN).
+// emit_mqk(r, s, value) sees each entry.
 template <class EmitMqk>
-__device__ __forceinline__ void reduce_mqk(ChunkQKG& cr, int p, int lane, EmitMqk&& emit_mqk) {
-  const f32x4 mq = sum_partials(cr, p, lane);
-  const int r0 = (p == 0 ? 0 : 16) + 4 * (lane >> 4), s = (p == 2 ? 16 : 0) + (lane & 15);
+__device__ __forceinline__ void reduce_mqk(ChunkQKG& cr, int w, int lane, EmitMqk&& emit_mqk) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s, s <= r0 + i ? mq[i] : 0.f);
-  if (p == 0) {
+  for (int p = 0; p < 3; ++p) {
+    if ((p == 1) != (w == 1)) continue;
+    const f32x4 mq = sum_partials(cr, p, lane);
+    const int r0 = (p == 0 ? 0 : 16) + 4 * (lane >> 4), s = (p == 2 ? 16 : 0) + (lane & 15);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s + 16, 0.f);
+    for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s, s <= r0 + i ? mq[i] : 0.f);
+    if (p == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) emit_mqk(r0 + i, s + 16, 0.f);
+    }
   }
 }
 
-// Steps 3b-4 for the triangular system, on one wave: the lower blocks of
-// A = Diag(b) stril(Akk) summed from their partials (as Mqk's) into iw.At
-// (A transposed, FP32), then T = (I + A)^{-1} by blocks.  With T11, T22 the
+// Steps 3b-4a for the triangular system, on two waves: wave `blk` sums its
+// lower blocks of A = Diag(b) stril(Akk) from their partials (as Mqk's) into
+// iw.At (A transposed, FP32) and solves with them.  With T11, T22 the
 // inverses of the 16x16 diagonal blocks of I + A and A21 its lower-left
-// block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.  Lanes 0-15 invert
-// I + A11 and lanes 16-31 I + A22, lane m forming column m from e_m, while
-// lanes 32-47 solve (I + A22) W = A21 from column m of A21 (lanes 48-63
-// repeat them and store nothing): forward substitution in FP32 with the
-// block's strict lower triangle read into registers first, so the 16
-// dependent steps wait on no LDS read.  T21 then takes four 16x16x4 FP32
-// matrix products.  The blocks pass between the lanes through LDS in the
-// wave's own order (no block barrier).  emit_t(row, col, value) receives
-// T11, T22 and T21 (T12 = 0 is the caller's, once).
+// block, T21 = -T22 A21 T11 = -W T11, W = T22 A21.  Wave 0 (block A11):
+// lanes 0-15 invert I + A11, lane m forming column m of T11 from e_m.  Wave
+// 1 (blocks A21, A22): lanes 0-15 invert I + A22 and lanes 16-31 solve
+// (I + A22) W = A21 from column m of A21, so W needs no wait for T22.
+// Forward substitution in FP32 with the block's strict lower triangle read
+// into registers first, so the 16 dependent steps wait on no LDS read; the
+// wave's other lanes repeat a solve and store nothing.  The blocks pass
+// between the wave's lanes through LDS in the wave's own order.  emit_t(row,
+// col, value) receives T11 and T22; T21 follows from iw.X and iw.Tf
+// (invert_offdiag, after a block barrier); T12 = 0 is the caller's, once.
 template <class EmitT>
-__device__ __forceinline__ void reduce_invert(InvWork& iw, ChunkQKG& cr, const float* beta, int lane,
-                                              EmitT&& emit_t) {
-  // A's tiles 3 + q: (0,0), (1,0), (1,1); At's block (0,1) is never read
+__device__ __forceinline__ void reduce_invert(InvWork& iw, ChunkQKG& cr, const float* beta, int blk,
+                                              int lane, EmitT&& emit_t) {
+  // A's tiles 3 + q: (0,0) for wave 0, (1,0) and (1,1) for wave 1; At's
+  // block (0,1) is never read
 #pragma unroll
   for (int q = 0; q < 3; ++q) {
+    if ((q == 0) != (blk == 0)) continue;
     const f32x4 ak = sum_partials(cr, 3 + q, lane);
     const int r0 = (q == 0 ? 0 : 16) + 4 * (lane >> 4), s = (q == 2 ? 16 : 0) + (lane & 15);
     f32x4 at;
@@ -691,8 +698,8 @@ __device__ __forceinline__ void reduce_invert(InvWork& iw, ChunkQKG& cr, const f
   }
   wave_lds_sync();
   const int grp = lane >> 4, m = lane & 15;
-  const bool w21 = grp >= 2;
-  const int base = grp == 0 ? 0 : 16;
+  const bool w21 = blk == 1 && grp >= 1;
+  const int base = blk == 0 ? 0 : 16;
   float x[16];
   if (w21) {
 #pragma unroll
@@ -722,26 +729,30 @@ __device__ __forceinline__ void reduce_invert(InvWork& iw, ChunkQKG& cr, const f
       for (int i = j + 1; i < 16; ++i) x[i] = fmaf(-c[j - j0][i >> 2][i & 3], x[j], x[i]);
     __builtin_amdgcn_sched_barrier(0);
   }
-  if (grp == 2) {
-#pragma unroll
-    for (int i = 0; i < 16; ++i) iw.X[i][m] = x[i];
-  } else if (grp < 2) {
+  if (grp == 0) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       iw.Tf[base + i][base + m] = x[i];
       emit_t(base + i, base + m, x[i]);
     }
+  } else if (blk == 1 && grp == 1) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) iw.X[i][m] = x[i];
   }
-  wave_lds_sync();
-  // T21 = -W T11: in step kk lane l supplies W[l % 16][4 kk + l / 16] and
-  // T11[4 kk + l / 16][l % 16] and ends with T21[4 (l / 16) + i][l % 16]
-  const int kq = lane >> 4;
+}
+
+// Step 4b: T21 = -W T11 as four 16x16x4 FP32 matrix products (K = 16): in
+// step kk lane l supplies W[l % 16][4 kk + l / 16] and T11[4 kk + l / 16][l %
+// 16] and ends with T21[4 (l / 16) + i][l % 16], i < 4.  One wave.
+template <class EmitT>
+__device__ __forceinline__ void invert_offdiag(const InvWork& iw, int lane, EmitT&& emit_t) {
+  const int r = lane & 15, kq = lane >> 4;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int kk = 0; kk < 4; ++kk)
-    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(iw.X[m][4 * kk + kq], iw.Tf[4 * kk + kq][m], acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x4f32(iw.X[r][4 * kk + kq], iw.Tf[4 * kk + kq][r], acc, 0, 0, 0);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) emit_t(16 + 4 * kq + i, m, -acc[i]);
+  for (int i = 0; i < 4; ++i) emit_t(16 + 4 * kq + i, r, -acc[i]);
 }
 
 }  // namespace chunk

@@ -215,13 +215,13 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       }
       lds_barrier();   // B2: split-K partials of chunk s+1 complete
       if (prep) {
-        // the triangular system and its inverse on one wave, Mqk's tiles on the others
-        if (pwave == 0)
-          reduce_invert(inv_of(sm.pw), cr, sn.beta, lane, [&](int r, int c, float t) {
+        // the triangular system's diagonal blocks and W on two waves, Mqk's tiles on the others
+        if (pwave < 2)
+          reduce_invert(inv_of(sm.pw), cr, sn.beta, pwave, lane, [&](int r, int c, float t) {
             sn.T[r][kslot(c)] = static_cast<_Float16>(t);
           });
         else
-          reduce_mqk(cr, pwave - 1, lane, [&](int r, int c, float m) {
+          reduce_mqk(cr, pwave - 2, lane, [&](int r, int c, float m) {
             sn.Mqk[r][kslot(c)] = static_cast<_Float16>(m);
           });
       }
@@ -430,6 +430,10 @@ __global__ __launch_bounds__(kThreads) void prefill_chunk_kernel(PrefillArgs a, 
       }
     }
     lds_barrier();   // B3
+    if (s + 1 < nch && wave == 0)   // chunk s+1's T21 = -W T11, beside the producers' staging of chunk s+2
+      invert_offdiag(inv_of(sm.pw), lane, [&](int r, int c, float t) {
+        sm.slot[(s + 1) & 1].T[r][kslot(c)] = static_cast<_Float16>(t);
+      });
   }
 
   if (const StateRef s1 = prefill_final_state(a, n, h)) {
