@@ -64,6 +64,10 @@ constexpr int kRecOffWl = 30720;
 constexpr int kRecStageBytes = 32768;
 constexpr int kRecOffU0 = 32768;
 constexpr int kRecBytes = 49152;
+// Waves per preparation block: consecutive chunks of one head, so that all
+// but the first take the previous chunk's restored keys and decays from its
+// record instead of re-reading and re-deriving them.
+constexpr int kPrepWaves = 4;
 
 // Window states after the records: per (sequence, head, window) the end
 // state E (zero-state end for windows >= 1, true end for window 0), the map
@@ -132,27 +136,39 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
 //    the transposed b Kg then gives M^T = (b Kg)^T T^T whose accumulators are
 //    the -M A fragments.
 template <int MODE, bool FE>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void prefill_split_prep(PrefillArgs a, float exp2C,
+__global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu(2))) void prefill_split_prep(PrefillArgs a, float exp2C,
                                                           uint8_t* __restrict__ ws) {
-  // (b Kg)^T hi fragments [0, 8) and lo fragments [8, 16), parked until T is
-  // known; once they are back in registers the same bytes hold the FP32
-  // system and its inverse, so eight waves per compute unit still fit.
-  __shared__ __align__(16) f16x8 park[16][64];
-  __shared__ __align__(16) float bl[CH];
+  // Per wave: (b Kg)^T hi fragments [0, 8) and lo fragments [8, 16), parked
+  // until T is known; once they are back in registers the same bytes hold
+  // the FP32 system and its inverse, so eight waves per compute unit still fit.
+  __shared__ __align__(16) f16x8 park_all[kPrepWaves][16][64];
+  __shared__ __align__(16) float bl_all[kPrepWaves][CH];
+  const int wv = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
+  f16x8 (*const park)[64] = park_all[wv];
+  float* const bl = bl_all[wv];
   float (*const Al)[36] = reinterpret_cast<float (*)[36]>(&park[0][0]);  // Diag(b) stril(Akk); rows 0..15 cols 16..31 hold A21 T11
   float (*const Tl)[36] = Al + CH;                                        // (I + A)^{-1}, lower triangle
   const int H = a.num_heads, N = a.num_seqs, T = a.total_tokens;
-  // XCD-aware order: consecutive block indices go to the eight XCDs in turn,
-  // so block b takes work item (b % 8) * per + b / 8 (items ordered head-major,
-  // then chunk slot).  Each XCD then walks a contiguous run of chunks of one
-  // head, and chunk c's re-read of chunk c-1's keys and gates (loaded by the
-  // previous block on the same XCD moments earlier) can hit its L2.
+  // Work items are (head, chunk slot), head-major; a block's kPrepWaves waves
+  // take consecutive slots of one head (the slots of a head padded to a
+  // multiple of kPrepWaves), so the waves after the first find the previous
+  // chunk's record in their own block.  XCD-aware order: consecutive block
+  // indices go to the eight XCDs in turn, so block b takes group (b % 8) *
+  // per + b / 8, and each XCD walks a contiguous run of chunks of one head
+  // (the first wave's re-read of the previous block's chunk can hit its L2).
   const int64_t slots = (int64_t)N + T / CH + 1;
-  const int64_t per = (slots * H + 7) / 8;
-  const int64_t item = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-  if (item >= slots * H) return;
-  const int h = (int)(item / slots), slot = (int)(item % slots);
-  const int lane = threadIdx.x, l16 = lane & 15, g4 = lane >> 4;
+  const int64_t slots_pad = (slots + kPrepWaves - 1) / kPrepWaves * kPrepWaves;
+  const int64_t groups = slots_pad / kPrepWaves * H;
+  const int64_t per = (groups + 7) / 8;
+  const int64_t grp = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  const int64_t item = grp * kPrepWaves + wv;
+  // Every wave passes the block's one barrier exactly once, working or not.
+  if (grp >= groups || item % slots_pad >= slots) {
+    __syncthreads();
+    return;
+  }
+  const int h = (int)(item / slots_pad), slot = (int)(item % slots_pad);
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const float C = a.anchor_log2;
 
   // Which (sequence, chunk) owns this slot: the largest n with
@@ -166,7 +182,10 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   const int bos = clamp_offset(a.cu_seqlens[n], T);
   const int eos = max(bos, clamp_offset(a.cu_seqlens[n + 1], T));
   const int c = slot - (n + bos / CH);
-  if (c < 0 || CH * c >= eos - bos) return;  // slot not used by any chunk
+  if (c < 0 || CH * c >= eos - bos) {   // slot not used by any chunk
+    __syncthreads();
+    return;
+  }
   const int t0 = bos + CH * c;
   const int L = min(CH, eos - t0);
   uint8_t* rec = ws + ((int64_t)slot * H + h) * kRecBytes;
@@ -183,10 +202,14 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // The previous chunk of the same sequence (chunk 0, and the first chunk of
   // a window: an empty range, so its keys and gates read as zero, which
   // gives W = 0 and M' = M and lets a chain start there).
+  // A wave after the block's first takes the previous chunk's restored keys
+  // and decays from that chunk's record, written by the wave before it in
+  // this block (`hand`); otherwise it re-reads that chunk's keys and gates.
   const int wcn = window_chunks_of(a, (eos - bos + CH - 1) / CH);
   const bool has_prev = c > 0 && (wcn <= 0 || c % wcn != 0);
+  const bool hand = has_prev && wv > 0;
   const int64_t base_prev = has_prev ? base - (int64_t)CH * H * D : base;
-  const uint32_t prev_bytes = has_prev ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
+  const uint32_t prev_bytes = has_prev && !hand ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
   const __amdgpu_buffer_rsrc_t rgp = make_buffer(a.g + base_prev, prev_bytes);
   const uint32_t tok_bytes = (uint32_t)H * D * 2;
@@ -474,13 +497,20 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     }
   }
   // The parked (b Kg)^T fragments back into registers; the barrier orders
-  // these reads before the system overwrites their bytes.
+  // these reads before the system overwrites their bytes.  It is also the
+  // block's one barrier: every wave's record so far (its restored keys and
+  // decays) is written before it and read by the next wave after it.  A
+  // work-group fence does not wait for global stores, so the wave first
+  // waits for its own (s_waitcnt fields: vmcnt bits 3:0 and 15:14 = 0, expcnt
+  // bits 6:4 = 7 and lgkmcnt bits 11:8 = 15, i.e. not waited on); the reads
+  // after it are the first accesses of this kernel to those bytes.
   f16x8 Xh[8], Xl[8];
 #pragma unroll
   for (int mc = 0; mc < 8; ++mc) {
     Xh[mc] = park[mc][lane];
     Xl[mc] = park[8 + mc][lane];
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
   // A = Diag(b) stril(Akk) to LDS.
 #pragma unroll
@@ -490,20 +520,16 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     Al[16 + l16][s] = beta[1] * acc[4][i];
     Al[16 + l16][16 + s] = s < l16 ? beta[1] * acc[5][i] : 0.f;
   }
-  // Everything the rest reads from memory is requested now, so that the
-  // inverse hides the latency: the value rows, and the previous chunk's keys
-  // and gates.
-  u32x4 vw[4][2], kpw[4][2], gpw[4][2];
+  // The value rows are requested now, so that the inverse hides their
+  // latency.
+  u32x4 vw[4][2];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
+    for (int hf = 0; hf < 2; ++hf)
       vw[p][hf] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
           rv, (uint32_t)(l16 + 16 * hf) * tok_bytes + (uint32_t)(32 * p + 8 * g4) * 2, 0, 0));
-      kpw[p][hf] = load8(rkp, hf, p);
-      gpw[p][hf] = load8(rgp, hf, p);
-    }
-  __syncthreads();
+  wave_lds_sync();
 
   // T = (I + A)^{-1}: diagonal 16x16 blocks by forward substitution (lane m
   // of each half-wave owns column m), then T21 = -T22 (A21 T11).
@@ -519,7 +545,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
 #pragma unroll
     for (int i = 0; i < 16; ++i) Tl[b0 + i][b0 + m] = x[i];
   }
-  __syncthreads();
+  wave_lds_sync();
   {
     const int m = l16;
     float acc4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -532,7 +558,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
 #pragma unroll
     for (int i = 0; i < 4; ++i) Al[4 * g4 + i][16 + m] = acc4[i];
   }
-  __syncthreads();
+  wave_lds_sync();
   {
     const int m = l16;
     float acc4[4] = {0.f, 0.f, 0.f, 0.f};
@@ -545,7 +571,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
 #pragma unroll
     for (int i = 0; i < 4; ++i) Tl[16 + 4 * g4 + i][m] = -acc4[i];
   }
-  __syncthreads();
+  wave_lds_sync();
 
   // T and T Diag(b) as fp16 hi / lo A fragments (row t = 16mt + l16, K-slot
   // 8g4 + j <-> token 4g4 + j or 16 + 4g4 + j - 4); T12 = 0.
@@ -570,6 +596,29 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
     }
   }
 
+
+  // The previous chunk's keys and gates -- or, handed over, that chunk's
+  // Kr^T fragments and decays from its record -- for M' and W (requested
+  // before U0's products, which cover part of their latency).
+  u32x4 kpw[4][2], gpw[4][2];
+  if (hand) {
+    const uint8_t* prec = rec - (int64_t)H * kRecBytes;   // slot - 1, same head
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        kpw[p][hf] = *reinterpret_cast<const u32x4*>(prec + kRecOffKrT + ((2 * p + hf) * 64 + lane) * 16);
+        gpw[p][hf] = *reinterpret_cast<const u32x4*>(prec + kRecOffDec + (32 * p + 16 * hf + 4 * g4) * 4);
+      }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        kpw[p][hf] = load8(rkp, hf, p);
+        gpw[p][hf] = load8(rgp, hf, p);
+      }
+  }
 
   // U0 = T Diag(b) V per 16-column tile: V transposed by the one-hot product.
 #pragma unroll
@@ -601,7 +650,7 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   // tokens s, column = token t) are the W A fragments.
   f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
   float nkp[2] = {1.f, 1.f};               // front-end norm of the previous chunk's keys
-  if (FE && a.fe.normalize_qk) {
+  if (FE && a.fe.normalize_qk && !hand) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float s2 = 0.f;
@@ -621,16 +670,39 @@ __global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(2))) void pr
   for (int p = 0; p < 4; ++p) {
     float dp[8];
     f16x8 krp[2];
+    if (hand) {
+      // Kr^T fragments (channel rows 32p.., 32p+16..) back to rows of tokens
+      // by the one-hot products (exact), decays as stored
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      // no previous chunk (an empty range): zero gates, so d_p = 1 and M' = M
-      const float s0 = row_scan16(gate(bf16_elem(gpw[p][0], j), has_prev));
-      const float b0 = __shfl(s0, 15, 16);
-      const float s1 = row_scan16(gate(bf16_elem(gpw[p][1], j), has_prev)) + b0;
-      const float gl = __shfl(s1, 15, 16) * kLog2e;
-      dp[j] = fast_exp2(gl);
-      krp[0][j] = static_cast<_Float16>(nkp[0] * bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
-      krp[1][j] = static_cast<_Float16>(nkp[1] * bf16_elem(kpw[p][1], j) * fast_exp2(gl - s1 * kLog2e));
+      for (int sh = 0; sh < 2; ++sh) {
+        const f32x4 r0 = mfma_f16(__builtin_bit_cast(f16x8, kpw[p][0]), E[sh], z);
+        const f32x4 r1 = mfma_f16(__builtin_bit_cast(f16x8, kpw[p][1]), E[sh], z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          krp[sh][i] = (_Float16)r0[i];
+          krp[sh][4 + i] = (_Float16)r1[i];
+        }
+      }
+      // (whole-vector casts: a cast of a single vector element has been
+      // compiled to the wrong element)
+      const f32x4 d0 = __builtin_bit_cast(f32x4, gpw[p][0]), d1 = __builtin_bit_cast(f32x4, gpw[p][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dp[i] = d0[i];
+        dp[4 + i] = d1[i];
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        // no previous chunk (an empty range): zero gates, so d_p = 1 and M' = M
+        const float s0 = row_scan16(gate(bf16_elem(gpw[p][0], j), has_prev));
+        const float b0 = __shfl(s0, 15, 16);
+        const float s1 = row_scan16(gate(bf16_elem(gpw[p][1], j), has_prev)) + b0;
+        const float gl = __shfl(s1, 15, 16) * kLog2e;
+        dp[j] = fast_exp2(gl);
+        krp[0][j] = static_cast<_Float16>(nkp[0] * bf16_elem(kpw[p][0], j) * fast_exp2(gl - s0 * kLog2e));
+        krp[1][j] = static_cast<_Float16>(nkp[1] * bf16_elem(kpw[p][1], j) * fast_exp2(gl - s1 * kLog2e));
+      }
     }
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
@@ -1375,9 +1447,10 @@ template <int MODE, bool FE>
 hipError_t launch_prep(const PrefillArgs& a, uint8_t* ws, hipStream_t s) {
   const float exp2C = MODE == 0 ? std::exp2(a.anchor_log2) : 0.f;
   const int64_t slots = (int64_t)a.num_seqs + a.total_tokens / CH + 1;
-  const int64_t blocks = 8 * ((slots * a.num_heads + 7) / 8);
+  const int64_t groups = (slots + kPrepWaves - 1) / kPrepWaves * a.num_heads;
+  const int64_t blocks = 8 * ((groups + 7) / 8);
   if (blocks > INT_MAX) return hipErrorInvalidValue;
-  prefill_split_prep<MODE, FE><<<(unsigned)blocks, 64, 0, s>>>(a, exp2C, ws);
+  prefill_split_prep<MODE, FE><<<(unsigned)blocks, 64 * kPrepWaves, 0, s>>>(a, exp2C, ws);
   return hipGetLastError();
 }
 
