@@ -162,13 +162,85 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   const int64_t per = (groups + 7) / 8;
   const int64_t grp = (int64_t)(blockIdx.x & 7) * per + (blockIdx.x >> 3);
   const int64_t item = grp * kPrepWaves + wv;
+  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   // Every wave passes the block's one barrier exactly once, working or not.
-  if (grp >= groups || item % slots_pad >= slots) {
+  if (grp >= groups) {
+    __syncthreads();
+    return;
+  }
+  // The block's first chunk takes its predecessor's restored keys and decays
+  // from the four waves together: wave w derives K step w (32 channels) of
+  // them from that chunk's keys and gates into LDS before the barrier (not
+  // with the front-end's key norm, which needs all channels: the first wave
+  // then re-derives them alone).
+  static_assert(kPrepWaves == 4, "one K step of the shared predecessor per wave");
+  __shared__ __align__(16) f16x8 prev_kr[kPrepWaves][2][64];   // [K step][token half][lane]
+  __shared__ __align__(16) float prev_dec[D];
+  bool share = false;
+  {
+    const int64_t item0 = grp * kPrepWaves;
+    const int slot0 = (int)(item0 % slots_pad), h0 = (int)(item0 / slots_pad);
+    if (slot0 < slots) {
+      int lo = 0, hi = N - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (mid + clamp_offset(a.cu_seqlens[mid], T) / CH <= slot0) lo = mid; else hi = mid - 1;
+      }
+      const int bos0 = clamp_offset(a.cu_seqlens[lo], T);
+      const int len0 = max(bos0, clamp_offset(a.cu_seqlens[lo + 1], T)) - bos0;
+      const int c0 = slot0 - (lo + bos0 / CH);
+      const int wcn0 = window_chunks_of(a, (len0 + CH - 1) / CH);
+      share = c0 > 0 && CH * c0 < len0 && (wcn0 <= 0 || c0 % wcn0 != 0) &&
+              !(FE && a.fe.normalize_qk);
+      if (share) {
+        const __amdgpu_buffer_rsrc_t rk0 = make_buffer(
+            a.k + ((int64_t)(bos0 + CH * (c0 - 1)) * H + h0) * D, (uint32_t)(((CH - 1) * H + 1) * D * 2));
+        const __amdgpu_buffer_rsrc_t rg0 = make_buffer(
+            a.g + ((int64_t)(bos0 + CH * (c0 - 1)) * H + h0) * D, (uint32_t)(((CH - 1) * H + 1) * D * 2));
+        const uint32_t tb = (uint32_t)H * D * 2;
+        u32x4 kq[2], gq[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const uint32_t off = (uint32_t)(l16 + 16 * hf) * tb + (uint32_t)(32 * wv + 4 * g4) * 2;
+          const u32x2 k0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk0, off, 0, 0));
+          const u32x2 k1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rk0, off + 32, 0, 0));
+          const u32x2 q0 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg0, off, 0, 0));
+          const u32x2 q1 = __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(rg0, off + 32, 0, 0));
+          kq[hf] = u32x4{k0[0], k0[1], k1[0], k1[1]};
+          gq[hf] = u32x4{q0[0], q0[1], q1[0], q1[1]};
+        }
+        f16x8 kr0, kr1;
+        f32x4 d0, d1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          float x0 = bf16_elem(gq[0], j), x1 = bf16_elem(gq[1], j);
+          if (FE) {
+            x0 = frontend_gate(a.fe, x0);
+            x1 = frontend_gate(a.fe, x1);
+          }
+          const float s0 = row_scan16(x0);
+          const float b0 = __shfl(s0, 15, 16);
+          const float s1 = row_scan16(x1) + b0;
+          const float gl = __shfl(s1, 15, 16) * kLog2e;
+          const float dv = fast_exp2(gl);
+          if (j < 4) d0[j] = dv; else d1[j - 4] = dv;
+          kr0[j] = static_cast<_Float16>(bf16_elem(kq[0], j) * fast_exp2(gl - s0 * kLog2e));
+          kr1[j] = static_cast<_Float16>(bf16_elem(kq[1], j) * fast_exp2(gl - s1 * kLog2e));
+        }
+        prev_kr[wv][0][lane] = kr0;
+        prev_kr[wv][1][lane] = kr1;
+        if (l16 == 0) {
+          *reinterpret_cast<f32x4*>(&prev_dec[32 * wv + 4 * g4]) = d0;
+          *reinterpret_cast<f32x4*>(&prev_dec[32 * wv + 16 + 4 * g4]) = d1;
+        }
+      }
+    }
+  }
+  if (item % slots_pad >= slots) {
     __syncthreads();
     return;
   }
   const int h = (int)(item / slots_pad), slot = (int)(item % slots_pad);
-  const int lane = threadIdx.x & 63, l16 = lane & 15, g4 = lane >> 4;
   const float C = a.anchor_log2;
 
   // Which (sequence, chunk) owns this slot: the largest n with
@@ -208,8 +280,10 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   const int wcn = window_chunks_of(a, (eos - bos + CH - 1) / CH);
   const bool has_prev = c > 0 && (wcn <= 0 || c % wcn != 0);
   const bool hand = has_prev && wv > 0;
+  const bool shared_prev = share && wv == 0;   // then has_prev too
   const int64_t base_prev = has_prev ? base - (int64_t)CH * H * D : base;
-  const uint32_t prev_bytes = has_prev && !hand ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
+  const uint32_t prev_bytes =
+      has_prev && !hand && !shared_prev ? (uint32_t)(((CH - 1) * H + 1) * D * 2) : 0u;
   const __amdgpu_buffer_rsrc_t rkp = make_buffer(a.k + base_prev, prev_bytes);
   const __amdgpu_buffer_rsrc_t rgp = make_buffer(a.g + base_prev, prev_bytes);
   const uint32_t tok_bytes = (uint32_t)H * D * 2;
@@ -610,7 +684,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
         kpw[p][hf] = *reinterpret_cast<const u32x4*>(prec + kRecOffKrT + ((2 * p + hf) * 64 + lane) * 16);
         gpw[p][hf] = *reinterpret_cast<const u32x4*>(prec + kRecOffDec + (32 * p + 16 * hf + 4 * g4) * 4);
       }
-  } else {
+  } else if (!shared_prev) {
 #pragma unroll
     for (int p = 0; p < 4; ++p)
 #pragma unroll
@@ -650,7 +724,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   // tokens s, column = token t) are the W A fragments.
   f32x4 wacc[2][2] = {{z, z}, {z, z}};   // [s half][t half]
   float nkp[2] = {1.f, 1.f};               // front-end norm of the previous chunk's keys
-  if (FE && a.fe.normalize_qk && !hand) {
+  if (FE && a.fe.normalize_qk && !hand && !shared_prev) {
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       float s2 = 0.f;
@@ -686,6 +760,16 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
       // (whole-vector casts: a cast of a single vector element has been
       // compiled to the wrong element)
       const f32x4 d0 = __builtin_bit_cast(f32x4, gpw[p][0]), d1 = __builtin_bit_cast(f32x4, gpw[p][1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        dp[i] = d0[i];
+        dp[4 + i] = d1[i];
+      }
+    } else if (shared_prev) {
+      krp[0] = prev_kr[p][0][lane];
+      krp[1] = prev_kr[p][1][lane];
+      const f32x4 d0 = *reinterpret_cast<const f32x4*>(&prev_dec[32 * p + 4 * g4]);
+      const f32x4 d1 = *reinterpret_cast<const f32x4*>(&prev_dec[32 * p + 16 + 4 * g4]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         dp[i] = d0[i];
