@@ -38,15 +38,16 @@
 //     the triangular system and its inverse -- into ring slot (c+1) % 2 (wave
 //     w owns key channels 32(w-4).. of the pairwise products, a split-K whose
 //     partials are summed in a fixed order, so results are deterministic;
-//     then one wave sums the system's blocks and inverts it while the others
-//     sum Mqk's), and fetch the rows of chunk c+2 into registers, writing
-//     them to LDS at the step's end;
+//     then two waves sum the system's blocks and form T11, T22 and W = T22
+//     A21 while the others sum Mqk's), and fetch the rows of chunk c+2 into
+//     registers, writing them to LDS at the step's end;
 //   * waves 0-3 (consumers) meanwhile run the serial state chain of chunk c
 //     from slot c % 2 on their own 16 * NT value columns (value columns
 //     evolve independently, so the chain needs no cross-wave exchange); the
 //     FP32 state stays in their MFMA accumulators for the whole sequence.
-//     In the phase where the chain has nothing to do they take half of
-//     chunk c+1's gate prefix.
+//     In the phases where the chain has nothing to do they take half of
+//     chunk c+1's gate prefix and (one wave) the inverse's off-diagonal block
+//     T21 = -W T11 (four FP32 matrix products).
 // Both sides meet at the same four block barriers per chunk (barriers that
 // order LDS only, so prefetches and output stores stay in flight across
 // them), and the chain's products with the state (matrix-core work) sit in

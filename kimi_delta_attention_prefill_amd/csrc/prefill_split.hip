@@ -9,7 +9,7 @@
 // kernels instead of across warps:
 //
 //   pass 1 (prefill_split_prep): one wave per (chunk, head), all chunks of
-//     all sequences at once.  Steps 1-3 of section 2 (gate prefix, anchored
+//     all sequences at once (four consecutive chunks of a head per block).  Steps 1-3 of section 2 (gate prefix, anchored
 //     Mqk/Akk, the 32x32 inverse T) and then everything that depends only on
 //     the chunk:
 //        U0 = T Diag(b) V          (what U would be from a zero state)
@@ -121,8 +121,9 @@ __device__ __forceinline__ float bf16_elem(const u32x4& w, int j) {
   return (j & 1) ? bf16hi(w[j >> 1]) : bf16lo(w[j >> 1]);
 }
 
-// Preparation pass: one wave per (chunk slot, head), no block barrier beyond
-// the wave's own, LDS only for the 32x32 triangular inverse.
+// Preparation pass: one wave per (chunk slot, head), four consecutive slots
+// of one head per block with one block barrier (the hand-over of each chunk's
+// predecessor, below); LDS for the 32x32 triangular inverse and that hand-over.
 //
 // Lane (g4 = lane/16, l16 = lane%16) owns tokens l16 and l16+16 of the chunk
 // and, for each 32-channel K step p, the channels whose fragment K-slots are
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
   // chunk's record in their own block.  XCD-aware order: consecutive block
   // indices go to the eight XCDs in turn, so block b takes group (b % 8) *
   // per + b / 8, and each XCD walks a contiguous run of chunks of one head
-  // (the first wave's re-read of the previous block's chunk can hit its L2).
+  // (the re-read of the previous block's last chunk can hit its L2).
   const int64_t slots = (int64_t)N + T / CH + 1;
   const int64_t slots_pad = (slots + kPrepWaves - 1) / kPrepWaves * kPrepWaves;
   const int64_t groups = slots_pad / kPrepWaves * H;
