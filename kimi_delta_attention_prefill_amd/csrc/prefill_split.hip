@@ -847,7 +847,8 @@ __global__ __launch_bounds__(64 * kPrepWaves) __attribute__((amdgpu_waves_per_eu
 //   O_c = scale (Qg_c S_c + Mqk_c U_c)
 // so in step c every wave only consumes what others produced in step c-1:
 //   waves 0-1 (state halves, key rows 0-63 / 64-127): S_c from U_{c-1}; fp16
-//            S_c for the output; their K-half of P_{c+1} (wave 0 adds U0);
+//            S_c for the output; their K-half of P_{c+1} (each adding half of
+//            U0's rows);
 //            the state stays in VGPRs for the whole sequence;
 //   wave 2 (U):   U_c = (P_c halves summed) - W_c U_{c-1}, split into fp16
 //            hi + lo for the state waves and the output;
@@ -877,9 +878,9 @@ constexpr int kChainTiles = 8 / kNT;                       // blocks per (sequen
 
 // Record fragments, as each wave consumes them.  Everything but U0 is the
 // same for all value columns, so a block with kNT subtiles loads it once.
-struct AOps {            // state half: -M' (its K half) and U0, of chunk c+1
+struct AOps {            // state half: -M' (its K half) and U0 (its row tile), of chunk c+1
   f16x8 am[2][2];
-  f32x4 u0[kNT][2];
+  f32x4 u0[kNT][2];        // only [t][hs] is used
 };
 struct BOps {            // state half: Kr^T rows of chunk c-1
   f16x8 ak[4];
@@ -1134,7 +1135,8 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
   // --------------------------------------------------------- state halves
   // Wave hs owns key rows 64hs..64hs+63: accumulator tiles mt = 4hs..4hs+3,
   // i.e. the fp16 B fragments (K steps) p = 2hs, 2hs+1.  The two halves are
-  // separate code (hs a constant): only half 0 adds U0, so only it loads U0.
+  // separate code (hs a constant): half hs adds U0's row tile mt = hs (tokens
+  // 16 hs..16 hs + 15) to its share of P, so each loads one U0 fragment.
   auto state_half = [&](auto hs_const) __attribute__((always_inline)) {
   constexpr int hs = decltype(hs_const)::value;
   f32x4 S[kNT][4];
@@ -1158,7 +1160,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
     for (int mt = 0; mt < 2; ++mt) {
 #pragma unroll
       for (int q = 0; q < 2; ++q) o.am[mt][q] = gfrag(r, kRecOffMneg, mt * 4 + 2 * hs + q);
-      if (hs == 0) {
+      if (mt == hs) {
 #pragma unroll
         for (int t = 0; t < kNT; ++t) o.u0[t][mt] = gacc(r, kRecOffU0 + (sub0 + t) * 2048, mt);
       }
@@ -1189,10 +1191,7 @@ __device__ __forceinline__ void chain_body(const PrefillArgs& a, const uint8_t* 
       f32x4 P[2];
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) P[mt] = z;
-      if (hs == 0 && job.with_u0) {
-#pragma unroll
-        for (int mt = 0; mt < 2; ++mt) P[mt] = o.u0[t][mt];
-      }
+      if (job.with_u0) P[hs] = o.u0[t][hs];
 #pragma unroll
       for (int q = 0; q < 2; ++q)
 #pragma unroll
