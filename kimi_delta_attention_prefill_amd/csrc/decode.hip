@@ -9,10 +9,11 @@
 //
 // The step moves 128 KiB (FP32) or 64 KiB (BF16) of state per item and does
 // ~7 flops per state element, so it is an HBM stream.  Each block owns one
-// item's value-column slice of COLS columns: thread t holds one 16-byte
-// vector per state row (four FP32 or eight BF16 columns) of the key rows
-// c = rg + RG * i, so every wave reads and writes whole 128-byte row pieces
-// (narrower pieces cost partial-line writes).  The two dk-reductions (w, p)
+// item's value-column slice of COLS columns: thread t holds one vector per
+// state row (16 bytes: four FP32 or eight BF16 columns; 8 bytes, four BF16
+// columns, in the BF16 64-column slices of calls with few items) of the key
+// rows c = rg + RG * i, so every wave reads and writes whole 128-byte row
+// pieces (narrower pieces cost partial-line writes).  The two dk-reductions (w, p)
 // and q . k are finished in registers inside a wave (a DPP butterfly, then
 // lane-swap reduce-scatter steps) and by one LDS fold across the waves; the
 // state is read once and written once.  Row counts too small to fill the
@@ -36,11 +37,13 @@ namespace {
 
 // The state of a row is read once and written once per step, so its traffic
 // is marked non-temporal (streamed past the caches).  Every thread moves one
-// 16-byte vector per state row: four FP32 or eight BF16 columns (narrower
-// BF16 vectors leave 64-byte row pieces, half a cache line, which cost a
-// partial-line write on every store).
+// vector per state row: 16 bytes, four FP32 or eight BF16 columns, or 8 bytes
+// of BF16 where a slice is 64 columns wide (a 32-column BF16 slice would leave
+// 64-byte row pieces, half a cache line, which cost a partial-line write on
+// every store).
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4v __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2v __attribute__((ext_vector_type(2)));
 
 // The item's state is read through one buffer resource (its base is uniform
 // over the block), so each thread keeps a single 32-bit offset and the
@@ -100,6 +103,40 @@ struct StateIO<true> {
     __builtin_nontemporal_store(w, (__attribute__((address_space(1))) u32x4v*)p);
   }
 };
+
+// BF16 state in 8-byte vectors (4 columns per thread).  In 64-column slices
+// of 512 threads a row then spans 16 threads (whole 128-byte lines still), so
+// each thread reduces 9 partial sums over 4 row groups of its wave instead of
+// 17 over 8: the shape for calls with few items, where the reductions'
+// latency rather than the bytes bounds the call.
+struct StateIOBf16Narrow {
+  using elem = uint16_t;
+  using raw = u32x2v;
+  static constexpr int CPT = 4;
+  static __device__ __forceinline__ raw load(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(raw, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT));
+  }
+  static __device__ __forceinline__ void unpack(const raw& w, float* x) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      x[2 * m] = bf16lo(w[m]);
+      x[2 * m + 1] = bf16hi(w[m]);
+    }
+  }
+  static __device__ __forceinline__ void store(__attribute__((address_space(1))) uint16_t* p,
+                                               const float* x) {
+    u32x2v w;
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+      w[m] = (uint32_t)f32_to_bf16(x[2 * m]) | ((uint32_t)f32_to_bf16(x[2 * m + 1]) << 16);
+    __builtin_nontemporal_store(w, (__attribute__((address_space(1))) u32x2v*)p);
+  }
+};
+
+template <int COLS, bool BF16, int NT>
+struct DecodeIO { using type = StateIO<BF16>; };
+template <>
+struct DecodeIO<64, true, 512> { using type = StateIOBf16Narrow; };
 
 // CPT consecutive bf16 values (8 or 16 bytes) as floats.
 template <int CPT>
@@ -206,7 +243,7 @@ __device__ __forceinline__ void wave_reduce_store(float* v, float* dst, int lane
 // contiguous run of rows.
 template <int COLS, bool BF16, int NT>
 struct DecodeBlock {
-  using IO = StateIO<BF16>;
+  using IO = typename DecodeIO<COLS, BF16, NT>::type;
   using elem = typename IO::elem;
   static constexpr int CPT = IO::CPT;
   static constexpr int TPR = COLS / CPT;
